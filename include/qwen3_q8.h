@@ -1,0 +1,219 @@
+/*
+ * qwen3_q8.h -- C ABI of the MI355X (gfx950) forward pass of a Qwen3 dense
+ * decoder over GGUF-style Q8_0 weights (or bf16 weights).
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *   - the forward pass: embedding rows, per layer RMSNorm -> Q/K/V
+ *     projections -> per-head Q/K RMSNorm -> NeoX RoPE -> KV append ->
+ *     causal grouped-query attention -> o_proj + residual -> RMSNorm ->
+ *     SwiGLU FFN + residual; final RMSNorm -> tied lm_head -> greedy argmax
+ *     (Fucina course, "A transformer from scratch", sections 12.3-12.6;
+ *     minfer, "Qwen3 Support Plan", sections 1-2);
+ *   - every Q8_0 linear quantises its f32 input row per 32-block to Q8_0 and
+ *     sums integer block dots rescaled by d_w * d_a (Fucina course, "Model
+ *     files and quantization", sections 11.7 and 11.9).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* are device pointers (HIP), h_* are host pointers.
+ *     The library never allocates device memory: everything it needs is
+ *     carved from the caller's workspace (qwen3_workspace_bytes).
+ *   - `stream` is a hipStream_t passed as void*.  Work is enqueued on it and
+ *     the call returns without waiting (except where stated).  Results in
+ *     device buffers are valid once the stream reaches that point.
+ *   - Return value: QWEN3_OK (0) or a negative QWEN3_E_* code; on error
+ *     qwen3_last_error() describes it (thread-local string) and the model
+ *     state (KV lengths, cache contents) is unchanged.  Every argument and
+ *     shape error is detected on the host before any launch.
+ *   - A handle is single-stream mutable state; it is not thread-safe.
+ */
+#ifndef QWEN3_Q8_H
+#define QWEN3_Q8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- error codes -------------------------------------------------------- */
+#define QWEN3_OK 0
+#define QWEN3_E_INVALID_ARGUMENT (-1)        /* null pointer, bad seq index, bad size */
+#define QWEN3_E_INVALID_CONFIG (-2)          /* zero/negative dims, heads not divisible, ... */
+#define QWEN3_E_INVALID_WEIGHT_SHAPE (-3)    /* size arithmetic overflows */
+#define QWEN3_E_UNSUPPORTED_WEIGHT_TYPE (-4) /* weight_type / kv_type not known */
+#define QWEN3_E_WORKSPACE_TOO_SMALL (-5)
+#define QWEN3_E_INVALID_SEQUENCE_LENGTH (-6) /* n <= 0 tokens */
+#define QWEN3_E_KV_CACHE_OVERFLOW (-7)       /* len + n > the sequence's capacity */
+#define QWEN3_E_TOKEN_OUT_OF_RANGE (-8)      /* a host token id outside [0, vocab) */
+#define QWEN3_E_DEVICE (-9)                  /* a HIP call failed */
+
+/* ---- element types -------------------------------------------------------- */
+#define QWEN3_W_Q8_0 0 /* projections and embedding in Q8_0 blocks */
+#define QWEN3_W_BF16 1 /* projections and embedding in bf16 */
+#define QWEN3_KV_F32 0
+#define QWEN3_KV_BF16 1
+
+/* Q8_0 block on the wire (Fucina course, "Model files and quantization",
+ * section 11.7): the f16 bits of the scale d, then 32 signed bytes; 34 bytes,
+ * no padding.  A row of K values is K/32 consecutive blocks. */
+#define QWEN3_Q8_0_BLOCK_VALUES 32
+#define QWEN3_Q8_0_BLOCK_BYTES 34
+
+/* Model geometry and cache plan ("A transformer from scratch", section 12.1:
+ * the config is nine numbers; head_dim is independent of hidden / heads,
+ * minfer plan section 2.1).  Validation (QWEN3_E_INVALID_CONFIG): every
+ * integer > 0; heads % kv_heads == 0; head_dim even and <= 256;
+ * hidden_size, heads * head_dim and intermediate_size multiples of 128;
+ * head_dim * heads/kv_heads <= 512; eps > 0; rope_theta > 1; max_seqs >= 1;
+ * every seq_capacity[i] >= 1. */
+typedef struct qwen3_config {
+  int32_t vocab_size;
+  int32_t hidden_size;
+  int32_t intermediate_size;
+  int32_t num_layers;
+  int32_t num_attention_heads;
+  int32_t num_key_value_heads;
+  int32_t head_dim;
+  float rms_norm_eps;
+  float rope_theta;
+  int32_t weight_type; /* QWEN3_W_* */
+  int32_t kv_type;     /* QWEN3_KV_* */
+  int32_t max_seqs;    /* independent KV caches held by the handle */
+  const int32_t* h_seq_capacity; /* host [max_seqs]: KV rows of each sequence */
+  int32_t max_batch_tokens; /* rows one pass may process; longer prompts are
+                               prefilled in chunks of this many tokens.
+                               Also the largest batch of qwen3_decode_batch.
+                               0 selects 1024. */
+} qwen3_config;
+
+/* Device pointers to one layer's tensors, GGUF names (minfer plan section 1).
+ * Projections are logical [out, in], row-major, `in` contiguous ("block row
+ * r is output r", "Model files and quantization", section 11.9): Q8_0 rows
+ * are in/32 blocks of 34 bytes; bf16 rows are `in` bf16 values.  Norm
+ * weights are f32.  There are no biases (minfer plan section 5, item 7).
+ *   attn_q [heads*hd, hidden]   attn_k, attn_v [kv_heads*hd, hidden]
+ *   attn_output [hidden, heads*hd]   attn_q_norm, attn_k_norm [hd]
+ *   ffn_gate, ffn_up [ffn, hidden]   ffn_down [hidden, ffn]
+ *   attn_norm, ffn_norm [hidden] */
+typedef struct qwen3_layer_weights {
+  const void* attn_norm;
+  const void* attn_q;
+  const void* attn_k;
+  const void* attn_v;
+  const void* attn_output;
+  const void* attn_q_norm;
+  const void* attn_k_norm;
+  const void* ffn_norm;
+  const void* ffn_gate;
+  const void* ffn_up;
+  const void* ffn_down;
+} qwen3_layer_weights;
+
+/* token_embd [vocab, hidden] doubles as the lm_head (tied weights, "A
+ * transformer from scratch", section 12.3.1).  `layers` is a HOST array of
+ * num_layers entries holding DEVICE pointers. */
+typedef struct qwen3_weights {
+  const void* token_embd;
+  const void* output_norm;
+  const qwen3_layer_weights* layers;
+} qwen3_weights;
+
+typedef struct qwen3_model qwen3_t;
+
+/* Bytes of device workspace a handle needs for `cfg` (weights repacked into
+ * the library's layout, KV caches, RoPE table and activations).  Returns 0
+ * if cfg is invalid (qwen3_last_error says why).  Host-only. */
+size_t qwen3_workspace_bytes(const qwen3_config* cfg);
+
+/* Build a handle.  Copies and repacks the weights (device pointers in the
+ * layout above) into `d_workspace`, builds the RoPE table, and sets every
+ * sequence's KV length to 0.  The weight buffers are only read during this
+ * call (enqueued on `stream`; the call synchronises the stream before
+ * returning, so the caller may free them afterwards).  The workspace is owned
+ * by the caller, must be at least qwen3_workspace_bytes(cfg) bytes, 256-byte
+ * aligned, and must outlive the handle; the library never frees it. */
+int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_workspace,
+                 size_t workspace_bytes, void* stream, qwen3_t** out);
+
+/* Destroy a handle (host state and captured graphs; no device frees). */
+void qwen3_destroy(qwen3_t* h);
+
+/* Prefill: append `n` tokens (host ids, validated) to sequence `seq` at its
+ * current length L and run the forward pass over them ("A transformer from
+ * scratch", section 12.5: the same forward serves prefill and decode).
+ * Writes the logits of the LAST token to d_logits [vocab] (f32) and its
+ * greedy argmax (lowest index among maxima) to d_argmax [1] (int32); either
+ * may be NULL.  Afterwards the length is L + n.  Errors:
+ * QWEN3_E_INVALID_SEQUENCE_LENGTH (n <= 0), QWEN3_E_KV_CACHE_OVERFLOW
+ * (L + n > capacity), QWEN3_E_TOKEN_OUT_OF_RANGE. */
+int qwen3_prefill(qwen3_t* h, int32_t seq, const int32_t* h_tokens, int32_t n, float* d_logits,
+                  int32_t* d_argmax, void* stream);
+
+/* One decode step of sequence `seq`: the token id is read on the device from
+ * d_token [1] (so the previous step's d_argmax can be passed straight back
+ * and the step needs no host round trip).  Writes d_logits [vocab] (may be
+ * NULL) and d_argmax [1] (required).  Length L -> L + 1; L + 1 > capacity is
+ * QWEN3_E_KV_CACHE_OVERFLOW.  A device token outside [0, vocab) is clamped
+ * into range (the host cannot check it without a synchronisation).  The
+ * step is replayed from a captured HIP graph keyed by (seq, d_token,
+ * d_logits, d_argmax); it allocates nothing. */
+int qwen3_decode_step(qwen3_t* h, int32_t seq, const int32_t* d_token, float* d_logits,
+                      int32_t* d_argmax, void* stream);
+
+/* Batched decode: one token for each of the `n` distinct sequences h_seqs
+ * [n] (host) in one pass: weights are read once for all n rows, while RoPE
+ * positions, KV appends and attention are per sequence ("A transformer from
+ * scratch", section 12.5, batch decode).  d_tokens [n] (device),
+ * d_logits [n, vocab] (may be NULL), d_argmax [n].  n <= max_batch_tokens. */
+int qwen3_decode_batch(qwen3_t* h, const int32_t* h_seqs, int32_t n, const int32_t* d_tokens,
+                       float* d_logits, int32_t* d_argmax, void* stream);
+
+/* Set sequence `seq`'s KV length to 0 (buffers retained; "The LLM stack",
+ * section 13.4, reset).  Enqueued on `stream`. */
+int qwen3_reset(qwen3_t* h, int32_t seq, void* stream);
+
+/* Host-side KV length of `seq` (counts every enqueued append). */
+int qwen3_kv_len(const qwen3_t* h, int32_t seq, int32_t* out);
+
+/* Thread-local description of the last error ("" if none). */
+const char* qwen3_last_error(void);
+
+/* ---- op-level entry points (kernel-boundary parity and input prep) ------- */
+
+/* Q8_0 encoder ("Model files and quantization", section 11.7) of n f32
+ * values (n a multiple of 32) into n/32 wire blocks (34 bytes each) at
+ * d_blocks: amax; d = amax/127 (f32); inv = d == 0 ? 0 : 1/d (f32);
+ * q = clamp(round-half-even(v*inv), -127, 127); stored scale f16(d) (RNE).
+ * Non-finite input gives unspecified codes. */
+int qwen3_q8_0_encode(const float* d_x, int64_t n, void* d_blocks, void* stream);
+
+/* f32 -> bf16 (round half to even) of n values: input prep for bf16 models. */
+int qwen3_bf16_encode(const float* d_x, int64_t n, uint16_t* d_out, void* stream);
+
+/* Repack a Q8_0 matrix [rows, k] from wire blocks into the library's planes:
+ * d_qs int8 [rows, k] and d_scale f16 [rows, k/32] (rows*k bytes and
+ * rows*k/16 bytes).  k a multiple of 32. */
+int qwen3_q8_0_repack(const void* d_blocks, int64_t rows, int64_t k, int8_t* d_qs,
+                      uint16_t* d_scale, void* stream);
+
+/* The Q8_0 linear on repacked planes: y[t, :] = linear(x[t, :]) for t < m,
+ * x f32 [m, k], y f32 [m, n].  m == 1 runs the decode GEMV kernel, m > 1 the
+ * prefill GEMM kernel (the same kernels the model uses).  k % 128 == 0;
+ * for m > 1 also n % 128 == 0.  d_work: scratch of qwen3_linear_work_bytes
+ * (m, k) bytes. */
+size_t qwen3_linear_work_bytes(int64_t m, int64_t k);
+int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs,
+                      const uint16_t* d_scale, int64_t n, float* d_y, void* d_work, void* stream);
+
+/* Test hook for the integer path: quantise x [m, k] the way the linears do
+ * (d_qa int8 [m, k], d_da f16 bits [m, k/32]) and write every integer block
+ * dot S[t, j, b] = sum_i qa[t, 32b+i] * qw[j, 32b+i] to d_s int32 [m, n, k/32],
+ * using the same device code as the decode GEMV. */
+int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs, int64_t n,
+                          int8_t* d_qa, uint16_t* d_da, int32_t* d_s, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QWEN3_Q8_H */

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) forward pass of a Qwen3 dense decoder over Q8_0 weights.
+
+The compute lives in the HIP library libqwen3q8.so behind the C ABI of
+include/qwen3_q8.h; this package is its ctypes binding.
+"""
+
+from ._lib import Qwen3Error, lib  # noqa: F401
+from .model import (  # noqa: F401
+    Qwen3Config,
+    Qwen3Model,
+    encode_bf16,
+    encode_q8_0,
+    q8_0_block_dots,
+    q8_0_linear,
+    repack_q8_0,
+    workspace_bytes,
+)

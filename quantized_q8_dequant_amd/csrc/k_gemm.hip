@@ -1,0 +1,183 @@
+// Prefill Q8_0 GEMM for gfx950 on int8 MFMA (v_mfma_i32_32x32x32_i8).
+//
+// C[m, n] = sum_b d_a[m, b] * d_w[n, b] * S_b[m, n] where S_b is the exact
+// integer dot of 32-block b (Fucina course, "Model files and quantization",
+// section 11.9).  One 32x32x32 MFMA covers exactly one Q8_0 block, so its
+// int32 result IS S_b for a 32x32 tile; it is converted and rescaled by the
+// product of the two f16 scales (exact in f32) into an f32 accumulator.
+//
+// Tiling: a 256-thread workgroup owns a 128 (tokens) x 128 (outputs) tile;
+// its 4 wavefronts each own 64 x 64 = 2 x 2 MFMA tiles.  K advances in
+// stages of 4 blocks (128 bytes); A/B stages are double-buffered in LDS
+// (rows padded by 16 bytes against bank conflicts), the next stage's global
+// loads are issued before the current stage's MFMAs.
+//
+// Epilogues: store, residual add into C, and SwiGLU of the paired gate/up
+// columns (the weight stack interleaves 32 gate rows and 32 up rows, so a
+// wavefront's 64 columns are one gate tile and its up tile).
+#include "kernels.h"
+#include "qdevice.h"
+
+using namespace q8;
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128;
+constexpr int KB = 4;            // 32-blocks per stage
+constexpr int SK = KB * 32;      // bytes of K per stage
+constexpr int LDS_ROW = SK + 16; // padded row stride (bytes)
+
+struct Stage {
+  v4i a[4], b[4];
+  float da[2], dw[2];
+};
+
+QDEV void gemm_lstore(const Stage& r, int8_t* sA, int8_t* sB, float (*sDa)[BM], float (*sDw)[BN]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / 8, c16 = idx % 8;
+    *reinterpret_cast<v4i*>(&sA[row * LDS_ROW + c16 * 16]) = r.a[i];
+    *reinterpret_cast<v4i*>(&sB[row * LDS_ROW + c16 * 16]) = r.b[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / KB, kb = idx % KB;
+    sDa[kb][row] = r.da[i];
+    sDw[kb][row] = r.dw[i];
+  }
+}
+
+QDEV void gemm_gload(const GemmArgs& a, Stage& r, int st, int m0, int n0, int nblk) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + 256 * i;  // 0..1023
+    const int row = idx / 8, c16 = idx % 8;
+    const int gm = min(m0 + row, a.M - 1);
+    const int gn = min(n0 + row, a.N - 1);
+    r.a[i] = *reinterpret_cast<const v4i*>(a.qa + (int64_t)gm * a.K + st * SK + c16 * 16);
+    r.b[i] = *reinterpret_cast<const v4i*>(a.qs + (int64_t)gn * a.K + st * SK + c16 * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i;  // 0..511
+    const int row = idx / KB, kb = idx % KB;
+    const int gm = min(m0 + row, a.M - 1);
+    const int gn = min(n0 + row, a.N - 1);
+    r.da[i] = a.da[(int64_t)gm * nblk + st * KB + kb];
+    r.dw[i] = f16_bits_to_f32(a.sc[(int64_t)gn * nblk + st * KB + kb]);
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
+  __shared__ __align__(16) int8_t sA[2][BM * LDS_ROW];
+  __shared__ __align__(16) int8_t sB[2][BN * LDS_ROW];
+  __shared__ __align__(16) float sDa[2][KB][BM];
+  __shared__ __align__(16) float sDw[2][KB][BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int nblk = a.K / 32;
+  const int nstage = a.K / SK;
+
+  Stage rs;  // global -> register staging: 4 x 16 bytes of A and of B per thread
+  float acc[2][2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+
+  const int lr = lane % 32, lg = lane / 32;
+  gemm_gload(a, rs, 0, m0, n0, nblk);
+  gemm_lstore(rs, sA[0], sB[0], sDa[0], sDw[0]);
+  __syncthreads();
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nstage) gemm_gload(a, rs, st + 1, m0, n0, nblk);
+#pragma unroll 1
+    for (int kb = 0; kb < KB; ++kb) {
+      v4i af[2], bf[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        af[mi] = *reinterpret_cast<const v4i*>(&sA[buf][(wm * 64 + mi * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bf[ni] = *reinterpret_cast<const v4i*>(&sB[buf][(wn * 64 + ni * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        float da[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&sDa[buf][kb][wm * 64 + mi * 32 + 8 * g4 + 4 * lg]);
+          da[4 * g4 + 0] = d4.x, da[4 * g4 + 1] = d4.y, da[4 * g4 + 2] = d4.z, da[4 * g4 + 3] = d4.w;
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const v16i zero = {};
+          const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], zero, 0, 0, 0);
+          const float dw = sDw[buf][kb][wn * 64 + ni * 32 + lr];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (float)S[j] * (da[j] * dw);
+        }
+      }
+    }
+    if (st + 1 < nstage) {
+      gemm_lstore(rs, sA[buf ^ 1], sB[buf ^ 1], sDa[buf ^ 1], sDw[buf ^ 1]);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: element j of tile (mi, ni) is row 8*(j/4) + 4*lg + j%4, column lr
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int m = m0 + wm * 64 + mi * 32 + 8 * (j / 4) + 4 * lg + (j % 4);
+      if (m >= a.M) continue;
+      if (EPI == EPI_SWIGLU) {
+        if (n0 + wn * 64 >= a.N) continue;
+        const int unit = ((n0 + wn * 64) / 64) * 32 + lr;
+        const float g = acc[mi][0][j], u = acc[mi][1][j];
+        a.out[(int64_t)m * a.ldc + unit] = (g / (1.0f + expf(-g))) * u;
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int n = n0 + wn * 64 + ni * 32 + lr;
+          if (n >= a.N) continue;
+          float* p = a.out + (int64_t)m * a.ldc + n;
+          if (EPI == EPI_STORE) *p = acc[mi][ni][j];
+          if (EPI == EPI_RESIDUAL) *p += acc[mi][ni][j];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+namespace q8k {
+
+hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm_q8<EPI_STORE>, grid, dim3(256), 0, s, a); break;
+    case EPI_RESIDUAL: hipLaunchKernelGGL(k_gemm_q8<EPI_RESIDUAL>, grid, dim3(256), 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_q8<EPI_SWIGLU>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q8k

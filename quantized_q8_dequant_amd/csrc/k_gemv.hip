@@ -1,0 +1,338 @@
+// Decode-step Q8_0 GEMV for gfx950: y[n] = sum_b d_w[n,b] * d_a[b] * S[n,b],
+// S the exact integer dot of one 32-block (Fucina course, "Model files and
+// quantization", section 11.9), with the activation quantised per 32-block
+// on the fly (same page, section 11.7).
+//
+// Layout: the weight matrix is two planes -- int8 codes [N][K] (row r is
+// output r) and f16 scales [N][K/32].  A wavefront streams rows with 16-byte
+// (128-bit) coalesced loads: LPR lanes cover one row, each lane holds 16-byte
+// chunks c = lane + j*LPR of it (half a block), so lanes 2i and 2i+1 hold the
+// two halves of block i and one DPP swap forms S exactly.  Weight loads are
+// issued before the prologue (weights do not depend on the activation), the
+// prologue quantises the activation into LDS, then 4 x v_dot4_i32_i8 per chunk.
+//
+// Prologues: RMSNorm + quantise (the norm of "A transformer from scratch",
+// section 12.3.2) or quantise only.  Epilogues: store, residual add (section
+// 12.3.7), SwiGLU of paired gate/up rows (section 12.3.6), and the tied
+// lm_head with the first pass of the greedy argmax (per-workgroup (max,
+// lowest index)); the last workgroup to finish runs the second pass.
+#include "kernels.h"
+#include "qdevice.h"
+
+using namespace q8;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+QDEV int swap_pair(int v) {  // value of lane ^ 1 (quad_perm 1,0,3,2)
+  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+}
+
+// Quantise src [K] (optionally RMSNorm'd with w) into LDS: s_qa [K] bytes,
+// s_da [K/32] f32 (the value of f16(d)).
+template <bool NORM>
+QDEV void prologue_quant(const float* __restrict__ src, const float* __restrict__ w, float eps, int K,
+                         int8_t* s_qa, float* s_da, float* s_red) {
+  float r = 1.f;
+  if (NORM) {
+    float ss = 0.f;
+    for (int c = threadIdx.x * 4; c < K; c += kThreads * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + c);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum<kThreads>(ss, s_red);
+    r = 1.0f / sqrtf(ss / (float)K + eps);
+  }
+  for (int base = 0; base < K; base += kThreads * 4) {
+    const int c = base + threadIdx.x * 4;
+    const bool live = c < K;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const float4 t = *reinterpret_cast<const float4*>(src + c);
+      v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+      if (NORM) {
+        const float4 w4 = *reinterpret_cast<const float4*>(w + c);
+        v[0] = (v[0] * r) * w4.x, v[1] = (v[1] * r) * w4.y, v[2] = (v[2] * r) * w4.z, v[3] = (v[3] * r) * w4.w;
+      }
+    }
+    float d;
+    const int packed = quant4_group8(v, &d);
+    if (live) {
+      *reinterpret_cast<int*>(s_qa + c) = packed;
+      if ((threadIdx.x & 7) == 0) s_da[c >> 5] = f16_round(d);
+    }
+  }
+  __syncthreads();
+}
+
+struct ArgBest {
+  float v;
+  int i;
+};
+QDEV ArgBest better(ArgBest a, ArgBest b) {  // larger value; ties -> lower index
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+QDEV ArgBest wave_best(ArgBest a) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    ArgBest b;
+    b.v = __shfl_xor(a.v, o);
+    b.i = __shfl_xor(a.i, o);
+    a = better(a, b);
+  }
+  return a;
+}
+
+// LPR lanes per row, CPL 16-byte chunks per lane per row (K = 16*LPR*CPL),
+// ROWS rows per lane group.  For EPI_SWIGLU the first ROWS/2 rows are gate
+// rows and the last ROWS/2 the matching up rows.
+template <int LPR, int CPL, int ROWS, bool NORM, int EPI>
+__global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float s_red[kWaves];
+  __shared__ ArgBest s_best[kWaves];
+  constexpr int K = 16 * LPR * CPL;
+  constexpr int GPW = kWave / LPR;  // lane groups per wave
+  int8_t* s_qa = reinterpret_cast<int8_t*>(smem);
+  float* s_da = reinterpret_cast<float*>(smem + K);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int li = lane % LPR, grp = lane / LPR;
+  const int groups_per_wg = kWaves * GPW;
+  const int64_t nb = K / 32;
+  const bool even = (li & 1) == 0;
+
+  // rows of the activation batch: blockIdx.y selects one batch row
+  const float* src = a.src + (int64_t)blockIdx.y * a.src_stride;
+  float* out = a.out ? a.out + (int64_t)blockIdx.y * a.out_stride : nullptr;
+
+  ArgBest best{-INFINITY, 0x7FFFFFFF};
+  bool have_act = false;
+
+  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int gg = tile * groups_per_wg + wave * GPW + grp;  // global lane-group index
+    int rows[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (EPI == EPI_SWIGLU) {
+        constexpr int P = ROWS / 2;
+        const int n = gg * P + (r % P);
+        rows[r] = (n / 32) * 64 + (r < P ? 0 : 32) + (n % 32);
+      } else {
+        rows[r] = gg * ROWS + r;
+      }
+    }
+    int4 wv[ROWS][CPL];
+    uint16_t ws[ROWS][CPL];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int64_t row = rows[r] < a.N ? rows[r] : a.N - 1;
+      const int8_t* wr = a.qs + row * (int64_t)K;
+      const uint16_t* sr = a.sc + row * nb;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = li + j * LPR;
+        wv[r][j] = *reinterpret_cast<const int4*>(wr + c * 16);
+        ws[r][j] = sr[c >> 1];
+      }
+    }
+    if (!have_act) {
+      prologue_quant<NORM>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
+      have_act = true;
+    }
+    float acc[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = li + j * LPR;
+      const int4 av = *reinterpret_cast<const int4*>(s_qa + c * 16);
+      const float da = s_da[c >> 1];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const int half = dot16_i8(wv[r][j], av);
+        const int S = half + swap_pair(half);
+        if (even) acc[r] += (float)S * (f16_bits_to_f32(ws[r][j]) * da);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum<LPR>(acc[r]);
+
+    if (li == 0) {
+      if (EPI == EPI_SWIGLU) {
+        constexpr int P = ROWS / 2;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int n = gg * P + i;
+          if (n < a.N / 2) {
+            const float g = acc[i], u = acc[P + i];
+            out[n] = (g / (1.0f + expf(-g))) * u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const int row = rows[r];
+          if (row < a.N) {
+            if (EPI == EPI_STORE) out[row] = acc[r];
+            if (EPI == EPI_RESIDUAL) out[row] += acc[r];
+            if (EPI == EPI_ARGMAX) {
+              if (a.logits) a.logits[(int64_t)blockIdx.y * a.N + row] = acc[r];
+              best = better(best, ArgBest{acc[r], row});
+            }
+          }
+        }
+      }
+    }
+  }
+
+  if (EPI == EPI_ARGMAX) {
+    best = wave_best(best);
+    if (lane == 0) s_best[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ArgBest b = s_best[0];
+      for (int i = 1; i < kWaves; ++i) b = better(b, s_best[i]);
+      const int64_t slot = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      a.part_v[slot] = b.v;
+      a.part_i[slot] = b.i;
+      __threadfence();
+      const unsigned prev = atomicAdd(a.counter + blockIdx.y, 1u);
+      s_red[0] = __uint_as_float(prev == gridDim.x - 1 ? 1u : 0u);
+    }
+    __syncthreads();
+    if (__float_as_uint(s_red[0]) == 1u) {  // last workgroup of this batch row: second pass
+      __threadfence();
+      ArgBest b{-INFINITY, 0x7FFFFFFF};
+      for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
+        const int64_t slot = (int64_t)blockIdx.y * gridDim.x + i;
+        b = better(b, ArgBest{__builtin_nontemporal_load(a.part_v + slot), __builtin_nontemporal_load(a.part_i + slot)});
+      }
+      b = wave_best(b);
+      if (lane == 0) s_best[wave] = b;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        ArgBest t = s_best[0];
+        for (int i = 1; i < kWaves; ++i) t = better(t, s_best[i]);
+        if (a.argmax) a.argmax[blockIdx.y] = t.i;
+        a.counter[blockIdx.y] = 0u;  // ready for the next launch
+        if (a.len_ptr) {
+          const int seq = a.len_seq ? a.len_seq[blockIdx.y] : 0;
+          a.len_ptr[seq] += a.len_add;
+        }
+      }
+    }
+  }
+}
+
+// Test hook: S[t][n][b] with the same half-block dot and pair swap.
+// One wavefront per (t, n) pair.
+__global__ void __launch_bounds__(kThreads) k_block_dots(const int8_t* __restrict__ qa, const int8_t* __restrict__ qs,
+                                                        int K, int N, int64_t pairs, int32_t* __restrict__ S) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t pair = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (pair >= pairs) return;  // uniform per wavefront
+  const int t = (int)(pair / N), n = (int)(pair % N);
+  const int nchunks = K / 16;
+  for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+    const int c = c0 + lane;
+    int half = 0;
+    if (c < nchunks) {
+      const int4 w = *reinterpret_cast<const int4*>(qs + (int64_t)n * K + c * 16);
+      const int4 x = *reinterpret_cast<const int4*>(qa + (int64_t)t * K + c * 16);
+      half = dot16_i8(w, x);
+    }
+    const int s = half + swap_pair(half);
+    if (c < nchunks && (c & 1) == 0) S[((int64_t)t * N + n) * (K / 32) + c / 2] = s;
+  }
+}
+
+template <int LPR, int CPL, int ROWS, bool NORM, int EPI>
+hipError_t launch_one(const GemvArgs& a, int grid_x, int grid_y, hipStream_t s) {
+  constexpr int K = 16 * LPR * CPL;
+  const size_t shm = K + (K / 32) * sizeof(float);
+  hipLaunchKernelGGL((k_gemv<LPR, CPL, ROWS, NORM, EPI>), dim3(grid_x, grid_y), dim3(kThreads), shm, s, a);
+  return hipGetLastError();
+}
+
+template <int LPR, int CPL, int ROWS>
+hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int max_grid, int grid_y, hipStream_t s) {
+  constexpr int GPW = kWave / LPR;
+  constexpr int groups = kWaves * GPW;
+  const int rows_per_tile = groups * (epi == EPI_SWIGLU ? ROWS : ROWS);
+  a.ntiles = (a.N + rows_per_tile - 1) / rows_per_tile;
+  int grid = a.ntiles;
+  if (max_grid > 0 && grid > max_grid) grid = max_grid;
+#define Q8_CASE(NORM_, EPI_) \
+  if (norm == NORM_ && epi == EPI_) return launch_one<LPR, CPL, ROWS, NORM_, EPI_>(a, grid, grid_y, s);
+  Q8_CASE(true, EPI_STORE)
+  Q8_CASE(false, EPI_STORE)
+  Q8_CASE(false, EPI_RESIDUAL)
+  Q8_CASE(true, EPI_SWIGLU)
+  Q8_CASE(true, EPI_ARGMAX)
+  Q8_CASE(false, EPI_ARGMAX)
+#undef Q8_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+namespace q8k {
+
+int gemv_argmax_grid(int N, int K) {
+  (void)K;
+  const int tiles = (N + 31) / 32;
+  return tiles < 2048 ? tiles : 2048;
+}
+
+// Dispatch on K: LPR = 64 when K % 1024 == 0, else 16 (K % 256 == 0).
+hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s) {
+  const int K = a.K;
+  const int max_grid = (epi == EPI_ARGMAX) ? gemv_argmax_grid(a.N, K) : 0;
+  if (K % 1024 == 0) {
+    switch (K / 1024) {
+      case 1: return launch_epi<64, 1, 8>(a, norm, epi, max_grid, grid_y, s);
+      case 2: return launch_epi<64, 2, 4>(a, norm, epi, max_grid, grid_y, s);
+      case 3: return launch_epi<64, 3, 2>(a, norm, epi, max_grid, grid_y, s);
+      case 4: return launch_epi<64, 4, 2>(a, norm, epi, max_grid, grid_y, s);
+      case 6: return launch_epi<64, 6, 2>(a, norm, epi, max_grid, grid_y, s);
+      case 8: return launch_epi<64, 8, 2>(a, norm, epi, max_grid, grid_y, s);
+      case 12: return launch_epi<64, 12, 2>(a, norm, epi, max_grid, grid_y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (K % 256 == 0) {
+    switch (K / 256) {
+      case 1: return launch_epi<16, 1, 4>(a, norm, epi, max_grid, grid_y, s);
+      case 2: return launch_epi<16, 2, 4>(a, norm, epi, max_grid, grid_y, s);
+      case 3: return launch_epi<16, 3, 2>(a, norm, epi, max_grid, grid_y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+bool gemv_supported_k(int K) {
+  if (K % 1024 == 0) {
+    const int c = K / 1024;
+    return c == 1 || c == 2 || c == 3 || c == 4 || c == 6 || c == 8 || c == 12;
+  }
+  if (K % 256 == 0) {
+    const int c = K / 256;
+    return c >= 1 && c <= 3;
+  }
+  return false;
+}
+
+hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s) {
+  const int64_t pairs = (int64_t)M * N;
+  const int64_t grid = (pairs + kWaves - 1) / kWaves;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_dots, dim3((unsigned)grid), dim3(kThreads), 0, s, qa, qs, K, N, pairs, S);
+  return hipGetLastError();
+}
+
+}  // namespace q8k

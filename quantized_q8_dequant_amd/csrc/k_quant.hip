@@ -1,0 +1,204 @@
+// Q8_0 encode / repack / embedding gather / row quantisation kernels (gfx950).
+//
+// Q8_0 block format and encoder: Fucina course, "Model files and
+// quantization", section 11.7.  Embedding gather: Fucina course, "A
+// transformer from scratch", section 12.3.1 (rows dequantised on the fly).
+// RMSNorm: the same page, section 12.3.2.
+#include "kernels.h"
+#include "qdevice.h"
+
+using namespace q8;
+
+// f32 values -> Q8_0 wire blocks (34 bytes: f16 d, 32 x int8).  One 8-lane
+// group per block, 4 values per lane.
+__global__ void __launch_bounds__(256) k_encode_q8_0(const float* __restrict__ x, int64_t nblocks,
+                                                     uint8_t* __restrict__ out) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gid >> 3;
+  const int sub = (int)(gid & 7);
+  const bool live = blk < nblocks;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const float4 t = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
+    v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+  }
+  float d;
+  const int packed = quant4_group8(v, &d);  // all 8 lanes of a group share liveness
+  if (live) {
+    uint8_t* b = out + blk * 34;
+    if (sub == 0) {
+      const uint16_t h = f32_to_f16_bits(d);
+      b[0] = (uint8_t)(h & 0xFF);
+      b[1] = (uint8_t)(h >> 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[2 + sub * 4 + i] = (uint8_t)((packed >> (8 * i)) & 0xFF);
+  }
+}
+
+__global__ void k_encode_bf16(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = f32_to_bf16_bits(x[i]);
+}
+
+// Wire blocks -> planes: qs int8 [rows, k] at row stride k, scales f16 [rows, k/32].
+// dst_row0 lets the runtime stack several matrices into one plane; `interleave`
+// > 0 places source row r at stacked row (r / 32) * 64 + interleave_off + r % 32
+// (gate/up pairing: each 64-row group = 32 gate rows then 32 up rows).
+__global__ void k_repack_q8_0(const uint8_t* __restrict__ src, int64_t rows, int64_t k, int8_t* __restrict__ qs,
+                              uint16_t* __restrict__ sc, int64_t dst_row0, int interleave_off) {
+  const int64_t nb = k / 32;
+  const int64_t total = rows * nb;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nb, b = i % nb;
+    int64_t dr = dst_row0 + r;
+    if (interleave_off >= 0) dr = dst_row0 + (r / 32) * 64 + interleave_off + (r % 32);
+    const uint8_t* s = src + i * 34;
+    sc[dr * nb + b] = (uint16_t)(s[0] | (s[1] << 8));
+    int8_t* q = qs + dr * k + b * 32;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) q[j] = (int8_t)s[2 + j];
+  }
+}
+
+// bf16 rows copied into a stacked plane (same stacking rules as above).
+__global__ void k_repack_bf16(const uint16_t* __restrict__ src, int64_t rows, int64_t k, uint16_t* __restrict__ dst,
+                              int64_t dst_row0, int interleave_off) {
+  const int64_t total = rows * k;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / k, c = i % k;
+    int64_t dr = dst_row0 + r;
+    if (interleave_off >= 0) dr = dst_row0 + (r / 32) * 64 + interleave_off + (r % 32);
+    dst[dr * k + c] = src[i];
+  }
+}
+
+// Embedding gather: x[t, :] = dequant(token_embd[tok[t], :]) (exact in f32).
+// Token ids are clamped into [0, vocab) (device-side ids cannot be checked
+// on the host without a synchronisation).
+__global__ void __launch_bounds__(256) k_embed_q8_0(const int32_t* __restrict__ tok, int vocab, int H,
+                                                    const int8_t* __restrict__ qs, const uint16_t* __restrict__ sc,
+                                                    float* __restrict__ x) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const int8_t* row = qs + (int64_t)id * H;
+  const uint16_t* srow = sc + (int64_t)id * (H / 32);
+  for (int c = threadIdx.x; c < H; c += blockDim.x)
+    x[(int64_t)t * H + c] = f16_bits_to_f32(srow[c >> 5]) * (float)row[c];
+}
+
+__global__ void __launch_bounds__(256) k_embed_bf16(const int32_t* __restrict__ tok, int vocab, int H,
+                                                    const uint16_t* __restrict__ w, float* __restrict__ x) {
+  const int t = blockIdx.x;
+  int id = tok[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  for (int c = threadIdx.x; c < H; c += blockDim.x)
+    x[(int64_t)t * H + c] = bf16_bits_to_f32(w[(int64_t)id * H + c]);
+}
+
+// Row-wise (optional RMSNorm) + Q8_0 quantisation: one workgroup per row.
+// x [T, K] f32 -> qa int8 [T, K], da f32 [T, K/32] (the f32 value of f16(d)).
+// norm_w == nullptr skips the norm.  K % 32 == 0.
+__global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x, int K, const float* __restrict__ norm_w,
+                                                    float eps, int8_t* __restrict__ qa, float* __restrict__ da,
+                                                    uint16_t* __restrict__ da_bits) {
+  __shared__ float s_red[4];
+  const int64_t t = blockIdx.x;
+  const float* xr = x + t * K;
+  float r = 1.f;
+  if (norm_w) {
+    float ss = 0.f;
+    for (int c = threadIdx.x * 4; c < K; c += 256 * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + c);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum<256>(ss, s_red);
+    r = 1.0f / sqrtf(ss / (float)K + eps);
+  }
+  // every thread takes part in each pass (groups of 8 lanes stay uniform)
+  for (int base = 0; base < K; base += 256 * 4) {
+    const int c = base + threadIdx.x * 4;
+    const bool live = c < K;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const float4 t4 = *reinterpret_cast<const float4*>(xr + c);
+      v[0] = t4.x, v[1] = t4.y, v[2] = t4.z, v[3] = t4.w;
+      if (norm_w) {
+        const float4 w4 = *reinterpret_cast<const float4*>(norm_w + c);
+        v[0] = (v[0] * r) * w4.x, v[1] = (v[1] * r) * w4.y, v[2] = (v[2] * r) * w4.z, v[3] = (v[3] * r) * w4.w;
+      }
+    }
+    float d;
+    const int packed = quant4_group8(v, &d);
+    if (live) {
+      *reinterpret_cast<int*>(qa + t * K + c) = packed;
+      if ((threadIdx.x & 7) == 0) {
+        const int64_t bi = t * (K / 32) + c / 32;
+        if (da) da[bi] = f16_round(d);
+        if (da_bits) da_bits[bi] = f32_to_f16_bits(d);
+      }
+    }
+  }
+}
+
+// ---- launchers -------------------------------------------------------------------------
+namespace q8k {
+
+hipError_t encode_q8_0(const float* x, int64_t n, void* out, hipStream_t s) {
+  const int64_t nb = n / 32;
+  if (nb == 0) return hipSuccess;
+  const int64_t threads = nb * 8;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_encode_q8_0, dim3((unsigned)grid), dim3(256), 0, s, x, nb, (uint8_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t encode_bf16(const float* x, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t grid = (n + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(k_encode_bf16, dim3((unsigned)grid), dim3(256), 0, s, x, n, out);
+  return hipGetLastError();
+}
+
+hipError_t repack_q8_0(const void* src, int64_t rows, int64_t k, int8_t* qs, uint16_t* sc, int64_t dst_row0,
+                       int interleave_off, hipStream_t s) {
+  const int64_t total = rows * (k / 32);
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(k_repack_q8_0, dim3((unsigned)grid), dim3(256), 0, s, (const uint8_t*)src, rows, k, qs, sc,
+                     dst_row0, interleave_off);
+  return hipGetLastError();
+}
+
+hipError_t repack_bf16(const void* src, int64_t rows, int64_t k, uint16_t* dst, int64_t dst_row0, int interleave_off,
+                       hipStream_t s) {
+  const int64_t total = rows * k;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(k_repack_bf16, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)src, rows, k, dst,
+                     dst_row0, interleave_off);
+  return hipGetLastError();
+}
+
+hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, const uint16_t* sc, bool bf16, float* x,
+                 hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(k_embed_bf16, dim3(T), dim3(256), 0, s, tok, vocab, H, (const uint16_t*)w, x);
+  else
+    hipLaunchKernelGGL(k_embed_q8_0, dim3(T), dim3(256), 0, s, tok, vocab, H, (const int8_t*)w, sc, x);
+  return hipGetLastError();
+}
+
+hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
+                      uint16_t* da_bits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rows_quant, dim3(T), dim3(256), 0, s, x, K, norm_w, eps, qa, da, da_bits);
+  return hipGetLastError();
+}
+
+}  // namespace q8k

@@ -1,0 +1,131 @@
+// Kernel launch interface between the C++ runtime and the gfx950 kernels.
+// Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+
+// Arguments of the decode GEMV family (see k_gemv.hip).
+struct GemvArgs {
+  const float* src;  // activation rows f32 [grid_y][K] (row stride src_stride)
+  int64_t src_stride;
+  const float* norm_w;  // RMSNorm weight [K] (prologue with norm)
+  float eps;
+  const int8_t* qs;    // codes [N][K]
+  const uint16_t* sc;  // f16 scales [N][K/32]
+  int N;               // stacked rows (SWIGLU: 2 * hidden units)
+  int K;
+  int ntiles;          // set by the launcher
+  float* out;          // STORE/RESIDUAL: [grid_y][N]; SWIGLU: [grid_y][N/2]
+  int64_t out_stride;
+  // ARGMAX epilogue (tied lm_head + two-pass argmax)
+  float* logits;      // [grid_y][N] or null
+  float* part_v;      // [grid_y][grid_x] per-workgroup maxima
+  int32_t* part_i;    // [grid_y][grid_x] their indices
+  unsigned* counter;  // [grid_y] zero between launches (the last workgroup resets it)
+  int32_t* argmax;    // [grid_y] or null
+  int32_t* len_ptr;   // KV lengths; the last workgroup adds len_add to len_ptr[seq]
+  const int32_t* len_seq;  // [grid_y] sequence of each batch row (null: sequence 0)
+  int32_t len_add;
+};
+
+// Decode attention over one layer's KV cache (see k_attn_decode.hip).
+// Cache layout: sequence s occupies [num_layers][2 (K, V)][nkv][cap_s][hd]
+// elements starting at element seq_base[s].
+struct AttnDecodeArgs {
+  const float* qkv;  // [nrows][qkv_stride] raw projections: q | k | v
+  int64_t qkv_stride;
+  const float* q_norm;  // [hd]
+  const float* k_norm;  // [hd]
+  float eps;
+  const float* rope_cos;  // [max_pos][hd/2]
+  const float* rope_sin;
+  void* kv;                  // cache base
+  const int64_t* seq_base;   // [max_seqs] element offset of each sequence
+  const int32_t* seq_cap;    // [max_seqs] capacity (rows) of each sequence
+  const int32_t* len;        // [max_seqs] KV lengths (position of the new token)
+  const int32_t* row_seq;    // [nrows] sequence of each batch row (null: sequence 0)
+  int layer;
+  float* part;        // partials [nrows][nkv][nsplit_max][G][hd + 2]
+  unsigned* counter;  // [nrows][nkv], zero between launches
+  float* out;         // attention output [nrows][out_stride], head h at h*hd
+  int64_t out_stride;
+  int nkv, nsplit_max, min_rows;
+  float scale;  // 1/sqrt(hd)
+};
+
+namespace q8k {
+
+hipError_t encode_q8_0(const float* x, int64_t n, void* out, hipStream_t s);
+hipError_t encode_bf16(const float* x, int64_t n, uint16_t* out, hipStream_t s);
+// interleave_off < 0: plain stacking at dst_row0; >= 0: 32-row gate/up interleave
+hipError_t repack_q8_0(const void* src, int64_t rows, int64_t k, int8_t* qs, uint16_t* sc, int64_t dst_row0,
+                       int interleave_off, hipStream_t s);
+hipError_t repack_bf16(const void* src, int64_t rows, int64_t k, uint16_t* dst, int64_t dst_row0, int interleave_off,
+                       hipStream_t s);
+hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, const uint16_t* sc, bool bf16, float* x,
+                 hipStream_t s);
+hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
+                      uint16_t* da_bits, hipStream_t s);
+
+bool gemv_supported_k(int K);
+int gemv_argmax_grid(int N, int K);
+hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s);
+hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s);
+
+bool attn_decode_supported(int hd, int group);
+hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
+
+hipError_t set_len(int32_t* len, int seq, int value, hipStream_t s);
+
+}  // namespace q8k
+
+// Prefill Q8_0 GEMM (see k_gemm.hip): C[M, N] from qa int8 [M][K] with
+// per-block scales da f32 [M][K/32] and the weight planes.
+struct GemmArgs {
+  const int8_t* qa;
+  const float* da;
+  const int8_t* qs;
+  const uint16_t* sc;
+  int M, N, K;
+  float* out;  // STORE/RESIDUAL: [M][ldc]; SWIGLU: [M][ldc] hidden units (N/2 of them)
+  int64_t ldc;
+};
+
+// Prefill per-token head work (see k_attn_prefill.hip).
+struct QkRopeArgs {
+  const float* qkv;  // [T][qkv_stride]
+  int64_t qkv_stride;
+  const float* q_norm;
+  const float* k_norm;
+  float eps;
+  const float* rope_cos;
+  const float* rope_sin;
+  _Float16* q16;  // [T][nh][hd]
+  void* kv;
+  int64_t kbase;  // element offset of this (sequence, layer) K block; V follows at + nkv*cap*hd
+  int cap;
+  int pos0;       // position of token 0
+  int nh, nkv;
+};
+
+struct AttnPrefillArgs {
+  const _Float16* q16;  // [T][nh][hd]
+  const void* kv;
+  int64_t kbase;
+  int cap;
+  int pos0;  // position of query token 0 (cache rows [0, pos0 + T) are valid)
+  int T;
+  int nh, nkv;
+  float scale;
+  float* out;  // [T][nh*hd]
+};
+
+namespace q8k {
+hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s);
+hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, bool kv_bf16, hipStream_t s);
+hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf16, hipStream_t s);
+bool attn_prefill_supported(int hd, int group);
+}  // namespace q8k

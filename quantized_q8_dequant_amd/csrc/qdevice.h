@@ -1,0 +1,128 @@
+// Device helpers shared by the gfx950 kernels: numeric conversions, the
+// Q8_0 block quantiser, the integer half-block dot and wavefront reductions.
+//
+// The quantiser follows the Q8_0 encoder of the Fucina course page "Model
+// files and quantization", section 11.7 (per 32 values: amax; d = amax/127;
+// inv = d == 0 ? 0 : 1/d; q = round(v * inv) clamped to +-127; the stored
+// scale is f16(d)) with round-half-to-even, the production rounding of
+// section 11.10.  Divisions are IEEE (the build does not enable fast math),
+// so the codes match a CPU encoder bit for bit on the same f32 input.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QDEV __device__ __forceinline__
+
+namespace q8 {
+
+constexpr int kWave = 64;
+
+// ---- conversions -------------------------------------------------------------
+QDEV float f16_bits_to_f32(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+QDEV uint16_t f32_to_f16_bits(float x) {  // v_cvt_f16_f32: round to nearest even
+  _Float16 h = (_Float16)x;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+QDEV float f16_round(float x) { return (float)(_Float16)x; }
+
+QDEV uint16_t f32_to_bf16_bits(float x) {  // round half to even on the dropped 16 bits
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+QDEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+QDEV float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+
+// ---- wavefront reductions ----------------------------------------------------------
+template <int WIDTH>
+QDEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
+  return v;
+}
+template <int WIDTH>
+QDEV float wave_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+
+// Block-wide sum of one float per thread (blockDim.x == NT, NT % 64 == 0).
+template <int NT>
+QDEV float block_sum(float v, float* s_red) {
+  v = wave_sum<kWave>(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) s_red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += s_red[i];
+  __syncthreads();
+  return t;
+}
+
+// ---- Q8_0 quantiser ---------------------------------------------------------------
+// One 32-block is held by 8 consecutive lanes, 4 values each (v[0..3] are
+// block elements 4*(lane%8) .. +3).  Returns the 4 codes packed in an int
+// (byte i = code of v[i]) and the f32 scale d through *d_out (every lane of
+// the group gets the same d).
+QDEV int quant4_group8(const float v[4], float* d_out) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  a = fmaxf(a, __shfl_xor(a, 1, 8));
+  a = fmaxf(a, __shfl_xor(a, 2, 8));
+  a = fmaxf(a, __shfl_xor(a, 4, 8));
+  const float d = a / 127.0f;
+  const float inv = d == 0.f ? 0.f : 1.0f / d;
+  int packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float q = rintf(v[i] * inv);
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    packed |= ((int)q & 0xFF) << (8 * i);
+  }
+  *d_out = d;
+  return packed;
+}
+
+// ---- integer dot of one 16-byte half block --------------------------------------------
+QDEV int dot16_i8(const int4 a, const int4 b) {
+  int s = __builtin_amdgcn_sdot4(a.x, b.x, 0, false);
+  s = __builtin_amdgcn_sdot4(a.y, b.y, s, false);
+  s = __builtin_amdgcn_sdot4(a.z, b.z, s, false);
+  s = __builtin_amdgcn_sdot4(a.w, b.w, s, false);
+  return s;
+}
+
+// Block dot from two lanes holding its halves (lanes l and l^1 of a group):
+// exact int32 sum of 32 products (|S| <= 32 * 127^2 < 2^20).
+QDEV int block_dot_pair(int half) { return half + __shfl_xor(half, 1, kWave); }
+
+// RMSNorm over one head (HD values in LDS) followed by the NeoX rotation of
+// pairs (i, i + HD/2) by the angle whose cos/sin are cs[i]/sn[i]; run by one
+// wavefront ("A transformer from scratch", sections 12.3.2 and 12.3.4).
+template <int HD>
+QDEV void norm_rope_wave(float* x, const float* __restrict__ w, float eps, const float* __restrict__ cs,
+                         const float* __restrict__ sn, float scale_out) {
+  const int lane = threadIdx.x % kWave;
+  float ss = 0.f;
+  for (int d = lane; d < HD; d += kWave) ss += x[d] * x[d];
+  ss = wave_sum<kWave>(ss);
+  const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+  constexpr int H2 = HD / 2;
+  for (int i = lane; i < H2; i += kWave) {
+    const float a = (x[i] * r) * w[i];
+    const float b = (x[i + H2] * r) * w[i + H2];
+    const float c = cs[i], s = sn[i];
+    x[i] = (a * c - b * s) * scale_out;
+    x[i + H2] = (a * s + b * c) * scale_out;
+  }
+}
+
+}  // namespace q8

@@ -1,0 +1,719 @@
+// Host runtime behind the C ABI in include/qwen3_q8.h: validation, the
+// workspace plan (every device byte comes from the caller's workspace), the
+// weight repack, the KV-cache bookkeeping, the launch sequences of prefill and
+// decode, and HIP-graph capture of the decode step.
+//
+// Forward pass order: Fucina course, "A transformer from scratch", sections
+// 12.3-12.5; the KV cache contract (append at len on every layer, advance
+// once, reject pos0 != len and overflow): same page, section 12.4.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <algorithm>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/qwen3_q8.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                                   \
+  do {                                                                                                  \
+    hipError_t e_ = (expr);                                                                             \
+    if (e_ != hipSuccess) return fail(QWEN3_E_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// checked multiply of non-negative sizes
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Bump allocator over the workspace; with base == nullptr it only measures.
+struct Carver {
+  uint8_t* base = nullptr;
+  size_t off = 0;
+  bool overflow = false;
+  void* take(size_t bytes) {
+    off = align_up(off);
+    void* p = base ? base + off : nullptr;
+    if (bytes > SIZE_MAX - off) overflow = true;
+    else off += bytes;
+    return p;
+  }
+  template <typename T>
+  T* arr(size_t n) {
+    size_t b;
+    if (!mul_ok(n, sizeof(T), &b)) {
+      overflow = true;
+      return nullptr;
+    }
+    return static_cast<T*>(take(b));
+  }
+};
+
+struct QPlane {  // repacked Q8_0 matrix, or bf16 rows
+  int8_t* qs = nullptr;
+  uint16_t* sc = nullptr;
+  uint16_t* bf = nullptr;
+  int64_t rows = 0, k = 0;
+};
+
+struct Layer {
+  QPlane qkv, o, gateup, down;
+  float *attn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr, *ffn_norm = nullptr;
+};
+
+int decode_nsplit_max(int nkv, int nrows) {
+  int n = 2048 / (nkv * nrows);
+  if (n > 64) n = 64;
+  if (n < 1) n = 1;
+  return n;
+}
+
+}  // namespace
+
+struct qwen3_model {
+  qwen3_config cfg{};
+  std::vector<int32_t> cap;
+  int R = 0;  // max_batch_tokens
+  int nh = 0, nkv = 0, hd = 0, H = 0, F = 0, V = 0, L = 0, G = 0, qw = 0, kvw = 0, nqkv = 0, kmax = 0;
+  bool wbf16 = false, kvbf16 = false;
+  int max_cap = 0;
+  // device
+  std::vector<Layer> layers;
+  QPlane emb;
+  float* out_norm = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  void* kv = nullptr;
+  int64_t* d_seq_base = nullptr;
+  int32_t* d_seq_cap = nullptr;
+  int32_t* d_len = nullptr;
+  int32_t* d_row_seq = nullptr;  // batch rows -> sequences
+  int32_t* d_seq_ids = nullptr;  // constant 0 .. max_seqs-1 (row map of single-sequence steps)
+  int32_t* d_tok = nullptr;
+  float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr;
+  int8_t* qa = nullptr;
+  float* da = nullptr;
+  _Float16* q16 = nullptr;
+  float* attn_part = nullptr;
+  unsigned* attn_cnt = nullptr;
+  float* am_part_v = nullptr;
+  int32_t* am_part_i = nullptr;
+  unsigned* am_cnt = nullptr;
+  size_t bytes = 0;
+  // host
+  std::vector<int64_t> seq_base;
+  std::vector<int32_t> h_len;
+  hipStream_t cap_stream = nullptr;
+  bool use_graphs = true;
+  std::map<std::tuple<int, const void*, const void*, const void*>, hipGraphExec_t> graphs;
+};
+
+namespace {
+
+int validate(const qwen3_config* c) {
+  if (!c) return fail(QWEN3_E_INVALID_ARGUMENT, "config is null");
+  if (c->vocab_size <= 0 || c->hidden_size <= 0 || c->intermediate_size <= 0 || c->num_layers <= 0 ||
+      c->num_attention_heads <= 0 || c->num_key_value_heads <= 0 || c->head_dim <= 0)
+    return fail(QWEN3_E_INVALID_CONFIG, "every config integer must be positive");
+  if (c->num_attention_heads % c->num_key_value_heads)
+    return fail(QWEN3_E_INVALID_CONFIG, "num_attention_heads must be a multiple of num_key_value_heads");
+  if (c->head_dim % 2) return fail(QWEN3_E_INVALID_CONFIG, "head_dim must be even (RoPE pairs)");
+  if (!(c->rms_norm_eps > 0.f) || !std::isfinite(c->rms_norm_eps))
+    return fail(QWEN3_E_INVALID_CONFIG, "rms_norm_eps must be positive");
+  if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
+    return fail(QWEN3_E_INVALID_CONFIG, "rope_theta must be > 1");
+  if (c->weight_type != QWEN3_W_Q8_0 && c->weight_type != QWEN3_W_BF16)
+    return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown weight_type");
+  if (c->weight_type == QWEN3_W_BF16)
+    return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "bf16 weights are not built in this library version");
+  if (c->kv_type != QWEN3_KV_F32 && c->kv_type != QWEN3_KV_BF16)
+    return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown kv_type");
+  const int qw = c->num_attention_heads * c->head_dim;
+  if (c->hidden_size % 128 || qw % 128 || c->intermediate_size % 128)
+    return fail(QWEN3_E_INVALID_CONFIG, "hidden_size, heads*head_dim and intermediate_size must be multiples of 128");
+  const int G = c->num_attention_heads / c->num_key_value_heads;
+  if (!q8k::attn_decode_supported(c->head_dim, G) || !q8k::attn_prefill_supported(c->head_dim, G))
+    return fail(QWEN3_E_INVALID_CONFIG, "head_dim must be 64 or 128 and heads/kv_heads one of 1, 2, 4, 8");
+  if (!q8k::gemv_supported_k(c->hidden_size) || !q8k::gemv_supported_k(qw) ||
+      !q8k::gemv_supported_k(c->intermediate_size))
+    return fail(QWEN3_E_INVALID_CONFIG,
+                "hidden_size, heads*head_dim and intermediate_size must each be 256, 512, 768 or "
+                "1024 * {1,2,3,4,6,8,12}");
+  if (c->max_seqs <= 0) return fail(QWEN3_E_INVALID_CONFIG, "max_seqs must be >= 1");
+  if (!c->h_seq_capacity) return fail(QWEN3_E_INVALID_ARGUMENT, "h_seq_capacity is null");
+  for (int i = 0; i < c->max_seqs; ++i)
+    if (c->h_seq_capacity[i] <= 0) return fail(QWEN3_E_INVALID_CONFIG, "every seq_capacity must be >= 1");
+  if (c->max_batch_tokens < 0) return fail(QWEN3_E_INVALID_CONFIG, "max_batch_tokens must be >= 0");
+  return QWEN3_OK;
+}
+
+// Lays out (or measures, with base == nullptr) the workspace.
+int plan(qwen3_model* m, uint8_t* base, size_t* total) {
+  const qwen3_config& c = m->cfg;
+  Carver cv;
+  cv.base = base;
+  const int64_t H = c.hidden_size, F = c.intermediate_size, V = c.vocab_size, hd = c.head_dim;
+  const int64_t nh = c.num_attention_heads, nkv = c.num_key_value_heads;
+  const int64_t qw = nh * hd, kvw = nkv * hd, nqkv = qw + 2 * kvw;
+  const int64_t R = m->R;
+  auto plane = [&](QPlane& p, int64_t rows, int64_t k) {
+    p.rows = rows;
+    p.k = k;
+    size_t n;
+    if (!mul_ok((size_t)rows, (size_t)k, &n)) cv.overflow = true;
+    p.qs = cv.arr<int8_t>(n);
+    p.sc = cv.arr<uint16_t>(n / 32);
+  };
+  m->layers.assign(c.num_layers, Layer{});
+  plane(m->emb, V, H);
+  m->out_norm = cv.arr<float>(H);
+  for (auto& ly : m->layers) {
+    plane(ly.qkv, nqkv, H);
+    plane(ly.o, H, qw);
+    plane(ly.gateup, 2 * F, H);
+    plane(ly.down, H, F);
+    ly.attn_norm = cv.arr<float>(H);
+    ly.q_norm = cv.arr<float>(hd);
+    ly.k_norm = cv.arr<float>(hd);
+    ly.ffn_norm = cv.arr<float>(H);
+  }
+  // RoPE table
+  m->rope_cos = cv.arr<float>((size_t)m->max_cap * (hd / 2));
+  m->rope_sin = cv.arr<float>((size_t)m->max_cap * (hd / 2));
+  // KV cache: sequence s holds [layers][K, V][nkv][cap_s][hd]
+  const size_t esz = m->kvbf16 ? 2 : 4;
+  m->seq_base.assign(c.max_seqs, 0);
+  size_t kv_elems = 0;
+  for (int s = 0; s < c.max_seqs; ++s) {
+    m->seq_base[s] = (int64_t)kv_elems;
+    size_t per;
+    if (!mul_ok((size_t)c.num_layers * 2 * nkv * hd, (size_t)m->cap[s], &per)) cv.overflow = true;
+    if (per > SIZE_MAX - kv_elems) cv.overflow = true;
+    else kv_elems += per;
+  }
+  size_t kv_bytes;
+  if (!mul_ok(kv_elems, esz, &kv_bytes)) cv.overflow = true;
+  m->kv = cv.take(kv_bytes);
+  m->d_seq_base = cv.arr<int64_t>(c.max_seqs);
+  m->d_seq_cap = cv.arr<int32_t>(c.max_seqs);
+  m->d_len = cv.arr<int32_t>(c.max_seqs);
+  m->d_row_seq = cv.arr<int32_t>(R);
+  m->d_seq_ids = cv.arr<int32_t>(c.max_seqs);
+  m->d_tok = cv.arr<int32_t>(R);
+  // activations (rows = R)
+  m->x = cv.arr<float>(R * H);
+  m->qkv = cv.arr<float>(R * nqkv);
+  m->attn = cv.arr<float>(R * qw);
+  m->h = cv.arr<float>(R * F);
+  m->qa = cv.arr<int8_t>(R * m->kmax);
+  m->da = cv.arr<float>(R * (m->kmax / 32));
+  m->q16 = cv.arr<_Float16>(R * qw);
+  // decode attention partials: rows * nsplit <= 2048 / nkv (see decode_nsplit_max)
+  const int64_t G = nh / nkv;
+  m->attn_part = cv.arr<float>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
+  m->attn_cnt = cv.arr<unsigned>(R * nkv);
+  const int64_t amg = q8k::gemv_argmax_grid(c.vocab_size, c.hidden_size);
+  m->am_part_v = cv.arr<float>(R * amg);
+  m->am_part_i = cv.arr<int32_t>(R * amg);
+  m->am_cnt = cv.arr<unsigned>(R);
+  if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
+  *total = align_up(cv.off);
+  return QWEN3_OK;
+}
+
+int fill_model_shape(qwen3_model* m, const qwen3_config* cfg) {
+  m->cfg = *cfg;
+  m->cap.assign(cfg->h_seq_capacity, cfg->h_seq_capacity + cfg->max_seqs);
+  m->cfg.h_seq_capacity = nullptr;
+  m->R = cfg->max_batch_tokens > 0 ? cfg->max_batch_tokens : 1024;
+  m->nh = cfg->num_attention_heads;
+  m->nkv = cfg->num_key_value_heads;
+  m->hd = cfg->head_dim;
+  m->H = cfg->hidden_size;
+  m->F = cfg->intermediate_size;
+  m->V = cfg->vocab_size;
+  m->L = cfg->num_layers;
+  m->G = m->nh / m->nkv;
+  m->qw = m->nh * m->hd;
+  m->kvw = m->nkv * m->hd;
+  m->nqkv = m->qw + 2 * m->kvw;
+  m->kmax = std::max(m->H, std::max(m->qw, m->F));
+  m->wbf16 = cfg->weight_type == QWEN3_W_BF16;
+  m->kvbf16 = cfg->kv_type == QWEN3_KV_BF16;
+  m->max_cap = 0;
+  for (int c : m->cap) m->max_cap = std::max(m->max_cap, c);
+  return QWEN3_OK;
+}
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int repack(const void* src, QPlane& p, int64_t rows, int64_t row0, int inter, hipStream_t s) {
+  if (!src) return fail(QWEN3_E_INVALID_ARGUMENT, "a weight pointer is null");
+  HIP_TRY(q8k::repack_q8_0(src, rows, p.k, p.qs, p.sc, row0, inter, s));
+  return QWEN3_OK;
+}
+
+int copy_f32(float* dst, const void* src, int64_t n, hipStream_t s) {
+  if (!src) return fail(QWEN3_E_INVALID_ARGUMENT, "a norm weight pointer is null");
+  HIP_TRY(hipMemcpyAsync(dst, src, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+  return QWEN3_OK;
+}
+
+#define TRY(expr)           \
+  do {                      \
+    int r_ = (expr);        \
+    if (r_ != QWEN3_OK) return r_; \
+  } while (0)
+
+// ---- launch sequences -----------------------------------------------------------------
+
+GemvArgs gemv_args(const QPlane& p, const float* src, int64_t src_stride, const float* norm_w, float eps,
+                   float* out, int64_t out_stride) {
+  GemvArgs a{};
+  a.src = src;
+  a.src_stride = src_stride;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.qs = p.qs;
+  a.sc = p.sc;
+  a.N = (int)p.rows;
+  a.K = (int)p.k;
+  a.out = out;
+  a.out_stride = out_stride;
+  return a;
+}
+
+// Enqueue one decode step for nrows batch rows (rows r -> sequence row_seq[r],
+// token tok[r]); positions come from d_len on the device.
+int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_t* d_row_seq, float* d_logits,
+                   int32_t* d_argmax, hipStream_t s) {
+  const float eps = m->cfg.rms_norm_eps;
+  HIP_TRY(q8k::embed(d_tok, nrows, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+  AttnDecodeArgs at{};
+  at.qkv = m->qkv;
+  at.qkv_stride = m->nqkv;
+  at.eps = eps;
+  at.rope_cos = m->rope_cos;
+  at.rope_sin = m->rope_sin;
+  at.kv = m->kv;
+  at.seq_base = m->d_seq_base;
+  at.seq_cap = m->d_seq_cap;
+  at.len = m->d_len;
+  at.row_seq = d_row_seq;
+  at.part = m->attn_part;
+  at.counter = m->attn_cnt;
+  at.out = m->attn;
+  at.out_stride = m->qw;
+  at.nkv = m->nkv;
+  at.nsplit_max = decode_nsplit_max(m->nkv, nrows);
+  at.min_rows = 32;
+  at.scale = 1.0f / std::sqrt((float)m->hd);
+  for (int l = 0; l < m->L; ++l) {
+    const Layer& ly = m->layers[l];
+    HIP_TRY(q8k::gemv(gemv_args(ly.qkv, m->x, m->H, ly.attn_norm, eps, m->qkv, m->nqkv), true, EPI_STORE, nrows, s));
+    at.q_norm = ly.q_norm;
+    at.k_norm = ly.k_norm;
+    at.layer = l;
+    HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvbf16, nrows, s));
+    HIP_TRY(q8k::gemv(gemv_args(ly.o, m->attn, m->qw, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
+    HIP_TRY(q8k::gemv(gemv_args(ly.gateup, m->x, m->H, ly.ffn_norm, eps, m->h, m->F), true, EPI_SWIGLU, nrows, s));
+    HIP_TRY(q8k::gemv(gemv_args(ly.down, m->h, m->F, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
+  }
+  GemvArgs a = gemv_args(m->emb, m->x, m->H, m->out_norm, eps, nullptr, 0);
+  a.logits = d_logits;
+  a.part_v = m->am_part_v;
+  a.part_i = m->am_part_i;
+  a.counter = m->am_cnt;
+  a.argmax = d_argmax;
+  a.len_ptr = m->d_len;
+  a.len_seq = d_row_seq;
+  a.len_add = 1;
+  HIP_TRY(q8k::gemv(a, true, EPI_ARGMAX, nrows, s));
+  return QWEN3_OK;
+}
+
+// One prefill chunk: T tokens (already in m->d_tok) at positions pos0.. of seq.
+int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, float* d_logits, int32_t* d_argmax,
+                          hipStream_t s) {
+  const float eps = m->cfg.rms_norm_eps;
+  HIP_TRY(q8k::embed(m->d_tok, T, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+  const int64_t head_elems = (int64_t)m->cap[seq] * m->hd;
+  for (int l = 0; l < m->L; ++l) {
+    const Layer& ly = m->layers[l];
+    const int64_t kbase = m->seq_base[seq] + (int64_t)l * 2 * m->nkv * head_elems;
+    GemmArgs g{};
+    g.qa = m->qa;
+    g.da = m->da;
+    g.M = T;
+    // attention input: RMSNorm + quantise, fused QKV GEMM
+    HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
+    g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
+    HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+    QkRopeArgs qr{};
+    qr.qkv = m->qkv;
+    qr.qkv_stride = m->nqkv;
+    qr.q_norm = ly.q_norm;
+    qr.k_norm = ly.k_norm;
+    qr.eps = eps;
+    qr.rope_cos = m->rope_cos;
+    qr.rope_sin = m->rope_sin;
+    qr.q16 = m->q16;
+    qr.kv = m->kv;
+    qr.kbase = kbase;
+    qr.cap = m->cap[seq];
+    qr.pos0 = pos0;
+    qr.nh = m->nh;
+    qr.nkv = m->nkv;
+    HIP_TRY(q8k::qk_rope_append(qr, T, m->hd, m->kvbf16, s));
+    AttnPrefillArgs ap{};
+    ap.q16 = m->q16;
+    ap.kv = m->kv;
+    ap.kbase = kbase;
+    ap.cap = m->cap[seq];
+    ap.pos0 = pos0;
+    ap.T = T;
+    ap.nh = m->nh;
+    ap.nkv = m->nkv;
+    ap.scale = 1.0f / std::sqrt((float)m->hd);
+    ap.out = m->attn;
+    HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvbf16, s));
+    // o_proj + residual
+    HIP_TRY(q8k::rows_quant(m->attn, T, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
+    g.qs = ly.o.qs, g.sc = ly.o.sc, g.N = (int)ly.o.rows, g.K = m->qw, g.out = m->x, g.ldc = m->H;
+    HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
+    // FFN: RMSNorm + quantise, gate/up with SwiGLU, quantise, down + residual
+    HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s));
+    g.qs = ly.gateup.qs, g.sc = ly.gateup.sc, g.N = (int)ly.gateup.rows, g.K = m->H, g.out = m->h, g.ldc = m->F;
+    HIP_TRY(q8k::gemm(g, EPI_SWIGLU, s));
+    HIP_TRY(q8k::rows_quant(m->h, T, m->F, nullptr, eps, m->qa, m->da, nullptr, s));
+    g.qs = ly.down.qs, g.sc = ly.down.sc, g.N = (int)ly.down.rows, g.K = m->F, g.out = m->x, g.ldc = m->H;
+    HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
+  }
+  if (last && (d_logits || d_argmax)) {
+    GemvArgs a = gemv_args(m->emb, m->x + (int64_t)(T - 1) * m->H, m->H, m->out_norm, eps, nullptr, 0);
+    a.logits = d_logits;
+    a.part_v = m->am_part_v;
+    a.part_i = m->am_part_i;
+    a.counter = m->am_cnt;
+    a.argmax = d_argmax;
+    HIP_TRY(q8k::gemv(a, true, EPI_ARGMAX, 1, s));
+  }
+  HIP_TRY(q8k::set_len(m->d_len, seq, pos0 + T, s));
+  return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwen3_last_error(void) { return g_err.c_str(); }
+
+size_t qwen3_workspace_bytes(const qwen3_config* cfg) {
+  g_err.clear();
+  if (validate(cfg) != QWEN3_OK) return 0;
+  qwen3_model m;
+  fill_model_shape(&m, cfg);
+  size_t total = 0;
+  if (plan(&m, nullptr, &total) != QWEN3_OK) return 0;
+  return total;
+}
+
+int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_workspace, size_t workspace_bytes,
+                 void* stream, qwen3_t** out) {
+  g_err.clear();
+  if (!out) return fail(QWEN3_E_INVALID_ARGUMENT, "out is null");
+  *out = nullptr;
+  TRY(validate(cfg));
+  if (!w || !w->layers || !w->token_embd || !w->output_norm)
+    return fail(QWEN3_E_INVALID_ARGUMENT, "weights (or a pointer in it) is null");
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    const qwen3_layer_weights& ly = w->layers[l];
+    const void* ps[] = {ly.attn_norm, ly.attn_q, ly.attn_k, ly.attn_v, ly.attn_output, ly.attn_q_norm,
+                        ly.attn_k_norm, ly.ffn_norm, ly.ffn_gate, ly.ffn_up, ly.ffn_down};
+    for (const void* p : ps)
+      if (!p) return fail(QWEN3_E_INVALID_ARGUMENT, "layer " + std::to_string(l) + " has a null weight pointer");
+  }
+  if (!d_workspace) return fail(QWEN3_E_INVALID_ARGUMENT, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign)
+    return fail(QWEN3_E_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  auto* m = new qwen3_model();
+  fill_model_shape(m, cfg);
+  size_t need = 0;
+  int rc = plan(m, nullptr, &need);
+  if (rc != QWEN3_OK) {
+    delete m;
+    return rc;
+  }
+  if (workspace_bytes < need) {
+    delete m;
+    return fail(QWEN3_E_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " + std::to_string(need));
+  }
+  plan(m, static_cast<uint8_t*>(d_workspace), &need);
+  m->bytes = need;
+  hipStream_t s = S(stream);
+  auto body = [&]() -> int {
+    const int64_t H = m->H, F = m->F, hd = m->hd;
+    TRY(repack(w->token_embd, m->emb, m->V, 0, -1, s));
+    TRY(copy_f32(m->out_norm, w->output_norm, H, s));
+    for (int l = 0; l < m->L; ++l) {
+      const qwen3_layer_weights& src = w->layers[l];
+      Layer& ly = m->layers[l];
+      TRY(repack(src.attn_q, ly.qkv, m->qw, 0, -1, s));
+      TRY(repack(src.attn_k, ly.qkv, m->kvw, m->qw, -1, s));
+      TRY(repack(src.attn_v, ly.qkv, m->kvw, m->qw + m->kvw, -1, s));
+      TRY(repack(src.attn_output, ly.o, H, 0, -1, s));
+      TRY(repack(src.ffn_gate, ly.gateup, F, 0, 0, s));
+      TRY(repack(src.ffn_up, ly.gateup, F, 0, 32, s));
+      TRY(repack(src.ffn_down, ly.down, H, 0, -1, s));
+      TRY(copy_f32(ly.attn_norm, src.attn_norm, H, s));
+      TRY(copy_f32(ly.q_norm, src.attn_q_norm, hd, s));
+      TRY(copy_f32(ly.k_norm, src.attn_k_norm, hd, s));
+      TRY(copy_f32(ly.ffn_norm, src.ffn_norm, H, s));
+    }
+    // RoPE table: angle(p, i) = p * theta^(-2i/hd) in f64, stored as f32 cos/sin
+    const int half = m->hd / 2;
+    std::vector<float> cs((size_t)m->max_cap * half), sn((size_t)m->max_cap * half);
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)m->cfg.rope_theta, -2.0 * i / (double)m->hd);
+      for (int p = 0; p < m->max_cap; ++p) {
+        const double ang = (double)p * inv;
+        cs[(size_t)p * half + i] = (float)std::cos(ang);
+        sn[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    }
+    HIP_TRY(hipMemcpyAsync(m->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(m->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(m->d_seq_base, m->seq_base.data(), m->seq_base.size() * 8, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(m->d_seq_cap, m->cap.data(), m->cap.size() * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemsetAsync(m->d_len, 0, m->cap.size() * 4, s));
+    {
+      std::vector<int32_t> ids(m->cap.size());
+      for (size_t i = 0; i < ids.size(); ++i) ids[i] = (int32_t)i;
+      HIP_TRY(hipMemcpyAsync(m->d_seq_ids, ids.data(), ids.size() * 4, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));  // ids is a host temporary
+    }
+    HIP_TRY(hipMemsetAsync(m->attn_cnt, 0, (size_t)m->R * m->nkv * 4, s));
+    HIP_TRY(hipMemsetAsync(m->am_cnt, 0, (size_t)m->R * 4, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+    return QWEN3_OK;
+  };
+  rc = body();
+  if (rc != QWEN3_OK) {
+    delete m;
+    return rc;
+  }
+  m->h_len.assign(m->cap.size(), 0);
+  const char* ng = std::getenv("QWEN3_NO_GRAPH");
+  m->use_graphs = !(ng && ng[0] == '1');
+  *out = m;
+  return QWEN3_OK;
+}
+
+void qwen3_destroy(qwen3_t* m) {
+  if (!m) return;
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+int qwen3_kv_len(const qwen3_t* m, int32_t seq, int32_t* out) {
+  if (!m || !out) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  *out = m->h_len[seq];
+  return QWEN3_OK;
+}
+
+int qwen3_reset(qwen3_t* m, int32_t seq, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  HIP_TRY(q8k::set_len(m->d_len, seq, 0, S(stream)));
+  m->h_len[seq] = 0;
+  return QWEN3_OK;
+}
+
+int qwen3_prefill(qwen3_t* m, int32_t seq, const int32_t* h_tokens, int32_t n, float* d_logits, int32_t* d_argmax,
+                  void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (n <= 0) return fail(QWEN3_E_INVALID_SEQUENCE_LENGTH, "prefill needs n >= 1 tokens");
+  if (!h_tokens) return fail(QWEN3_E_INVALID_ARGUMENT, "h_tokens is null");
+  const int len = m->h_len[seq];
+  if ((int64_t)len + n > m->cap[seq])
+    return fail(QWEN3_E_KV_CACHE_OVERFLOW, "len " + std::to_string(len) + " + " + std::to_string(n) +
+                                               " exceeds capacity " + std::to_string(m->cap[seq]));
+  for (int i = 0; i < n; ++i)
+    if (h_tokens[i] < 0 || h_tokens[i] >= m->V)
+      return fail(QWEN3_E_TOKEN_OUT_OF_RANGE, "token " + std::to_string(i) + " = " + std::to_string(h_tokens[i]) +
+                                                  " outside [0, vocab)");
+  hipStream_t s = S(stream);
+  for (int c0 = 0; c0 < n; c0 += m->R) {
+    const int T = std::min(m->R, n - c0);
+    HIP_TRY(hipMemcpyAsync(m->d_tok, h_tokens + c0, (size_t)T * 4, hipMemcpyHostToDevice, s));
+    TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits, d_argmax, s));
+  }
+  m->h_len[seq] = len + n;
+  return QWEN3_OK;
+}
+
+int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_logits, int32_t* d_argmax,
+                      void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (!d_token || !d_argmax) return fail(QWEN3_E_INVALID_ARGUMENT, "d_token and d_argmax are required");
+  if (m->h_len[seq] + 1 > m->cap[seq])
+    return fail(QWEN3_E_KV_CACHE_OVERFLOW, "decode at len " + std::to_string(m->h_len[seq]) + " exceeds capacity");
+  hipStream_t s = S(stream);
+  if (!m->use_graphs) {
+    TRY(enqueue_decode(m, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, s));
+    m->h_len[seq] += 1;
+    return QWEN3_OK;
+  }
+  auto key = std::make_tuple((int)seq, (const void*)d_token, (const void*)d_logits, (const void*)d_argmax);
+  auto it = m->graphs.find(key);
+  if (it == m->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue_decode(m, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, m->cap_stream);
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
+    if (rc != QWEN3_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph capture: ") + hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
+    it = m->graphs.emplace(key, exec).first;
+  }
+  HIP_TRY(hipGraphLaunch(it->second, s));
+  m->h_len[seq] += 1;
+  return QWEN3_OK;
+}
+
+int qwen3_decode_batch(qwen3_t* m, const int32_t* h_seqs, int32_t n, const int32_t* d_tokens, float* d_logits,
+                       int32_t* d_argmax, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (n <= 0) return fail(QWEN3_E_INVALID_SEQUENCE_LENGTH, "batch needs n >= 1");
+  if (n > m->R) return fail(QWEN3_E_INVALID_ARGUMENT, "batch larger than max_batch_tokens");
+  if (!h_seqs || !d_tokens || !d_argmax) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  std::vector<char> seen(m->h_len.size(), 0);
+  for (int i = 0; i < n; ++i) {
+    const int sq = h_seqs[i];
+    if (sq < 0 || sq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+    if (seen[sq]) return fail(QWEN3_E_INVALID_ARGUMENT, "a sequence appears twice in one batch");
+    seen[sq] = 1;
+    if (m->h_len[sq] + 1 > m->cap[sq]) return fail(QWEN3_E_KV_CACHE_OVERFLOW, "a sequence is at capacity");
+  }
+  hipStream_t s = S(stream);
+  HIP_TRY(hipMemcpyAsync(m->d_row_seq, h_seqs, (size_t)n * 4, hipMemcpyHostToDevice, s));
+  TRY(enqueue_decode(m, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
+  for (int i = 0; i < n; ++i) m->h_len[h_seqs[i]] += 1;
+  return QWEN3_OK;
+}
+
+// ---- op-level entry points ---------------------------------------------------------------
+
+int qwen3_q8_0_encode(const float* d_x, int64_t n, void* d_blocks, void* stream) {
+  g_err.clear();
+  if (n < 0 || n % 32) return fail(QWEN3_E_INVALID_ARGUMENT, "n must be a non-negative multiple of 32");
+  if (n && (!d_x || !d_blocks)) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  HIP_TRY(q8k::encode_q8_0(d_x, n, d_blocks, S(stream)));
+  return QWEN3_OK;
+}
+
+int qwen3_bf16_encode(const float* d_x, int64_t n, uint16_t* d_out, void* stream) {
+  g_err.clear();
+  if (n < 0) return fail(QWEN3_E_INVALID_ARGUMENT, "n must be >= 0");
+  if (n && (!d_x || !d_out)) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  HIP_TRY(q8k::encode_bf16(d_x, n, d_out, S(stream)));
+  return QWEN3_OK;
+}
+
+int qwen3_q8_0_repack(const void* d_blocks, int64_t rows, int64_t k, int8_t* d_qs, uint16_t* d_scale, void* stream) {
+  g_err.clear();
+  if (rows < 0 || k <= 0 || k % 32) return fail(QWEN3_E_INVALID_ARGUMENT, "k must be a positive multiple of 32");
+  if (rows && (!d_blocks || !d_qs || !d_scale)) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  HIP_TRY(q8k::repack_q8_0(d_blocks, rows, k, d_qs, d_scale, 0, -1, S(stream)));
+  return QWEN3_OK;
+}
+
+size_t qwen3_linear_work_bytes(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0) return 0;
+  return align_up((size_t)(m * k)) + align_up((size_t)(m * (k / 32)) * 4) + 4096;
+}
+
+int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs, const uint16_t* d_scale, int64_t n,
+                      float* d_y, void* d_work, void* stream) {
+  g_err.clear();
+  if (m <= 0 || n <= 0 || k <= 0) return fail(QWEN3_E_INVALID_ARGUMENT, "m, n, k must be positive");
+  if (!d_x || !d_qs || !d_scale || !d_y) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  if (k % 128 || !q8k::gemv_supported_k((int)k)) return fail(QWEN3_E_INVALID_ARGUMENT, "unsupported k");
+  if (m > 1 && !d_work) return fail(QWEN3_E_INVALID_ARGUMENT, "d_work is required for m > 1");
+  if (m > INT32_MAX || n > INT32_MAX) return fail(QWEN3_E_INVALID_ARGUMENT, "size too large");
+  hipStream_t s = S(stream);
+  if (m == 1) {
+    QPlane p;
+    p.qs = const_cast<int8_t*>(d_qs);
+    p.sc = const_cast<uint16_t*>(d_scale);
+    p.rows = n;
+    p.k = k;
+    HIP_TRY(q8k::gemv(gemv_args(p, d_x, k, nullptr, 1e-6f, d_y, n), false, EPI_STORE, 1, s));
+    return QWEN3_OK;
+  }
+  int8_t* qa = static_cast<int8_t*>(d_work);
+  float* da = reinterpret_cast<float*>(static_cast<uint8_t*>(d_work) + align_up((size_t)(m * k)));
+  HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, qa, da, nullptr, s));
+  GemmArgs g{};
+  g.qa = qa;
+  g.da = da;
+  g.qs = d_qs;
+  g.sc = d_scale;
+  g.M = (int)m;
+  g.N = (int)n;
+  g.K = (int)k;
+  g.out = d_y;
+  g.ldc = n;
+  HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+  return QWEN3_OK;
+}
+
+int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs, int64_t n, int8_t* d_qa,
+                          uint16_t* d_da, int32_t* d_s, void* stream) {
+  g_err.clear();
+  if (m <= 0 || n <= 0 || k <= 0 || k % 32) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sizes");
+  if (!d_x || !d_qs || !d_qa || !d_da || !d_s) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return fail(QWEN3_E_INVALID_ARGUMENT, "size too large");
+  hipStream_t s = S(stream);
+  HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, d_qa, nullptr, d_da, s));
+  HIP_TRY(q8k::block_dots(d_qa, d_qs, (int)m, (int)k, (int)n, d_s, s));
+  return QWEN3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+sizes workspaces, and rejects bad arguments on the host before any launch.
+No compute call is made (there is no GPU here)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from quantized_q8_dequant_amd import _lib
+from quantized_q8_dequant_amd.model import Qwen3Config, workspace_bytes
+from synthetic import QWEN3_0_6B, QWEN3_8B, TINY
+
+HEADER = os.path.join(ROOT, "include", "qwen3_q8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwen3_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = _lib.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def _cfg(shape, **kw):
+    c = Qwen3Config.from_shape(shape)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes_cover_weights_and_cache():
+    s = QWEN3_0_6B
+    n = workspace_bytes(_cfg(s), [768])
+    per_layer = (s.q_width + 2 * s.kv_width) * s.hidden_size + s.hidden_size * s.q_width
+    per_layer += 3 * s.intermediate_size * s.hidden_size
+    q8 = (per_layer * s.num_layers + s.vocab_size * s.hidden_size) * 34 // 32
+    kv = 768 * s.num_layers * 2 * s.kv_width * 4
+    assert n >= q8 + kv
+    assert n < (q8 + kv) * 1.5
+    # a bf16 cache halves the KV part
+    n2 = workspace_bytes(_cfg(s, kv_type="bf16"), [768])
+    assert n - n2 >= kv // 2 - 1024 * 1024
+    # 8B at 32k context fits easily in 288 GB
+    assert workspace_bytes(_cfg(QWEN3_8B), [32776]) < 20e9
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(num_key_value_heads=3), -2),
+        (dict(head_dim=65), -2),
+        (dict(head_dim=96), -2),
+        (dict(hidden_size=0), -2),
+        (dict(intermediate_size=700), -2),
+        (dict(rms_norm_eps=0.0), -2),
+        (dict(rope_theta=1.0), -2),
+        (dict(weight_type="q4_k"), -4),
+        (dict(kv_type="f16"), -4),
+    ],
+)
+def test_invalid_configs_rejected(kw, code):
+    c, keep = _cfg(TINY, **kw).to_c([64], 0)
+    assert _lib.lib().qwen3_workspace_bytes(C.byref(c)) == 0
+    assert _lib.last_error()
+    h = C.c_void_p()
+    w = _lib.Weights(None, None, None)
+    rc = _lib.lib().qwen3_create(C.byref(c), C.byref(w), None, 0, None, C.byref(h))
+    assert rc == code, _lib.last_error()
+    assert not h.value
+
+
+def test_bad_capacity_rejected():
+    c, keep = _cfg(TINY).to_c([64, 0], 0)
+    assert _lib.lib().qwen3_workspace_bytes(C.byref(c)) == 0
+
+
+def _fake_weights(L):
+    layers = (_lib.LayerWeights * L)()
+    for i in range(L):
+        for f in _lib.LAYER_FIELDS:
+            setattr(layers[i], f, 0x1000)
+    return _lib.Weights(0x1000, 0x1000, layers), layers
+
+
+def test_create_argument_errors_before_any_launch():
+    lib = _lib.lib()
+    c, keep = _cfg(TINY).to_c([64], 0)
+    w, layers = _fake_weights(TINY.num_layers)
+    h = C.c_void_p()
+    need = lib.qwen3_workspace_bytes(C.byref(c))
+    # null workspace
+    assert lib.qwen3_create(C.byref(c), C.byref(w), None, need, None, C.byref(h)) == -1
+    # misaligned workspace
+    assert lib.qwen3_create(C.byref(c), C.byref(w), 0x100010, need, None, C.byref(h)) == -1
+    # too small
+    assert lib.qwen3_create(C.byref(c), C.byref(w), 0x100000, need - 1, None, C.byref(h)) == -5
+    assert "needs" in _lib.last_error()
+    # a null layer pointer
+    layers[1].ffn_up = None
+    assert lib.qwen3_create(C.byref(c), C.byref(w), 0x100000, need, None, C.byref(h)) == -1
+    assert "layer 1" in _lib.last_error()
+    assert not h.value
+
+
+def test_null_handle_and_op_argument_errors():
+    lib = _lib.lib()
+    toks = (C.c_int32 * 2)(1, 2)
+    assert lib.qwen3_prefill(None, 0, toks, 2, None, None, None) == -1
+    assert lib.qwen3_decode_step(None, 0, None, None, None, None) == -1
+    assert lib.qwen3_reset(None, 0, None) == -1
+    out = C.c_int32()
+    assert lib.qwen3_kv_len(None, 0, C.byref(out)) == -1
+    assert lib.qwen3_q8_0_encode(0x1000, 33, 0x2000, None) == -1
+    assert lib.qwen3_q8_0_repack(0x1000, 4, 48, 0x2000, 0x3000, None) == -1
+    assert lib.qwen3_q8_0_linear(0x1000, 1, 100, 0x2000, 0x3000, 8, 0x4000, None, None) == -1
+    assert lib.qwen3_q8_0_linear(0x1000, 2, 1024, 0x2000, 0x3000, 8, 0x4000, None, None) == -1
+    assert lib.qwen3_q8_0_block_dots(0x1000, 1, 48, 0x2000, 4, 0x3000, 0x4000, 0x5000, None) == -1
+    assert lib.qwen3_linear_work_bytes(4, 1024) >= 4 * 1024 + 4 * 32 * 4
+    # encoding zero values enqueues nothing
+    assert lib.qwen3_q8_0_encode(None, 0, None, None) == 0

@@ -1,0 +1,105 @@
+"""Kernel-boundary parity of the HIP library against the CPU oracle.
+
+Bit-exact: the Q8_0 encoder (codes and f16 scales), the repack, the
+activation quantisation inside the linears and every integer block dot.
+Within f32 summation error: the Q8_0 linear (GEMV for one row, MFMA GEMM
+for several), whose block terms the GPU sums in a different f32 order than
+the oracle's exact-then-rounded sum.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import q8_0 as oq
+from synthetic import gen_normal_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _special_rows(k):
+    rows = [np.zeros(k, np.float32)]
+    spike = np.zeros(k, np.float32)
+    spike[5] = 3.25
+    spike[k - 1] = -1e-3
+    rows.append(spike)
+    ties = np.zeros(k, np.float32)
+    ties[:11] = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5, -1.5, 126.5, -126.5]
+    rows.append(ties)
+    tiny = np.full(k, 1e-30, np.float32)  # subnormal-range scale -> f16 flush
+    rows.append(tiny)
+    big = gen_normal_rows((k,), seed=77, scale=1e4)
+    rows.append(big)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("k", [256, 1024, 3072])
+def test_encode_bit_exact(k):
+    from quantized_q8_dequant_amd import encode_q8_0
+
+    x = np.concatenate([gen_normal_rows((300, k), seed=k, scale=0.02), _special_rows(k)])
+    got = encode_q8_0(torch.from_numpy(x).to(DEV)).cpu().numpy()
+    want = oq.to_gguf(*oq.encode(x))
+    assert got.shape == want.shape
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:5]}"
+
+
+def test_repack_round_trip():
+    from quantized_q8_dequant_amd import encode_q8_0, repack_q8_0
+
+    x = gen_normal_rows((77, 768), seed=5, scale=0.02)
+    blocks = encode_q8_0(torch.from_numpy(x).to(DEV))
+    qs, sc = repack_q8_0(blocks, 77, 768)
+    wq, wd = oq.encode(x)
+    assert np.array_equal(qs.cpu().numpy(), wq)
+    assert np.array_equal(sc.cpu().numpy().view(np.float16), wd)
+
+
+def _weights(n, k, seed):
+    from quantized_q8_dequant_amd import encode_q8_0, repack_q8_0
+
+    w = gen_normal_rows((n, k), seed=seed, scale=0.02)
+    qs, sc = repack_q8_0(encode_q8_0(torch.from_numpy(w).to(DEV)), n, k)
+    return w, oq.Q8Weight(w), qs, sc
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 256, 64), (3, 1024, 96), (2, 3072, 40), (5, 768, 33)])
+def test_block_dots_bit_exact(m, k, n):
+    from quantized_q8_dequant_amd import q8_0_block_dots
+
+    x = gen_normal_rows((m, k), seed=m * 1000 + k, scale=1.3)
+    _, ow, qs, _ = _weights(n, k, seed=k + n)
+    qa, da, S = q8_0_block_dots(torch.from_numpy(x).to(DEV), qs)
+    oqa, oda = oq.encode(x)
+    assert np.array_equal(qa.cpu().numpy(), oqa)
+    assert np.array_equal(da.cpu().numpy().view(np.float16), oda)
+    assert np.array_equal(S.cpu().numpy().astype(np.int64), oq.block_dots(oqa, ow.qs))
+
+
+def _linear_bound(x, ow):
+    """|f32 result - exact| bound: every block term and partial sum rounded."""
+    qa, da = oq.encode(x)
+    S = oq.block_dots(qa, ow.qs).astype(np.float64)
+    terms = np.abs(S * ow.d.astype(np.float64)[None] * da.astype(np.float64)[:, None, :])
+    nb = ow.K // 32
+    return (2 * nb + 4) * 2.0**-24 * terms.sum(axis=2) + 1e-30
+
+
+@pytest.mark.parametrize(
+    "m,k,n",
+    [(1, 1024, 4096), (1, 3072, 1024), (1, 2048, 1024), (1, 256, 512), (1, 768, 256), (1, 4096, 384),
+     (1, 12288, 256), (2, 1024, 256), (7, 1024, 256), (128, 1024, 512), (300, 3072, 384), (129, 256, 128)],
+)
+def test_linear_matches_oracle(m, k, n):
+    from quantized_q8_dequant_amd import q8_0_linear
+
+    x = gen_normal_rows((m, k), seed=7 * m + k, scale=1.0)
+    _, ow, qs, sc = _weights(n, k, seed=3 * k + n)
+    y = q8_0_linear(torch.from_numpy(x).to(DEV), qs, sc).cpu().numpy().astype(np.float64)
+    ref = oq.linear(x, ow).astype(np.float64)
+    bound = _linear_bound(x, ow)
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
