@@ -14,11 +14,12 @@ def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
 
     ("A transformer from scratch", section 12.3.2; the same form serves the
     per-head Q/K norm over head_dim, minfer "Qwen3 Support Plan" section 2.2.)
-    Parity: pinned (mean(y^2) closed form, grouping equivalence).
+    eps is a config field stored as f32 (section 12.1), so its f32 value is
+    used.  Parity: pinned (mean(y^2) closed form, grouping equivalence).
     """
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     ms = np.mean(x64 * x64, axis=-1, keepdims=True)
-    r = 1.0 / np.sqrt(ms + eps)
+    r = 1.0 / np.sqrt(ms + float(np.float32(eps)))
     return (x64 * r * np.asarray(w, dtype=np.float32).astype(np.float64)).astype(np.float32)
 
 
