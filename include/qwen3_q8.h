@@ -176,6 +176,12 @@ int qwen3_reset(qwen3_t* h, int32_t seq, void* stream);
 /* Host-side KV length of `seq` (counts every enqueued append). */
 int qwen3_kv_len(const qwen3_t* h, int32_t seq, int32_t* out);
 
+/* Copy layer `layer` of sequence `seq`'s KV cache, positions [0, len), to
+ * d_k and d_v, each f32 [kv_heads, len, head_dim] (bf16 caches are widened
+ * exactly).  K rows are post-RoPE, V rows raw ("A transformer from scratch",
+ * section 12.4).  Enqueued on `stream`; len is the host-side length. */
+int qwen3_kv_export(const qwen3_t* h, int32_t seq, int32_t layer, float* d_k, float* d_v, void* stream);
+
 /* Thread-local description of the last error ("" if none). */
 const char* qwen3_last_error(void);
 

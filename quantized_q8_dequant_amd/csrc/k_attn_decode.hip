@@ -37,13 +37,14 @@ QDEV float load_kv(const void* base, int64_t idx) {
 
 template <int HD, int G, bool BF16>
 __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
-  __shared__ float s_q[G][HD];
+  __shared__ float s_qf[G][HD];
+  __shared__ double s_q[G][HD];
   __shared__ float s_knew[HD];
   __shared__ float s_vnew[HD];
   __shared__ float s_k[TJ][HD + 1];
   __shared__ float s_v[TJ][HD];
-  __shared__ float s_p[G][TJ];
-  __shared__ float s_alpha[G];
+  __shared__ double s_p[G][TJ];
+  __shared__ double s_alpha[G];
   __shared__ int s_last;
 
   const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
@@ -65,11 +66,11 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   const int64_t vbase = kbase + (int64_t)nkv * head_elems;
   const float* qkv = a.qkv + (int64_t)row * a.qkv_stride;
   const int nh = nkv * G;
-  const float* cs = a.rope_cos + (int64_t)p * (HD / 2);
-  const float* sn = a.rope_sin + (int64_t)p * (HD / 2);
+  const double* cs = a.rope_cos + (int64_t)p * (HD / 2);
+  const double* sn = a.rope_sin + (int64_t)p * (HD / 2);
 
   // stage raw q (G heads), and the new k / v of head g
-  for (int e = threadIdx.x; e < G * HD; e += kThreads) s_q[e / HD][e % HD] = qkv[(int64_t)(g * G) * HD + e];
+  for (int e = threadIdx.x; e < G * HD; e += kThreads) s_qf[e / HD][e % HD] = qkv[(int64_t)(g * G) * HD + e];
   const bool has_new = j1 == ctx;  // this split holds position p
   if (has_new) {
     for (int d = threadIdx.x; d < HD; d += kThreads) {
@@ -78,9 +79,10 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int h = wave; h < G; h += kWaves) norm_rope_wave<HD>(s_q[h], a.q_norm, a.eps, cs, sn, a.scale);
-  if (has_new && wave == kWaves - 1) norm_rope_wave<HD>(s_knew, a.k_norm, a.eps, cs, sn, 1.0f);
+  for (int h = wave; h < G; h += kWaves) norm_rope_wave<HD>(s_qf[h], a.q_norm, a.eps, cs, sn);
+  if (has_new && wave == kWaves - 1) norm_rope_wave<HD>(s_knew, a.k_norm, a.eps, cs, sn);
   __syncthreads();
+  for (int e = threadIdx.x; e < G * HD; e += kThreads) s_q[e / HD][e % HD] = (double)s_qf[e / HD][e % HD];
   if (has_new) {
     // append: the cache stores post-RoPE K and raw V (bf16 caches round here,
     // and the rounded values are the ones attended below)
@@ -97,19 +99,20 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
         reinterpret_cast<float*>(a.kv)[vi] = s_vnew[d];
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // online softmax state: wave h (< G) owns head h's (m, l); outputs are
+  // online softmax in f64: wave h (< G) owns head h's (m, l); outputs are
   // spread over threads as e = tid + 256*i -> (head e / HD, dim e % HD)
   constexpr int OUT_PER_T = (G * HD + kThreads - 1) / kThreads;
-  float o[OUT_PER_T];
+  double o[OUT_PER_T];
 #pragma unroll
-  for (int i = 0; i < OUT_PER_T; ++i) o[i] = 0.f;
+  for (int i = 0; i < OUT_PER_T; ++i) o[i] = 0.0;
   constexpr int HPW = (G + kWaves - 1) / kWaves;  // heads per wavefront
-  float m_run[HPW], l_run[HPW];  // head wave + kWaves*i, held by that wavefront
+  double m_run[HPW], l_run[HPW];  // head wave + kWaves*i, held by that wavefront
 #pragma unroll
-  for (int i = 0; i < HPW; ++i) m_run[i] = -INFINITY, l_run[i] = 0.f;
+  for (int i = 0; i < HPW; ++i) m_run[i] = -INFINITY, l_run[i] = 0.0;
+  const double scale = a.scale;
 
   for (int t0 = j0; t0 < j1; t0 += TJ) {
     const int nrow = min(TJ, j1 - t0);
@@ -131,14 +134,15 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
       s_v[r][d] = kv_v;
     }
     __syncthreads();
-    // scores: thread -> (row r = tid % TJ, head h = tid / TJ)
+    // scores (f64): thread -> (row r = tid % TJ, head h = tid / TJ)
     for (int e = threadIdx.x; e < G * TJ; e += kThreads) {
       const int r = e % TJ, h = e / TJ;
-      float s = -INFINITY;
+      double s = -INFINITY;
       if (r < nrow) {
-        s = 0.f;
+        s = 0.0;
 #pragma unroll 8
-        for (int d = 0; d < HD; ++d) s += s_q[h][d] * s_k[r][d];
+        for (int d = 0; d < HD; ++d) s += s_q[h][d] * (double)s_k[r][d];
+        s *= scale;
       }
       s_p[h][r] = s;
     }
@@ -148,12 +152,12 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     for (int i = 0; i < HPW; ++i) {
       const int h = wave + i * kWaves;
       if (h < G) {
-        const float s = s_p[h][lane];
-        const float mt = wave_max<kWave>(s);
-        const float m_new = fmaxf(m_run[i], mt);
-        const float pr = (s == -INFINITY) ? 0.f : expf(s - m_new);
-        const float lt = wave_sum<kWave>(pr);
-        const float alpha = (m_run[i] == -INFINITY) ? 0.f : expf(m_run[i] - m_new);
+        const double s = s_p[h][lane];
+        const double mt = wave_max_d<kWave>(s);
+        const double m_new = fmax(m_run[i], mt);
+        const double pr = (s == -INFINITY) ? 0.0 : exp(s - m_new);
+        const double lt = wave_sum_d<kWave>(pr);
+        const double alpha = (m_run[i] == -INFINITY) ? 0.0 : exp(m_run[i] - m_new);
         l_run[i] = l_run[i] * alpha + lt;
         m_run[i] = m_new;
         s_p[h][lane] = pr;
@@ -166,8 +170,8 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
       const int e = threadIdx.x + i * kThreads;
       if (e < G * HD) {
         const int h = e / HD, d = e % HD;
-        float acc = o[i] * s_alpha[h];
-        for (int r = 0; r < nrow; ++r) acc += s_p[h][r] * s_v[r][d];
+        double acc = o[i] * s_alpha[h];
+        for (int r = 0; r < nrow; ++r) acc += s_p[h][r] * (double)s_v[r][d];
         o[i] = acc;
       }
     }
@@ -176,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
 
   // write this split's partial: [row][g][split][h][0..HD-1] = o, [HD] = m, [HD+1] = l
   const int64_t pstride = (int64_t)G * (HD + 2);
-  float* part = a.part + (((int64_t)row * nkv + g) * a.nsplit_max + split) * pstride;
+  double* part = a.part + (((int64_t)row * nkv + g) * a.nsplit_max + split) * pstride;
 #pragma unroll
   for (int i = 0; i < OUT_PER_T; ++i) {
     const int e = threadIdx.x + i * kThreads;
@@ -201,23 +205,23 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  // merge the nsplit partials of the G heads
-  const float* pb = a.part + (((int64_t)row * nkv + g) * a.nsplit_max) * pstride;
+  // merge the nsplit partials of the G heads (f64), round once to f32
+  const double* pb = a.part + (((int64_t)row * nkv + g) * a.nsplit_max) * pstride;
   for (int e = threadIdx.x; e < G * HD; e += kThreads) {
     const int h = e / HD, d = e % HD;
-    float M = -INFINITY;
+    double M = -INFINITY;
     for (int sidx = 0; sidx < nsplit; ++sidx)
-      M = fmaxf(M, __builtin_nontemporal_load(pb + sidx * pstride + h * (HD + 2) + HD));
-    float L = 0.f, O = 0.f;
+      M = fmax(M, __builtin_nontemporal_load(pb + sidx * pstride + h * (HD + 2) + HD));
+    double L = 0.0, O = 0.0;
     for (int sidx = 0; sidx < nsplit; ++sidx) {
-      const float* ps = pb + sidx * pstride + h * (HD + 2);
-      const float ms = __builtin_nontemporal_load(ps + HD);
+      const double* ps = pb + sidx * pstride + h * (HD + 2);
+      const double ms = __builtin_nontemporal_load(ps + HD);
       if (ms == -INFINITY) continue;
-      const float wgt = expf(ms - M);
+      const double wgt = exp(ms - M);
       L += __builtin_nontemporal_load(ps + HD + 1) * wgt;
       O += __builtin_nontemporal_load(ps + d) * wgt;
     }
-    a.out[(int64_t)row * a.out_stride + (int64_t)(g * G + h) * HD + d] = O / L;
+    a.out[(int64_t)row * a.out_stride + (int64_t)(g * G + h) * HD + d] = (float)(O / L);
   }
 }
 

@@ -1,20 +1,25 @@
 // Prefill attention path for gfx950.
 //
 // k_qk_rope_append: per (token, head) -- per-head RMSNorm of q and k, NeoX
-// RoPE at the token's absolute position, q written as f16 for the MFMA
+// RoPE at the token's absolute position, q written (f32) for the MFMA
 // kernel, post-RoPE k and raw v appended to the KV cache (Fucina course, "A
 // transformer from scratch", sections 12.3.2, 12.3.4, 12.4; minfer "Qwen3
 // Support Plan", section 2.2).
 //
 // k_attn_prefill: causal grouped-query flash attention (section 12.3.5) on
-// f16 MFMA (v_mfma_f32_32x32x16_f16) with an f32 online softmax.  A
-// wavefront owns 32 queries of one head and computes S^T = K Q^T, so its
-// accumulator holds the scores of ONE query per lane (lane % 32) over 16 keys;
-// the row max / sum need a single exchange with lane ^ 32, and the
-// probabilities are already in the B-operand layout of O^T = V^T P^T (the
-// V tile is staged transposed in LDS with the matching key order).  The
-// workgroup's waves share one KV head, so a K/V tile staged in LDS serves
-// all of its query heads.
+// f64 MFMA (v_mfma_f64_16x16x4_f64) with an f64 online softmax; the output
+// is rounded to f32 once.  The attention output is quantised to Q8_0 right
+// after, so it must round exactly like a reference that reduces in f64: an
+// f32-accurate attention flips a share of those codes and moves the logits
+// by several 1e-3 of their range.  (On gfx950 the f64 matrix and vector
+// rates are equal, so MFMA is used for its register-fed operands.)
+//
+// A wavefront owns 16 queries of one head and computes S^T = K Q^T: lane
+// (g = lane/16, q = lane%16) then holds the scores of query q for keys
+// 4*item + g, so the row max / sum need two lane exchanges and each item is
+// already the B operand of one O^T += V^T P^T step (keys 4*item .. +3).  The
+// workgroup's waves share one KV head, so a K/V tile staged in LDS serves all
+// of its query heads.
 #include "kernels.h"
 #include "qdevice.h"
 
@@ -22,9 +27,7 @@ using namespace q8;
 
 namespace {
 
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <bool BF16>
 QDEV float ld_kv(const void* base, int64_t idx) {
@@ -38,19 +41,19 @@ __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
   const int t = blockIdx.x, h = blockIdx.y;
   const int pos = a.pos0 + t;
   const float* row = a.qkv + (int64_t)t * a.qkv_stride;
-  const float* cs = a.rope_cos + (int64_t)pos * (HD / 2);
-  const float* sn = a.rope_sin + (int64_t)pos * (HD / 2);
+  const double* cs = a.rope_cos + (int64_t)pos * (HD / 2);
+  const double* sn = a.rope_sin + (int64_t)pos * (HD / 2);
   if (h < a.nh) {
     for (int d = threadIdx.x; d < HD; d += 64) x[d] = row[(int64_t)h * HD + d];
     __syncthreads();
-    norm_rope_wave<HD>(x, a.q_norm, a.eps, cs, sn, 1.0f);
+    norm_rope_wave<HD>(x, a.q_norm, a.eps, cs, sn);
     __syncthreads();
-    for (int d = threadIdx.x; d < HD; d += 64) a.q16[((int64_t)t * a.nh + h) * HD + d] = (_Float16)x[d];
+    for (int d = threadIdx.x; d < HD; d += 64) a.q32[((int64_t)t * a.nh + h) * HD + d] = x[d];
   } else {
     const int g = h - a.nh;
     for (int d = threadIdx.x; d < HD; d += 64) x[d] = row[(int64_t)(a.nh + g) * HD + d];
     __syncthreads();
-    norm_rope_wave<HD>(x, a.k_norm, a.eps, cs, sn, 1.0f);
+    norm_rope_wave<HD>(x, a.k_norm, a.eps, cs, sn);
     __syncthreads();
     const int64_t head_elems = (int64_t)a.cap * HD;
     const int64_t kb = a.kbase + g * head_elems + (int64_t)pos * HD;
@@ -73,43 +76,41 @@ constexpr int KT = 64;  // keys per LDS tile
 template <int HD, int G, bool BF16>
 __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   constexpr int HW = G < 4 ? G : 4;  // query heads per workgroup
-  constexpr int TPW = 4 / HW;        // 32-token sub-tiles per workgroup
-  constexpr int QT = 32 * TPW;       // tokens per workgroup
-  constexpr int KROW = HD + 8;       // halves per K row in LDS
-  constexpr int VROW = KT + 8;       // halves per transposed V row
-  constexpr int NDT = HD / 32;       // 32-wide d tiles
-  constexpr int NST = HD / 16;       // K=16 steps over head_dim
-  __shared__ __align__(16) _Float16 sK[KT * KROW];
-  __shared__ __align__(16) _Float16 sVt[HD * VROW];
+  constexpr int TPW = 4 / HW;        // 16-token sub-tiles per workgroup
+  constexpr int QT = 16 * TPW;       // tokens per workgroup
+  constexpr int KROW = HD + 1;       // f32 per K row in LDS (padded)
+  constexpr int VROW = HD + 16;      // f32 per V row in LDS (padded)
+  constexpr int NST = HD / 4;        // k=4 steps over head_dim
+  constexpr int NDT = HD / 16;       // 16-wide d tiles of the output
+  __shared__ float sK[KT * KROW];
+  __shared__ float sV[KT * VROW];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int lq = lane % 32, lg = lane / 32;
+  const int lq = lane % 16, lg = lane / 16;
   const int hb_per_g = G / HW;
   const int g = blockIdx.y / hb_per_g, hb = blockIdx.y % hb_per_g;
   const int h = g * G + hb * HW + (wave % HW);
   const int t0 = blockIdx.x * QT;
-  const int tw0 = t0 + (wave / HW) * 32;  // first token of this wavefront
+  const int tw0 = t0 + (wave / HW) * 16;  // first token of this wavefront
   const int T = a.T;
 
   // this lane's query (clamped so padded lanes stay finite; never stored)
   const int tq = min(tw0 + lq, T - 1);
   const int qpos = a.pos0 + tq;
-  v8h qf[NST];
+  double qf[NST];
+  const float* qrow = a.q32 + ((int64_t)tq * a.nh + h) * HD;
 #pragma unroll
-  for (int st = 0; st < NST; ++st)
-    qf[st] = *reinterpret_cast<const v8h*>(a.q16 + ((int64_t)tq * a.nh + h) * HD + st * 16 + lg * 8);
+  for (int st = 0; st < NST; ++st) qf[st] = (double)qrow[4 * st + lg];
 
   const int64_t head_elems = (int64_t)a.cap * HD;
   const int64_t kb0 = a.kbase + (int64_t)g * head_elems;
   const int64_t vb0 = kb0 + (int64_t)a.nkv * head_elems;
   const int kend = a.pos0 + min(T, t0 + QT);  // keys [0, kend) matter for this workgroup
 
-  v16f o[NDT];
+  v4d o[NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = v4d{0.0, 0.0, 0.0, 0.0};
+  double m_run = -INFINITY, l_run = 0.0;
 
   for (int kbase = 0; kbase < kend; kbase += KT) {
     __syncthreads();
@@ -121,89 +122,80 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
         kval = ld_kv<BF16>(a.kv, kb0 + (int64_t)key * HD + d);
         vval = ld_kv<BF16>(a.kv, vb0 + (int64_t)key * HD + d);
       }
-      sK[kr * KROW + d] = (_Float16)kval;
-      sVt[d * VROW + kr] = (_Float16)vval;
+      sK[kr * KROW + d] = kval;
+      sV[kr * VROW + d] = vval;
     }
     __syncthreads();
 
-    // S^T tiles: keys kt*32 + (8*(j/4) + 4*lg + j%4), query lq
-    v16f s[2];
+    // scores S^T for 4 sub-tiles of 16 keys; lane holds keys 4*item + lg
+    v4d s[KT / 16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT / 16; ++kt) {
+      s[kt] = v4d{0.0, 0.0, 0.0, 0.0};
+      const float* kr = &sK[(kt * 16 + lq) * KROW + lg];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const v8h kf = *reinterpret_cast<const v8h*>(&sK[(kt * 32 + lq) * KROW + st * 16 + lg * 8]);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[st], s[kt], 0, 0, 0);
-      }
+      for (int st = 0; st < NST; ++st)
+        s[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * st], qf[st], s[kt], 0, 0, 0);
     }
-    float rmax = -INFINITY;
+    double rmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = kbase + kt * 32 + 8 * (j / 4) + 4 * lg + (j % 4);
-        const float v = (key <= qpos) ? s[kt][j] * a.scale : -INFINITY;
-        s[kt][j] = v;
-        rmax = fmaxf(rmax, v);
+      for (int it = 0; it < 4; ++it) {
+        const int key = kbase + kt * 16 + 4 * it + lg;
+        const double v = (key <= qpos) ? s[kt][it] * a.scale : -INFINITY;
+        s[kt][it] = v;
+        rmax = fmax(rmax, v);
       }
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-    const float m_new = fmaxf(m_run, rmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-    float rsum = 0.f;
+    rmax = fmax(rmax, __shfl_xor(rmax, 16));
+    rmax = fmax(rmax, __shfl_xor(rmax, 32));
+    const double m_new = fmax(m_run, rmax);
+    const double alpha = (m_run == -INFINITY) ? 0.0 : exp(m_run - m_new);
+    double rsum = 0.0;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = (s[kt][j] == -INFINITY) ? 0.f : expf(s[kt][j] - m_new);
-        s[kt][j] = p;
+      for (int it = 0; it < 4; ++it) {
+        const double p = (s[kt][it] == -INFINITY) ? 0.0 : exp(s[kt][it] - m_new);
+        s[kt][it] = p;
         rsum += p;
       }
+    rsum += __shfl_xor(rsum, 16);
     rsum += __shfl_xor(rsum, 32);
     l_run = l_run * alpha + rsum;
     m_run = m_new;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
 
-    // O^T += V^T P^T; half hf of key tile kt covers keys kt*32 + 16*hf + {4lg..4lg+3, 8+4lg..8+4lg+3}
+    // O^T += V^T P^T: step (kt, it) covers keys kt*16 + 4*it + {0..3}; lane lg
+    // supplies key kt*16 + 4*it + lg, which is exactly its score item it
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT / 16; ++kt) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        v8h pb;
+      for (int it = 0; it < 4; ++it) {
+        const float* vr = &sV[(kt * 16 + 4 * it + lg) * VROW + lq];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (_Float16)s[kt][8 * hf + i];
-        const int kofs = kt * 32 + 16 * hf + 4 * lg;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const _Float16* vr = &sVt[(dt * 32 + lq) * VROW + kofs];
-          const v4h lo = *reinterpret_cast<const v4h*>(vr);
-          const v4h hi = *reinterpret_cast<const v4h*>(vr + 8);
-          const v8h va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * dt], s[kt][it], o[dt], 0, 0, 0);
       }
     }
   }
 
+  // O^T layout: lane (lg, lq) holds d = 16*dt + 4*item + lg of query lq
   const int tout = tw0 + lq;
   if (tout < T) {
-    const float inv = 1.0f / l_run;
     float* orow = a.out + (int64_t)tout * a.nh * HD + (int64_t)h * HD;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) orow[dt * 32 + 8 * (j / 4) + 4 * lg + (j % 4)] = o[dt][j] * inv;
+      for (int it = 0; it < 4; ++it) orow[16 * dt + 4 * it + lg] = (float)(o[dt][it] / l_run);
   }
 }
 
 template <int HD, int G>
 hipError_t launch_attn(const AttnPrefillArgs& a, bool bf16, hipStream_t s) {
   constexpr int HW = G < 4 ? G : 4;
-  constexpr int QT = 32 * (4 / HW);
+  constexpr int QT = 16 * (4 / HW);
   const dim3 grid((a.T + QT - 1) / QT, a.nkv * (G / HW));
   if (bf16)
     hipLaunchKernelGGL((k_attn_prefill<HD, G, true>), grid, dim3(256), 0, s, a);

@@ -22,7 +22,6 @@ using namespace q8;
 
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128;
@@ -90,13 +89,15 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   const int nstage = a.K / SK;
 
   Stage rs;  // global -> register staging: 4 x 16 bytes of A and of B per thread
-  float acc[2][2][16];
+  // block terms d_a * d_w * S are exact in f64; the sum is rounded to f32
+  // once, in the epilogue
+  double acc[2][2][16];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0;
 
   const int lr = lane % 32, lg = lane / 32;
   gemm_gload(a, rs, 0, m0, n0, nblk);
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
           const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], zero, 0, 0, 0);
           const float dw = sDw[buf][kb][wn * 64 + ni * 32 + lr];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (float)S[j] * (da[j] * dw);
+          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (double)S[j] * (double)(da[j] * dw);
         }
       }
     }
@@ -148,16 +149,16 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
       if (EPI == EPI_SWIGLU) {
         if (n0 + wn * 64 >= a.N) continue;
         const int unit = ((n0 + wn * 64) / 64) * 32 + lr;
-        const float g = acc[mi][0][j], u = acc[mi][1][j];
-        a.out[(int64_t)m * a.ldc + unit] = (g / (1.0f + expf(-g))) * u;
+        a.out[(int64_t)m * a.ldc + unit] = swiglu_f64((float)acc[mi][0][j], (float)acc[mi][1][j]);
       } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
           const int n = n0 + wn * 64 + ni * 32 + lr;
           if (n >= a.N) continue;
           float* p = a.out + (int64_t)m * a.ldc + n;
-          if (EPI == EPI_STORE) *p = acc[mi][ni][j];
-          if (EPI == EPI_RESIDUAL) *p += acc[mi][ni][j];
+          const float y = (float)acc[mi][ni][j];
+          if (EPI == EPI_STORE) *p = y;
+          if (EPI == EPI_RESIDUAL) *p = *p + y;
         }
       }
     }

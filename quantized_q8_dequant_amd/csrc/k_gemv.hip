@@ -4,12 +4,12 @@
 // on the fly (same page, section 11.7).
 //
 // Layout: the weight matrix is two planes -- int8 codes [N][K] (row r is
-// output r) and f16 scales [N][K/32].  A wavefront streams rows with 16-byte
-// (128-bit) coalesced loads: LPR lanes cover one row, each lane holds 16-byte
-// chunks c = lane + j*LPR of it (half a block), so lanes 2i and 2i+1 hold the
-// two halves of block i and one DPP swap forms S exactly.  Weight loads are
-// issued before the prologue (weights do not depend on the activation), the
-// prologue quantises the activation into LDS, then 4 x v_dot4_i32_i8 per chunk.
+// output r) and f16 scales [N][K/32].  A wavefront streams rows with 128-bit
+// loads: LPR lanes cover one row and each lane owns whole 32-byte blocks
+// b = lane + j*LPR (two 16-byte loads; the pair of load instructions covers
+// the row's bytes contiguously), so S is formed in one lane by 8 x v_dot4.
+// Weight loads are issued before the prologue (weights do not depend on the
+// activation); the prologue quantises the activation into LDS.
 //
 // Prologues: RMSNorm + quantise (the norm of "A transformer from scratch",
 // section 12.3.2) or quantise only.  Epilogues: store, residual add (section
@@ -26,24 +26,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-QDEV int swap_pair(int v) {  // value of lane ^ 1 (quad_perm 1,0,3,2)
-  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-}
-
 // Quantise src [K] (optionally RMSNorm'd with w) into LDS: s_qa [K] bytes,
 // s_da [K/32] f32 (the value of f16(d)).
 template <bool NORM>
 QDEV void prologue_quant(const float* __restrict__ src, const float* __restrict__ w, float eps, int K,
-                         int8_t* s_qa, float* s_da, float* s_red) {
-  float r = 1.f;
+                         int8_t* s_qa, float* s_da, double* s_red) {
+  double r = 1.0;
   if (NORM) {
-    float ss = 0.f;
+    double ss = 0.0;
     for (int c = threadIdx.x * 4; c < K; c += kThreads * 4) {
       const float4 v = *reinterpret_cast<const float4*>(src + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
     }
-    ss = block_sum<kThreads>(ss, s_red);
-    r = 1.0f / sqrtf(ss / (float)K + eps);
+    ss = block_sum_d<kThreads>(ss, s_red);
+    r = rms_scale(ss, K, eps);
   }
   for (int base = 0; base < K; base += kThreads * 4) {
     const int c = base + threadIdx.x * 4;
@@ -54,7 +50,8 @@ QDEV void prologue_quant(const float* __restrict__ src, const float* __restrict_
       v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
       if (NORM) {
         const float4 w4 = *reinterpret_cast<const float4*>(w + c);
-        v[0] = (v[0] * r) * w4.x, v[1] = (v[1] * r) * w4.y, v[2] = (v[2] * r) * w4.z, v[3] = (v[3] * r) * w4.w;
+        v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
+        v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
       }
     }
     float d;
@@ -86,15 +83,16 @@ QDEV ArgBest wave_best(ArgBest a) {
   return a;
 }
 
-// LPR lanes per row, CPL 16-byte chunks per lane per row (K = 16*LPR*CPL),
+// LPR lanes per row, BPL 32-value blocks per lane per row (K = 32*LPR*BPL),
 // ROWS rows per lane group.  For EPI_SWIGLU the first ROWS/2 rows are gate
 // rows and the last ROWS/2 the matching up rows.
-template <int LPR, int CPL, int ROWS, bool NORM, int EPI>
+template <int LPR, int BPL, int ROWS, bool NORM, int EPI>
 __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ float s_red[kWaves];
+  __shared__ double s_red[kWaves];
   __shared__ ArgBest s_best[kWaves];
-  constexpr int K = 16 * LPR * CPL;
+  __shared__ int s_last;
+  constexpr int K = 32 * LPR * BPL;
   constexpr int GPW = kWave / LPR;  // lane groups per wave
   int8_t* s_qa = reinterpret_cast<int8_t*>(smem);
   float* s_da = reinterpret_cast<float*>(smem + K);
@@ -103,7 +101,6 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   const int li = lane % LPR, grp = lane / LPR;
   const int groups_per_wg = kWaves * GPW;
   const int64_t nb = K / 32;
-  const bool even = (li & 1) == 0;
 
   // rows of the activation batch: blockIdx.y selects one batch row
   const float* src = a.src + (int64_t)blockIdx.y * a.src_stride;
@@ -125,41 +122,44 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         rows[r] = gg * ROWS + r;
       }
     }
-    int4 wv[ROWS][CPL];
-    uint16_t ws[ROWS][CPL];
+    v4i w0[ROWS][BPL], w1[ROWS][BPL];
+    uint16_t ws[ROWS][BPL];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = rows[r] < a.N ? rows[r] : a.N - 1;
       const int8_t* wr = a.qs + row * (int64_t)K;
       const uint16_t* sr = a.sc + row * nb;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = li + j * LPR;
-        wv[r][j] = *reinterpret_cast<const int4*>(wr + c * 16);
-        ws[r][j] = sr[c >> 1];
+      for (int j = 0; j < BPL; ++j) {
+        const int b = li + j * LPR;
+        w0[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32);
+        w1[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32 + 16);
+        ws[r][j] = sr[b];
       }
     }
     if (!have_act) {
       prologue_quant<NORM>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
       have_act = true;
     }
-    float acc[ROWS];
+    // block terms d_w * d_a * S are exact in f64; their sum is rounded to
+    // f32 once, in the epilogue
+    double acc[ROWS];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
+    for (int r = 0; r < ROWS; ++r) acc[r] = 0.0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = li + j * LPR;
-      const int4 av = *reinterpret_cast<const int4*>(s_qa + c * 16);
-      const float da = s_da[c >> 1];
+    for (int j = 0; j < BPL; ++j) {
+      const int b = li + j * LPR;
+      const v4i a0 = *reinterpret_cast<const v4i*>(s_qa + b * 32);
+      const v4i a1 = *reinterpret_cast<const v4i*>(s_qa + b * 32 + 16);
+      const float da = s_da[b];
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
-        const int half = dot16_i8(wv[r][j], av);
-        const int S = half + swap_pair(half);
-        if (even) acc[r] += (float)S * (f16_bits_to_f32(ws[r][j]) * da);
+        const int S = dot32_i8(w0[r][j], w1[r][j], a0, a1);
+        acc[r] += (double)S * (double)(f16_bits_to_f32(ws[r][j]) * da);
       }
     }
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum<LPR>(acc[r]);
+    for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum_d<LPR>(acc[r]);
 
     if (li == 0) {
       if (EPI == EPI_SWIGLU) {
@@ -168,8 +168,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         for (int i = 0; i < P; ++i) {
           const int n = gg * P + i;
           if (n < a.N / 2) {
-            const float g = acc[i], u = acc[P + i];
-            out[n] = (g / (1.0f + expf(-g))) * u;
+            out[n] = swiglu_f64((float)acc[i], (float)acc[P + i]);
           }
         }
       } else {
@@ -177,11 +176,12 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
         for (int r = 0; r < ROWS; ++r) {
           const int row = rows[r];
           if (row < a.N) {
-            if (EPI == EPI_STORE) out[row] = acc[r];
-            if (EPI == EPI_RESIDUAL) out[row] += acc[r];
+            const float y = (float)acc[r];
+            if (EPI == EPI_STORE) out[row] = y;
+            if (EPI == EPI_RESIDUAL) out[row] = out[row] + y;
             if (EPI == EPI_ARGMAX) {
-              if (a.logits) a.logits[(int64_t)blockIdx.y * a.N + row] = acc[r];
-              best = better(best, ArgBest{acc[r], row});
+              if (a.logits) a.logits[(int64_t)blockIdx.y * a.N + row] = y;
+              best = better(best, ArgBest{y, row});
             }
           }
         }
@@ -201,10 +201,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       a.part_i[slot] = b.i;
       __threadfence();
       const unsigned prev = atomicAdd(a.counter + blockIdx.y, 1u);
-      s_red[0] = __uint_as_float(prev == gridDim.x - 1 ? 1u : 0u);
+      s_last = prev == gridDim.x - 1 ? 1 : 0;
     }
     __syncthreads();
-    if (__float_as_uint(s_red[0]) == 1u) {  // last workgroup of this batch row: second pass
+    if (s_last) {  // last workgroup of this batch row: second pass
       __threadfence();
       ArgBest b{-INFINITY, 0x7FFFFFFF};
       for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
@@ -228,37 +228,33 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   }
 }
 
-// Test hook: S[t][n][b] with the same half-block dot and pair swap.
-// One wavefront per (t, n) pair.
+// Test hook: S[t][n][b] with the same per-lane block dot as the GEMV.
+// One wavefront per (t, n) pair, one lane per block.
 __global__ void __launch_bounds__(kThreads) k_block_dots(const int8_t* __restrict__ qa, const int8_t* __restrict__ qs,
                                                         int K, int N, int64_t pairs, int32_t* __restrict__ S) {
   const int lane = threadIdx.x % kWave;
   const int64_t pair = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   if (pair >= pairs) return;  // uniform per wavefront
   const int t = (int)(pair / N), n = (int)(pair % N);
-  const int nchunks = K / 16;
-  for (int c0 = 0; c0 < nchunks; c0 += kWave) {
-    const int c = c0 + lane;
-    int half = 0;
-    if (c < nchunks) {
-      const int4 w = *reinterpret_cast<const int4*>(qs + (int64_t)n * K + c * 16);
-      const int4 x = *reinterpret_cast<const int4*>(qa + (int64_t)t * K + c * 16);
-      half = dot16_i8(w, x);
-    }
-    const int s = half + swap_pair(half);
-    if (c < nchunks && (c & 1) == 0) S[((int64_t)t * N + n) * (K / 32) + c / 2] = s;
+  const int nblocks = K / 32;
+  for (int b = lane; b < nblocks; b += kWave) {
+    const int8_t* w = qs + (int64_t)n * K + b * 32;
+    const int8_t* x = qa + (int64_t)t * K + b * 32;
+    const int s = dot32_i8(*reinterpret_cast<const v4i*>(w), *reinterpret_cast<const v4i*>(w + 16),
+                           *reinterpret_cast<const v4i*>(x), *reinterpret_cast<const v4i*>(x + 16));
+    S[((int64_t)t * N + n) * nblocks + b] = s;
   }
 }
 
-template <int LPR, int CPL, int ROWS, bool NORM, int EPI>
+template <int LPR, int BPL, int ROWS, bool NORM, int EPI>
 hipError_t launch_one(const GemvArgs& a, int grid_x, int grid_y, hipStream_t s) {
-  constexpr int K = 16 * LPR * CPL;
+  constexpr int K = 32 * LPR * BPL;
   const size_t shm = K + (K / 32) * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<LPR, CPL, ROWS, NORM, EPI>), dim3(grid_x, grid_y), dim3(kThreads), shm, s, a);
+  hipLaunchKernelGGL((k_gemv<LPR, BPL, ROWS, NORM, EPI>), dim3(grid_x, grid_y), dim3(kThreads), shm, s, a);
   return hipGetLastError();
 }
 
-template <int LPR, int CPL, int ROWS>
+template <int LPR, int BPL, int ROWS>
 hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int max_grid, int grid_y, hipStream_t s) {
   constexpr int GPW = kWave / LPR;
   constexpr int groups = kWaves * GPW;
@@ -267,7 +263,7 @@ hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int max_grid, int grid_y,
   int grid = a.ntiles;
   if (max_grid > 0 && grid > max_grid) grid = max_grid;
 #define Q8_CASE(NORM_, EPI_) \
-  if (norm == NORM_ && epi == EPI_) return launch_one<LPR, CPL, ROWS, NORM_, EPI_>(a, grid, grid_y, s);
+  if (norm == NORM_ && epi == EPI_) return launch_one<LPR, BPL, ROWS, NORM_, EPI_>(a, grid, grid_y, s);
   Q8_CASE(true, EPI_STORE)
   Q8_CASE(false, EPI_STORE)
   Q8_CASE(false, EPI_RESIDUAL)
@@ -288,43 +284,32 @@ int gemv_argmax_grid(int N, int K) {
   return tiles < 2048 ? tiles : 2048;
 }
 
-// Dispatch on K: LPR = 64 when K % 1024 == 0, else 16 (K % 256 == 0).
+// Dispatch on K = 32 * LPR * BPL with LPR the largest power of two <= 64
+// dividing K/32.
 hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s) {
-  const int K = a.K;
-  const int max_grid = (epi == EPI_ARGMAX) ? gemv_argmax_grid(a.N, K) : 0;
-  if (K % 1024 == 0) {
-    switch (K / 1024) {
-      case 1: return launch_epi<64, 1, 8>(a, norm, epi, max_grid, grid_y, s);
-      case 2: return launch_epi<64, 2, 4>(a, norm, epi, max_grid, grid_y, s);
-      case 3: return launch_epi<64, 3, 2>(a, norm, epi, max_grid, grid_y, s);
-      case 4: return launch_epi<64, 4, 2>(a, norm, epi, max_grid, grid_y, s);
-      case 6: return launch_epi<64, 6, 2>(a, norm, epi, max_grid, grid_y, s);
-      case 8: return launch_epi<64, 8, 2>(a, norm, epi, max_grid, grid_y, s);
-      case 12: return launch_epi<64, 12, 2>(a, norm, epi, max_grid, grid_y, s);
-      default: return hipErrorInvalidValue;
-    }
+  const int max_grid = (epi == EPI_ARGMAX) ? gemv_argmax_grid(a.N, a.K) : 0;
+  switch (a.K) {
+    case 256: return launch_epi<8, 1, 4>(a, norm, epi, max_grid, grid_y, s);
+    case 512: return launch_epi<16, 1, 4>(a, norm, epi, max_grid, grid_y, s);
+    case 768: return launch_epi<8, 3, 2>(a, norm, epi, max_grid, grid_y, s);
+    case 1024: return launch_epi<32, 1, 4>(a, norm, epi, max_grid, grid_y, s);
+    case 2048: return launch_epi<64, 1, 4>(a, norm, epi, max_grid, grid_y, s);
+    case 3072: return launch_epi<32, 3, 2>(a, norm, epi, max_grid, grid_y, s);
+    case 4096: return launch_epi<64, 2, 2>(a, norm, epi, max_grid, grid_y, s);
+    case 6144: return launch_epi<64, 3, 2>(a, norm, epi, max_grid, grid_y, s);
+    case 8192: return launch_epi<64, 4, 2>(a, norm, epi, max_grid, grid_y, s);
+    case 12288: return launch_epi<64, 6, 2>(a, norm, epi, max_grid, grid_y, s);
+    default: return hipErrorInvalidValue;
   }
-  if (K % 256 == 0) {
-    switch (K / 256) {
-      case 1: return launch_epi<16, 1, 4>(a, norm, epi, max_grid, grid_y, s);
-      case 2: return launch_epi<16, 2, 4>(a, norm, epi, max_grid, grid_y, s);
-      case 3: return launch_epi<16, 3, 2>(a, norm, epi, max_grid, grid_y, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  return hipErrorInvalidValue;
 }
 
 bool gemv_supported_k(int K) {
-  if (K % 1024 == 0) {
-    const int c = K / 1024;
-    return c == 1 || c == 2 || c == 3 || c == 4 || c == 6 || c == 8 || c == 12;
+  switch (K) {
+    case 256: case 512: case 768: case 1024: case 2048: case 3072: case 4096: case 6144: case 8192: case 12288:
+      return true;
+    default:
+      return false;
   }
-  if (K % 256 == 0) {
-    const int c = K / 256;
-    return c >= 1 && c <= 3;
-  }
-  return false;
 }
 
 hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s) {

@@ -42,8 +42,9 @@ __global__ void k_encode_bf16(const float* __restrict__ x, int64_t n, uint16_t* 
 }
 
 // Wire blocks -> planes: qs int8 [rows, k] at row stride k, scales f16 [rows, k/32].
-// dst_row0 lets the runtime stack several matrices into one plane; `interleave`
-// > 0 places source row r at stacked row (r / 32) * 64 + interleave_off + r % 32
+// dst_row0 lets the runtime stack several matrices into one plane;
+// interleave_off >= 0 places source row r at stacked row
+// dst_row0 + (r / 32) * 64 + interleave_off + r % 32
 // (gate/up pairing: each 64-row group = 32 gate rows then 32 up rows).
 __global__ void k_repack_q8_0(const uint8_t* __restrict__ src, int64_t rows, int64_t k, int8_t* __restrict__ qs,
                               uint16_t* __restrict__ sc, int64_t dst_row0, int interleave_off) {
@@ -103,18 +104,18 @@ __global__ void __launch_bounds__(256) k_embed_bf16(const int32_t* __restrict__ 
 __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x, int K, const float* __restrict__ norm_w,
                                                     float eps, int8_t* __restrict__ qa, float* __restrict__ da,
                                                     uint16_t* __restrict__ da_bits) {
-  __shared__ float s_red[4];
+  __shared__ double s_red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * K;
-  float r = 1.f;
+  double r = 1.0;
   if (norm_w) {
-    float ss = 0.f;
+    double ss = 0.0;
     for (int c = threadIdx.x * 4; c < K; c += 256 * 4) {
       const float4 v = *reinterpret_cast<const float4*>(xr + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
     }
-    ss = block_sum<256>(ss, s_red);
-    r = 1.0f / sqrtf(ss / (float)K + eps);
+    ss = block_sum_d<256>(ss, s_red);
+    r = rms_scale(ss, K, eps);
   }
   // every thread takes part in each pass (groups of 8 lanes stay uniform)
   for (int base = 0; base < K; base += 256 * 4) {
@@ -126,7 +127,8 @@ __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x,
       v[0] = t4.x, v[1] = t4.y, v[2] = t4.z, v[3] = t4.w;
       if (norm_w) {
         const float4 w4 = *reinterpret_cast<const float4*>(norm_w + c);
-        v[0] = (v[0] * r) * w4.x, v[1] = (v[1] * r) * w4.y, v[2] = (v[2] * r) * w4.z, v[3] = (v[3] * r) * w4.w;
+        v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
+        v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
       }
     }
     float d;
@@ -139,6 +141,16 @@ __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x,
         if (da_bits) da_bits[bi] = f32_to_f16_bits(d);
       }
     }
+  }
+}
+
+// KV slab export: [nkv][cap][hd] (f32 or bf16) rows [0, len) -> f32 [nkv][len][hd].
+__global__ void k_kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* __restrict__ dst) {
+  const int64_t total = (int64_t)nkv * len * hd;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t g = i / ((int64_t)len * hd), rem = i % ((int64_t)len * hd);
+    const int64_t si = g * (int64_t)cap * hd + rem;
+    dst[i] = bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[si]) : reinterpret_cast<const float*>(src)[si];
   }
 }
 
@@ -191,6 +203,15 @@ hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, con
     hipLaunchKernelGGL(k_embed_bf16, dim3(T), dim3(256), 0, s, tok, vocab, H, (const uint16_t*)w, x);
   else
     hipLaunchKernelGGL(k_embed_q8_0, dim3(T), dim3(256), 0, s, tok, vocab, H, (const int8_t*)w, sc, x);
+  return hipGetLastError();
+}
+
+hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* dst, hipStream_t s) {
+  const int64_t total = (int64_t)nkv * len * hd;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(k_kv_export, dim3((unsigned)grid), dim3(256), 0, s, src, bf16, nkv, cap, len, hd, dst);
   return hipGetLastError();
 }
 

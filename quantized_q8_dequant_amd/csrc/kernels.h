@@ -40,20 +40,20 @@ struct AttnDecodeArgs {
   const float* q_norm;  // [hd]
   const float* k_norm;  // [hd]
   float eps;
-  const float* rope_cos;  // [max_pos][hd/2]
-  const float* rope_sin;
+  const double* rope_cos;  // [max_pos][hd/2]
+  const double* rope_sin;
   void* kv;                  // cache base
   const int64_t* seq_base;   // [max_seqs] element offset of each sequence
   const int32_t* seq_cap;    // [max_seqs] capacity (rows) of each sequence
   const int32_t* len;        // [max_seqs] KV lengths (position of the new token)
   const int32_t* row_seq;    // [nrows] sequence of each batch row (null: sequence 0)
   int layer;
-  float* part;        // partials [nrows][nkv][nsplit_max][G][hd + 2]
+  double* part;       // partials [nrows][nkv][nsplit_max][G][hd + 2]
   unsigned* counter;  // [nrows][nkv], zero between launches
   float* out;         // attention output [nrows][out_stride], head h at h*hd
   int64_t out_stride;
   int nkv, nsplit_max, min_rows;
-  float scale;  // 1/sqrt(hd)
+  double scale;  // 1/sqrt(hd)
 };
 
 namespace q8k {
@@ -67,6 +67,7 @@ hipError_t repack_bf16(const void* src, int64_t rows, int64_t k, uint16_t* dst, 
                        hipStream_t s);
 hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, const uint16_t* sc, bool bf16, float* x,
                  hipStream_t s);
+hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* dst, hipStream_t s);
 hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
                       uint16_t* da_bits, hipStream_t s);
 
@@ -101,9 +102,9 @@ struct QkRopeArgs {
   const float* q_norm;
   const float* k_norm;
   float eps;
-  const float* rope_cos;
-  const float* rope_sin;
-  _Float16* q16;  // [T][nh][hd]
+  const double* rope_cos;
+  const double* rope_sin;
+  float* q32;  // [T][nh][hd] normalised + roped queries
   void* kv;
   int64_t kbase;  // element offset of this (sequence, layer) K block; V follows at + nkv*cap*hd
   int cap;
@@ -112,14 +113,14 @@ struct QkRopeArgs {
 };
 
 struct AttnPrefillArgs {
-  const _Float16* q16;  // [T][nh][hd]
+  const float* q32;  // [T][nh][hd]
   const void* kv;
   int64_t kbase;
   int cap;
   int pos0;  // position of query token 0 (cache rows [0, pos0 + T) are valid)
   int T;
   int nh, nkv;
-  float scale;
+  double scale;  // 1/sqrt(hd)
   float* out;  // [T][nh*hd]
 };
 

@@ -54,6 +54,49 @@ QDEV float wave_max(float v) {
   return v;
 }
 
+template <int WIDTH>
+QDEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
+  return v;
+}
+template <int WIDTH>
+QDEV double wave_max_d(double v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+
+// Block-wide sum of one double per thread (blockDim.x == NT, NT % 64 == 0).
+template <int NT>
+QDEV double block_sum_d(double v, double* s_red) {
+  v = wave_sum_d<kWave>(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) s_red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += s_red[i];
+  __syncthreads();
+  return t;
+}
+
+// RMSNorm scale r = 1 / sqrt(mean(x^2) + eps) from the f64 sum of squares
+// (each square is exact in f64), then y = f32((x * r) * w) evaluated in f64:
+// the value rounded once to f32, as a reference computing in f64 would.
+QDEV double rms_scale(double sumsq, int n, float eps) { return 1.0 / sqrt(sumsq / (double)n + (double)eps); }
+QDEV float rms_apply(float x, double r, float w) {
+#pragma clang fp contract(off)
+  return (float)(((double)x * r) * (double)w);
+}
+
+// silu(g) * u in f64 from the f32 values of g and u, rounded once to f32.
+QDEV float swiglu_f64(float g, float u) {
+#pragma clang fp contract(off)
+  const double gd = (double)g;
+  return (float)((gd / (1.0 + exp(-gd))) * (double)u);
+}
+
 // Block-wide sum of one float per thread (blockDim.x == NT, NT % 64 == 0).
 template <int NT>
 QDEV float block_sum(float v, float* s_red) {
@@ -91,37 +134,45 @@ QDEV int quant4_group8(const float v[4], float* d_out) {
   return packed;
 }
 
-// ---- integer dot of one 16-byte half block --------------------------------------------
-QDEV int dot16_i8(const int4 a, const int4 b) {
-  int s = __builtin_amdgcn_sdot4(a.x, b.x, 0, false);
-  s = __builtin_amdgcn_sdot4(a.y, b.y, s, false);
-  s = __builtin_amdgcn_sdot4(a.z, b.z, s, false);
-  s = __builtin_amdgcn_sdot4(a.w, b.w, s, false);
+// ---- integer dot of one 32-value block ---------------------------------------------
+// S = sum_{i<32} a_i * b_i over signed bytes, exact in int32 (|S| <= 32 * 127^2),
+// from two 16-byte halves per operand: 8 x v_dot4 in one lane (no cross-lane
+// step, so the result never depends on another lane's timing).
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+QDEV int dot32_i8(const v4i a0, const v4i a1, const v4i b0, const v4i b1) {
+  int s = __builtin_amdgcn_sdot4(a0.x, b0.x, 0, false);
+  s = __builtin_amdgcn_sdot4(a0.y, b0.y, s, false);
+  s = __builtin_amdgcn_sdot4(a0.z, b0.z, s, false);
+  s = __builtin_amdgcn_sdot4(a0.w, b0.w, s, false);
+  s = __builtin_amdgcn_sdot4(a1.x, b1.x, s, false);
+  s = __builtin_amdgcn_sdot4(a1.y, b1.y, s, false);
+  s = __builtin_amdgcn_sdot4(a1.z, b1.z, s, false);
+  s = __builtin_amdgcn_sdot4(a1.w, b1.w, s, false);
   return s;
 }
 
-// Block dot from two lanes holding its halves (lanes l and l^1 of a group):
-// exact int32 sum of 32 products (|S| <= 32 * 127^2 < 2^20).
-QDEV int block_dot_pair(int half) { return half + __shfl_xor(half, 1, kWave); }
-
-// RMSNorm over one head (HD values in LDS) followed by the NeoX rotation of
-// pairs (i, i + HD/2) by the angle whose cos/sin are cs[i]/sn[i]; run by one
-// wavefront ("A transformer from scratch", sections 12.3.2 and 12.3.4).
+// RMSNorm over one head (HD values in LDS, rounded to f32 as a separate
+// step) followed by the NeoX rotation of pairs (i, i + HD/2) by the angle
+// whose f64 cos/sin are cs[i]/sn[i], each output evaluated in f64 and rounded
+// once to f32; run by one wavefront ("A transformer from scratch", sections
+// 12.3.2 and 12.3.4).
 template <int HD>
-QDEV void norm_rope_wave(float* x, const float* __restrict__ w, float eps, const float* __restrict__ cs,
-                         const float* __restrict__ sn, float scale_out) {
+QDEV void norm_rope_wave(float* x, const float* __restrict__ w, float eps, const double* __restrict__ cs,
+                         const double* __restrict__ sn) {
+#pragma clang fp contract(off)
   const int lane = threadIdx.x % kWave;
-  float ss = 0.f;
-  for (int d = lane; d < HD; d += kWave) ss += x[d] * x[d];
-  ss = wave_sum<kWave>(ss);
-  const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+  double ss = 0.0;
+  for (int d = lane; d < HD; d += kWave) ss += (double)x[d] * (double)x[d];
+  ss = wave_sum_d<kWave>(ss);
+  const double r = rms_scale(ss, HD, eps);
   constexpr int H2 = HD / 2;
   for (int i = lane; i < H2; i += kWave) {
-    const float a = (x[i] * r) * w[i];
-    const float b = (x[i + H2] * r) * w[i + H2];
-    const float c = cs[i], s = sn[i];
-    x[i] = (a * c - b * s) * scale_out;
-    x[i + H2] = (a * s + b * c) * scale_out;
+    const double a = (double)rms_apply(x[i], r, w[i]);
+    const double b = (double)rms_apply(x[i + H2], r, w[i + H2]);
+    const double c = cs[i], s = sn[i];
+    x[i] = (float)(a * c - b * s);
+    x[i + H2] = (float)(a * s + b * c);
   }
 }
 

@@ -102,7 +102,7 @@ struct qwen3_model {
   std::vector<Layer> layers;
   QPlane emb;
   float* out_norm = nullptr;
-  float *rope_cos = nullptr, *rope_sin = nullptr;
+  double *rope_cos = nullptr, *rope_sin = nullptr;
   void* kv = nullptr;
   int64_t* d_seq_base = nullptr;
   int32_t* d_seq_cap = nullptr;
@@ -113,8 +113,8 @@ struct qwen3_model {
   float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr;
   int8_t* qa = nullptr;
   float* da = nullptr;
-  _Float16* q16 = nullptr;
-  float* attn_part = nullptr;
+  float* q32 = nullptr;
+  double* attn_part = nullptr;
   unsigned* attn_cnt = nullptr;
   float* am_part_v = nullptr;
   int32_t* am_part_i = nullptr;
@@ -157,8 +157,8 @@ int validate(const qwen3_config* c) {
   if (!q8k::gemv_supported_k(c->hidden_size) || !q8k::gemv_supported_k(qw) ||
       !q8k::gemv_supported_k(c->intermediate_size))
     return fail(QWEN3_E_INVALID_CONFIG,
-                "hidden_size, heads*head_dim and intermediate_size must each be 256, 512, 768 or "
-                "1024 * {1,2,3,4,6,8,12}");
+                "hidden_size, heads*head_dim and intermediate_size must each be one of 256, 512, 768, "
+                "1024, 2048, 3072, 4096, 6144, 8192, 12288");
   if (c->max_seqs <= 0) return fail(QWEN3_E_INVALID_CONFIG, "max_seqs must be >= 1");
   if (!c->h_seq_capacity) return fail(QWEN3_E_INVALID_ARGUMENT, "h_seq_capacity is null");
   for (int i = 0; i < c->max_seqs; ++i)
@@ -198,8 +198,8 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     ly.ffn_norm = cv.arr<float>(H);
   }
   // RoPE table
-  m->rope_cos = cv.arr<float>((size_t)m->max_cap * (hd / 2));
-  m->rope_sin = cv.arr<float>((size_t)m->max_cap * (hd / 2));
+  m->rope_cos = cv.arr<double>((size_t)m->max_cap * (hd / 2));
+  m->rope_sin = cv.arr<double>((size_t)m->max_cap * (hd / 2));
   // KV cache: sequence s holds [layers][K, V][nkv][cap_s][hd]
   const size_t esz = m->kvbf16 ? 2 : 4;
   m->seq_base.assign(c.max_seqs, 0);
@@ -227,10 +227,10 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->h = cv.arr<float>(R * F);
   m->qa = cv.arr<int8_t>(R * m->kmax);
   m->da = cv.arr<float>(R * (m->kmax / 32));
-  m->q16 = cv.arr<_Float16>(R * qw);
+  m->q32 = cv.arr<float>(R * qw);
   // decode attention partials: rows * nsplit <= 2048 / nkv (see decode_nsplit_max)
   const int64_t G = nh / nkv;
-  m->attn_part = cv.arr<float>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
+  m->attn_part = cv.arr<double>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   const int64_t amg = q8k::gemv_argmax_grid(c.vocab_size, c.hidden_size);
   m->am_part_v = cv.arr<float>(R * amg);
@@ -327,7 +327,7 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
   at.nkv = m->nkv;
   at.nsplit_max = decode_nsplit_max(m->nkv, nrows);
   at.min_rows = 32;
-  at.scale = 1.0f / std::sqrt((float)m->hd);
+  at.scale = 1.0 / std::sqrt((double)m->hd);
   for (int l = 0; l < m->L; ++l) {
     const Layer& ly = m->layers[l];
     HIP_TRY(q8k::gemv(gemv_args(ly.qkv, m->x, m->H, ly.attn_norm, eps, m->qkv, m->nqkv), true, EPI_STORE, nrows, s));
@@ -377,7 +377,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     qr.eps = eps;
     qr.rope_cos = m->rope_cos;
     qr.rope_sin = m->rope_sin;
-    qr.q16 = m->q16;
+    qr.q32 = m->q32;
     qr.kv = m->kv;
     qr.kbase = kbase;
     qr.cap = m->cap[seq];
@@ -386,7 +386,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     qr.nkv = m->nkv;
     HIP_TRY(q8k::qk_rope_append(qr, T, m->hd, m->kvbf16, s));
     AttnPrefillArgs ap{};
-    ap.q16 = m->q16;
+    ap.q32 = m->q32;
     ap.kv = m->kv;
     ap.kbase = kbase;
     ap.cap = m->cap[seq];
@@ -394,7 +394,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     ap.T = T;
     ap.nh = m->nh;
     ap.nkv = m->nkv;
-    ap.scale = 1.0f / std::sqrt((float)m->hd);
+    ap.scale = 1.0 / std::sqrt((double)m->hd);
     ap.out = m->attn;
     HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvbf16, s));
     // o_proj + residual
@@ -491,19 +491,19 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
       TRY(copy_f32(ly.k_norm, src.attn_k_norm, hd, s));
       TRY(copy_f32(ly.ffn_norm, src.ffn_norm, H, s));
     }
-    // RoPE table: angle(p, i) = p * theta^(-2i/hd) in f64, stored as f32 cos/sin
+    // RoPE table: angle(p, i) = p * theta^(-2i/hd), cos/sin kept in f64
     const int half = m->hd / 2;
-    std::vector<float> cs((size_t)m->max_cap * half), sn((size_t)m->max_cap * half);
+    std::vector<double> cs((size_t)m->max_cap * half), sn((size_t)m->max_cap * half);
     for (int i = 0; i < half; ++i) {
       const double inv = std::pow((double)m->cfg.rope_theta, -2.0 * i / (double)m->hd);
       for (int p = 0; p < m->max_cap; ++p) {
         const double ang = (double)p * inv;
-        cs[(size_t)p * half + i] = (float)std::cos(ang);
-        sn[(size_t)p * half + i] = (float)std::sin(ang);
+        cs[(size_t)p * half + i] = std::cos(ang);
+        sn[(size_t)p * half + i] = std::sin(ang);
       }
     }
-    HIP_TRY(hipMemcpyAsync(m->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemcpyAsync(m->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(m->rope_cos, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(m->rope_sin, sn.data(), sn.size() * 8, hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(m->d_seq_base, m->seq_base.data(), m->seq_base.size() * 8, hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(m->d_seq_cap, m->cap.data(), m->cap.size() * 4, hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemsetAsync(m->d_len, 0, m->cap.size() * 4, s));
@@ -635,6 +635,22 @@ int qwen3_decode_batch(qwen3_t* m, const int32_t* h_seqs, int32_t n, const int32
   HIP_TRY(hipMemcpyAsync(m->d_row_seq, h_seqs, (size_t)n * 4, hipMemcpyHostToDevice, s));
   TRY(enqueue_decode(m, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
   for (int i = 0; i < n; ++i) m->h_len[h_seqs[i]] += 1;
+  return QWEN3_OK;
+}
+
+int qwen3_kv_export(const qwen3_t* m, int32_t seq, int32_t layer, float* d_k, float* d_v, void* stream) {
+  g_err.clear();
+  if (!m || !d_k || !d_v) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (layer < 0 || layer >= m->L) return fail(QWEN3_E_INVALID_ARGUMENT, "bad layer index");
+  const int cap = m->cap[seq], len = m->h_len[seq];
+  const int64_t head_elems = (int64_t)cap * m->hd;
+  const int64_t kbase = m->seq_base[seq] + (int64_t)layer * 2 * m->nkv * head_elems;
+  const int64_t vbase = kbase + (int64_t)m->nkv * head_elems;
+  const size_t esz = m->kvbf16 ? 2 : 4;
+  const uint8_t* base = static_cast<const uint8_t*>(m->kv);
+  HIP_TRY(q8k::kv_export(base + kbase * esz, m->kvbf16, m->nkv, cap, len, m->hd, d_k, S(stream)));
+  HIP_TRY(q8k::kv_export(base + vbase * esz, m->kvbf16, m->nkv, cap, len, m->hd, d_v, S(stream)));
   return QWEN3_OK;
 }
 

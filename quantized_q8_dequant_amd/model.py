@@ -247,6 +247,15 @@ class Qwen3Model:
     def reset(self, seq: int = 0):
         check(lib().qwen3_reset(self.handle, seq, _stream()))
 
+    def kv_export(self, seq: int, layer: int):
+        """(K, V) of one layer as f32 tensors [kv_heads, len, head_dim]."""
+        n = self.kv_len(seq)
+        shape = (self.cfg.num_key_value_heads, n, self.cfg.head_dim)
+        k = torch.empty(shape, dtype=torch.float32, device=self.device)
+        v = torch.empty(shape, dtype=torch.float32, device=self.device)
+        check(lib().qwen3_kv_export(self.handle, seq, layer, k.data_ptr(), v.data_ptr(), _stream()))
+        return k, v
+
     def kv_len(self, seq: int = 0) -> int:
         out = C.c_int32()
         check(lib().qwen3_kv_len(self.handle, seq, C.byref(out)))
