@@ -182,6 +182,16 @@ int qwen3_kv_len(const qwen3_t* h, int32_t seq, int32_t* out);
  * section 12.4).  Enqueued on `stream`; len is the host-side length. */
 int qwen3_kv_export(const qwen3_t* h, int32_t seq, int32_t layer, float* d_k, float* d_v, void* stream);
 
+/* Benchmark hook: enqueue `reps` launches of one kernel of sequence `seq`'s
+ * decode step, in the step's own launch configuration at the sequence's
+ * current length, so that its duration can be timed with events on
+ * `stream`.  kind: 0 fused QKV GEMV, 1 decode attention, 2 o_proj GEMV,
+ * 3 gate/up SwiGLU GEMV, 4 down GEMV (all of layer `layer`), 5 tied lm_head
+ * with the argmax.  Side effects stay in the library's scratch buffers and
+ * in cache row `len` (which the next decode step rewrites); no length is
+ * advanced.  Enqueue after at least one decode step of `seq`. */
+int qwen3_replay_kernel(qwen3_t* h, int32_t seq, int32_t kind, int32_t layer, int32_t reps, void* stream);
+
 /* Thread-local description of the last error ("" if none). */
 const char* qwen3_last_error(void);
 

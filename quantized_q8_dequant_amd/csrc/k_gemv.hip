@@ -23,25 +23,23 @@ using namespace q8;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 
 // Quantise src [K] (optionally RMSNorm'd with w) into LDS: s_qa [K] bytes,
 // s_da [K/32] f32 (the value of f16(d)).
-template <bool NORM>
+template <bool NORM, int NT>
 QDEV void prologue_quant(const float* __restrict__ src, const float* __restrict__ w, float eps, int K,
                          int8_t* s_qa, float* s_da, double* s_red) {
   double r = 1.0;
   if (NORM) {
     double ss = 0.0;
-    for (int c = threadIdx.x * 4; c < K; c += kThreads * 4) {
+    for (int c = threadIdx.x * 4; c < K; c += NT * 4) {
       const float4 v = *reinterpret_cast<const float4*>(src + c);
       ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
     }
-    ss = block_sum_d<kThreads>(ss, s_red);
+    ss = block_sum_d<NT>(ss, s_red);
     r = rms_scale(ss, K, eps);
   }
-  for (int base = 0; base < K; base += kThreads * 4) {
+  for (int base = 0; base < K; base += NT * 4) {
     const int c = base + threadIdx.x * 4;
     const bool live = c < K;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
@@ -72,7 +70,7 @@ QDEV ArgBest better(ArgBest a, ArgBest b) {  // larger value; ties -> lower inde
   if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
   return a;
 }
-QDEV ArgBest wave_best(ArgBest a) {
+QDEV ArgBest wave_best(ArgBest a) {  // over the 64 lanes
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {
     ArgBest b;
@@ -86,12 +84,13 @@ QDEV ArgBest wave_best(ArgBest a) {
 // LPR lanes per row, BPL 32-value blocks per lane per row (K = 32*LPR*BPL),
 // ROWS rows per lane group.  For EPI_SWIGLU the first ROWS/2 rows are gate
 // rows and the last ROWS/2 the matching up rows.
-template <int LPR, int BPL, int ROWS, bool NORM, int EPI>
-__global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
+template <int LPR, int BPL, int ROWS, int WAVES, bool NORM, int EPI>
+__global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kWaves = WAVES;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ double s_red[kWaves];
   __shared__ ArgBest s_best[kWaves];
-  __shared__ int s_last;
   constexpr int K = 32 * LPR * BPL;
   constexpr int GPW = kWave / LPR;  // lane groups per wave
   int8_t* s_qa = reinterpret_cast<int8_t*>(smem);
@@ -138,7 +137,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
       }
     }
     if (!have_act) {
-      prologue_quant<NORM>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
+      prologue_quant<NORM, kThreads>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
       have_act = true;
     }
     // block terms d_w * d_a * S are exact in f64; their sum is rounded to
@@ -190,35 +189,28 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
   }
 
   if (EPI == EPI_ARGMAX) {
+    // first pass: this workgroup's (max, lowest index), folded into one
+    // 64-bit key per batch row with an atomic max (order-preserving float
+    // bits above, inverted index below, so equal maxima keep the lowest
+    // index); second pass: the last workgroup reads the key
     best = wave_best(best);
     if (lane == 0) s_best[wave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
       ArgBest b = s_best[0];
       for (int i = 1; i < kWaves; ++i) b = better(b, s_best[i]);
-      const int64_t slot = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-      a.part_v[slot] = b.v;
-      a.part_i[slot] = b.i;
-      __threadfence();
-      const unsigned prev = atomicAdd(a.counter + blockIdx.y, 1u);
-      s_last = prev == gridDim.x - 1 ? 1 : 0;
-    }
-    __syncthreads();
-    if (s_last) {  // last workgroup of this batch row: second pass
-      __threadfence();
-      ArgBest b{-INFINITY, 0x7FFFFFFF};
-      for (int i = threadIdx.x; i < (int)gridDim.x; i += kThreads) {
-        const int64_t slot = (int64_t)blockIdx.y * gridDim.x + i;
-        b = better(b, ArgBest{__builtin_nontemporal_load(a.part_v + slot), __builtin_nontemporal_load(a.part_i + slot)});
-      }
-      b = wave_best(b);
-      if (lane == 0) s_best[wave] = b;
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        ArgBest t = s_best[0];
-        for (int i = 1; i < kWaves; ++i) t = better(t, s_best[i]);
-        if (a.argmax) a.argmax[blockIdx.y] = t.i;
-        a.counter[blockIdx.y] = 0u;  // ready for the next launch
+      const uint32_t u = __float_as_uint(b.v + 0.0f);  // -0 -> +0
+      const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      const unsigned long long key = ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (uint32_t)b.i);
+      __hip_atomic_fetch_max(a.best_key + blockIdx.y, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory();
+      const unsigned prev = arrive(a.counter + blockIdx.y);
+      if (prev == gridDim.x - 1) {  // last workgroup of this batch row
+        const unsigned long long k =
+            __hip_atomic_fetch_add(a.best_key + blockIdx.y, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (a.argmax) a.argmax[blockIdx.y] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        st_coherent(a.best_key + blockIdx.y, 0ull);  // ready for the next launch
+        st_coherent(a.counter + blockIdx.y, 0u);
         if (a.len_ptr) {
           const int seq = a.len_seq ? a.len_seq[blockIdx.y] : 0;
           a.len_ptr[seq] += a.len_add;
@@ -230,10 +222,11 @@ __global__ void __launch_bounds__(kThreads) k_gemv(GemvArgs a) {
 
 // Test hook: S[t][n][b] with the same per-lane block dot as the GEMV.
 // One wavefront per (t, n) pair, one lane per block.
-__global__ void __launch_bounds__(kThreads) k_block_dots(const int8_t* __restrict__ qa, const int8_t* __restrict__ qs,
+constexpr int kBdThreads = 256;
+__global__ void __launch_bounds__(kBdThreads) k_block_dots(const int8_t* __restrict__ qa, const int8_t* __restrict__ qs,
                                                         int K, int N, int64_t pairs, int32_t* __restrict__ S) {
   const int lane = threadIdx.x % kWave;
-  const int64_t pair = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int64_t pair = (int64_t)blockIdx.x * (kBdThreads / kWave) + threadIdx.x / kWave;
   if (pair >= pairs) return;  // uniform per wavefront
   const int t = (int)(pair / N), n = (int)(pair % N);
   const int nblocks = K / 32;
@@ -246,77 +239,98 @@ __global__ void __launch_bounds__(kThreads) k_block_dots(const int8_t* __restric
   }
 }
 
-template <int LPR, int BPL, int ROWS, bool NORM, int EPI>
+template <int LPR, int BPL, int ROWS, int WAVES, bool NORM, int EPI>
 hipError_t launch_one(const GemvArgs& a, int grid_x, int grid_y, hipStream_t s) {
   constexpr int K = 32 * LPR * BPL;
   const size_t shm = K + (K / 32) * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<LPR, BPL, ROWS, NORM, EPI>), dim3(grid_x, grid_y), dim3(kThreads), shm, s, a);
+  hipLaunchKernelGGL((k_gemv<LPR, BPL, ROWS, WAVES, NORM, EPI>), dim3(grid_x, grid_y), dim3(64 * WAVES), shm, s, a);
   return hipGetLastError();
 }
 
-template <int LPR, int BPL, int ROWS>
-hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int max_grid, int grid_y, hipStream_t s) {
-  constexpr int GPW = kWave / LPR;
-  constexpr int groups = kWaves * GPW;
-  const int rows_per_tile = groups * (epi == EPI_SWIGLU ? ROWS : ROWS);
-  a.ntiles = (a.N + rows_per_tile - 1) / rows_per_tile;
-  int grid = a.ntiles;
-  if (max_grid > 0 && grid > max_grid) grid = max_grid;
+constexpr int rows_per_tile(int lpr, int rows, int waves) { return waves * (64 / lpr) * rows; }
+
+template <int LPR, int BPL, int ROWS, int WAVES>
+hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int grid_y, hipStream_t s) {
+  const int rpt = rows_per_tile(LPR, ROWS, WAVES);
+  a.ntiles = (a.N + rpt - 1) / rpt;
+  const int grid = a.ntiles;
 #define Q8_CASE(NORM_, EPI_) \
-  if (norm == NORM_ && epi == EPI_) return launch_one<LPR, BPL, ROWS, NORM_, EPI_>(a, grid, grid_y, s);
+  if (norm == NORM_ && epi == EPI_) return launch_one<LPR, BPL, ROWS, WAVES, NORM_, EPI_>(a, grid, grid_y, s);
   Q8_CASE(true, EPI_STORE)
   Q8_CASE(false, EPI_STORE)
   Q8_CASE(false, EPI_RESIDUAL)
-  Q8_CASE(true, EPI_SWIGLU)
+  if constexpr (ROWS % 2 == 0) {
+    Q8_CASE(true, EPI_SWIGLU)
+  }
   Q8_CASE(true, EPI_ARGMAX)
   Q8_CASE(false, EPI_ARGMAX)
 #undef Q8_CASE
   return hipErrorInvalidValue;
 }
 
+// Launch shapes per K (LPR = lanes per row, BPL = blocks per lane, ROWS per
+// lane group, WAVES per workgroup): small-N matrices get few rows per
+// workgroup so that every launch spreads over all 256 CUs.
+#define Q8_SHAPES(X)                                                                     \
+  X(256, 8, 1, 2, 4) X(512, 16, 1, 2, 4) X(768, 8, 3, 2, 4)                            \
+  X(1024, 32, 1, 2, 4) X(2048, 64, 1, 2, 4) X(3072, 32, 3, 2, 4) X(4096, 64, 2, 2, 4)  \
+  X(6144, 64, 3, 2, 4) X(8192, 64, 4, 2, 4) X(12288, 64, 6, 2, 4)
+#define Q8_SMALL(X) X(2048, 64, 1, 1, 4) X(3072, 32, 3, 1, 2) X(4096, 64, 2, 1, 4) X(6144, 64, 3, 1, 4) \
+  X(8192, 64, 4, 1, 4) X(12288, 64, 6, 1, 4)
+#define Q8_ARGMAX(X) X(1024, 32, 1, 8, 4) X(4096, 64, 2, 4, 4)
+
 }  // namespace
 
 namespace q8k {
 
+namespace {
+// shape used for (K, epilogue): ARGMAX on K=1024 takes 32-row tiles, the
+// other non-SwiGLU launches the single-row shapes where they exist
+struct Shape {
+  int lpr, bpl, rows, waves;
+};
+bool pick(int K, int epi, Shape* sh) {
+#define Q8_PICK(K_, L_, B_, R_, W_) \
+  if (K == K_) { *sh = Shape{L_, B_, R_, W_}; found = true; }
+  bool found = false;
+  Q8_SHAPES(Q8_PICK)
+  if (epi != EPI_SWIGLU) { Q8_SMALL(Q8_PICK) }
+  if (epi == EPI_ARGMAX) { Q8_ARGMAX(Q8_PICK) }
+#undef Q8_PICK
+  return found;
+}
+}  // namespace
+
 int gemv_argmax_grid(int N, int K) {
-  (void)K;
-  const int tiles = (N + 31) / 32;
-  return tiles < 2048 ? tiles : 2048;
+  Shape sh;
+  if (!pick(K, EPI_ARGMAX, &sh)) return 0;
+  const int rpt = sh.waves * (64 / sh.lpr) * sh.rows;
+  return (N + rpt - 1) / rpt;
 }
 
-// Dispatch on K = 32 * LPR * BPL with LPR the largest power of two <= 64
-// dividing K/32.
 hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s) {
-  const int max_grid = (epi == EPI_ARGMAX) ? gemv_argmax_grid(a.N, a.K) : 0;
-  switch (a.K) {
-    case 256: return launch_epi<8, 1, 4>(a, norm, epi, max_grid, grid_y, s);
-    case 512: return launch_epi<16, 1, 4>(a, norm, epi, max_grid, grid_y, s);
-    case 768: return launch_epi<8, 3, 2>(a, norm, epi, max_grid, grid_y, s);
-    case 1024: return launch_epi<32, 1, 4>(a, norm, epi, max_grid, grid_y, s);
-    case 2048: return launch_epi<64, 1, 4>(a, norm, epi, max_grid, grid_y, s);
-    case 3072: return launch_epi<32, 3, 2>(a, norm, epi, max_grid, grid_y, s);
-    case 4096: return launch_epi<64, 2, 2>(a, norm, epi, max_grid, grid_y, s);
-    case 6144: return launch_epi<64, 3, 2>(a, norm, epi, max_grid, grid_y, s);
-    case 8192: return launch_epi<64, 4, 2>(a, norm, epi, max_grid, grid_y, s);
-    case 12288: return launch_epi<64, 6, 2>(a, norm, epi, max_grid, grid_y, s);
-    default: return hipErrorInvalidValue;
-  }
+  Shape sh;
+  if (!pick(a.K, epi, &sh)) return hipErrorInvalidValue;
+#define Q8_GO(K_, L_, B_, R_, W_) \
+  if (a.K == K_ && sh.lpr == L_ && sh.bpl == B_ && sh.rows == R_ && sh.waves == W_) \
+    return launch_epi<L_, B_, R_, W_>(a, norm, epi, grid_y, s);
+  Q8_SHAPES(Q8_GO)
+  Q8_SMALL(Q8_GO)
+  Q8_ARGMAX(Q8_GO)
+#undef Q8_GO
+  return hipErrorInvalidValue;
 }
 
 bool gemv_supported_k(int K) {
-  switch (K) {
-    case 256: case 512: case 768: case 1024: case 2048: case 3072: case 4096: case 6144: case 8192: case 12288:
-      return true;
-    default:
-      return false;
-  }
+  Shape sh;
+  return pick(K, EPI_STORE, &sh);
 }
 
 hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s) {
   const int64_t pairs = (int64_t)M * N;
-  const int64_t grid = (pairs + kWaves - 1) / kWaves;
+  const int64_t grid = (pairs + kBdThreads / kWave - 1) / (kBdThreads / kWave);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_block_dots, dim3((unsigned)grid), dim3(kThreads), 0, s, qa, qs, K, N, pairs, S);
+  hipLaunchKernelGGL(k_block_dots, dim3((unsigned)grid), dim3(kBdThreads), 0, s, qa, qs, K, N, pairs, S);
   return hipGetLastError();
 }
 

@@ -22,8 +22,7 @@ struct GemvArgs {
   int64_t out_stride;
   // ARGMAX epilogue (tied lm_head + two-pass argmax)
   float* logits;      // [grid_y][N] or null
-  float* part_v;      // [grid_y][grid_x] per-workgroup maxima
-  int32_t* part_i;    // [grid_y][grid_x] their indices
+  unsigned long long* best_key;  // [grid_y] running (max, lowest index) key, zero between launches
   unsigned* counter;  // [grid_y] zero between launches (the last workgroup resets it)
   int32_t* argmax;    // [grid_y] or null
   int32_t* len_ptr;   // KV lengths; the last workgroup adds len_add to len_ptr[seq]

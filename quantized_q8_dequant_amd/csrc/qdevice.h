@@ -40,6 +40,29 @@ QDEV uint16_t f32_to_bf16_bits(float x) {  // round half to even on the dropped 
 QDEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 QDEV float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
+// ---- cross-workgroup hand-off without cache-wide fences ---------------------------
+// A device-wide fence writes back and invalidates the whole L2 of the XCD;
+// thousands of workgroups doing that stall each other.  Data handed to
+// another workgroup of the same launch is instead written and read with
+// agent-scope atomic accesses (coherent across XCDs on their own), and the
+// writer waits for its stores before it bumps the arrival counter.
+template <typename T>
+QDEV void st_coherent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+QDEV T ld_coherent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+QDEV void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the compiler from moving accesses across
+  __builtin_amdgcn_s_waitcnt(0);            // vmcnt = expcnt = lgkmcnt = 0
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+QDEV unsigned arrive(unsigned* counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- wavefront reductions ----------------------------------------------------------
 template <int WIDTH>
 QDEV float wave_sum(float v) {

@@ -84,7 +84,7 @@ struct Layer {
 
 int decode_nsplit_max(int nkv, int nrows) {
   int n = 2048 / (nkv * nrows);
-  if (n > 64) n = 64;
+  if (n > 128) n = 128;
   if (n < 1) n = 1;
   return n;
 }
@@ -116,8 +116,7 @@ struct qwen3_model {
   float* q32 = nullptr;
   double* attn_part = nullptr;
   unsigned* attn_cnt = nullptr;
-  float* am_part_v = nullptr;
-  int32_t* am_part_i = nullptr;
+  unsigned long long* am_key = nullptr;
   unsigned* am_cnt = nullptr;
   size_t bytes = 0;
   // host
@@ -232,9 +231,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   const int64_t G = nh / nkv;
   m->attn_part = cv.arr<double>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
-  const int64_t amg = q8k::gemv_argmax_grid(c.vocab_size, c.hidden_size);
-  m->am_part_v = cv.arr<float>(R * amg);
-  m->am_part_i = cv.arr<int32_t>(R * amg);
+  m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
   if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
   *total = align_up(cv.off);
@@ -303,16 +300,11 @@ GemvArgs gemv_args(const QPlane& p, const float* src, int64_t src_stride, const 
   return a;
 }
 
-// Enqueue one decode step for nrows batch rows (rows r -> sequence row_seq[r],
-// token tok[r]); positions come from d_len on the device.
-int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_t* d_row_seq, float* d_logits,
-                   int32_t* d_argmax, hipStream_t s) {
-  const float eps = m->cfg.rms_norm_eps;
-  HIP_TRY(q8k::embed(d_tok, nrows, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+AttnDecodeArgs attn_args(const qwen3_model* m, const int32_t* d_row_seq, int nrows) {
   AttnDecodeArgs at{};
   at.qkv = m->qkv;
   at.qkv_stride = m->nqkv;
-  at.eps = eps;
+  at.eps = m->cfg.rms_norm_eps;
   at.rope_cos = m->rope_cos;
   at.rope_sin = m->rope_sin;
   at.kv = m->kv;
@@ -328,28 +320,62 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
   at.nsplit_max = decode_nsplit_max(m->nkv, nrows);
   at.min_rows = 32;
   at.scale = 1.0 / std::sqrt((double)m->hd);
-  for (int l = 0; l < m->L; ++l) {
-    const Layer& ly = m->layers[l];
-    HIP_TRY(q8k::gemv(gemv_args(ly.qkv, m->x, m->H, ly.attn_norm, eps, m->qkv, m->nqkv), true, EPI_STORE, nrows, s));
-    at.q_norm = ly.q_norm;
-    at.k_norm = ly.k_norm;
-    at.layer = l;
-    HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvbf16, nrows, s));
-    HIP_TRY(q8k::gemv(gemv_args(ly.o, m->attn, m->qw, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
-    HIP_TRY(q8k::gemv(gemv_args(ly.gateup, m->x, m->H, ly.ffn_norm, eps, m->h, m->F), true, EPI_SWIGLU, nrows, s));
-    HIP_TRY(q8k::gemv(gemv_args(ly.down, m->h, m->F, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
+  return at;
+}
+
+// Kernels of one decode step.  kind: 0 QKV GEMV, 1 attention, 2 o_proj,
+// 3 gate/up SwiGLU, 4 down, 5 lm_head + argmax (len_add advances lengths).
+int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32_t* d_row_seq, float* d_logits,
+                         int32_t* d_argmax, int32_t len_add, hipStream_t s) {
+  const float eps = m->cfg.rms_norm_eps;
+  if (kind == 5) {
+    GemvArgs a = gemv_args(m->emb, m->x, m->H, m->out_norm, eps, nullptr, 0);
+    a.logits = d_logits;
+    a.best_key = m->am_key;
+    a.counter = m->am_cnt;
+    a.argmax = d_argmax;
+    a.len_ptr = len_add ? m->d_len : nullptr;
+    a.len_seq = d_row_seq;
+    a.len_add = len_add;
+    HIP_TRY(q8k::gemv(a, true, EPI_ARGMAX, nrows, s));
+    return QWEN3_OK;
   }
-  GemvArgs a = gemv_args(m->emb, m->x, m->H, m->out_norm, eps, nullptr, 0);
-  a.logits = d_logits;
-  a.part_v = m->am_part_v;
-  a.part_i = m->am_part_i;
-  a.counter = m->am_cnt;
-  a.argmax = d_argmax;
-  a.len_ptr = m->d_len;
-  a.len_seq = d_row_seq;
-  a.len_add = 1;
-  HIP_TRY(q8k::gemv(a, true, EPI_ARGMAX, nrows, s));
+  const Layer& ly = m->layers[l];
+  switch (kind) {
+    case 0:
+      HIP_TRY(q8k::gemv(gemv_args(ly.qkv, m->x, m->H, ly.attn_norm, eps, m->qkv, m->nqkv), true, EPI_STORE, nrows, s));
+      break;
+    case 1: {
+      AttnDecodeArgs at = attn_args(m, d_row_seq, nrows);
+      at.q_norm = ly.q_norm;
+      at.k_norm = ly.k_norm;
+      at.layer = l;
+      HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvbf16, nrows, s));
+      break;
+    }
+    case 2:
+      HIP_TRY(q8k::gemv(gemv_args(ly.o, m->attn, m->qw, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
+      break;
+    case 3:
+      HIP_TRY(q8k::gemv(gemv_args(ly.gateup, m->x, m->H, ly.ffn_norm, eps, m->h, m->F), true, EPI_SWIGLU, nrows, s));
+      break;
+    case 4:
+      HIP_TRY(q8k::gemv(gemv_args(ly.down, m->h, m->F, nullptr, eps, m->x, m->H), false, EPI_RESIDUAL, nrows, s));
+      break;
+    default:
+      return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind");
+  }
   return QWEN3_OK;
+}
+
+// Enqueue one decode step for nrows batch rows (rows r -> sequence row_seq[r],
+// token tok[r]); positions come from d_len on the device.
+int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_t* d_row_seq, float* d_logits,
+                   int32_t* d_argmax, hipStream_t s) {
+  HIP_TRY(q8k::embed(d_tok, nrows, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+  for (int l = 0; l < m->L; ++l)
+    for (int kind = 0; kind < 5; ++kind) TRY(launch_decode_kernel(m, kind, l, nrows, d_row_seq, nullptr, nullptr, 0, s));
+  return launch_decode_kernel(m, 5, 0, nrows, d_row_seq, d_logits, d_argmax, 1, s);
 }
 
 // One prefill chunk: T tokens (already in m->d_tok) at positions pos0.. of seq.
@@ -412,8 +438,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
   if (last && (d_logits || d_argmax)) {
     GemvArgs a = gemv_args(m->emb, m->x + (int64_t)(T - 1) * m->H, m->H, m->out_norm, eps, nullptr, 0);
     a.logits = d_logits;
-    a.part_v = m->am_part_v;
-    a.part_i = m->am_part_i;
+    a.best_key = m->am_key;
     a.counter = m->am_cnt;
     a.argmax = d_argmax;
     HIP_TRY(q8k::gemv(a, true, EPI_ARGMAX, 1, s));
@@ -515,6 +540,7 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
     }
     HIP_TRY(hipMemsetAsync(m->attn_cnt, 0, (size_t)m->R * m->nkv * 4, s));
     HIP_TRY(hipMemsetAsync(m->am_cnt, 0, (size_t)m->R * 4, s));
+    HIP_TRY(hipMemsetAsync(m->am_key, 0, (size_t)m->R * 8, s));
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
     return QWEN3_OK;
@@ -635,6 +661,18 @@ int qwen3_decode_batch(qwen3_t* m, const int32_t* h_seqs, int32_t n, const int32
   HIP_TRY(hipMemcpyAsync(m->d_row_seq, h_seqs, (size_t)n * 4, hipMemcpyHostToDevice, s));
   TRY(enqueue_decode(m, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
   for (int i = 0; i < n; ++i) m->h_len[h_seqs[i]] += 1;
+  return QWEN3_OK;
+}
+
+int qwen3_replay_kernel(qwen3_t* m, int32_t seq, int32_t kind, int32_t layer, int32_t reps, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (kind < 0 || kind > 5 || layer < 0 || layer >= m->L || reps < 0)
+    return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind, layer or reps");
+  if (m->h_len[seq] + 1 > m->cap[seq]) return fail(QWEN3_E_KV_CACHE_OVERFLOW, "sequence is at capacity");
+  for (int r = 0; r < reps; ++r)
+    TRY(launch_decode_kernel(m, kind, layer, 1, m->d_seq_ids + seq, nullptr, nullptr, 0, S(stream)));
   return QWEN3_OK;
 }
 

@@ -256,6 +256,10 @@ class Qwen3Model:
         check(lib().qwen3_kv_export(self.handle, seq, layer, k.data_ptr(), v.data_ptr(), _stream()))
         return k, v
 
+    def replay_kernel(self, kind: int, layer: int = 0, reps: int = 1, seq: int = 0):
+        """Enqueue `reps` launches of one decode-step kernel (benchmark hook)."""
+        check(lib().qwen3_replay_kernel(self.handle, seq, kind, layer, reps, _stream()))
+
     def kv_len(self, seq: int = 0) -> int:
         out = C.c_int32()
         check(lib().qwen3_kv_len(self.handle, seq, C.byref(out)))
