@@ -229,6 +229,14 @@ int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs
 int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs, int64_t n,
                           int8_t* d_qa, uint16_t* d_da, int32_t* d_s, void* stream);
 
+/* The bf16-weight linear the bf16 models use (prefill and batched decode):
+ * y[t, j] = f32( sum_i w[j, i] * x[t, i] ) for t < m, j < n, with x f32
+ * [m, k] (row stride k), w bf16 bits [n, k] widened exactly, every product
+ * and the sum in f64, rounded once (the exact in-register widening of the
+ * "fucina_llm" reference page, section 13).  k % 32 == 0; y f32 [m, n]. */
+int qwen3_bf16_linear(const float* d_x, int64_t m, int64_t k, const uint16_t* d_w, int64_t n,
+                      float* d_y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ from ._lib import Qwen3Error, lib  # noqa: F401
 from .model import (  # noqa: F401
     Qwen3Config,
     Qwen3Model,
+    bf16_linear,
     encode_bf16,
     encode_q8_0,
     q8_0_block_dots,

@@ -123,8 +123,29 @@ struct AttnPrefillArgs {
   float* out;  // [T][nh*hd]
 };
 
+// Linear with bf16 weights (see k_gemm_bf16.hip): C[M, N] = X . W^T.
+struct GemmBf16Args {
+  const float* x;  // [M][lda] f32 activations
+  int64_t lda;
+  const uint16_t* w;  // [N][K] bf16 bits
+  int M, N, K;
+  float* out;  // STORE/RESIDUAL: [M][ldc]; SWIGLU: [M][ldc] hidden units (N/2 of them)
+  int64_t ldc;
+  // ARGMAX epilogue (as GemvArgs, one key per row, one counter per 64/128-row tile)
+  float* logits;  // [M][N] or null
+  unsigned long long* best_key;
+  unsigned* counter;
+  int32_t* argmax;
+  int32_t* len_ptr;
+  const int32_t* len_seq;
+  int32_t len_add;
+};
+
 namespace q8k {
 hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s);
+hipError_t gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
+hipError_t rows_norm(const float* x, int64_t ldx, int T, int K, const float* w, float eps, float* y, int64_t ldy,
+                     hipStream_t s);
 hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, bool kv_bf16, hipStream_t s);
 hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf16, hipStream_t s);
 bool attn_prefill_supported(int hd, int group);

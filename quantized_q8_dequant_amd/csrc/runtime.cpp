@@ -114,6 +114,7 @@ struct qwen3_model {
   int8_t* qa = nullptr;
   float* da = nullptr;
   float* q32 = nullptr;
+  float* xn = nullptr;  // normalised rows (bf16-weight models: the norm is not fused)
   double* attn_part = nullptr;
   unsigned* attn_cnt = nullptr;
   unsigned long long* am_key = nullptr;
@@ -143,8 +144,6 @@ int validate(const qwen3_config* c) {
     return fail(QWEN3_E_INVALID_CONFIG, "rope_theta must be > 1");
   if (c->weight_type != QWEN3_W_Q8_0 && c->weight_type != QWEN3_W_BF16)
     return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown weight_type");
-  if (c->weight_type == QWEN3_W_BF16)
-    return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "bf16 weights are not built in this library version");
   if (c->kv_type != QWEN3_KV_F32 && c->kv_type != QWEN3_KV_BF16)
     return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown kv_type");
   const int qw = c->num_attention_heads * c->head_dim;
@@ -153,8 +152,9 @@ int validate(const qwen3_config* c) {
   const int G = c->num_attention_heads / c->num_key_value_heads;
   if (!q8k::attn_decode_supported(c->head_dim, G) || !q8k::attn_prefill_supported(c->head_dim, G))
     return fail(QWEN3_E_INVALID_CONFIG, "head_dim must be 64 or 128 and heads/kv_heads one of 1, 2, 4, 8");
-  if (!q8k::gemv_supported_k(c->hidden_size) || !q8k::gemv_supported_k(qw) ||
-      !q8k::gemv_supported_k(c->intermediate_size))
+  if (c->weight_type == QWEN3_W_Q8_0 &&
+      (!q8k::gemv_supported_k(c->hidden_size) || !q8k::gemv_supported_k(qw) ||
+       !q8k::gemv_supported_k(c->intermediate_size)))
     return fail(QWEN3_E_INVALID_CONFIG,
                 "hidden_size, heads*head_dim and intermediate_size must each be one of 256, 512, 768, "
                 "1024, 2048, 3072, 4096, 6144, 8192, 12288");
@@ -180,8 +180,12 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     p.k = k;
     size_t n;
     if (!mul_ok((size_t)rows, (size_t)k, &n)) cv.overflow = true;
-    p.qs = cv.arr<int8_t>(n);
-    p.sc = cv.arr<uint16_t>(n / 32);
+    if (m->wbf16) {
+      p.bf = cv.arr<uint16_t>(n);
+    } else {
+      p.qs = cv.arr<int8_t>(n);
+      p.sc = cv.arr<uint16_t>(n / 32);
+    }
   };
   m->layers.assign(c.num_layers, Layer{});
   plane(m->emb, V, H);
@@ -227,6 +231,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->qa = cv.arr<int8_t>(R * m->kmax);
   m->da = cv.arr<float>(R * (m->kmax / 32));
   m->q32 = cv.arr<float>(R * qw);
+  if (m->wbf16) m->xn = cv.arr<float>(R * H);
   // decode attention partials: rows * nsplit <= 2048 / nkv (see decode_nsplit_max)
   const int64_t G = nh / nkv;
   m->attn_part = cv.arr<double>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
@@ -266,8 +271,26 @@ hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int repack(const void* src, QPlane& p, int64_t rows, int64_t row0, int inter, hipStream_t s) {
   if (!src) return fail(QWEN3_E_INVALID_ARGUMENT, "a weight pointer is null");
-  HIP_TRY(q8k::repack_q8_0(src, rows, p.k, p.qs, p.sc, row0, inter, s));
+  if (p.bf)
+    HIP_TRY(q8k::repack_bf16(src, rows, p.k, p.bf, row0, inter, s));
+  else
+    HIP_TRY(q8k::repack_q8_0(src, rows, p.k, p.qs, p.sc, row0, inter, s));
   return QWEN3_OK;
+}
+
+const void* plane_rows(const QPlane& p) { return p.bf ? (const void*)p.bf : (const void*)p.qs; }
+
+GemmBf16Args bf16_args(const QPlane& p, const float* x, int64_t lda, int M, float* out, int64_t ldc) {
+  GemmBf16Args g{};
+  g.x = x;
+  g.lda = lda;
+  g.w = p.bf;
+  g.M = M;
+  g.N = (int)p.rows;
+  g.K = (int)p.k;
+  g.out = out;
+  g.ldc = ldc;
+  return g;
 }
 
 int copy_f32(float* dst, const void* src, int64_t n, hipStream_t s) {
@@ -328,6 +351,43 @@ AttnDecodeArgs attn_args(const qwen3_model* m, const int32_t* d_row_seq, int nro
 int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32_t* d_row_seq, float* d_logits,
                          int32_t* d_argmax, int32_t len_add, hipStream_t s) {
   const float eps = m->cfg.rms_norm_eps;
+  if (m->wbf16 && kind != 1) {
+    // bf16 weights: RMSNorm rows (where the step has one), then the f64-MFMA linear
+    const int64_t H = m->H;
+    if (kind == 5) {
+      HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, m->out_norm, eps, m->xn, H, s));
+      GemmBf16Args g = bf16_args(m->emb, m->xn, H, nrows, nullptr, 0);
+      g.logits = d_logits;
+      g.best_key = m->am_key;
+      g.counter = m->am_cnt;
+      g.argmax = d_argmax;
+      g.len_ptr = len_add ? m->d_len : nullptr;
+      g.len_seq = d_row_seq;
+      g.len_add = len_add;
+      HIP_TRY(q8k::gemm_bf16(g, EPI_ARGMAX, s));
+      return QWEN3_OK;
+    }
+    const Layer& ly = m->layers[l];
+    switch (kind) {
+      case 0:
+        HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, ly.attn_norm, eps, m->xn, H, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.qkv, m->xn, H, nrows, m->qkv, m->nqkv), EPI_STORE, s));
+        break;
+      case 2:
+        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.o, m->attn, m->qw, nrows, m->x, H), EPI_RESIDUAL, s));
+        break;
+      case 3:
+        HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, ly.ffn_norm, eps, m->xn, H, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.gateup, m->xn, H, nrows, m->h, m->F), EPI_SWIGLU, s));
+        break;
+      case 4:
+        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.down, m->h, m->F, nrows, m->x, H), EPI_RESIDUAL, s));
+        break;
+      default:
+        return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind");
+    }
+    return QWEN3_OK;
+  }
   if (kind == 5) {
     GemvArgs a = gemv_args(m->emb, m->x, m->H, m->out_norm, eps, nullptr, 0);
     a.logits = d_logits;
@@ -372,7 +432,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
 // token tok[r]); positions come from d_len on the device.
 int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_t* d_row_seq, float* d_logits,
                    int32_t* d_argmax, hipStream_t s) {
-  HIP_TRY(q8k::embed(d_tok, nrows, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+  HIP_TRY(q8k::embed(d_tok, nrows, m->V, m->H, plane_rows(m->emb), m->emb.sc, m->wbf16, m->x, s));
   for (int l = 0; l < m->L; ++l)
     for (int kind = 0; kind < 5; ++kind) TRY(launch_decode_kernel(m, kind, l, nrows, d_row_seq, nullptr, nullptr, 0, s));
   return launch_decode_kernel(m, 5, 0, nrows, d_row_seq, d_logits, d_argmax, 1, s);
@@ -382,7 +442,7 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
 int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, float* d_logits, int32_t* d_argmax,
                           hipStream_t s) {
   const float eps = m->cfg.rms_norm_eps;
-  HIP_TRY(q8k::embed(m->d_tok, T, m->V, m->H, m->emb.qs, m->emb.sc, m->wbf16, m->x, s));
+  HIP_TRY(q8k::embed(m->d_tok, T, m->V, m->H, plane_rows(m->emb), m->emb.sc, m->wbf16, m->x, s));
   const int64_t head_elems = (int64_t)m->cap[seq] * m->hd;
   for (int l = 0; l < m->L; ++l) {
     const Layer& ly = m->layers[l];
@@ -392,9 +452,14 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     g.da = m->da;
     g.M = T;
     // attention input: RMSNorm + quantise, fused QKV GEMM
-    HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
-    g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
-    HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+    if (m->wbf16) {
+      HIP_TRY(q8k::rows_norm(m->x, m->H, T, m->H, ly.attn_norm, eps, m->xn, m->H, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.qkv, m->xn, m->H, T, m->qkv, m->nqkv), EPI_STORE, s));
+    } else {
+      HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
+      g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
+      HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+    }
     QkRopeArgs qr{};
     qr.qkv = m->qkv;
     qr.qkv_stride = m->nqkv;
@@ -423,6 +488,14 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     ap.scale = 1.0 / std::sqrt((double)m->hd);
     ap.out = m->attn;
     HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvbf16, s));
+    if (m->wbf16) {
+      const int64_t H = m->H;
+      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.o, m->attn, m->qw, T, m->x, H), EPI_RESIDUAL, s));
+      HIP_TRY(q8k::rows_norm(m->x, H, T, m->H, ly.ffn_norm, eps, m->xn, H, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.gateup, m->xn, H, T, m->h, m->F), EPI_SWIGLU, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.down, m->h, m->F, T, m->x, H), EPI_RESIDUAL, s));
+      continue;
+    }
     // o_proj + residual
     HIP_TRY(q8k::rows_quant(m->attn, T, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
     g.qs = ly.o.qs, g.sc = ly.o.sc, g.N = (int)ly.o.rows, g.K = m->qw, g.out = m->x, g.ldc = m->H;
@@ -435,7 +508,16 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     g.qs = ly.down.qs, g.sc = ly.down.sc, g.N = (int)ly.down.rows, g.K = m->F, g.out = m->x, g.ldc = m->H;
     HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
   }
-  if (last && (d_logits || d_argmax)) {
+  if (last && (d_logits || d_argmax) && m->wbf16) {
+    const int64_t H = m->H;
+    HIP_TRY(q8k::rows_norm(m->x + (int64_t)(T - 1) * H, H, 1, m->H, m->out_norm, eps, m->xn, H, s));
+    GemmBf16Args g = bf16_args(m->emb, m->xn, H, 1, nullptr, 0);
+    g.logits = d_logits;
+    g.best_key = m->am_key;
+    g.counter = m->am_cnt;
+    g.argmax = d_argmax;
+    HIP_TRY(q8k::gemm_bf16(g, EPI_ARGMAX, s));
+  } else if (last && (d_logits || d_argmax)) {
     GemvArgs a = gemv_args(m->emb, m->x + (int64_t)(T - 1) * m->H, m->H, m->out_norm, eps, nullptr, 0);
     a.logits = d_logits;
     a.best_key = m->am_key;
@@ -767,6 +849,21 @@ int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* 
   hipStream_t s = S(stream);
   HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, d_qa, nullptr, d_da, s));
   HIP_TRY(q8k::block_dots(d_qa, d_qs, (int)m, (int)k, (int)n, d_s, s));
+  return QWEN3_OK;
+}
+
+int qwen3_bf16_linear(const float* d_x, int64_t m, int64_t k, const uint16_t* d_w, int64_t n, float* d_y,
+                      void* stream) {
+  g_err.clear();
+  if (m <= 0 || n <= 0 || k <= 0) return fail(QWEN3_E_INVALID_ARGUMENT, "m, n, k must be positive");
+  if (k % 32) return fail(QWEN3_E_INVALID_ARGUMENT, "k must be a multiple of 32");
+  if (!d_x || !d_w || !d_y) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX) return fail(QWEN3_E_INVALID_ARGUMENT, "size too large");
+  QPlane p;
+  p.bf = const_cast<uint16_t*>(d_w);
+  p.rows = n;
+  p.k = k;
+  HIP_TRY(q8k::gemm_bf16(bf16_args(p, d_x, k, (int)m, d_y, n), EPI_STORE, S(stream)));
   return QWEN3_OK;
 }
 

@@ -122,6 +122,15 @@ def q8_0_linear(x: torch.Tensor, qs: torch.Tensor, sc: torch.Tensor) -> torch.Te
     return y
 
 
+def bf16_linear(x: torch.Tensor, w_bits: torch.Tensor) -> torch.Tensor:
+    """x f32 [m, k] times bf16 weights (int16 bits [n, k]) transposed -> f32 [m, n]."""
+    m, k = x.shape
+    n = w_bits.shape[0]
+    y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    check(lib().qwen3_bf16_linear(x.data_ptr(), m, k, w_bits.data_ptr(), n, y.data_ptr(), _stream()))
+    return y
+
+
 def q8_0_block_dots(x: torch.Tensor, qs: torch.Tensor):
     """(qa int8 [m, k], da f16 bits int16 [m, k/32], S int32 [m, n, k/32])."""
     m, k = x.shape

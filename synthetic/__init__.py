@@ -23,5 +23,6 @@ from .gen import (  # noqa: F401
     iter_weights,
     gen_prompt,
     gen_lengths,
+    gen_prompts,
     gen_normal_rows,
 )

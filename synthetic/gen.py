@@ -130,3 +130,13 @@ def gen_normal_rows(shp: tuple[int, ...], seed: int, scale: float = 1.0) -> np.n
     if scale != 1.0:
         out *= np.float32(scale)
     return out
+
+
+def gen_prompts(vocab: int, lengths, seed: int) -> list[np.ndarray]:
+    """One uniform-random prompt per length, each from its own child stream
+    of SeedSequence(seed) (the ragged batch of independent sequences)."""
+    kids = np.random.SeedSequence(seed).spawn(len(lengths))
+    return [
+        np.random.Generator(np.random.PCG64(k)).integers(0, vocab, size=int(n), dtype=np.int32)
+        for k, n in zip(kids, lengths)
+    ]

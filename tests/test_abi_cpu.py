@@ -50,6 +50,11 @@ def test_workspace_bytes_cover_weights_and_cache():
     # a bf16 cache halves the KV part
     n2 = workspace_bytes(_cfg(s, kv_type="bf16"), [768])
     assert n - n2 >= kv // 2 - 1024 * 1024
+    # bf16 weights take two bytes per weight
+    nb = workspace_bytes(_cfg(s, weight_type="bf16", kv_type="bf16"), [768])
+    bf = (per_layer * s.num_layers + s.vocab_size * s.hidden_size) * 2
+    assert nb >= bf + kv // 2
+    assert nb < (bf + kv // 2) * 1.5
     # 8B at 32k context fits easily in 288 GB
     assert workspace_bytes(_cfg(QWEN3_8B), [32776]) < 20e9
 
@@ -126,5 +131,8 @@ def test_null_handle_and_op_argument_errors():
     assert lib.qwen3_q8_0_linear(0x1000, 2, 1024, 0x2000, 0x3000, 8, 0x4000, None, None) == -1
     assert lib.qwen3_q8_0_block_dots(0x1000, 1, 48, 0x2000, 4, 0x3000, 0x4000, 0x5000, None) == -1
     assert lib.qwen3_linear_work_bytes(4, 1024) >= 4 * 1024 + 4 * 32 * 4
+    assert lib.qwen3_bf16_linear(0x1000, 2, 48, 0x2000, 8, 0x3000, None) == -1  # k % 32
+    assert lib.qwen3_bf16_linear(0x1000, 0, 64, 0x2000, 8, 0x3000, None) == -1
+    assert lib.qwen3_bf16_linear(None, 2, 64, 0x2000, 8, 0x3000, None) == -1
     # encoding zero values enqueues nothing
     assert lib.qwen3_q8_0_encode(None, 0, None, None) == 0

@@ -190,3 +190,202 @@ def test_qwen3_0_6b_prefill_and_decode_matches_oracle():
     del w
     rtoks, rlogits = ref.generate(prompt, steps, ref.new_cache(wl.kv_capacity))
     check_against_oracle(toks, logits, rtoks, rlogits)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_qwen3_0_6b_prefill_4096_one_call_matches_oracle():
+    """The prefill-dominated workload: a 4096-token prompt in one prefill call
+    (a single 4096-row chunk through the MFMA GEMM and attention tiles), then
+    32 greedy decode steps."""
+    wl = WORKLOADS["0.6b-prefill4096"]
+    w = gen_weights(QWEN3_0_6B, wl.weight_seed)
+    prompt = gen_prompt(QWEN3_0_6B.vocab_size, wl.prompt_len, wl.prompt_seed)
+    gpu = make(QWEN3_0_6B, w, [wl.kv_capacity], max_batch_tokens=wl.prompt_len)
+    toks, logits = gpu_generate(gpu, prompt, wl.decode_steps)
+    # the same prompt in 1024-row chunks gives the same cache and logits
+    chunked = make(QWEN3_0_6B, w, [wl.kv_capacity], max_batch_tokens=1024)
+    lg_c, am_c = chunked.prefill(prompt)
+    assert int(am_c.item()) == toks[0]
+    assert rel_err(lg_c.cpu().numpy(), logits[0]) <= TOL
+    for layer in (0, QWEN3_0_6B.num_layers - 1):
+        k1, v1 = gpu.kv_export(0, layer)
+        k2, v2 = chunked.kv_export(0, layer)
+        assert torch.equal(k1[:, : wl.prompt_len], k2) and torch.equal(v1[:, : wl.prompt_len], v2)
+    chunked.close()
+    gpu.close()
+    del gpu, chunked
+    torch.cuda.empty_cache()
+    ref = om.Model(QWEN3_0_6B, w)
+    del w
+    rtoks, rlogits = ref.generate(prompt, wl.decode_steps, ref.new_cache(wl.kv_capacity))
+    check_against_oracle(toks, logits, rtoks, rlogits)
+
+
+# ---- bf16 weights (f32 activations x exactly widened bf16, f64 sums) ----------------
+
+TINY_BF16 = TINY.with_(name="tiny-bf16", weight_type="bf16", kv_type="bf16")
+
+
+@pytest.fixture(scope="module")
+def tiny_bf16_w():
+    return gen_weights(TINY_BF16, 101)
+
+
+@pytest.fixture(scope="module")
+def tiny_bf16_ref(tiny_bf16_w):
+    return om.Model(TINY_BF16, tiny_bf16_w)
+
+
+def test_tiny_bf16_weights_match_oracle(tiny_bf16_w, tiny_bf16_ref):
+    prompt = gen_prompt(TINY_BF16.vocab_size, 45, 31)
+    for mbt in (0, 16):  # one chunk; 16-row chunks with a ragged tail
+        gpu = make(TINY_BF16, tiny_bf16_w, [64], max_batch_tokens=mbt)
+        toks, logits = gpu_generate(gpu, prompt, 8)
+        rtoks, rlogits = tiny_bf16_ref.generate(prompt, 8, tiny_bf16_ref.new_cache(64))
+        check_against_oracle(toks, logits, rtoks, rlogits)
+        for lg, t in zip(logits, toks):
+            assert int(np.argmax(lg)) == t
+
+
+def test_tiny_bf16_batched_decode_matches_oracle(tiny_bf16_w, tiny_bf16_ref):
+    prompts = [gen_prompt(TINY_BF16.vocab_size, n, 40 + n) for n in (3, 20, 61, 9)]
+    gpu = make(TINY_BF16, tiny_bf16_w, [72] * 4)
+    first = [int(gpu.prefill(p, seq=s)[1].item()) for s, p in enumerate(prompts)]
+    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
+    logits = torch.empty((4, TINY_BF16.vocab_size), dtype=torch.float32, device="cuda:0")
+    am = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    outs = []
+    for _ in range(5):
+        gpu.decode_batch([0, 1, 2, 3], toks, logits, am)
+        outs.append((logits.cpu().numpy().copy(), am.cpu().numpy().copy()))
+        toks = am.clone()
+    for s, p in enumerate(prompts):
+        rt, rl = tiny_bf16_ref.generate(p, 5, tiny_bf16_ref.new_cache(72))
+        assert rt[0] == first[s]
+        for i in range(5):
+            assert rel_err(outs[i][0][s], rl[i + 1]) <= TOL
+            assert outs[i][1][s] == rt[i + 1]
+
+
+def oracle_cache_from_gpu(ref, gpu, seq, capacity):
+    """An oracle KV cache holding the GPU's cache of one sequence."""
+    s = ref.shape
+    cache = ref.new_cache(capacity)
+    n = gpu.kv_len(seq)
+    for layer in range(s.num_layers):
+        k, v = gpu.kv_export(seq, layer)
+        cache.k[layer][:n] = k.cpu().numpy().transpose(1, 0, 2)
+        cache.v[layer][:n] = v.cpu().numpy().transpose(1, 0, 2)
+    cache.len = n
+    return cache
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_qwen3_0_6b_bf16_ragged_batch_matches_oracle():
+    """bf16 0.6B, four sequences of ragged lengths, full oracle runs."""
+    from synthetic import QWEN3_0_6B_BF16, gen_prompts
+
+    shape = QWEN3_0_6B_BF16
+    w = gen_weights(shape, 501)
+    lengths = [37, 300, 129, 1030]
+    prompts = gen_prompts(shape.vocab_size, lengths, 502)
+    steps = 3
+    gpu = make(shape, w, [n + steps + 1 for n in lengths])
+    first = [int(gpu.prefill(p, seq=s)[1].item()) for s, p in enumerate(prompts)]
+    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
+    logits = torch.empty((4, shape.vocab_size), dtype=torch.float32, device="cuda:0")
+    am = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    outs = []
+    for _ in range(steps):
+        gpu.decode_batch([0, 1, 2, 3], toks, logits, am)
+        outs.append((logits.cpu().numpy().copy(), am.cpu().numpy().copy()))
+        toks = am.clone()
+    gpu.close()
+    del gpu
+    torch.cuda.empty_cache()
+    ref = om.Model(shape, w)
+    del w
+    for s, p in enumerate(prompts):
+        rt, rl = ref.generate(p, steps, ref.new_cache(len(p) + steps + 1))
+        assert rt[0] == first[s]
+        for i in range(steps):
+            assert rel_err(outs[i][0][s], rl[i + 1]) <= TOL, (s, i)
+            assert outs[i][1][s] == rt[i + 1], (s, i)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_bf16_batch64_ragged_workload():
+    """The batched bf16 workload at full size: 64 sequences with lengths drawn
+    from 1024..16384, each filled by prefill, then 128 lockstep greedy steps.
+
+    Checked: every step's token is the argmax of its own logits; for the
+    shortest and the longest sequence, the first 32 cache rows of every layer
+    equal the oracle's (rows of early positions do not depend on later
+    tokens), and the oracle, started from the GPU's cache, reproduces the
+    logits and tokens of the first two batched steps and of the last one."""
+    from synthetic import QWEN3_0_6B_BF16, gen_lengths, gen_prompts
+
+    wl = WORKLOADS["0.6b-bf16-batch64"]
+    shape = QWEN3_0_6B_BF16
+    lengths = gen_lengths(wl.n_seqs, wl.min_len, wl.max_len, wl.length_seed)
+    prompts = gen_prompts(shape.vocab_size, lengths, wl.prompt_seed)
+    w = gen_weights(shape, wl.weight_seed)
+    caps = [int(n) + wl.decode_steps for n in lengths]
+    gpu = make(shape, w, caps)
+    first = []
+    for s, p in enumerate(prompts):
+        first.append(int(gpu.prefill(p, seq=s, logits=False)[1].item()))
+    n = wl.n_seqs
+    seqs = list(range(n))
+    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
+    logits = torch.empty((n, shape.vocab_size), dtype=torch.float32, device="cuda:0")
+    am = torch.empty(n, dtype=torch.int32, device="cuda:0")
+    picks = [int(np.argmin(lengths)), int(np.argmax(lengths))]
+    kept = {}
+    ref = om.Model(shape, w)
+    del w
+    caches = {}
+    for step in range(wl.decode_steps):
+        if step == wl.decode_steps - 1:  # oracle caches just before the last step
+            caches_last = {s: oracle_cache_from_gpu(ref, gpu, s, caps[s]) for s in picks}
+            tok_last = {s: int(toks[s].item()) for s in picks}
+        if step == 0:
+            caches = {s: oracle_cache_from_gpu(ref, gpu, s, caps[s]) for s in picks}
+        gpu.decode_batch(seqs, toks, logits, am)
+        lg = logits.cpu().numpy()
+        amh = am.cpu().numpy()
+        assert np.array_equal(np.argmax(lg, axis=1), amh), f"step {step}"
+        if step in (0, 1, wl.decode_steps - 1):
+            kept[step] = (lg[picks].copy(), amh[picks].copy())
+        toks = am.clone()
+    for s in picks:
+        assert gpu.kv_len(s) == lengths[s] + wl.decode_steps
+    # early cache rows against the oracle's own prefill of the first 32 tokens
+    for i, s in enumerate(picks):
+        rc = ref.new_cache(32)
+        ref.forward(prompts[s][:32], rc)
+        for layer in (0, shape.num_layers // 2, shape.num_layers - 1):
+            k, v = gpu.kv_export(s, layer)
+            for g, o in ((k, rc.k[layer][:32]), (v, rc.v[layer][:32])):
+                g = g.cpu().numpy()[:, :32].transpose(1, 0, 2)
+                # both sides round to bf16 on store: at most one bf16 ulp apart
+                assert np.all(np.abs(g - o) <= 2.0**-8 * np.abs(o)), (s, layer)
+                assert np.mean(g == o) >= 0.99, (s, layer)
+    gpu.close()
+    del gpu
+    torch.cuda.empty_cache()
+    for i, s in enumerate(picks):
+        cache = caches[s]
+        tok = first[s]
+        for step in (0, 1):
+            lr = ref.forward([tok], cache)[0]
+            assert rel_err(kept[step][0][i], lr) <= TOL, (s, step)
+            assert kept[step][1][i] == int(np.argmax(lr)), (s, step)
+            tok = int(kept[step][1][i])
+        lr = ref.forward([tok_last[s]], caches_last[s])[0]
+        last = wl.decode_steps - 1
+        assert rel_err(kept[last][0][i], lr) <= TOL, (s, last)
+        assert kept[last][1][i] == int(np.argmax(lr)), (s, last)

@@ -103,3 +103,24 @@ def test_linear_matches_oracle(m, k, n):
     bound = _linear_bound(x, ow)
     err = np.abs(y - ref)
     assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+
+
+@pytest.mark.parametrize(
+    "m,k,n",
+    [(1, 1024, 4096), (7, 256, 64), (64, 1024, 1024), (64, 2048, 1000), (130, 3072, 320), (200, 1024, 151)],
+)
+def test_bf16_linear_matches_oracle(m, k, n):
+    """bf16 weights x f32 activations: products and sum in f64, rounded once,
+    as the oracle does; only the f64 summation order differs, so results
+    agree exactly but for a rounding tie (at most one f32 ulp)."""
+    from oracle import ops
+    from quantized_q8_dequant_amd import bf16_linear, encode_bf16
+
+    x = gen_normal_rows((m, k), seed=11 * m + k, scale=1.0)
+    w = gen_normal_rows((n, k), seed=13 * n + k, scale=0.02)
+    wb = encode_bf16(torch.from_numpy(w).to(DEV))
+    y = bf16_linear(torch.from_numpy(x).to(DEV), wb).cpu().numpy()
+    ref = ops.bf16_linear(x, ops.bf16_round(w))
+    ulps = np.abs(y.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, f"max {ulps.max()} ulps"
+    assert (ulps == 0).mean() >= 0.999
