@@ -91,18 +91,28 @@ class Model:
     encoder; bf16 models round them to bf16.  Norm weights stay f32.
     """
 
-    def __init__(self, shape, weights: dict):
+    def __init__(self, shape, weights: dict, threads: int = 1):
+        """threads > 1 encodes the tensors in a thread pool (same results;
+        the encoder is independent per tensor)."""
         self.shape = shape
-        self.w = {}
-        for name, arr in weights.items():
+        if shape.weight_type not in ("q8_0", "bf16"):
+            raise ValueError(shape.weight_type)
+
+        def prep(arr):
             if arr.ndim == 1:
-                self.w[name] = np.asarray(arr, dtype=np.float32)
-            elif shape.weight_type == "q8_0":
-                self.w[name] = q8_0.Q8Weight(arr)
-            elif shape.weight_type == "bf16":
-                self.w[name] = ops.bf16_round(arr)
-            else:
-                raise ValueError(shape.weight_type)
+                return np.asarray(arr, dtype=np.float32)
+            if shape.weight_type == "q8_0":
+                return q8_0.Q8Weight(arr)
+            return ops.bf16_round(arr)
+
+        if threads > 1:
+            import concurrent.futures as cf
+
+            with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+                futs = {name: ex.submit(prep, arr) for name, arr in weights.items()}
+                self.w = {name: f.result() for name, f in futs.items()}
+        else:
+            self.w = {name: prep(arr) for name, arr in weights.items()}
 
     # -- building blocks -------------------------------------------------
     def linear(self, x: np.ndarray, name: str) -> np.ndarray:

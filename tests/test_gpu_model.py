@@ -20,6 +20,11 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
 
+def progress(msg):
+    """A progress line for long cases (visible with pytest -s)."""
+    print(f"[{os.path.basename(__file__)}] {msg}", flush=True)
+
+
 def rel_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
@@ -389,3 +394,94 @@ def test_bf16_batch64_ragged_workload():
         last = wl.decode_steps - 1
         assert rel_err(kept[last][0][i], lr) <= TOL, (s, last)
         assert kept[last][1][i] == int(np.argmax(lr)), (s, last)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(2400)
+def test_qwen3_8b_long_context_matches_oracle():
+    """Qwen3-8B shape, Q8_0 weights, bf16 KV cache: the 2048-token prompt, one
+    decode step, then decode steps at KV lengths 16384 and 32768 (each cache
+    filled by prefilling a seeded random prompt of that length).
+
+    The oracle cannot redo a 2048..32768-token prefill of an 8B model on the
+    host, so it starts from the GPU's cache: rows of the first 16 positions
+    are checked against the oracle's own 16-token prefill (one bf16 ulp),
+    the prefill's last-row logits against the oracle's forward of the last
+    prompt token over the GPU's first 2047 rows, and each decode step's
+    logits and token against the oracle's step over the GPU's cache."""
+    from synthetic import QWEN3_8B
+
+    wl = WORKLOADS["8b-longctx"]
+    shape = QWEN3_8B
+    w = gen_weights(shape, wl.weight_seed)
+    progress("8B weights drawn")
+    prompt = gen_prompt(shape.vocab_size, wl.prompt_len, wl.prompt_seed)
+    gpu = make(shape, w, [wl.kv_capacity], max_batch_tokens=2048)
+    progress("8B model created on the GPU")
+    L_ = shape.num_layers
+
+    def export_all():
+        n = gpu.kv_len(0)
+        ks, vs = [], []
+        for layer in range(L_):
+            k, v = gpu.kv_export(0, layer)
+            ks.append(k.cpu().numpy().transpose(1, 0, 2).copy())
+            vs.append(v.cpu().numpy().transpose(1, 0, 2).copy())
+        return n, ks, vs
+
+    lg, am = gpu.prefill(prompt)
+    pre_logits, pre_tok = lg.cpu().numpy().copy(), int(am.item())
+    n2048, ks2048, vs2048 = export_all()
+    lg, am = gpu.decode_step()
+    step_logits, step_tok = lg.cpu().numpy().copy(), int(am.item())
+    long = {}
+    for L in wl.decode_contexts[1:]:
+        gpu.reset()
+        p = gen_prompt(shape.vocab_size, L, wl.prompt_seed + L)
+        _, am = gpu.prefill(p, logits=False)
+        t0 = int(am.item())
+        n, ks, vs = export_all()
+        lg, am = gpu.decode_step()
+        long[L] = (t0, n, ks, vs, lg.cpu().numpy().copy(), int(am.item()))
+        progress(f"GPU prefill {L} + decode step done")
+    gpu.close()
+    del gpu
+    torch.cuda.empty_cache()
+    ref = om.Model(shape, w, threads=16)
+    del w
+    progress("oracle model built")
+
+    def cache_of(n, ks, vs, rows):
+        c = ref.new_cache(n + 1)
+        for layer in range(L_):
+            c.k[layer][:rows] = ks[layer][:rows]
+            c.v[layer][:rows] = vs[layer][:rows]
+        c.len = rows
+        return c
+
+    # early rows
+    rc = ref.new_cache(16)
+    ref.forward(prompt[:16], rc)
+    for layer in (0, L_ // 2, L_ - 1):
+        for g, o in ((ks2048[layer][:16], rc.k[layer][:16]), (vs2048[layer][:16], rc.v[layer][:16])):
+            assert np.all(np.abs(g - o) <= 2.0**-8 * np.abs(o)), layer
+            assert np.mean(g == o) >= 0.99, layer
+    # the prefill's last row, then the decode step at len 2048
+    assert n2048 == wl.prompt_len
+    c = cache_of(n2048, ks2048, vs2048, n2048 - 1)
+    lr = ref.forward(prompt[-1:], c)[0]
+    assert rel_err(pre_logits, lr) <= TOL
+    assert pre_tok == int(np.argmax(lr))
+    progress("oracle: prefill last row checked")
+    lr = ref.forward([pre_tok], c)[0]
+    assert rel_err(step_logits, lr) <= TOL
+    assert step_tok == int(np.argmax(lr))
+    del c, ks2048, vs2048
+    for L, (t0, n, ks, vs, lg, tok) in long.items():
+        assert n == L
+        c = cache_of(n, ks, vs, n)
+        lr = ref.forward([t0], c)[0]
+        assert rel_err(lg, lr) <= TOL, L
+        assert tok == int(np.argmax(lr)), L
+        progress(f"oracle: decode at {L} checked")
+        del c
