@@ -2,17 +2,21 @@
 """Benchmark of the MI355X forward pass of a Qwen3 dense decoder over Q8_0
 weights.
 
-Workload (one "step"): the Qwen3-0.6B shape with synthetic Q8_0 weights
-(N(0, 0.02) quantised; f32 norm weights 1 + N(0, 0.1)), one prefill of a
-512-token uniform-random prompt, then 256 greedy decode steps fed their own
-argmax on the device, f32 KV cache, batch 1.  Timed with HIP events on the
-stream the library launches on; inputs are resident in HBM before timing.
+Default workload (one "step"): the Qwen3-0.6B shape with synthetic Q8_0
+weights (N(0, 0.02) quantised; f32 norm weights 1 + N(0, 0.1)), one prefill
+of a 512-token uniform-random prompt, then 256 greedy decode steps fed their
+own argmax on the device, f32 KV cache, batch 1.  Timed with HIP events on
+the stream the library launches on; inputs are resident in HBM before timing.
 
 Prints ONE JSON line: decode tokens/s (`value`), the whole-step decode HBM
 rate, prefill tokens/s, the roofline of the dominant decode kernel (its
-algorithmic bytes per launch over its event-timed average duration) and the
+algorithmic bytes per launch over its event-timed average duration), the
+prefill-dominated variant (4096 tokens in one call, same weights) and the
 CPU oracle timed on a bounded sample of the same workload.
-"""
+
+Other workloads (`--workload`): `8b-longctx` (Qwen3-8B shape, bf16 KV,
+decode at KV lengths 2048/16384/32768) and `0.6b-bf16-batch64` (bf16
+weights, 64 ragged sequences, batched decode)."""
 
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA
 KIND_NAMES = ["qkv_gemv", "attention", "o_proj_gemv", "gate_up_swiglu_gemv", "down_gemv", "lm_head_argmax_gemv"]
 
 
@@ -56,6 +61,172 @@ def decode_token_bytes(shape, ctx: int) -> float:
     """Algorithmic HBM bytes of one decode step whose new token sits at ctx."""
     per_layer = sum(kernel_bytes(shape, k, ctx) for k in range(5))
     return shape.num_layers * per_layer + kernel_bytes(shape, 5, ctx) + 4 * shape.vocab_size
+
+
+def prefill_int8_ops(shape, T: int) -> int:
+    """int8 MACs x 2 of the projection GEMMs of a T-token prefill (the
+    lm_head runs on the last row only and is left out)."""
+    H, F = shape.hidden_size, shape.intermediate_size
+    per_layer = (shape.q_width + 2 * shape.kv_width) * H + H * shape.q_width + 2 * F * H + H * F
+    return 2 * T * per_layer * shape.num_layers
+
+
+def weight_bytes(shape) -> float:
+    """Bytes of all projection and embedding weights (read once per decode step)."""
+    H, F, V = shape.hidden_size, shape.intermediate_size, shape.vocab_size
+    per_layer = (shape.q_width + 2 * shape.kv_width) * H + H * shape.q_width + 2 * F * H + H * F
+    n = per_layer * shape.num_layers + V * H
+    return q8_bytes(n) if shape.weight_type == "q8_0" else 2.0 * n
+
+
+def kv_bytes_per_position(shape) -> int:
+    return shape.num_layers * 2 * shape.kv_width * (4 if shape.kv_type == "f32" else 2)
+
+
+def timed(fn, reps: int) -> float:
+    """Median milliseconds of fn() over reps runs, HIP events on the current stream."""
+    import torch
+
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return sorted(out)[len(out) // 2]
+
+
+def bench_8b(args) -> int:
+    """Qwen3-8B shape, Q8_0, bf16 KV: prefill 2048, decode at 2048/16384/32768."""
+    import torch
+
+    from quantized_q8_dequant_amd import Qwen3Config, Qwen3Model
+    from synthetic import WORKLOADS, gen_prompt, gen_weights
+
+    wl = WORKLOADS["8b-longctx"]
+    shape = wl.shape
+    weights = gen_weights(shape, wl.weight_seed)
+    model = Qwen3Model(Qwen3Config.from_shape(shape), weights, [wl.kv_capacity], max_batch_tokens=2048)
+    del weights
+    steps = max(args.steps, 1) * 4
+    out = {}
+    t0 = time.perf_counter()
+    for L in wl.decode_contexts:
+        prompt = gen_prompt(shape.vocab_size, L, wl.prompt_seed if L == wl.prompt_len else wl.prompt_seed + L)
+        model.reset()
+        model.prefill(prompt[:1024])  # warm-up
+        model.reset()
+        pre_ms = timed(lambda: (model.reset(), model.prefill(prompt, logits=False)), 1)
+        for _ in range(args.warmup):
+            model.decode_step()
+        ctx0 = model.kv_len()
+        n_steps = max(1, min(steps, wl.kv_capacity - ctx0))
+        ms = timed(lambda: [model.decode_step() for _ in range(n_steps)], 1) / n_steps
+        nbytes = weight_bytes(shape) + kv_bytes_per_position(shape) * (ctx0 + n_steps / 2)
+        out[str(L)] = {
+            "prefill_ms": round(pre_ms, 2),
+            "prefill_tokens_per_s": round(L / (pre_ms / 1000.0), 1),
+            "prefill_int8_frac_of_whole_prefill": round(prefill_int8_ops(shape, L) / (pre_ms / 1000.0) / INT8_PEAK_OPS, 4),
+            "decode_steps_timed": n_steps,
+            "decode_ms_per_token": round(ms, 4),
+            "decode_tokens_per_s": round(1000.0 / ms, 2),
+            "decode_hbm_GBps": round(nbytes / (ms / 1000.0) / 1e9, 1),
+            "decode_hbm_frac": round(nbytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        }
+    t1 = time.perf_counter()
+    line = {
+        "metric": "decode tokens/s and HBM GB/s at KV lengths 2048/16384/32768; prefill tokens/s, Qwen3-8B Q8_0",
+        "value": out[str(wl.decode_contexts[0])]["decode_tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1000.0, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B shape, Q8_0 weights, bf16 KV cache: a prompt of L random tokens in "
+            "2048-row chunks, then greedy decode steps at KV length L, L = 2048, 16384, 32768, batch 1",
+            "weights": "q8_0",
+            "kv_cache": "bf16",
+            "parallelism": "single GPU",
+        },
+        "contexts": out,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_batch64(args) -> int:
+    """bf16 0.6B: 64 sequences with lengths 1024..16384, lockstep greedy steps."""
+    import numpy as np
+    import torch
+
+    from quantized_q8_dequant_amd import Qwen3Config, Qwen3Model
+    from synthetic import WORKLOADS, gen_lengths, gen_prompts, gen_weights
+
+    wl = WORKLOADS["0.6b-bf16-batch64"]
+    shape = wl.shape
+    lengths = gen_lengths(wl.n_seqs, wl.min_len, wl.max_len, wl.length_seed)
+    prompts = gen_prompts(shape.vocab_size, lengths, wl.prompt_seed)
+    weights = gen_weights(shape, wl.weight_seed)
+    caps = [int(n) + wl.decode_steps for n in lengths]
+    model = Qwen3Model(Qwen3Config.from_shape(shape), weights, caps)
+    del weights
+    n = wl.n_seqs
+    t0 = time.perf_counter()
+    first = [int(model.prefill(p, seq=s, logits=False)[1].item()) for s, p in enumerate(prompts)]
+    fill_s = time.perf_counter() - t0
+    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
+    am = torch.empty(n, dtype=torch.int32, device="cuda:0")
+    seqs = list(range(n))
+    steps = min(wl.decode_steps, max(1, args.steps) * 32)
+    warm = min(args.warmup * 4, wl.decode_steps - steps)
+
+    def step():
+        nonlocal toks
+        model.decode_batch(seqs, toks, None, am)
+        toks = am.clone()
+
+    for _ in range(warm):
+        step()
+    ctx0 = np.asarray(lengths, np.float64) + warm
+    ms = timed(lambda: [step() for _ in range(steps)], 1) / steps
+    kv = kv_bytes_per_position(shape) * float(np.sum(ctx0 + steps / 2.0))
+    nbytes = weight_bytes(shape) + kv
+    line = {
+        "metric": "batched decode tokens/s (64 ragged sequences) + achieved HBM GB/s, Qwen3-0.6B bf16",
+        "value": round(n / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-0.6B shape with bf16 weights and bf16 KV: 64 independent sequences, KV lengths "
+            "uniform in 1024..16384 (each filled by prefill), lockstep greedy batched decode steps",
+            "weights": "bf16",
+            "kv_cache": "bf16",
+            "parallelism": "single GPU",
+        },
+        "hbm_GBps": round(nbytes / (ms / 1000.0) / 1e9, 1),
+        "hbm_frac": round(nbytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(nbytes),
+        "cache_fill_s": round(fill_s, 2),
+        "mean_kv_length": float(np.mean(ctx0)),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
@@ -106,6 +277,10 @@ def main() -> int:
     from quantized_q8_dequant_amd import Qwen3Config, Qwen3Model
     from synthetic import WORKLOADS, gen_prompt, gen_weights
 
+    if args.workload == "8b-longctx":
+        return bench_8b(args)
+    if args.workload == "0.6b-bf16-batch64":
+        return bench_batch64(args)
     wl = WORKLOADS[args.workload]
     shape = wl.shape
     weights = gen_weights(shape, wl.weight_seed)
@@ -179,11 +354,43 @@ def main() -> int:
         "traffic": None,
     }
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    # the prefill-dominated workload on the same weights: 4096 tokens in one call
+    p4 = None
+    if args.workload == "0.6b-decode":
         model.close()
         del model
         torch.cuda.empty_cache()
+        wl4 = WORKLOADS["0.6b-prefill4096"]
+        prompt4 = gen_prompt(shape.vocab_size, wl4.prompt_len, wl4.prompt_seed)
+        m4 = Qwen3Model(Qwen3Config.from_shape(shape), weights, [wl4.kv_capacity], max_batch_tokens=wl4.prompt_len)
+        times = []
+        for _ in range(args.warmup + args.steps):
+            m4.reset()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            m4.prefill(prompt4)
+            b_.record()
+            torch.cuda.synchronize()
+            times.append(a_.elapsed_time(b_))
+        t4 = sorted(times[args.warmup:])[len(times[args.warmup:]) // 2]
+        ops = prefill_int8_ops(shape, wl4.prompt_len)
+        p4 = {
+            "prompt_tokens": wl4.prompt_len,
+            "ms": round(t4, 3),
+            "tokens_per_s": round(wl4.prompt_len / (t4 / 1000.0), 1),
+            "projection_int8_ops": ops,
+            "int8_mfma_frac_of_whole_prefill": round(ops / (t4 / 1000.0) / INT8_PEAK_OPS, 4),
+        }
+        m4.close()
+        del m4
+        torch.cuda.empty_cache()
+    else:
+        model.close()
+        del model
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, weights, prompt, args.cpu_decode_steps)
 
     line = {
@@ -215,6 +422,7 @@ def main() -> int:
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(prefill_tps, 1),
         "kernels_at_mean_ctx": kernels,
+        "prefill_4096_one_call": p4,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -106,11 +106,15 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
   float* out = a.out ? a.out + (int64_t)blockIdx.y * a.out_stride : nullptr;
 
   ArgBest best{-INFINITY, 0x7FFFFFFF};
-  bool have_act = false;
 
-  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+  // weights of one tile in registers; two buffers so that the next tile's
+  // loads are in flight while the current tile is reduced
+  struct WTile {
+    v4i w0[ROWS][BPL], w1[ROWS][BPL];
+    uint16_t ws[ROWS][BPL];
+  };
+  auto tile_rows = [&](int tile, int (&rows)[ROWS]) {
     const int gg = tile * groups_per_wg + wave * GPW + grp;  // global lane-group index
-    int rows[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       if (EPI == EPI_SWIGLU) {
@@ -121,8 +125,10 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
         rows[r] = gg * ROWS + r;
       }
     }
-    v4i w0[ROWS][BPL], w1[ROWS][BPL];
-    uint16_t ws[ROWS][BPL];
+  };
+  auto load = [&](WTile& t, int tile) {
+    int rows[ROWS];
+    tile_rows(tile, rows);
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = rows[r] < a.N ? rows[r] : a.N - 1;
@@ -131,15 +137,16 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
 #pragma unroll
       for (int j = 0; j < BPL; ++j) {
         const int b = li + j * LPR;
-        w0[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32);
-        w1[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32 + 16);
-        ws[r][j] = sr[b];
+        t.w0[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32);
+        t.w1[r][j] = *reinterpret_cast<const v4i*>(wr + b * 32 + 16);
+        t.ws[r][j] = sr[b];
       }
     }
-    if (!have_act) {
-      prologue_quant<NORM, kThreads>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
-      have_act = true;
-    }
+  };
+  auto compute = [&](const WTile& t, int tile) {
+    int rows[ROWS];
+    tile_rows(tile, rows);
+    const int gg = tile * groups_per_wg + wave * GPW + grp;
     // block terms d_w * d_a * S are exact in f64; their sum is rounded to
     // f32 once, in the epilogue
     double acc[ROWS];
@@ -153,8 +160,8 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
       const float da = s_da[b];
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
-        const int S = dot32_i8(w0[r][j], w1[r][j], a0, a1);
-        acc[r] += (double)S * (double)(f16_bits_to_f32(ws[r][j]) * da);
+        const int S = dot32_i8(t.w0[r][j], t.w1[r][j], a0, a1);
+        acc[r] += (double)S * (double)(f16_bits_to_f32(t.ws[r][j]) * da);
       }
     }
 #pragma unroll
@@ -185,6 +192,27 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
           }
         }
       }
+    }
+  };
+
+  // grid-stride over tiles: the activation is quantised once per workgroup
+  // (weights of the first tile already in flight), later tiles' weights are
+  // loaded one tile ahead
+  int tile = blockIdx.x;
+  if (tile < a.ntiles) {
+    WTile A, B;
+    load(A, tile);
+    prologue_quant<NORM, kThreads>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
+    for (;;) {
+      const int t1 = tile + gridDim.x;
+      if (t1 < a.ntiles) load(B, t1);
+      compute(A, tile);
+      if (t1 >= a.ntiles) break;
+      const int t2 = t1 + gridDim.x;
+      if (t2 < a.ntiles) load(A, t2);
+      compute(B, t1);
+      if (t2 >= a.ntiles) break;
+      tile = t2;
     }
   }
 
@@ -248,12 +276,36 @@ hipError_t launch_one(const GemvArgs& a, int grid_x, int grid_y, hipStream_t s) 
 }
 
 constexpr int rows_per_tile(int lpr, int rows, int waves) { return waves * (64 / lpr) * rows; }
+constexpr int kMaxGrid = 1024;
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Workgroups of one launch.  Small matrices: one tile each (up to 1024, the
+// tail strides).  Large matrices: one 512-thread workgroup per CU at most,
+// with the tiles spread evenly, so the activation is quantised a few hundred
+// times rather than once per tile.
+int grid_for(int ntiles, bool large) {
+  if (!large) return ntiles < kMaxGrid ? ntiles : kMaxGrid;
+  const int cus = cu_count();
+  const int per = (ntiles + cus - 1) / cus;
+  return (ntiles + per - 1) / per;
+}
 
 template <int LPR, int BPL, int ROWS, int WAVES>
-hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int grid_y, hipStream_t s) {
+hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int grid_y, bool large, hipStream_t s) {
   const int rpt = rows_per_tile(LPR, ROWS, WAVES);
   a.ntiles = (a.N + rpt - 1) / rpt;
-  const int grid = a.ntiles;
+  const int grid = grid_for(a.ntiles, large);
 #define Q8_CASE(NORM_, EPI_) \
   if (norm == NORM_ && epi == EPI_) return launch_one<LPR, BPL, ROWS, WAVES, NORM_, EPI_>(a, grid, grid_y, s);
   Q8_CASE(true, EPI_STORE)
@@ -278,6 +330,10 @@ hipError_t launch_epi(GemvArgs& a, bool norm, int epi, int grid_y, hipStream_t s
 #define Q8_SMALL(X) X(2048, 64, 1, 1, 4) X(3072, 32, 3, 1, 2) X(4096, 64, 2, 1, 4) X(6144, 64, 3, 1, 4) \
   X(8192, 64, 4, 1, 4) X(12288, 64, 6, 1, 4)
 #define Q8_ARGMAX(X) X(1024, 32, 1, 8, 4) X(4096, 64, 2, 4, 4)
+// matrices of at least kLargeElems weights (8B-class layers): 8 waves
+#define Q8_LARGE(X) X(4096, 64, 2, 1, 8) X(6144, 64, 3, 1, 8) X(8192, 64, 4, 1, 8) X(12288, 64, 6, 1, 8)
+#define Q8_LARGE_SW(X) X(2048, 64, 1, 2, 8) X(4096, 64, 2, 2, 8)
+constexpr int64_t kLargeElems = 16ll << 20;
 
 }  // namespace
 
@@ -288,42 +344,57 @@ namespace {
 // other non-SwiGLU launches the single-row shapes where they exist
 struct Shape {
   int lpr, bpl, rows, waves;
+  bool large;
 };
-bool pick(int K, int epi, Shape* sh) {
+bool pick(int K, int64_t N, int epi, Shape* sh) {
 #define Q8_PICK(K_, L_, B_, R_, W_) \
-  if (K == K_) { *sh = Shape{L_, B_, R_, W_}; found = true; }
+  if (K == K_) { *sh = Shape{L_, B_, R_, W_, false}; found = true; }
+#define Q8_PICK_L(K_, L_, B_, R_, W_) \
+  if (K == K_) { *sh = Shape{L_, B_, R_, W_, true}; found = true; }
   bool found = false;
+  if (epi != EPI_ARGMAX && N * K >= kLargeElems) {
+    if (epi == EPI_SWIGLU) {
+      Q8_LARGE_SW(Q8_PICK_L)
+    } else {
+      Q8_LARGE(Q8_PICK_L)
+    }
+    if (found) return true;
+  }
   Q8_SHAPES(Q8_PICK)
   if (epi != EPI_SWIGLU) { Q8_SMALL(Q8_PICK) }
   if (epi == EPI_ARGMAX) { Q8_ARGMAX(Q8_PICK) }
 #undef Q8_PICK
+#undef Q8_PICK_L
   return found;
 }
 }  // namespace
 
 int gemv_argmax_grid(int N, int K) {
   Shape sh;
-  if (!pick(K, EPI_ARGMAX, &sh)) return 0;
+  if (!pick(K, N, EPI_ARGMAX, &sh)) return 0;
   const int rpt = sh.waves * (64 / sh.lpr) * sh.rows;
-  return (N + rpt - 1) / rpt;
+  const int ntiles = (N + rpt - 1) / rpt;
+  return ntiles < kMaxGrid ? ntiles : kMaxGrid;
 }
 
 hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s) {
   Shape sh;
-  if (!pick(a.K, epi, &sh)) return hipErrorInvalidValue;
+  if (!pick(a.K, a.N, epi, &sh)) return hipErrorInvalidValue;
 #define Q8_GO(K_, L_, B_, R_, W_) \
   if (a.K == K_ && sh.lpr == L_ && sh.bpl == B_ && sh.rows == R_ && sh.waves == W_) \
-    return launch_epi<L_, B_, R_, W_>(a, norm, epi, grid_y, s);
+    return launch_epi<L_, B_, R_, W_>(a, norm, epi, grid_y, sh.large, s);
   Q8_SHAPES(Q8_GO)
   Q8_SMALL(Q8_GO)
   Q8_ARGMAX(Q8_GO)
+  Q8_LARGE(Q8_GO)
+  Q8_LARGE_SW(Q8_GO)
 #undef Q8_GO
   return hipErrorInvalidValue;
 }
 
 bool gemv_supported_k(int K) {
   Shape sh;
-  return pick(K, EPI_STORE, &sh);
+  return pick(K, 0, EPI_STORE, &sh);
 }
 
 hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s) {

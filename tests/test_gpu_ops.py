@@ -91,7 +91,8 @@ def _linear_bound(x, ow):
 @pytest.mark.parametrize(
     "m,k,n",
     [(1, 1024, 4096), (1, 3072, 1024), (1, 2048, 1024), (1, 256, 512), (1, 768, 256), (1, 4096, 384),
-     (1, 12288, 256), (2, 1024, 256), (7, 1024, 256), (128, 1024, 512), (300, 3072, 384), (129, 256, 128)],
+     (1, 12288, 256), (1, 4096, 4100), (1, 12288, 1400), (2, 1024, 256), (7, 1024, 256), (128, 1024, 512),
+     (300, 3072, 384), (129, 256, 128)],
 )
 def test_linear_matches_oracle(m, k, n):
     from quantized_q8_dequant_amd import q8_0_linear
