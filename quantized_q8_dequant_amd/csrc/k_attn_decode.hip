@@ -21,96 +21,105 @@
 #include "kernels.h"
 #include "qdevice.h"
 
+#include <type_traits>
+
 using namespace q8;
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int TJ = 32;  // cache rows per tile
-constexpr int kMaxSplit = 128;  // bound of nsplit_max
+// cache rows per staged tile: 16 KB of K or V either way
+template <bool BF16>
+constexpr int kTileRows = BF16 ? 64 : 32;
+constexpr int kMaxSplit = 64;    // bound of nsplit_max
+constexpr int kScoreSlots = 4096;  // f64 scores a workgroup keeps: G heads x (4096 / G) rows
+constexpr int kLdsRow = 4;       // padding of a staged row (keeps rows 16-byte aligned)
 
-// One tile of K and V rows staged through registers: every thread issues
-// all of its 16-byte loads for the tile at once (one memory round trip),
-// and the next tile's loads are in flight while the current tile is used.
+// One tile of K or V rows staged through registers: every thread issues all
+// of its 16-byte loads for a tile at once; two tiles are in flight ahead of
+// the one being used.
 template <int HD, bool BF16>
 struct TileRegs {
-  static constexpr int ELEMS = TJ * HD;                  // per matrix
-  static constexpr int PER_LOAD = BF16 ? 8 : 4;           // elements per 16 bytes
-  static constexpr int LOADS = ELEMS / PER_LOAD / kThreads;  // per thread per matrix
-  int4 k[LOADS], v[LOADS];
+  static constexpr int TJ = kTileRows<BF16>;
+  static constexpr int PER_LOAD = BF16 ? 8 : 4;                   // elements per 16 bytes
+  static constexpr int LOADS = TJ * HD / PER_LOAD / kThreads;    // per thread
+  v4i x[LOADS];
 };
 
+// Every thread issues the same loads whatever the tile (rows past the end
+// re-read the tile's last row and are never used), so the compiler can keep
+// the older tile's loads in flight while waiting for the newer one.
 template <int HD, bool BF16>
-QDEV void tile_load(TileRegs<HD, BF16>& t, const void* kv, int64_t kbase, int64_t vbase, int row0, int nrow) {
+QDEV void tile_load(TileRegs<HD, BF16>& t, const void* kv, int64_t base, int row0, int nrow) {
   constexpr int PER = TileRegs<HD, BF16>::PER_LOAD;
   constexpr int ESZ = BF16 ? 2 : 4;
 #pragma unroll
   for (int i = 0; i < TileRegs<HD, BF16>::LOADS; ++i) {
     const int e = (threadIdx.x + i * kThreads) * PER;  // element index in the tile
-    const int r = e / HD;
-    if (r < nrow) {
-      const int64_t off = (int64_t)(row0 + r) * HD + (e % HD);
-      t.k[i] = *reinterpret_cast<const int4*>(static_cast<const uint8_t*>(kv) + (kbase + off) * ESZ);
-      t.v[i] = *reinterpret_cast<const int4*>(static_cast<const uint8_t*>(kv) + (vbase + off) * ESZ);
-    } else {
-      t.k[i] = int4{0, 0, 0, 0};
-      t.v[i] = int4{0, 0, 0, 0};
-    }
+    const int r = min(e / HD, nrow - 1);
+    const int64_t off = (int64_t)(row0 + r) * HD + (e % HD);
+    t.x[i] = *reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(kv) + (base + off) * ESZ);
   }
 }
 
 template <int HD, bool BF16>
-QDEV void tile_store(const TileRegs<HD, BF16>& t, float (*s_k)[HD + 1], float (*s_v)[HD + 1]) {
+QDEV void tile_store(const TileRegs<HD, BF16>& t, float (*s_t)[HD + kLdsRow]) {
   constexpr int PER = TileRegs<HD, BF16>::PER_LOAD;
 #pragma unroll
   for (int i = 0; i < TileRegs<HD, BF16>::LOADS; ++i) {
     const int e = (threadIdx.x + i * kThreads) * PER;
     const int r = e / HD, d = e % HD;
     if (BF16) {
-      const uint32_t kw[4] = {(uint32_t)t.k[i].x, (uint32_t)t.k[i].y, (uint32_t)t.k[i].z, (uint32_t)t.k[i].w};
-      const uint32_t vw[4] = {(uint32_t)t.v[i].x, (uint32_t)t.v[i].y, (uint32_t)t.v[i].z, (uint32_t)t.v[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s_k[r][d + 2 * j] = __uint_as_float(kw[j] << 16);
-        s_k[r][d + 2 * j + 1] = __uint_as_float(kw[j] & 0xFFFF0000u);
-        s_v[r][d + 2 * j] = __uint_as_float(vw[j] << 16);
-        s_v[r][d + 2 * j + 1] = __uint_as_float(vw[j] & 0xFFFF0000u);
-      }
+      const uint32_t w[4] = {(uint32_t)t.x[i][0], (uint32_t)t.x[i][1], (uint32_t)t.x[i][2], (uint32_t)t.x[i][3]};
+      float4 lo, hi;
+      lo.x = __uint_as_float(w[0] << 16), lo.y = __uint_as_float(w[0] & 0xFFFF0000u);
+      lo.z = __uint_as_float(w[1] << 16), lo.w = __uint_as_float(w[1] & 0xFFFF0000u);
+      hi.x = __uint_as_float(w[2] << 16), hi.y = __uint_as_float(w[2] & 0xFFFF0000u);
+      hi.z = __uint_as_float(w[3] << 16), hi.w = __uint_as_float(w[3] & 0xFFFF0000u);
+      *reinterpret_cast<float4*>(&s_t[r][d]) = lo;
+      *reinterpret_cast<float4*>(&s_t[r][d + 4]) = hi;
     } else {
-      s_k[r][d] = __int_as_float(t.k[i].x), s_k[r][d + 1] = __int_as_float(t.k[i].y);
-      s_k[r][d + 2] = __int_as_float(t.k[i].z), s_k[r][d + 3] = __int_as_float(t.k[i].w);
-      s_v[r][d] = __int_as_float(t.v[i].x), s_v[r][d + 1] = __int_as_float(t.v[i].y);
-      s_v[r][d + 2] = __int_as_float(t.v[i].z), s_v[r][d + 3] = __int_as_float(t.v[i].w);
+      *reinterpret_cast<v4i*>(&s_t[r][d]) = t.x[i];
     }
   }
 }
 
 template <int HD, int G, bool BF16>
 __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
-  // score work split: thread -> (row r, head h, d-part) with NP parts of HD/NP
-  constexpr int NP = kThreads / (TJ * G) > 0 ? kThreads / (TJ * G) : 1;
-  constexpr int DPP = HD / NP;  // dims per part
-  constexpr int SC_PASSES = (TJ * G * NP + kThreads - 1) / kThreads;
-  constexpr bool QREG = DPP <= 32;  // query slice in registers, else read from LDS
+  constexpr int TJ = kTileRows<BF16>;
+  // scores: thread -> (head h, d-part pt, row group rg of RPT rows); part pt
+  // holds dims 4*pt + 4*NP*i + c (c < 4), interleaved so that the float4
+  // reads of 16 lanes (4 rows x 4 parts, rows 132 or 68 floats apart) fall
+  // on distinct LDS banks; the thread keeps its q dims in f64 registers
+  constexpr int NP = (G == 1) ? 8 : 4;
+  constexpr int DPP = HD / NP;
+  constexpr int RPT = TJ * G * NP / kThreads;
+  constexpr int RG = TJ / RPT;  // row groups
+  static_assert(RPT >= 1 && RPT * kThreads == TJ * G * NP, "score map");
+  // outputs: thread -> (head, DPT consecutive dims); threads >= OUT_T idle
+  constexpr int DPT = (G * HD / kThreads) > 0 ? G * HD / kThreads : 1;
+  constexpr int OUT_T = G * HD / DPT;
+  constexpr int TPH = HD / DPT;  // output threads per head
+  constexpr int MAXR = kScoreSlots / G;  // rows per split
   __shared__ float s_qf[G][HD];
-  __shared__ double s_qd[QREG ? 1 : G][HD];
   __shared__ float s_knew[HD];
   __shared__ float s_vnew[HD];
-  __shared__ float s_k[TJ][HD + 1];
-  __shared__ float s_v[TJ][HD + 1];
-  __shared__ double s_part[NP][G][TJ];
-  __shared__ double s_p[G][TJ];
-  __shared__ double s_alpha[G];
+  __shared__ __align__(16) float s_t[TJ][HD + kLdsRow];
+  __shared__ double s_s[G][MAXR];
+  __shared__ double s_m[G];
+  __shared__ double s_l[G];
   __shared__ int s_last;
 
   const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int seq = a.row_seq ? a.row_seq[row] : 0;
   const int p = a.len[seq];
   const int ctx = p + 1;
   int nsplit = (ctx + a.min_rows - 1) / a.min_rows;
   if (nsplit > a.nsplit_max) nsplit = a.nsplit_max;
+  const int need = (ctx + MAXR - 1) / MAXR;  // the host keeps ctx <= kMaxSplit * MAXR
+  if (nsplit < need) nsplit = need;
   if (split >= nsplit) return;  // uniform per workgroup; not counted below
   const int chunk = (ctx + nsplit - 1) / nsplit;
   const int j0 = split * chunk;
@@ -126,17 +135,30 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   const double* cs = a.rope_cos + (int64_t)p * (HD / 2);
   const double* sn = a.rope_sin + (int64_t)p * (HD / 2);
 
-  // first cache tile in flight before anything else (rows < p only; row p
-  // comes from this step's projections)
-  TileRegs<HD, BF16> tr;
-  const int cache_end = min(j1, p);  // rows [j0, cache_end) are read from the cache
-  if (j0 < cache_end) tile_load<HD, BF16>(tr, a.kv, kbase, vbase, j0, min(TJ, cache_end - j0));
+  // the split streams its K tiles, then its V tiles; stream index i < nt is
+  // K tile i, i >= nt is V tile i - nt.  Rows >= p are not read from the
+  // cache (row p comes from this step's projections).
+  const int nt = j0 < j1 ? (j1 - j0 + TJ - 1) / TJ : 0;
+  const int cache_end = min(j1, p);
+  // loads of stream element i < 2 * nt; an element without cache rows (one
+  // that holds only row p) reads its first row's slot instead, unused
+  auto stream_load = [&](TileRegs<HD, BF16>& r, int i) {
+    const bool isv = i >= nt;
+    const int t0 = j0 + (isv ? i - nt : i) * TJ;
+    const bool live = t0 < cache_end;
+    tile_load<HD, BF16>(r, a.kv, isv ? vbase : kbase, live ? t0 : j0, live ? min(TJ, cache_end - t0) : 1);
+  };
+  TileRegs<HD, BF16> tA, tB;
+  if (nt > 0) {  // 2 * nt >= 2 elements
+    stream_load(tA, 0);
+    stream_load(tB, 1);
+  }
 
   // stage raw q (G heads), and the new k / v of head g
-  for (int e = threadIdx.x; e < G * HD; e += kThreads) s_qf[e / HD][e % HD] = qkv[(int64_t)(g * G) * HD + e];
+  for (int e = tid; e < G * HD; e += kThreads) s_qf[e / HD][e % HD] = qkv[(int64_t)(g * G) * HD + e];
   const bool has_new = j0 < j1 && j1 == ctx;  // this split holds position p
   if (has_new) {
-    for (int d = threadIdx.x; d < HD; d += kThreads) {
+    for (int d = tid; d < HD; d += kThreads) {
       s_knew[d] = qkv[(int64_t)nh * HD + (int64_t)g * HD + d];
       s_vnew[d] = qkv[(int64_t)(nh + nkv) * HD + (int64_t)g * HD + d];
     }
@@ -148,7 +170,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   if (has_new) {
     // append: the cache stores post-RoPE K and raw V (bf16 caches round here,
     // and the rounded values are the ones attended below)
-    for (int d = threadIdx.x; d < HD; d += kThreads) {
+    for (int d = tid; d < HD; d += kThreads) {
       const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
       if (BF16) {
         const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
@@ -163,124 +185,135 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     }
   }
 
-  // this thread's query slice, in f64 (registers when it is small)
-  int sc_r[SC_PASSES], sc_h[SC_PASSES], sc_pt[SC_PASSES];
-  double qreg[QREG ? SC_PASSES : 1][QREG ? DPP : 1];
+  // this thread's score role and q slice (f64)
+  const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_h = tid / (NP * RG);
+  double qreg[DPP];
 #pragma unroll
-  for (int ps = 0; ps < SC_PASSES; ++ps) {
-    const int e = threadIdx.x + ps * kThreads;
-    sc_r[ps] = e % TJ;
-    sc_h[ps] = (e / TJ) % G;
-    sc_pt[ps] = e / (TJ * G);
-    if (QREG) {
+  for (int i = 0; i < DPP; ++i) qreg[i] = (double)s_qf[sc_h][4 * sc_pt + 4 * NP * (i / 4) + (i % 4)];
+  // this thread's outputs
+  const bool out_live = tid < OUT_T;
+  const int o_h = out_live ? tid / TPH : 0, o_d = out_live ? (tid % TPH) * DPT : 0;
+  double o[DPT];
 #pragma unroll
-      for (int i = 0; i < (QREG ? DPP : 1); ++i)
-        qreg[QREG ? ps : 0][i] = (e < TJ * G * NP) ? (double)s_qf[sc_h[ps]][sc_pt[ps] * DPP + i] : 0.0;
-    }
-  }
-  if (!QREG)
-    for (int e = threadIdx.x; e < G * HD; e += kThreads) s_qd[QREG ? 0 : e / HD][e % HD] = (double)s_qf[e / HD][e % HD];
-
-  // online softmax in f64: wave h (< G) owns head h's (m, l); outputs are
-  // spread over threads as e = tid + 256*i -> (head e / HD, dim e % HD)
-  constexpr int OUT_PER_T = (G * HD + kThreads - 1) / kThreads;
-  double o[OUT_PER_T];
-#pragma unroll
-  for (int i = 0; i < OUT_PER_T; ++i) o[i] = 0.0;
-  constexpr int HPW = (G + kWaves - 1) / kWaves;  // heads per wavefront
-  double m_run[HPW], l_run[HPW];
-#pragma unroll
-  for (int i = 0; i < HPW; ++i) m_run[i] = -INFINITY, l_run[i] = 0.0;
+  for (int i = 0; i < DPT; ++i) o[i] = 0.0;
   const double scale = a.scale;
 
-  for (int t0 = j0; t0 < j1; t0 += TJ) {
+  // softmax over the split's scores, once (f64): s_s becomes exp(s - m)
+  auto softmax = [&]() {
+    const int n = j1 - j0;
+    for (int h = wave; h < G; h += kWaves) {
+      double m = -INFINITY;
+      for (int r = lane; r < n; r += kWave) m = fmax(m, s_s[h][r]);
+      m = wave_max_d<kWave>(m);
+      double l = 0.0;
+      for (int r = lane; r < n; r += kWave) {
+        const double e = exp(s_s[h][r] - m);
+        s_s[h][r] = e;
+        l += e;
+      }
+      l = wave_sum_d<kWave>(l);
+      if (lane == 0) s_m[h] = m, s_l[h] = l;
+    }
+  };
+
+  // stream element i: stage it in LDS, start the load of element i + 2 into
+  // the freed registers, then scores (K) or P.V (V)
+  auto process = [&](TileRegs<HD, BF16>& tr, int i, auto prefetch) {
+    constexpr bool PREFETCH = decltype(prefetch)::value;
+    const bool isv = i >= nt;
+    const int t0 = j0 + (isv ? i - nt : i) * TJ;
     const int nrow = min(TJ, j1 - t0);
-    __syncthreads();  // previous tile fully consumed
-    if (t0 < cache_end) tile_store<HD, BF16>(tr, s_k, s_v);
+    __syncthreads();  // previous tile (and, before the first V tile, the scores) consumed
+    if (i == nt) {
+      softmax();
+      __syncthreads();
+    }
+    if (t0 < cache_end) tile_store<HD, BF16>(tr, s_t);
+    if (PREFETCH) stream_load(tr, i + 2);
     if (t0 + nrow > p) {  // the tile holds row p: take it from this step's values
       __syncthreads();    // (after the tile store, which zero-fills that row)
       const int r = p - t0;
-      for (int d = threadIdx.x; d < HD; d += kThreads) {
-        s_k[r][d] = s_knew[d];
-        s_v[r][d] = s_vnew[d];
-      }
+      const float* src = isv ? s_vnew : s_knew;
+      for (int d = tid; d < HD; d += kThreads) s_t[r][d] = src[d];
     }
     __syncthreads();
-    const int tn = t0 + TJ;  // prefetch the next tile while this one is used
-    if (tn < cache_end) tile_load<HD, BF16>(tr, a.kv, kbase, vbase, tn, min(TJ, cache_end - tn));
-    // partial scores over each thread's d slice (f64)
+    if (!isv) {
 #pragma unroll
-    for (int ps = 0; ps < SC_PASSES; ++ps) {
-      const int e = threadIdx.x + ps * kThreads;
-      if (e < TJ * G * NP) {
+      for (int j = 0; j < RPT; ++j) {
+        const int r = sc_rg * RPT + j;
+        const float* kr = &s_t[r][4 * sc_pt];
         double acc = 0.0;
-        const float* kr = &s_k[sc_r[ps]][sc_pt[ps] * DPP];
-        if (QREG) {
 #pragma unroll
-          for (int i = 0; i < (QREG ? DPP : 1); ++i) acc += qreg[QREG ? ps : 0][i] * (double)kr[i];
-        } else {
-          const double* qd = &s_qd[QREG ? 0 : sc_h[ps]][sc_pt[ps] * DPP];
-#pragma unroll 16
-          for (int i = 0; i < DPP; ++i) acc += qd[i] * (double)kr[i];
+        for (int d = 0; d < DPP; d += 4) {
+          const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
+          acc += qreg[d] * (double)k4.x;
+          acc += qreg[d + 1] * (double)k4.y;
+          acc += qreg[d + 2] * (double)k4.z;
+          acc += qreg[d + 3] * (double)k4.w;
         }
-        s_part[sc_pt[ps]][sc_h[ps]][sc_r[ps]] = acc;
+        acc = wave_sum_d<NP>(acc);
+        if (sc_pt == 0 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
+      }
+    } else if (out_live) {
+      const double* pr = &s_s[o_h][t0 - j0];
+      auto pv_row = [&](int r) {
+        const double w = pr[r];
+        const float* vr = &s_t[r][o_d];
+        if (DPT == 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(vr);
+          o[0] += w * (double)v4.x;
+          o[DPT > 1 ? 1 : 0] += w * (double)v4.y;
+          o[DPT > 2 ? 2 : 0] += w * (double)v4.z;
+          o[DPT > 3 ? 3 : 0] += w * (double)v4.w;
+        } else if (DPT == 2) {
+          const float2 v2 = *reinterpret_cast<const float2*>(vr);
+          o[0] += w * (double)v2.x;
+          o[DPT > 1 ? 1 : 0] += w * (double)v2.y;
+        } else {
+          o[0] += w * (double)vr[0];
+        }
+      };
+      // full tiles unrolled, so the LDS reads of many rows are in flight
+      // together (row by row, each would wait out the LDS latency)
+      if (nrow == TJ) {
+#pragma unroll
+        for (int r = 0; r < TJ; ++r) pv_row(r);
+      } else {
+#pragma unroll 8
+        for (int r = 0; r < nrow; ++r) pv_row(r);
       }
     }
-    __syncthreads();
-    // per-head scores, max / exp / sum: wave handles heads wave + 4i, half-waves
-    // share one head's 32 rows
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      const int h = wave + i * kWaves;
-      if (h < G) {
-        const int r = lane % TJ;
-        double s = 0.0;
-#pragma unroll
-        for (int pt = 0; pt < NP; ++pt) s += s_part[pt][h][r];
-        s = (r < nrow) ? s * scale : -INFINITY;
-        const double mt = wave_max_d<TJ>(s);
-        const double m_new = fmax(m_run[i], mt);
-        const double pr = (s == -INFINITY) ? 0.0 : exp(s - m_new);
-        const double lt = wave_sum_d<TJ>(pr);
-        const double alpha = (m_run[i] == -INFINITY) ? 0.0 : exp(m_run[i] - m_new);
-        l_run[i] = l_run[i] * alpha + lt;
-        m_run[i] = m_new;
-        if (lane < TJ) s_p[h][r] = pr;
-        if (lane == 0) s_alpha[h] = alpha;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < OUT_PER_T; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      if (e < G * HD) {
-        const int h = e / HD, d = e % HD;
-        double acc = o[i] * s_alpha[h];
-        for (int r = 0; r < nrow; ++r) acc += s_p[h][r] * (double)s_v[r][d];
-        o[i] = acc;
-      }
-    }
+  };
+
+  // pairs of elements with the pair after next in flight, then the last
+  // pair (2 * nt is even); every load issued is used, and the number of
+  // loads between two waits is fixed
+  if (tid < G) s_m[tid] = -INFINITY, s_l[tid] = 0.0;  // an empty split contributes nothing
+  int i = 0;
+  for (; i + 2 < 2 * nt; i += 2) {
+    process(tA, i, std::true_type{});
+    process(tB, i + 1, std::true_type{});
   }
+  if (nt > 0) {
+    process(tA, i, std::false_type{});
+    process(tB, i + 1, std::false_type{});
+  }
+  __syncthreads();
 
   // write this split's partial: [row][g][split][h][0..HD-1] = o, [HD] = m, [HD+1] = l
   const int64_t pstride = (int64_t)G * (HD + 2);
   double* part = a.part + (((int64_t)row * nkv + g) * a.nsplit_max + split) * pstride;
+  if (out_live) {
 #pragma unroll
-  for (int i = 0; i < OUT_PER_T; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    if (e < G * HD) st_coherent(part + (e / HD) * (HD + 2) + (e % HD), o[i]);
+    for (int i = 0; i < DPT; ++i) st_coherent(part + o_h * (HD + 2) + o_d + i, o[i]);
   }
-#pragma unroll
-  for (int i = 0; i < HPW; ++i) {
-    const int h = wave + i * kWaves;
-    if (h < G && lane == 0) {
-      st_coherent(part + h * (HD + 2) + HD, m_run[i]);
-      st_coherent(part + h * (HD + 2) + HD + 1, l_run[i]);
-    }
+  if (tid < G) {
+    st_coherent(part + tid * (HD + 2) + HD, s_m[tid]);
+    st_coherent(part + tid * (HD + 2) + HD + 1, s_l[tid]);
   }
   wait_memory();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     unsigned* cnt = a.counter + (int64_t)row * nkv + g;
     const unsigned prev = arrive(cnt);
     s_last = prev == (unsigned)(nsplit - 1);
@@ -288,64 +321,61 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  // merge the nsplit partials of the G heads (f64), round once to f32.  All
-  // loads of a phase are issued together (each one crosses the device-wide
-  // fence, so a load-per-iteration loop would pay that latency nsplit times).
+  // combine the nsplit partials of the G heads (f64), round once to f32;
+  // the loads of a batch are all issued before any is used
   const double* pb = a.part + (((int64_t)row * nkv + g) * a.nsplit_max) * pstride;
   __shared__ double s_w[G][kMaxSplit];
-  __shared__ double s_l[G][kMaxSplit];
+  __shared__ double s_ls[G][kMaxSplit];
+  __shared__ double s_M[G];
   __shared__ double s_L[G];
-  for (int e = threadIdx.x; e < G * nsplit; e += kThreads) {
+  for (int e = tid; e < G * nsplit; e += kThreads) {
     const int h = e / nsplit, sidx = e % nsplit;
     s_w[h][sidx] = ld_coherent(pb + sidx * pstride + h * (HD + 2) + HD);
-    s_l[h][sidx] = ld_coherent(pb + sidx * pstride + h * (HD + 2) + HD + 1);
+    s_ls[h][sidx] = ld_coherent(pb + sidx * pstride + h * (HD + 2) + HD + 1);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
+  if (tid < G) {
+    const int h = tid;
     double M = -INFINITY;
     for (int sidx = 0; sidx < nsplit; ++sidx) M = fmax(M, s_w[h][sidx]);
-    s_alpha[h] = M;
+    s_M[h] = M;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * nsplit; e += kThreads) {
+  for (int e = tid; e < G * nsplit; e += kThreads) {
     const int h = e / nsplit, sidx = e % nsplit;
-    const double ms = s_w[h][sidx];
-    s_w[h][sidx] = (ms == -INFINITY) ? 0.0 : exp(ms - s_alpha[h]);
+    s_w[h][sidx] = exp(s_w[h][sidx] - s_M[h]);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
+  if (tid < G) {
+    const int h = tid;
     double L = 0.0;
-    for (int sidx = 0; sidx < nsplit; ++sidx) L += s_w[h][sidx] * s_l[h][sidx];
+    for (int sidx = 0; sidx < nsplit; ++sidx) L += s_w[h][sidx] * s_ls[h][sidx];
     s_L[h] = L;
   }
-  double O[OUT_PER_T];
+  __syncthreads();
+  if (out_live) {
+    constexpr int BATCH = 16 / DPT;  // splits per batch: 16 loads in flight
+    double O[DPT];
 #pragma unroll
-  for (int i = 0; i < OUT_PER_T; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    O[i] = 0.0;
-    if (e < G * HD) {
-      const int h = e / HD, d = e % HD;
-      int sidx = 0;
-      for (; sidx + 16 <= nsplit; sidx += 16) {
-        double v[16];
+    for (int i = 0; i < DPT; ++i) O[i] = 0.0;
+    const double* ob = pb + o_h * (HD + 2) + o_d;
+    for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
+      double v[BATCH][DPT];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = ld_coherent(pb + (sidx + u) * pstride + h * (HD + 2) + d);
+      for (int u = 0; u < BATCH; ++u)
 #pragma unroll
-        for (int u = 0; u < 16; ++u) O[i] += s_w[h][sidx + u] * v[u];
-      }
-      for (; sidx < nsplit; ++sidx) O[i] += s_w[h][sidx] * ld_coherent(pb + sidx * pstride + h * (HD + 2) + d);
+        for (int i = 0; i < DPT; ++i) v[u][i] = (s0 + u < nsplit) ? ld_coherent(ob + (s0 + u) * pstride + i) : 0.0;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (s0 + u < nsplit) {
+          const double wgt = s_w[o_h][s0 + u];
+#pragma unroll
+          for (int i = 0; i < DPT; ++i) O[i] += wgt * v[u][i];
+        }
     }
-  }
-  __syncthreads();  // s_L ready
 #pragma unroll
-  for (int i = 0; i < OUT_PER_T; ++i) {
-    const int e = threadIdx.x + i * kThreads;
-    if (e < G * HD) {
-      const int h = e / HD, d = e % HD;
-      a.out[(int64_t)row * a.out_stride + (int64_t)(g * G + h) * HD + d] = (float)(O[i] / s_L[h]);
-    }
+    for (int i = 0; i < DPT; ++i)
+      a.out[(int64_t)row * a.out_stride + (int64_t)(g * G + o_h) * HD + o_d + i] = (float)(O[i] / s_L[o_h]);
   }
 }
 
@@ -368,6 +398,8 @@ namespace q8k {
 bool attn_decode_supported(int hd, int group) {
   return (hd == 64 || hd == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
+
+int attn_decode_max_ctx(int group) { return kMaxSplit * (kScoreSlots / group); }
 
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s) {
 #define Q8_ATT(HD_, G_) \

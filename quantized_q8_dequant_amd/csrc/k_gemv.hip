@@ -198,21 +198,28 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
   // grid-stride over tiles: the activation is quantised once per workgroup
   // (weights of the first tile already in flight), later tiles' weights are
   // loaded one tile ahead
+  // (the prefetch is issued unconditionally -- past the last tile it
+  // re-reads the tile just loaded, a cache hit -- so that the compiler keeps
+  // it in flight while it waits for the older tile)
   int tile = blockIdx.x;
   if (tile < a.ntiles) {
     WTile A, B;
     load(A, tile);
     prologue_quant<NORM, kThreads>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
-    for (;;) {
-      const int t1 = tile + gridDim.x;
-      if (t1 < a.ntiles) load(B, t1);
+    if (tile + (int)gridDim.x >= a.ntiles) {
       compute(A, tile);
-      if (t1 >= a.ntiles) break;
-      const int t2 = t1 + gridDim.x;
-      if (t2 < a.ntiles) load(A, t2);
-      compute(B, t1);
-      if (t2 >= a.ntiles) break;
-      tile = t2;
+    } else {
+      for (;;) {
+        const int t1 = tile + gridDim.x;
+        load(B, t1 < a.ntiles ? t1 : tile);
+        compute(A, tile);
+        if (t1 >= a.ntiles) break;
+        const int t2 = t1 + gridDim.x;
+        load(A, t2 < a.ntiles ? t2 : t1);
+        compute(B, t1);
+        if (t2 >= a.ntiles) break;
+        tile = t2;
+      }
     }
   }
 

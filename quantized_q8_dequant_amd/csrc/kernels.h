@@ -76,6 +76,7 @@ hipError_t gemv(GemvArgs a, bool norm, int epi, int grid_y, hipStream_t s);
 hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, int32_t* S, hipStream_t s);
 
 bool attn_decode_supported(int hd, int group);
+int attn_decode_max_ctx(int group);  // longest context (cache capacity) the decode attention takes
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
 
 hipError_t set_len(int32_t* len, int seq, int value, hipStream_t s);

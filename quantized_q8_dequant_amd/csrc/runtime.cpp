@@ -82,10 +82,15 @@ struct Layer {
   float *attn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr, *ffn_norm = nullptr;
 };
 
-int decode_nsplit_max(int nkv, int nrows) {
-  int n = 2048 / (nkv * nrows);
-  if (n > 128) n = 128;
-  if (n < 1) n = 1;
+// Splits of the decode attention per (batch row, KV head): about 1024
+// workgroups per launch, at most 32 by that rule, and never fewer than the
+// longest cache needs (a split holds at most 4096 / group rows).
+int decode_splits_needed(int max_cap, int group) { return (max_cap + 4096 / group - 1) / (4096 / group); }
+int decode_nsplit_max(int nkv, int nrows, int needed) {
+  const int units = nkv * nrows;
+  int n = (1024 + units - 1) / units;
+  if (n > 32) n = 32;
+  if (n < needed) n = needed;
   return n;
 }
 
@@ -163,6 +168,10 @@ int validate(const qwen3_config* c) {
   for (int i = 0; i < c->max_seqs; ++i)
     if (c->h_seq_capacity[i] <= 0) return fail(QWEN3_E_INVALID_CONFIG, "every seq_capacity must be >= 1");
   if (c->max_batch_tokens < 0) return fail(QWEN3_E_INVALID_CONFIG, "max_batch_tokens must be >= 0");
+  for (int i = 0; i < c->max_seqs; ++i)
+    if (c->h_seq_capacity[i] > q8k::attn_decode_max_ctx(G))
+      return fail(QWEN3_E_INVALID_CONFIG, "a seq_capacity exceeds the decode attention limit of " +
+                                              std::to_string(q8k::attn_decode_max_ctx(G)) + " rows");
   return QWEN3_OK;
 }
 
@@ -232,9 +241,11 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->da = cv.arr<float>(R * (m->kmax / 32));
   m->q32 = cv.arr<float>(R * qw);
   if (m->wbf16) m->xn = cv.arr<float>(R * H);
-  // decode attention partials: rows * nsplit <= 2048 / nkv (see decode_nsplit_max)
+  // decode attention partials: rows * nkv * nsplit_max <= max(1024 + R * nkv, R * nkv * needed)
   const int64_t G = nh / nkv;
-  m->attn_part = cv.arr<double>((size_t)std::max<int64_t>(2048, R * nkv) * G * (hd + 2));
+  const int64_t needed = decode_splits_needed(m->max_cap, (int)G);
+  const int64_t slots = std::max<int64_t>(1024 + R * nkv, R * nkv * needed);
+  m->attn_part = cv.arr<double>((size_t)slots * G * (hd + 2));
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
@@ -340,8 +351,8 @@ AttnDecodeArgs attn_args(const qwen3_model* m, const int32_t* d_row_seq, int nro
   at.out = m->attn;
   at.out_stride = m->qw;
   at.nkv = m->nkv;
-  at.nsplit_max = decode_nsplit_max(m->nkv, nrows);
-  at.min_rows = 32;
+  at.nsplit_max = decode_nsplit_max(m->nkv, nrows, decode_splits_needed(m->max_cap, m->G));
+  at.min_rows = 64;
   at.scale = 1.0 / std::sqrt((double)m->hd);
   return at;
 }
