@@ -1,0 +1,701 @@
+// One launch per decode step (single sequence, Q8_0 weights): a persistent
+// grid of 256 workgroups, one per CU, runs every layer and the tied lm_head.
+//
+// What is computed is the decode step of the Fucina course page "A transformer
+// from scratch" (sections 12.3-12.6) with the Q8_0 linears of "Model files and
+// quantization" (sections 11.7 and 11.9), exactly as the per-kernel path
+// computes it (same f64 reductions, same per-row block order):
+//   x = embed(token); per layer:
+//     A  qkv = W_qkv . quant(rmsnorm(x, attn_norm))
+//     B  per KV head g: q/k norm + RoPE, append k/v at row p, attention over
+//        rows 0..p split across workgroups, last arrival combines
+//     C  x = x + W_o . quant(att)
+//     D  h = silu(W_gate . b) * (W_up . b), b = quant(rmsnorm(x, ffn_norm))
+//     E  x = x + W_down . quant(h)
+//   logits = W_emb . quant(rmsnorm(x, output_norm)); token = argmax.
+//
+// Between phases every workgroup needs values written by others.  Each
+// activation word is stored as (f32 value, 32-bit epoch) in one 64-bit
+// agent-coherent store; a reader polls the words it needs until all carry
+// the epoch it expects, so the data is its own flag and no barrier or fence
+// is used.  A phase issues the loads of its weight slice before it starts
+// polling, so HBM streams while the workgroup waits.  Each buffer is
+// written once per layer with a new epoch, and the phase order guarantees
+// that every reader of one epoch has finished before the next is written.
+//
+// Every wait is bounded: after a spin limit the workgroup sets an error word
+// and leaves, the others see the word and leave too, and the step's argmax
+// is -1.  The grid must be co-resident (the host checks occupancy).
+#include "kernels.h"
+#include "qdevice.h"
+
+using namespace q8;
+
+namespace {
+
+typedef unsigned long long u64;
+constexpr int NT = 256;        // threads per workgroup
+constexpr int kWavesP = NT / kWave;
+constexpr int TJ = 32;         // KV rows per staged tile
+constexpr int kSpin = 1 << 21;  // poll rounds before a wait gives up
+
+QDEV u64 tag_word(float v, unsigned tag) { return ((u64)tag << 32) | (u64)__float_as_uint(v); }
+QDEV void put_tagged(u64* p, float v, unsigned tag) {
+  __hip_atomic_store(p, tag_word(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+QDEV unsigned ld_err(const unsigned* err) { return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Wait until the N words at src all carry `tag`, then copy their values to
+// dst (LDS).  False when the spin limit is reached or another workgroup has
+// reported an error.
+template <int N>
+QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
+  constexpr int PER = (N + NT - 1) / NT;
+  for (int spin = 0; spin < kSpin; ++spin) {
+    u64 v[PER];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = threadIdx.x + j * NT;
+      v[j] = (i < N) ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_word(0.f, tag);
+      ok = ok && (unsigned)(v[j] >> 32) == tag;
+    }
+    if (__syncthreads_and(ok)) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x + j * NT;
+        if (i < N) dst[i] = __uint_as_float((unsigned)v[j]);
+      }
+      __syncthreads();
+      return true;
+    }
+    if ((spin & 63) == 63 && __syncthreads_or(threadIdx.x == 0 && ld_err(err) != 0)) return false;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// The same for three ranges at once (one round trip per poll round).
+template <int N1, int N2, int N3>
+QDEV bool poll3(const u64* s1, const u64* s2, const u64* s3, unsigned tag, float* d1, float* d2, float* d3,
+                unsigned* err) {
+  constexpr int N = N1 + N2 + N3;
+  constexpr int PER = (N + NT - 1) / NT;
+  auto src = [&](int i) { return i < N1 ? s1 + i : i < N1 + N2 ? s2 + (i - N1) : s3 + (i - N1 - N2); };
+  auto dst = [&](int i) { return i < N1 ? d1 + i : i < N1 + N2 ? d2 + (i - N1) : d3 + (i - N1 - N2); };
+  for (int spin = 0; spin < kSpin; ++spin) {
+    u64 v[PER];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = threadIdx.x + j * NT;
+      v[j] = (i < N) ? __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_word(0.f, tag);
+      ok = ok && (unsigned)(v[j] >> 32) == tag;
+    }
+    if (__syncthreads_and(ok)) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x + j * NT;
+        if (i < N) *dst(i) = __uint_as_float((unsigned)v[j]);
+      }
+      __syncthreads();
+      return true;
+    }
+    if ((spin & 63) == 63 && __syncthreads_or(threadIdx.x == 0 && ld_err(err) != 0)) return false;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// Quantise the K values in LDS (optionally RMSNorm'd with w) to Q8_0 codes
+// and f16-valued scales in LDS; the same arithmetic and summation order as
+// the decode GEMV's prologue.
+template <int K, bool NORM>
+QDEV void quantize_lds(const float* s_x, const float* __restrict__ w, float eps, int8_t* s_qa, float* s_da,
+                       double* s_red) {
+  double r = 1.0;
+  if (NORM) {
+    double ss = 0.0;
+    for (int c = threadIdx.x * 4; c < K; c += NT * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(s_x + c);
+      ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+    }
+    ss = block_sum_d<NT>(ss, s_red);
+    r = rms_scale(ss, K, eps);
+  }
+  for (int base = 0; base < K; base += NT * 4) {
+    const int c = base + threadIdx.x * 4;
+    const bool live = c < K;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      const float4 t = *reinterpret_cast<const float4*>(s_x + c);
+      v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+      if (NORM) {
+        const float4 w4 = *reinterpret_cast<const float4*>(w + c);
+        v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
+        v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
+      }
+    }
+    float d;
+    const int packed = quant4_group8(v, &d);
+    if (live) {
+      *reinterpret_cast<int*>(s_qa + c) = packed;
+      if ((threadIdx.x & 7) == 0) s_da[c >> 5] = f16_round(d);
+    }
+  }
+  __syncthreads();
+}
+
+// A workgroup's slice of a Q8_0 matrix: R rows of K values.  LPR lanes share
+// a row, each lane owns BPL whole blocks (the decode GEMV's layout for K, so
+// the per-row summation order is the same); RPP rows per pass of the 256
+// threads.
+template <int K, int R>
+struct Slice {
+  static constexpr int NB = K / 32;
+  static constexpr int LPR = (NB % 64 == 0) ? 64 : (NB % 32 == 0) ? 32 : (NB % 16 == 0) ? 16 : 8;
+  static constexpr int BPL = NB / LPR;
+  static constexpr int RPP = NT / LPR;
+  static constexpr int PASSES = (R + RPP - 1) / RPP;
+  static_assert(NB % LPR == 0, "block count");
+  v4i w0[PASSES][BPL], w1[PASSES][BPL];
+  uint16_t ws[PASSES][BPL];
+
+  // row(lr) maps a local row < R to a matrix row; rows past R load row(0)
+  template <typename RowOf>
+  QDEV void load(const int8_t* __restrict__ qs, const uint16_t* __restrict__ sc, RowOf row) {
+    const int li = threadIdx.x % LPR;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int lr = ps * RPP + threadIdx.x / LPR;
+      const int64_t r = row(lr < R ? lr : 0);
+      const int8_t* wr = qs + r * (int64_t)K;
+      const uint16_t* sr = sc + r * (int64_t)NB;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        const int b = li + j * LPR;
+        w0[ps][j] = *reinterpret_cast<const v4i*>(wr + b * 32);
+        w1[ps][j] = *reinterpret_cast<const v4i*>(wr + b * 32 + 16);
+        ws[ps][j] = sr[b];
+      }
+    }
+  }
+
+  // emit(lr, acc) runs on the first lane of each row with the row's f64 sum
+  template <typename Emit>
+  QDEV void compute(const int8_t* s_qa, const float* s_da, Emit emit) const {
+    const int li = threadIdx.x % LPR;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        const int b = li + j * LPR;
+        const v4i a0 = *reinterpret_cast<const v4i*>(s_qa + b * 32);
+        const v4i a1 = *reinterpret_cast<const v4i*>(s_qa + b * 32 + 16);
+        const int S = dot32_i8(w0[ps][j], w1[ps][j], a0, a1);
+        acc += (double)S * (double)(f16_bits_to_f32(ws[ps][j]) * s_da[b]);
+      }
+      acc = wave_sum_d<LPR>(acc);
+      const int lr = ps * RPP + threadIdx.x / LPR;
+      if (li == 0 && lr < R) emit(lr, acc);
+    }
+  }
+};
+
+// KV rows of one tile in registers (16-byte loads, same count whatever the tile)
+template <int HD, bool BF16>
+struct KvTile {
+  static constexpr int PER = BF16 ? 8 : 4;
+  static constexpr int LOADS = (TJ * HD / PER + NT - 1) / NT;
+  v4i x[LOADS];
+  QDEV void load(const void* kv, int64_t base, int row0, int nrow) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = min((threadIdx.x + i * NT) * PER, TJ * HD - PER);
+      const int r = min(e / HD, nrow - 1);
+      const int64_t off = (int64_t)(row0 + r) * HD + (e % HD);
+      x[i] = *reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(kv) + (base + off) * ESZ);
+    }
+  }
+  QDEV void store(float (*s_t)[HD + 4]) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = (threadIdx.x + i * NT) * PER;
+      if (e >= TJ * HD) continue;
+      const int r = e / HD, d = e % HD;
+      if (BF16) {
+        float4 lo, hi;
+        lo.x = __uint_as_float((uint32_t)x[i][0] << 16), lo.y = __uint_as_float((uint32_t)x[i][0] & 0xFFFF0000u);
+        lo.z = __uint_as_float((uint32_t)x[i][1] << 16), lo.w = __uint_as_float((uint32_t)x[i][1] & 0xFFFF0000u);
+        hi.x = __uint_as_float((uint32_t)x[i][2] << 16), hi.y = __uint_as_float((uint32_t)x[i][2] & 0xFFFF0000u);
+        hi.z = __uint_as_float((uint32_t)x[i][3] << 16), hi.w = __uint_as_float((uint32_t)x[i][3] & 0xFFFF0000u);
+        *reinterpret_cast<float4*>(&s_t[r][d]) = lo;
+        *reinterpret_cast<float4*>(&s_t[r][d + 4]) = hi;
+      } else {
+        *reinterpret_cast<v4i*>(&s_t[r][d]) = x[i];
+      }
+    }
+  }
+};
+
+struct ArgBest {
+  float v;
+  int i;
+};
+QDEV ArgBest better(ArgBest a, ArgBest b) {  // larger value; ties -> lower index
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+// H hidden, QW = heads * HD, F FFN width, S attention splits per KV head,
+// MAXR rows per split at most.
+template <int H, int QW, int F, int HD, int G, bool KVBF16, int S, int MAXR>
+__global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
+  constexpr int NKV = QW / (HD * G);
+  constexpr int KVW = NKV * HD;
+  constexpr int NQKV = QW + 2 * KVW;
+  constexpr int NWG = kPersistWorkgroups;
+  constexpr int RA = NQKV / NWG;  // QKV rows per workgroup
+  constexpr int RC = H / NWG;     // hidden rows per workgroup (o_proj, down, embedding)
+  constexpr int UD = F / NWG;     // FFN units per workgroup
+  static_assert(RA * NWG == NQKV && RC * NWG == H && UD * NWG == F, "shape does not split over the grid");
+  static_assert(NKV * S <= NWG, "attention units exceed the grid");
+  constexpr int XMAX = (H > QW ? (H > F ? H : F) : (QW > F ? QW : F));
+  // attention maps (as the decode attention kernel)
+  constexpr int NP = (G == 1) ? 8 : 4;
+  constexpr int DPP = HD / NP;
+  constexpr int RPT = TJ * G * NP / NT;
+  constexpr int RG = TJ / RPT;
+  static_assert(RPT >= 1 && RPT * NT == TJ * G * NP, "score map");
+  constexpr int DPT = (G * HD / NT) > 0 ? G * HD / NT : 1;
+  constexpr int OUT_T = G * HD / DPT;
+  constexpr int TPH = HD / DPT;
+
+  __shared__ __align__(16) float s_x[XMAX];
+  __shared__ __align__(16) int8_t s_qa[XMAX];
+  __shared__ float s_da[XMAX / 32];
+  __shared__ double s_red[kWavesP];
+  __shared__ float s_xkeep[RC];   // this workgroup's rows of x entering o_proj
+  __shared__ float s_xckeep[RC];  // ... and entering the down projection
+  __shared__ float s_gu[2 * UD];
+  __shared__ float s_qf[G][HD];
+  __shared__ float s_knew[HD];
+  __shared__ float s_vnew[HD];
+  __shared__ __align__(16) float s_t[TJ][HD + 4];
+  __shared__ double s_s[G][MAXR];
+  __shared__ double s_m[G], s_l[G], s_M[G], s_L[G];
+  __shared__ double s_w[G][S], s_ls[G][S];
+  __shared__ ArgBest s_best[kWavesP];
+  __shared__ int s_last;
+
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int seq = a.seq;
+  const int p = a.len[seq];
+  const int ctx = p + 1;
+  const unsigned T0 = a.pstep * (unsigned)(a.L + 1) + 1u;  // epoch of layer 0
+  const float eps = a.eps;
+
+  // ---- embedding rows of this workgroup (exact f16(d) * q) ------------------
+  {
+    const int tok = a.token[0];
+    if (tid < RC) {
+      const int n = b * RC + tid;
+      const float x = f16_bits_to_f32(a.emb_sc[(int64_t)tok * (H / 32) + n / 32]) * (float)a.emb_qs[(int64_t)tok * H + n];
+      put_tagged(a.xa + n, x, T0);
+      s_xkeep[tid] = x;
+    }
+  }
+
+  // attention unit of this workgroup
+  const bool attn_unit = b < NKV * S;
+  const int ag = b / S, asplit = b % S;
+  const int chunk = (ctx + S - 1) / S;
+  const int j0 = min(ctx, asplit * chunk), j1 = min(ctx, j0 + chunk);
+  const int nt = j0 < j1 ? (j1 - j0 + TJ - 1) / TJ : 0;
+  const int cache_end = min(j1, p);
+  const bool has_new = j0 < j1 && j1 == ctx;
+  const int64_t cap = a.seq_cap[seq];
+
+  for (int l = 0; l < a.L; ++l) {
+    const unsigned T = T0 + (unsigned)l;
+    const PLayer P = a.layers[l];
+    const int64_t head_elems = cap * HD;
+    const int64_t kbase = a.seq_base[seq] + ((int64_t)l * 2 * NKV + ag) * head_elems;
+    const int64_t vbase = kbase + (int64_t)NKV * head_elems;
+
+    // the attention split's first two tiles (stream element i < nt is K tile
+    // i, nt <= i < 2 nt is V tile i - nt) are requested before anything else
+    KvTile<HD, KVBF16> tA, tB;
+    auto stream_load = [&](KvTile<HD, KVBF16>& r, int i) {
+      const bool isv = i >= nt;
+      const int t0 = j0 + (isv ? i - nt : i) * TJ;
+      const bool live = t0 < cache_end;
+      r.load(a.kv, isv ? vbase : kbase, live ? t0 : 0, live ? min(TJ, cache_end - t0) : 1);
+    };
+    if (attn_unit && nt > 0) {
+      stream_load(tA, 0);
+      stream_load(tB, 1);
+    }
+
+    // ---- A: QKV projection --------------------------------------------------
+    {
+      Slice<H, RA> w;
+      w.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
+      if (!poll_vec<H>(a.xa, T, s_x, a.err)) goto fail;
+      quantize_lds<H, true>(s_x, P.attn_norm, eps, s_qa, s_da, s_red);
+      w.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
+    }
+
+    // ---- B: attention of KV head ag over rows [j0, j1) -------------------------
+    if (attn_unit) {
+      const double* cs = a.rope_cos + (int64_t)p * (HD / 2);
+      const double* sn = a.rope_sin + (int64_t)p * (HD / 2);
+      if (!poll3<G * HD, HD, HD>(a.qkv + ag * G * HD, a.qkv + QW + ag * HD, a.qkv + QW + KVW + ag * HD, T,
+                                 &s_qf[0][0], s_knew, s_vnew, a.err))
+        goto fail;
+      for (int h = wave; h < G; h += kWavesP) norm_rope_wave<HD>(s_qf[h], P.q_norm, eps, cs, sn);
+      if (has_new && wave == kWavesP - 1) norm_rope_wave<HD>(s_knew, P.k_norm, eps, cs, sn);
+      __syncthreads();
+      if (has_new) {
+        for (int d = tid; d < HD; d += NT) {
+          const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
+          if (KVBF16) {
+            const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
+            reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
+            reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
+            s_knew[d] = bf16_bits_to_f32(kb);
+            s_vnew[d] = bf16_bits_to_f32(vb);
+          } else {
+            reinterpret_cast<float*>(a.kv)[ki] = s_knew[d];
+            reinterpret_cast<float*>(a.kv)[vi] = s_vnew[d];
+          }
+        }
+      }
+      const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_h = tid / (NP * RG);
+      double qreg[DPP];
+#pragma unroll
+      for (int i = 0; i < DPP; ++i) qreg[i] = (double)s_qf[sc_h][4 * sc_pt + 4 * NP * (i / 4) + (i % 4)];
+      const bool out_live = tid < OUT_T;
+      const int o_h = out_live ? tid / TPH : 0, o_d = out_live ? (tid % TPH) * DPT : 0;
+      double o[DPT];
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) o[i] = 0.0;
+      if (tid < G) s_m[tid] = -INFINITY, s_l[tid] = 0.0;
+      const double scale = a.scale;
+
+      auto process = [&](KvTile<HD, KVBF16>& tr, int i, bool prefetch) {
+        const bool isv = i >= nt;
+        const int t0 = j0 + (isv ? i - nt : i) * TJ;
+        const int nrow = min(TJ, j1 - t0);
+        __syncthreads();
+        if (i == nt) {  // all scores written: softmax over the split, once
+          const int n = j1 - j0;
+          for (int h = wave; h < G; h += kWavesP) {
+            double m = -INFINITY;
+            for (int r = lane; r < n; r += kWave) m = fmax(m, s_s[h][r]);
+            m = wave_max_d<kWave>(m);
+            double lsum = 0.0;
+            for (int r = lane; r < n; r += kWave) {
+              const double e = exp(s_s[h][r] - m);
+              s_s[h][r] = e;
+              lsum += e;
+            }
+            lsum = wave_sum_d<kWave>(lsum);
+            if (lane == 0) s_m[h] = m, s_l[h] = lsum;
+          }
+          __syncthreads();
+        }
+        if (t0 < cache_end) tr.store(s_t);
+        if (prefetch) stream_load(tr, i + 2);
+        if (t0 + nrow > p) {  // row p from this step's values (after the tile store)
+          __syncthreads();
+          const float* src = isv ? s_vnew : s_knew;
+          for (int d = tid; d < HD; d += NT) s_t[p - t0][d] = src[d];
+        }
+        __syncthreads();
+        if (!isv) {
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) {
+            const int r = sc_rg * RPT + j;
+            const float* kr = &s_t[r][4 * sc_pt];
+            double acc = 0.0;
+#pragma unroll
+            for (int d = 0; d < DPP; d += 4) {
+              const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
+              acc += qreg[d] * (double)k4.x;
+              acc += qreg[d + 1] * (double)k4.y;
+              acc += qreg[d + 2] * (double)k4.z;
+              acc += qreg[d + 3] * (double)k4.w;
+            }
+            acc = wave_sum_d<NP>(acc);
+            if (sc_pt == 0 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
+          }
+        } else if (out_live) {
+          const double* pr = &s_s[o_h][t0 - j0];
+#pragma unroll 8
+          for (int r = 0; r < nrow; ++r) {
+            const double wgt = pr[r];
+#pragma unroll
+            for (int i2 = 0; i2 < DPT; ++i2) o[i2] += wgt * (double)s_t[r][o_d + i2];
+          }
+        }
+      };
+      int i = 0;
+      for (; i + 2 < 2 * nt; i += 2) {
+        process(tA, i, true);
+        process(tB, i + 1, true);
+      }
+      if (nt > 0) {
+        process(tA, i, false);
+        process(tB, i + 1, false);
+      }
+      __syncthreads();
+      // partial (o, m, l) of this split, then the last arrival combines
+      const int64_t pstride = (int64_t)G * (HD + 2);
+      double* part = a.part + ((int64_t)ag * S + asplit) * pstride;
+      if (out_live) {
+#pragma unroll
+        for (int i2 = 0; i2 < DPT; ++i2) st_coherent(part + o_h * (HD + 2) + o_d + i2, o[i2]);
+      }
+      if (tid < G) {
+        st_coherent(part + tid * (HD + 2) + HD, s_m[tid]);
+        st_coherent(part + tid * (HD + 2) + HD + 1, s_l[tid]);
+      }
+      wait_memory();
+      __syncthreads();
+      if (tid == 0) {
+        unsigned* cnt = a.attn_cnt + (int64_t)l * NKV + ag;
+        const unsigned prev = arrive(cnt);
+        s_last = prev == (unsigned)(S - 1);
+        if (s_last) st_coherent(cnt, 0u);
+      }
+      __syncthreads();
+      if (s_last) {
+        const double* pb = a.part + (int64_t)ag * S * pstride;
+        for (int e = tid; e < G * S; e += NT) {
+          const int h = e / S, si = e % S;
+          s_w[h][si] = ld_coherent(pb + si * pstride + h * (HD + 2) + HD);
+          s_ls[h][si] = ld_coherent(pb + si * pstride + h * (HD + 2) + HD + 1);
+        }
+        __syncthreads();
+        if (tid < G) {
+          double M = -INFINITY;
+          for (int si = 0; si < S; ++si) M = fmax(M, s_w[tid][si]);
+          s_M[tid] = M;
+        }
+        __syncthreads();
+        for (int e = tid; e < G * S; e += NT) {
+          const int h = e / S, si = e % S;
+          const double ms = s_w[h][si];
+          s_w[h][si] = (ms == -INFINITY) ? 0.0 : exp(ms - s_M[h]);
+        }
+        __syncthreads();
+        if (tid < G) {
+          double L = 0.0;
+          for (int si = 0; si < S; ++si) L += s_w[tid][si] * s_ls[tid][si];
+          s_L[tid] = L;
+        }
+        __syncthreads();
+        if (out_live) {
+          double O[DPT];
+#pragma unroll
+          for (int i2 = 0; i2 < DPT; ++i2) O[i2] = 0.0;
+          const double* ob = pb + o_h * (HD + 2) + o_d;
+          double v[S][DPT];
+#pragma unroll
+          for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int i2 = 0; i2 < DPT; ++i2) v[si][i2] = ld_coherent(ob + si * pstride + i2);
+#pragma unroll
+          for (int si = 0; si < S; ++si)
+#pragma unroll
+            for (int i2 = 0; i2 < DPT; ++i2) O[i2] += s_w[o_h][si] * v[si][i2];
+#pragma unroll
+          for (int i2 = 0; i2 < DPT; ++i2)
+            put_tagged(a.att + (ag * G + o_h) * HD + o_d + i2, (float)(O[i2] / s_L[o_h]), T);
+        }
+      }
+    }
+
+    // ---- C: o_proj + residual ----------------------------------------------------
+    {
+      Slice<QW, RC> w;
+      w.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
+      if (!poll_vec<QW>(a.att, T, s_x, a.err)) goto fail;
+      quantize_lds<QW, false>(s_x, nullptr, eps, s_qa, s_da, s_red);
+      w.compute(s_qa, s_da, [&](int lr, double acc) {
+        const float xn = s_xkeep[lr] + (float)acc;
+        put_tagged(a.xc + b * RC + lr, xn, T);
+        s_xckeep[lr] = xn;
+      });
+    }
+
+    // ---- D: gate/up + SwiGLU (rows of units u: gate (u/32)*64 + u%32, up +32) ----
+    {
+      Slice<H, 2 * UD> w;
+      w.load(P.gu_qs, P.gu_sc, [&](int lr) {
+        const int u = b * UD + (lr % UD);
+        return (u / 32) * 64 + (u % 32) + (lr < UD ? 0 : 32);
+      });
+      if (!poll_vec<H>(a.xc, T, s_x, a.err)) goto fail;
+      quantize_lds<H, true>(s_x, P.ffn_norm, eps, s_qa, s_da, s_red);
+      w.compute(s_qa, s_da, [&](int lr, double acc) { s_gu[lr] = (float)acc; });
+      __syncthreads();
+      if (tid < UD) put_tagged(a.h + b * UD + tid, swiglu_f64(s_gu[tid], s_gu[UD + tid]), T);
+    }
+
+    // ---- E: down + residual (x of the next layer) ----------------------------------
+    {
+      Slice<F, RC> w;
+      w.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
+      if (!poll_vec<F>(a.h, T, s_x, a.err)) goto fail;
+      quantize_lds<F, false>(s_x, nullptr, eps, s_qa, s_da, s_red);
+      w.compute(s_qa, s_da, [&](int lr, double acc) {
+        const float xn = s_xckeep[lr] + (float)acc;
+        put_tagged(a.xa + b * RC + lr, xn, T + 1u);
+        s_xkeep[lr] = xn;
+      });
+    }
+  }
+
+  // ---- lm_head over rows [b*RV, ...) + greedy argmax ---------------------------------
+  {
+    using LS = Slice<H, Slice<H, 1>::RPP>;  // one pass of RPP rows per buffer
+    constexpr int RPP = LS::RPP;
+    const int V = a.V;
+    const int RV = (V + NWG - 1) / NWG;
+    const int r0 = b * RV;
+    const int rend = min(V, r0 + RV);
+    const int npass = r0 < rend ? (rend - r0 + RPP - 1) / RPP : 0;
+    auto rowof = [&](int ps) { return [&, ps](int lr) { return min(r0 + ps * RPP + lr, V - 1); }; };
+    LS wa, wb, wc, wd;
+    if (npass > 0) wa.load(a.emb_qs, a.emb_sc, rowof(0));
+    if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
+    if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
+    if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
+    if (!poll_vec<H>(a.xa, T0 + (unsigned)a.L, s_x, a.err)) goto fail;
+    quantize_lds<H, true>(s_x, a.out_norm, eps, s_qa, s_da, s_red);
+    ArgBest best{-INFINITY, 0x7FFFFFFF};
+    auto run = [&](const LS& w, int ps) {
+      w.compute(s_qa, s_da, [&](int lr, double acc) {
+        const int row = r0 + ps * RPP + lr;
+        if (row < rend) {
+          const float y = (float)acc;
+          if (a.logits) a.logits[row] = y;
+          best = better(best, ArgBest{y, row});
+        }
+      });
+    };
+    // four passes in flight; past the end a buffer re-reads the last pass
+    // (a cache hit), so every wait covers a fixed number of loads
+    int ps = 0;
+    for (; ps + 4 < npass; ps += 4) {
+      run(wa, ps);
+      wa.load(a.emb_qs, a.emb_sc, rowof(ps + 4));
+      run(wb, ps + 1);
+      wb.load(a.emb_qs, a.emb_sc, rowof(min(ps + 5, npass - 1)));
+      run(wc, ps + 2);
+      wc.load(a.emb_qs, a.emb_sc, rowof(min(ps + 6, npass - 1)));
+      run(wd, ps + 3);
+      wd.load(a.emb_qs, a.emb_sc, rowof(min(ps + 7, npass - 1)));
+    }
+    if (ps < npass) run(wa, ps);
+    if (ps + 1 < npass) run(wb, ps + 1);
+    if (ps + 2 < npass) run(wc, ps + 2);
+    if (ps + 3 < npass) run(wd, ps + 3);
+    // (max, lowest index) of the workgroup -> one 64-bit key; the last
+    // workgroup to arrive writes the token and advances the length
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      ArgBest c;
+      c.v = __shfl_xor(best.v, o);
+      c.i = __shfl_xor(best.i, o);
+      best = better(best, c);
+    }
+    if (lane == 0) s_best[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      ArgBest bb = s_best[0];
+      for (int i = 1; i < kWavesP; ++i) bb = better(bb, s_best[i]);
+      const uint32_t u = __float_as_uint(bb.v + 0.0f);
+      const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      const unsigned long long key = ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (uint32_t)bb.i);
+      __hip_atomic_fetch_max(a.best_key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory();
+      const unsigned prev = arrive(a.am_cnt);
+      if (prev == gridDim.x - 1) {
+        const unsigned long long k = __hip_atomic_fetch_add(a.best_key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.argmax[0] = ld_err(a.err) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        st_coherent(a.best_key, 0ull);
+        st_coherent(a.am_cnt, 0u);
+        a.len[seq] = p + 1;
+      }
+    }
+  }
+  return;
+fail:
+  if (tid == 0) {
+    __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.argmax[0] = -1;
+  }
+}
+
+}  // namespace
+
+namespace q8k {
+
+namespace {
+template <int H, int QW, int F, int HD, int G, int S, int MAXR>
+bool persist_try(const PersistShape& sh, bool kvbf16, const PersistArgs* a, hipStream_t s, hipError_t* err,
+                 int* max_ctx) {
+  if (sh.H != H || sh.QW != QW || sh.F != F || sh.HD != HD || sh.G != G) return false;
+  if (max_ctx) *max_ctx = S * MAXR;
+  if (!a) return true;
+  if (kvbf16)
+    hipLaunchKernelGGL((k_decode_persistent<H, QW, F, HD, G, true, S, MAXR>), dim3(kPersistWorkgroups), dim3(NT), 0,
+                       s, *a);
+  else
+    hipLaunchKernelGGL((k_decode_persistent<H, QW, F, HD, G, false, S, MAXR>), dim3(kPersistWorkgroups), dim3(NT), 0,
+                       s, *a);
+  *err = hipGetLastError();
+  return true;
+}
+
+}  // namespace
+
+// The shapes the persistent step is built for: Qwen3-0.6B and the tiny test
+// model: every workgroup takes an attention split (32 per KV head for
+// 0.6B, 16 for the tiny model), each of up to 512 rows.
+
+int persist_max_ctx(const PersistShape& sh) {
+  int mc = 0;
+  if (persist_try<1024, 2048, 3072, 128, 2, 32, 512>(sh, false, nullptr, nullptr, nullptr, &mc)) return mc;
+  if (persist_try<256, 256, 768, 64, 2, 16, 512>(sh, false, nullptr, nullptr, nullptr, &mc)) return mc;
+  return 0;
+}
+
+int persist_occupancy(const PersistShape& sh, bool kvbf16) {
+  int occ = 0;
+  auto q = [&](auto kern) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, NT, 0) != hipSuccess) occ = 0;
+  };
+  if (sh.H == 1024 && sh.QW == 2048 && sh.F == 3072 && sh.HD == 128 && sh.G == 2) {
+    if (kvbf16) q(k_decode_persistent<1024, 2048, 3072, 128, 2, true, 32, 512>);
+    else q(k_decode_persistent<1024, 2048, 3072, 128, 2, false, 32, 512>);
+  } else if (sh.H == 256 && sh.QW == 256 && sh.F == 768 && sh.HD == 64 && sh.G == 2) {
+    if (kvbf16) q(k_decode_persistent<256, 256, 768, 64, 2, true, 16, 512>);
+    else q(k_decode_persistent<256, 256, 768, 64, 2, false, 16, 512>);
+  }
+  return occ;
+}
+
+hipError_t decode_persistent(const PersistShape& sh, bool kvbf16, const PersistArgs& a, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+  if (persist_try<1024, 2048, 3072, 128, 2, 32, 512>(sh, kvbf16, &a, s, &e, nullptr)) return e;
+  if (persist_try<256, 256, 768, 64, 2, 16, 512>(sh, kvbf16, &a, s, &e, nullptr)) return e;
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q8k

@@ -151,3 +151,44 @@ hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, bool kv_bf16, hipS
 hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf16, hipStream_t s);
 bool attn_prefill_supported(int hd, int group);
 }  // namespace q8k
+
+// One-launch decode step (see k_decode_persistent.hip).
+constexpr int kPersistWorkgroups = 256;
+struct PLayer {  // a layer's repacked weights
+  const int8_t *qkv_qs, *o_qs, *gu_qs, *dn_qs;
+  const uint16_t *qkv_sc, *o_sc, *gu_sc, *dn_sc;
+  const float *attn_norm, *q_norm, *k_norm, *ffn_norm;
+};
+struct PersistArgs {
+  const PLayer* layers;  // device [L]
+  int L, V;
+  float eps;
+  double scale;  // 1/sqrt(hd)
+  const int8_t* emb_qs;
+  const uint16_t* emb_sc;
+  const float* out_norm;
+  const double *rope_cos, *rope_sin;
+  void* kv;
+  const int64_t* seq_base;
+  const int32_t* seq_cap;
+  int32_t* len;
+  int seq;
+  const int32_t* token;  // device [1]
+  float* logits;         // [V] or null
+  int32_t* argmax;       // [1]
+  unsigned long long *xa, *xc, *qkv, *att, *h;  // (value, epoch) words
+  double* part;          // [nkv][splits per KV head][G][hd + 2]
+  unsigned* attn_cnt;    // [L][nkv], zero between steps
+  unsigned long long* best_key;
+  unsigned* am_cnt;
+  unsigned* err;         // set on a timed-out wait
+  unsigned pstep;        // launch counter (epochs)
+};
+struct PersistShape {
+  int H, QW, F, HD, G;
+};
+namespace q8k {
+int persist_max_ctx(const PersistShape& sh);  // 0: no persistent step for this shape
+int persist_occupancy(const PersistShape& sh, bool kv_bf16);
+hipError_t decode_persistent(const PersistShape& sh, bool kv_bf16, const PersistArgs& a, hipStream_t s);
+}  // namespace q8k

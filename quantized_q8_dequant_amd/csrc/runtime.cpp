@@ -124,6 +124,14 @@ struct qwen3_model {
   unsigned* attn_cnt = nullptr;
   unsigned long long* am_key = nullptr;
   unsigned* am_cnt = nullptr;
+  // one-launch decode step (shapes it is built for; see k_decode_persistent.hip)
+  PersistShape psh{};
+  bool persist_capable = false, persist = false;
+  PLayer* d_players = nullptr;
+  unsigned long long *p_xa = nullptr, *p_xc = nullptr, *p_qkv = nullptr, *p_att = nullptr, *p_h = nullptr;
+  unsigned* p_cnt = nullptr;
+  unsigned* p_err = nullptr;
+  unsigned pstep = 0;
   size_t bytes = 0;
   // host
   std::vector<int64_t> seq_base;
@@ -249,6 +257,16 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
+  if (m->persist_capable) {
+    m->d_players = cv.arr<PLayer>(c.num_layers);
+    m->p_xa = cv.arr<unsigned long long>(H);
+    m->p_xc = cv.arr<unsigned long long>(H);
+    m->p_qkv = cv.arr<unsigned long long>(nqkv);
+    m->p_att = cv.arr<unsigned long long>(qw);
+    m->p_h = cv.arr<unsigned long long>(F);
+    m->p_cnt = cv.arr<unsigned>((size_t)c.num_layers * nkv);
+    m->p_err = cv.arr<unsigned>(1);
+  }
   if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
   *total = align_up(cv.off);
   return QWEN3_OK;
@@ -275,6 +293,8 @@ int fill_model_shape(qwen3_model* m, const qwen3_config* cfg) {
   m->kvbf16 = cfg->kv_type == QWEN3_KV_BF16;
   m->max_cap = 0;
   for (int c : m->cap) m->max_cap = std::max(m->max_cap, c);
+  m->psh = PersistShape{m->H, m->qw, m->F, m->hd, m->G};
+  m->persist_capable = !m->wbf16 && q8k::persist_max_ctx(m->psh) > 0;
   return QWEN3_OK;
 }
 
@@ -634,6 +654,23 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
     HIP_TRY(hipMemsetAsync(m->attn_cnt, 0, (size_t)m->R * m->nkv * 4, s));
     HIP_TRY(hipMemsetAsync(m->am_cnt, 0, (size_t)m->R * 4, s));
     HIP_TRY(hipMemsetAsync(m->am_key, 0, (size_t)m->R * 8, s));
+    if (m->persist_capable) {
+      std::vector<PLayer> tab(m->L);
+      for (int l = 0; l < m->L; ++l) {
+        const Layer& ly = m->layers[l];
+        tab[l] = PLayer{ly.qkv.qs, ly.o.qs, ly.gateup.qs, ly.down.qs, ly.qkv.sc, ly.o.sc, ly.gateup.sc, ly.down.sc,
+                        ly.attn_norm, ly.q_norm, ly.k_norm, ly.ffn_norm};
+      }
+      HIP_TRY(hipMemcpyAsync(m->d_players, tab.data(), tab.size() * sizeof(PLayer), hipMemcpyHostToDevice, s));
+      HIP_TRY(hipMemsetAsync(m->p_xa, 0, (size_t)m->H * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_xc, 0, (size_t)m->H * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_qkv, 0, (size_t)m->nqkv * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_att, 0, (size_t)m->qw * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_cnt, 0, (size_t)m->L * m->nkv * 4, s));
+      HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
+      HIP_TRY(hipStreamSynchronize(s));  // tab is a host temporary
+    }
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
     return QWEN3_OK;
@@ -646,6 +683,17 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
   m->h_len.assign(m->cap.size(), 0);
   const char* ng = std::getenv("QWEN3_NO_GRAPH");
   m->use_graphs = !(ng && ng[0] == '1');
+  // the one-launch decode step needs every workgroup of its grid resident at
+  // once: at least kPersistWorkgroups CUs, and one workgroup fitting per CU
+  if (m->persist_capable && m->max_cap <= q8k::persist_max_ctx(m->psh)) {
+    const char* pe = std::getenv("QWEN3_PERSISTENT");
+    int dev = 0, cus = 0;
+    const bool on = !(pe && pe[0] == '0');
+    if (on && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus >= kPersistWorkgroups && q8k::persist_occupancy(m->psh, m->kvbf16) >= 1)
+      m->persist = true;
+  }
   *out = m;
   return QWEN3_OK;
 }
@@ -669,6 +717,7 @@ int qwen3_reset(qwen3_t* m, int32_t seq, void* stream) {
   if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
   if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
   HIP_TRY(q8k::set_len(m->d_len, seq, 0, S(stream)));
+  if (m->p_err) HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, S(stream)));
   m->h_len[seq] = 0;
   return QWEN3_OK;
 }
@@ -707,6 +756,38 @@ int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_
   if (m->h_len[seq] + 1 > m->cap[seq])
     return fail(QWEN3_E_KV_CACHE_OVERFLOW, "decode at len " + std::to_string(m->h_len[seq]) + " exceeds capacity");
   hipStream_t s = S(stream);
+  if (m->persist) {
+    PersistArgs a{};
+    a.layers = m->d_players;
+    a.L = m->L;
+    a.V = m->V;
+    a.eps = m->cfg.rms_norm_eps;
+    a.scale = 1.0 / std::sqrt((double)m->hd);
+    a.emb_qs = m->emb.qs;
+    a.emb_sc = m->emb.sc;
+    a.out_norm = m->out_norm;
+    a.rope_cos = m->rope_cos;
+    a.rope_sin = m->rope_sin;
+    a.kv = m->kv;
+    a.seq_base = m->d_seq_base;
+    a.seq_cap = m->d_seq_cap;
+    a.len = m->d_len;
+    a.seq = seq;
+    a.token = d_token;
+    a.logits = d_logits;
+    a.argmax = d_argmax;
+    a.xa = m->p_xa, a.xc = m->p_xc, a.qkv = m->p_qkv, a.att = m->p_att, a.h = m->p_h;
+    a.part = m->attn_part;
+    a.attn_cnt = m->p_cnt;
+    a.best_key = m->am_key;
+    a.am_cnt = m->am_cnt;
+    a.err = m->p_err;
+    a.pstep = m->pstep;
+    HIP_TRY(q8k::decode_persistent(m->psh, m->kvbf16, a, s));
+    m->pstep += 1;
+    m->h_len[seq] += 1;
+    return QWEN3_OK;
+  }
   if (!m->use_graphs) {
     TRY(enqueue_decode(m, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, s));
     m->h_len[seq] += 1;

@@ -485,3 +485,37 @@ def test_qwen3_8b_long_context_matches_oracle():
         assert tok == int(np.argmax(lr)), L
         progress(f"oracle: decode at {L} checked")
         del c
+
+
+# ---- the one-launch decode step against the per-kernel step -------------------------
+
+
+@pytest.mark.parametrize("shape_name", ["tiny", "0.6b"])
+def test_persistent_decode_matches_per_kernel_decode(shape_name, monkeypatch):
+    """The one-launch decode step computes what the per-kernel step computes
+    (same reductions; only the attention split differs, in f64): tokens equal,
+    logits within the tolerance and nearly all bit-identical; both against
+    the oracle for the tiny model."""
+    shape, wseed, plen, steps, cap = (
+        (TINY, 101, 37, 12, 64) if shape_name == "tiny" else (QWEN3_0_6B, 201, 300, 6, 320)
+    )
+    w = gen_weights(shape, wseed)
+    prompt = gen_prompt(shape.vocab_size, plen, 55)
+    monkeypatch.setenv("QWEN3_PERSISTENT", "1")
+    a = make(shape, w, [cap])
+    ta, la = gpu_generate(a, prompt, steps)
+    a.close()
+    monkeypatch.setenv("QWEN3_PERSISTENT", "0")
+    b = make(shape, w, [cap])
+    tb, lb = gpu_generate(b, prompt, steps)
+    b.close()
+    assert ta == tb
+    same = 0.0
+    for x, y in zip(la, lb):
+        assert rel_err(x, y) <= TOL
+        same += float(np.mean(x == y))
+    assert same / len(la) >= 0.999
+    if shape_name == "tiny":
+        ref = om.Model(shape, w)
+        rt, rl = ref.generate(prompt, steps, ref.new_cache(cap))
+        check_against_oracle(ta, la, rt, rl)
