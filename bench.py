@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
+PERSISTENT_SRC = os.path.join(ROOT, "quantized_q8_dequant_amd", "csrc", "k_decode_persistent.hip")
 INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA
 KIND_NAMES = ["qkv_gemv", "attention", "o_proj_gemv", "gate_up_swiglu_gemv", "down_gemv", "lm_head_argmax_gemv"]
 
@@ -61,6 +63,28 @@ def decode_token_bytes(shape, ctx: int) -> float:
     """Algorithmic HBM bytes of one decode step whose new token sits at ctx."""
     per_layer = sum(kernel_bytes(shape, k, ctx) for k in range(5))
     return shape.num_layers * per_layer + kernel_bytes(shape, 5, ctx) + 4 * shape.vocab_size
+
+
+def source_sha(path: str) -> str:
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None if
+    there are none or the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("source_sha256") != source_sha(PERSISTENT_SRC):
+        return None
+    return k.get("bytes_per_launch")
 
 
 def prefill_int8_ops(shape, T: int) -> int:
@@ -264,6 +288,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-steps", type=int, default=8)
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument(
+        "--pmc-calibrate",
+        action="store_true",
+        help="finish with a 1 GiB device-to-device copy (the known-size kernel hardware counters are scaled by)",
+    )
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -341,9 +370,21 @@ def main() -> int:
             "bytes_per_launch": int(nbytes),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
         }
-    dom = max(kernels, key=lambda k: kernels[k]["us_per_launch"] * kernels[k]["launches_per_token"])
-    dk = kernels[dom]
-    achieved = dk["GBps"]
+    launches = model.decode_launches()
+    if launches == 1:
+        # the decode step is one kernel: its algorithmic bytes per launch (the
+        # step at the mean KV length) over its event-timed duration
+        mean_bytes = step_bytes / wl.decode_steps
+        us = decode_ms * 1000.0 / wl.decode_steps
+        dom = "decode_step (one launch)"
+        achieved = round(mean_bytes / (us * 1e-6) / 1e9, 1)
+        traffic = measured_traffic("decode_step")
+        kernel_info = {"us_per_launch": round(us, 3), "bytes_per_launch": int(mean_bytes)}
+    else:
+        dom = max(kernels, key=lambda k: kernels[k]["us_per_launch"] * kernels[k]["launches_per_token"])
+        achieved = kernels[dom]["GBps"]
+        traffic = None
+        kernel_info = kernels[dom]
     roofline = {
         "kernel": dom,
         "bound": "hbm",
@@ -351,7 +392,8 @@ def main() -> int:
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": traffic,
+        "launch": kernel_info,
     }
 
     # the prefill-dominated workload on the same weights: 4096 tokens in one call
@@ -389,6 +431,15 @@ def main() -> int:
         del model
         torch.cuda.empty_cache()
 
+    if args.pmc_calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape, weights, prompt, args.cpu_decode_steps)
@@ -421,6 +472,7 @@ def main() -> int:
         "decode_hbm_frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(prefill_tps, 1),
+        "decode_launches_per_token": launches,
         "kernels_at_mean_ctx": kernels,
         "prefill_4096_one_call": p4,
         "roofline": roofline,

@@ -195,6 +195,13 @@ int qwen3_replay_kernel(qwen3_t* h, int32_t seq, int32_t kind, int32_t layer, in
 /* Thread-local description of the last error ("" if none). */
 const char* qwen3_last_error(void);
 
+/* Kernel launches one qwen3_decode_step enqueues: 1 when the model's shape
+ * has the one-launch (persistent) decode step and the device can hold its
+ * grid resident (every CU holds one of its workgroups), else the per-kernel
+ * step's count (one embedding launch, five launches per layer, one lm_head
+ * launch).  Host-only; -1 on a null handle. */
+int32_t qwen3_decode_launches(const qwen3_t* h);
+
 /* ---- op-level entry points (kernel-boundary parity and input prep) ------- */
 
 /* Q8_0 encoder ("Model files and quantization", section 11.7) of n f32

@@ -47,6 +47,7 @@ EXPORTS = (
     "qwen3_kv_export",
     "qwen3_replay_kernel",
     "qwen3_bf16_linear",
+    "qwen3_decode_launches",
 )
 
 
@@ -138,6 +139,7 @@ def lib() -> C.CDLL:
         "qwen3_kv_export": (C.c_int, [vp, i32, i32, vp, vp, vp]),
         "qwen3_replay_kernel": (C.c_int, [vp, i32, i32, i32, i32, vp]),
         "qwen3_bf16_linear": (C.c_int, [vp, i64, i64, vp, i64, vp, vp]),
+        "qwen3_decode_launches": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -566,6 +566,11 @@ extern "C" {
 
 const char* qwen3_last_error(void) { return g_err.c_str(); }
 
+int32_t qwen3_decode_launches(const qwen3_t* m) {
+  if (!m) return -1;
+  return m->persist ? 1 : 5 * m->L + 2;
+}
+
 size_t qwen3_workspace_bytes(const qwen3_config* cfg) {
   g_err.clear();
   if (validate(cfg) != QWEN3_OK) return 0;

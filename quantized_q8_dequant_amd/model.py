@@ -269,6 +269,10 @@ class Qwen3Model:
         """Enqueue `reps` launches of one decode-step kernel (benchmark hook)."""
         check(lib().qwen3_replay_kernel(self.handle, seq, kind, layer, reps, _stream()))
 
+    def decode_launches(self) -> int:
+        """Kernel launches per decode step (1: the one-launch step)."""
+        return int(lib().qwen3_decode_launches(self.handle))
+
     def kv_len(self, seq: int = 0) -> int:
         out = C.c_int32()
         check(lib().qwen3_kv_len(self.handle, seq, C.byref(out)))

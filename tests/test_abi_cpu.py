@@ -134,5 +134,6 @@ def test_null_handle_and_op_argument_errors():
     assert lib.qwen3_bf16_linear(0x1000, 2, 48, 0x2000, 8, 0x3000, None) == -1  # k % 32
     assert lib.qwen3_bf16_linear(0x1000, 0, 64, 0x2000, 8, 0x3000, None) == -1
     assert lib.qwen3_bf16_linear(None, 2, 64, 0x2000, 8, 0x3000, None) == -1
+    assert lib.qwen3_decode_launches(None) == -1
     # encoding zero values enqueues nothing
     assert lib.qwen3_q8_0_encode(None, 0, None, None) == 0

@@ -503,10 +503,12 @@ def test_persistent_decode_matches_per_kernel_decode(shape_name, monkeypatch):
     prompt = gen_prompt(shape.vocab_size, plen, 55)
     monkeypatch.setenv("QWEN3_PERSISTENT", "1")
     a = make(shape, w, [cap])
+    assert a.decode_launches() == 1
     ta, la = gpu_generate(a, prompt, steps)
     a.close()
     monkeypatch.setenv("QWEN3_PERSISTENT", "0")
     b = make(shape, w, [cap])
+    assert b.decode_launches() == 5 * shape.num_layers + 2
     tb, lb = gpu_generate(b, prompt, steps)
     b.close()
     assert ta == tb
