@@ -29,12 +29,6 @@ namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-template <bool BF16>
-QDEV float ld_kv(const void* base, int64_t idx) {
-  if (BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
-  return reinterpret_cast<const float*>(base)[idx];
-}
-
 template <int HD, bool BF16>
 __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
   __shared__ float x[HD];
@@ -73,17 +67,65 @@ __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
 
 constexpr int KT = 64;  // keys per LDS tile
 
+// One K/V tile (KT rows of HD) in registers: 16-byte loads, the same count
+// for every tile (rows past `kend` re-read row kend - 1: finite values whose
+// scores are masked and whose probabilities are 0).
+template <int HD, bool BF16>
+struct KVTile {
+  static constexpr int PER = BF16 ? 8 : 4;  // elements per 16-byte load
+  static constexpr int LOADS = KT * HD / PER / 256;
+  v4i k[LOADS], v[LOADS];
+  QDEV void load(const void* kv, int64_t kb0, int64_t vb0, int kbase, int kend) {
+    constexpr int ESZ = BF16 ? 2 : 4;
+    const uint8_t* base = static_cast<const uint8_t*>(kv);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = (threadIdx.x + i * 256) * PER;
+      const int key = min(kbase + e / HD, kend - 1);
+      const int64_t off = (int64_t)key * HD + (e % HD);
+      k[i] = *reinterpret_cast<const v4i*>(base + (kb0 + off) * ESZ);
+      v[i] = *reinterpret_cast<const v4i*>(base + (vb0 + off) * ESZ);
+    }
+  }
+  QDEV void store(float* sK, int krow, float* sV, int vrow) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = (threadIdx.x + i * 256) * PER;
+      const int r = e / HD, d = e % HD;
+      if (BF16) {
+        float4 a0, a1, b0, b1;
+        a0.x = __uint_as_float((uint32_t)k[i][0] << 16), a0.y = __uint_as_float((uint32_t)k[i][0] & 0xFFFF0000u);
+        a0.z = __uint_as_float((uint32_t)k[i][1] << 16), a0.w = __uint_as_float((uint32_t)k[i][1] & 0xFFFF0000u);
+        a1.x = __uint_as_float((uint32_t)k[i][2] << 16), a1.y = __uint_as_float((uint32_t)k[i][2] & 0xFFFF0000u);
+        a1.z = __uint_as_float((uint32_t)k[i][3] << 16), a1.w = __uint_as_float((uint32_t)k[i][3] & 0xFFFF0000u);
+        b0.x = __uint_as_float((uint32_t)v[i][0] << 16), b0.y = __uint_as_float((uint32_t)v[i][0] & 0xFFFF0000u);
+        b0.z = __uint_as_float((uint32_t)v[i][1] << 16), b0.w = __uint_as_float((uint32_t)v[i][1] & 0xFFFF0000u);
+        b1.x = __uint_as_float((uint32_t)v[i][2] << 16), b1.y = __uint_as_float((uint32_t)v[i][2] & 0xFFFF0000u);
+        b1.z = __uint_as_float((uint32_t)v[i][3] << 16), b1.w = __uint_as_float((uint32_t)v[i][3] & 0xFFFF0000u);
+        *reinterpret_cast<float4*>(sK + r * krow + d) = a0;
+        *reinterpret_cast<float4*>(sK + r * krow + d + 4) = a1;
+        *reinterpret_cast<float4*>(sV + r * vrow + d) = b0;
+        *reinterpret_cast<float4*>(sV + r * vrow + d + 4) = b1;
+      } else {
+        *reinterpret_cast<v4i*>(sK + r * krow + d) = k[i];
+        *reinterpret_cast<v4i*>(sV + r * vrow + d) = v[i];
+      }
+    }
+  }
+};
+
 template <int HD, int G, bool BF16>
 __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   constexpr int HW = G < 4 ? G : 4;  // query heads per workgroup
   constexpr int TPW = 4 / HW;        // 16-token sub-tiles per workgroup
   constexpr int QT = 16 * TPW;       // tokens per workgroup
-  constexpr int KROW = HD + 1;       // f32 per K row in LDS (padded)
+  constexpr int KROW = HD + 4;       // f32 per K row in LDS (padded: the 16 x 4 lanes of
+                                     // a K operand read hit 64 distinct banks)
   constexpr int VROW = HD + 16;      // f32 per V row in LDS (padded)
   constexpr int NST = HD / 4;        // k=4 steps over head_dim
   constexpr int NDT = HD / 16;       // 16-wide d tiles of the output
-  __shared__ float sK[KT * KROW];
-  __shared__ float sV[KT * VROW];
+  __shared__ __align__(16) float sK[KT * KROW];
+  __shared__ __align__(16) float sV[KT * VROW];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int lq = lane % 16, lg = lane / 16;
@@ -112,19 +154,14 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = v4d{0.0, 0.0, 0.0, 0.0};
   double m_run = -INFINITY, l_run = 0.0;
 
+  // the next tile's loads are issued right after the current tile is
+  // staged, so they land while the current tile is used
+  KVTile<HD, BF16> tile;
+  tile.load(a.kv, kb0, vb0, 0, kend);
   for (int kbase = 0; kbase < kend; kbase += KT) {
     __syncthreads();
-    for (int e = tid; e < KT * HD; e += 256) {
-      const int kr = e / HD, d = e % HD;
-      const int key = kbase + kr;
-      float kval = 0.f, vval = 0.f;
-      if (key < kend) {
-        kval = ld_kv<BF16>(a.kv, kb0 + (int64_t)key * HD + d);
-        vval = ld_kv<BF16>(a.kv, vb0 + (int64_t)key * HD + d);
-      }
-      sK[kr * KROW + d] = kval;
-      sV[kr * VROW + d] = vval;
-    }
+    tile.store(sK, KROW, sV, VROW);
+    tile.load(a.kv, kb0, vb0, kbase + KT < kend ? kbase + KT : kbase, kend);
     __syncthreads();
 
     // scores S^T for 4 sub-tiles of 16 keys; lane holds keys 4*item + lg
