@@ -181,7 +181,7 @@ struct Slice {
     }
   }
 
-  // emit(lr, acc) runs on the first lane of each row with the row's f64 sum
+  // emit(lr, acc) runs on the last lane of each row with the row's f64 sum
   template <typename Emit>
   QDEV void compute(const int8_t* s_qa, const float* s_da, Emit emit) const {
     const int li = threadIdx.x % LPR;
@@ -196,9 +196,9 @@ struct Slice {
         const int S = dot32_i8(w0[ps][j], w1[ps][j], a0, a1);
         acc += (double)S * (double)(f16_bits_to_f32(ws[ps][j]) * s_da[b]);
       }
-      acc = wave_sum_d<LPR>(acc);
+      acc = group_sum_d<LPR>(acc);
       const int lr = ps * RPP + threadIdx.x / LPR;
-      if (li == 0 && lr < R) emit(lr, acc);
+      if (li == LPR - 1 && lr < R) emit(lr, acc);
     }
   }
 };

@@ -165,9 +165,9 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
       }
     }
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum_d<LPR>(acc[r]);
+    for (int r = 0; r < ROWS; ++r) acc[r] = group_sum_d<LPR>(acc[r]);
 
-    if (li == 0) {
+    if (li == LPR - 1) {  // the lane holding the row sums
       if (EPI == EPI_SWIGLU) {
         constexpr int P = ROWS / 2;
 #pragma unroll

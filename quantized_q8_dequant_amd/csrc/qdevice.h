@@ -90,12 +90,43 @@ QDEV double wave_max_d(double v) {
   return v;
 }
 
+// Sums of doubles over aligned groups of WIDTH lanes (WIDTH = 2..64) with DPP
+// lane moves of the two 32-bit halves: quad permutes, the row mirrors and the
+// GFX9 row broadcasts, a few cycles per step instead of an LDS-permute round
+// trip.  The group's total is valid in its LAST lane (other lanes hold
+// partial sums).
+template <int CTRL, int ROW_MASK = 0xF>
+QDEV double dpp_move_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+template <int WIDTH>
+QDEV double group_sum_d(double v) {
+  static_assert(WIDTH == 1 || WIDTH == 2 || WIDTH == 4 || WIDTH == 8 || WIDTH == 16 || WIDTH == 32 || WIDTH == 64,
+                "group width");
+  if (WIDTH >= 2) v += dpp_move_d<0xB1>(v);        // quad_perm [1,0,3,2]
+  if (WIDTH >= 4) v += dpp_move_d<0x4E>(v);        // quad_perm [2,3,0,1]
+  if (WIDTH >= 8) v += dpp_move_d<0x141>(v);       // row_half_mirror
+  if (WIDTH >= 16) v += dpp_move_d<0x140>(v);      // row_mirror
+  if (WIDTH >= 32) v += dpp_move_d<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  if (WIDTH >= 64) v += dpp_move_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// The wavefront's total in every lane.
+QDEV double wave_total_d(double v) {
+  v = group_sum_d<kWave>(v);
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), kWave - 1);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), kWave - 1);
+  return __hiloint2double(hi, lo);
+}
+
 // Block-wide sum of one double per thread (blockDim.x == NT, NT % 64 == 0).
 template <int NT>
 QDEV double block_sum_d(double v, double* s_red) {
-  v = wave_sum_d<kWave>(v);
+  v = group_sum_d<kWave>(v);
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  if (l == 0) s_red[w] = v;
+  if (l == kWave - 1) s_red[w] = v;
   __syncthreads();
   double t = 0.0;
 #pragma unroll
@@ -187,7 +218,7 @@ QDEV void norm_rope_wave(float* x, const float* __restrict__ w, float eps, const
   const int lane = threadIdx.x % kWave;
   double ss = 0.0;
   for (int d = lane; d < HD; d += kWave) ss += (double)x[d] * (double)x[d];
-  ss = wave_sum_d<kWave>(ss);
+  ss = wave_total_d(ss);
   const double r = rms_scale(ss, HD, eps);
   constexpr int H2 = HD / 2;
   for (int i = lane; i < H2; i += kWave) {
