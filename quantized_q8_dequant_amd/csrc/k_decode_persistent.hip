@@ -395,14 +395,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
           for (int h = wave; h < G; h += kWavesP) {
             double m = -INFINITY;
             for (int r = lane; r < n; r += kWave) m = fmax(m, s_s[h][r]);
-            m = wave_max_d<kWave>(m);
+            m = wave_max_all_d(m);
             double lsum = 0.0;
             for (int r = lane; r < n; r += kWave) {
               const double e = exp(s_s[h][r] - m);
               s_s[h][r] = e;
               lsum += e;
             }
-            lsum = wave_sum_d<kWave>(lsum);
+            lsum = wave_total_d(lsum);
             if (lane == 0) s_m[h] = m, s_l[h] = lsum;
           }
           __syncthreads();
@@ -429,8 +429,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
               acc += qreg[d + 2] * (double)k4.z;
               acc += qreg[d + 3] * (double)k4.w;
             }
-            acc = wave_sum_d<NP>(acc);
-            if (sc_pt == 0 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
+            acc = group_sum_d<NP>(acc);
+            if (sc_pt == NP - 1 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
           }
         } else if (out_live) {
           const double* pr = &s_s[o_h][t0 - j0];

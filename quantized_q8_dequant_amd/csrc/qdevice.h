@@ -95,10 +95,11 @@ QDEV double wave_max_d(double v) {
 // GFX9 row broadcasts, a few cycles per step instead of an LDS-permute round
 // trip.  The group's total is valid in its LAST lane (other lanes hold
 // partial sums).
+// (lanes of rows outside ROW_MASK receive `old`)
 template <int CTRL, int ROW_MASK = 0xF>
-QDEV double dpp_move_d(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
+QDEV double dpp_move_d(double v, double old = 0.0) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(old), __double2loint(v), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(old), __double2hiint(v), CTRL, ROW_MASK, 0xF, false);
   return __hiloint2double(hi, lo);
 }
 template <int WIDTH>
@@ -113,12 +114,21 @@ QDEV double group_sum_d(double v) {
   if (WIDTH >= 64) v += dpp_move_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
-// The wavefront's total in every lane.
-QDEV double wave_total_d(double v) {
-  v = group_sum_d<kWave>(v);
+QDEV double bcast_last_d(double v) {
   const int lo = __builtin_amdgcn_readlane(__double2loint(v), kWave - 1);
   const int hi = __builtin_amdgcn_readlane(__double2hiint(v), kWave - 1);
   return __hiloint2double(hi, lo);
+}
+// The wavefront's total / maximum in every lane.
+QDEV double wave_total_d(double v) { return bcast_last_d(group_sum_d<kWave>(v)); }
+QDEV double wave_max_all_d(double v) {
+  v = fmax(v, dpp_move_d<0xB1>(v));
+  v = fmax(v, dpp_move_d<0x4E>(v));
+  v = fmax(v, dpp_move_d<0x141>(v));
+  v = fmax(v, dpp_move_d<0x140>(v));
+  v = fmax(v, dpp_move_d<0x142, 0xA>(v, -INFINITY));
+  v = fmax(v, dpp_move_d<0x143, 0xC>(v, -INFINITY));
+  return bcast_last_d(v);
 }
 
 // Block-wide sum of one double per thread (blockDim.x == NT, NT % 64 == 0).
@@ -172,9 +182,10 @@ QDEV float block_sum(float v, float* s_red) {
 // the group gets the same d).
 QDEV int quant4_group8(const float v[4], float* d_out) {
   float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  a = fmaxf(a, __shfl_xor(a, 1, 8));
-  a = fmaxf(a, __shfl_xor(a, 2, 8));
-  a = fmaxf(a, __shfl_xor(a, 4, 8));
+  // max over the 8 lanes (DPP: quad permutes, then the half-row mirror)
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xF, 0xF, false)));
   const float d = a / 127.0f;
   const float inv = d == 0.f ? 0.f : 1.0f / d;
   int packed = 0;
