@@ -473,7 +473,15 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       }
       __syncthreads();
       if (s_last) {
+        // every load of the combine is issued in one round: the O partials of
+        // this thread's outputs together with the (m, l) pairs
         const double* pb = a.part + (int64_t)ag * S * pstride;
+        const double* ob = pb + o_h * (HD + 2) + o_d;
+        double v[S][DPT];
+#pragma unroll
+        for (int si = 0; si < S; ++si)
+#pragma unroll
+          for (int i2 = 0; i2 < DPT; ++i2) v[si][i2] = out_live ? ld_coherent(ob + si * pstride + i2) : 0.0;
         for (int e = tid; e < G * S; e += NT) {
           const int h = e / S, si = e % S;
           s_w[h][si] = ld_coherent(pb + si * pstride + h * (HD + 2) + HD);
@@ -502,12 +510,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
           double O[DPT];
 #pragma unroll
           for (int i2 = 0; i2 < DPT; ++i2) O[i2] = 0.0;
-          const double* ob = pb + o_h * (HD + 2) + o_d;
-          double v[S][DPT];
-#pragma unroll
-          for (int si = 0; si < S; ++si)
-#pragma unroll
-            for (int i2 = 0; i2 < DPT; ++i2) v[si][i2] = ld_coherent(ob + si * pstride + i2);
 #pragma unroll
           for (int si = 0; si < S; ++si)
 #pragma unroll
