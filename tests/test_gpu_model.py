@@ -521,3 +521,23 @@ def test_persistent_decode_matches_per_kernel_decode(shape_name, monkeypatch):
         ref = om.Model(shape, w)
         rt, rl = ref.generate(prompt, steps, ref.new_cache(cap))
         check_against_oracle(ta, la, rt, rl)
+
+
+def test_tiny_decode_steps_interleaved_over_sequences(tiny_w, tiny_ref):
+    """decode_step on three sequences in turn (each its own cache region,
+    length and argmax buffer) gives each sequence the oracle's tokens."""
+    prompts = [gen_prompt(TINY.vocab_size, n, 60 + n) for n in (4, 29, 13)]
+    gpu = make(TINY, tiny_w, [48, 48, 48])
+    toks = {s: [int(gpu.prefill(p, seq=s)[1].item())] for s, p in enumerate(prompts)}
+    logits = {s: [] for s in range(3)}
+    for _ in range(5):
+        for s in (2, 0, 1):
+            lg, am = gpu.decode_step(seq=s)
+            toks[s].append(int(am.item()))
+            logits[s].append(lg.cpu().numpy().copy())
+    for s, p in enumerate(prompts):
+        rt, rl = tiny_ref.generate(p, 5, tiny_ref.new_cache(48))
+        assert toks[s] == list(rt)
+        for i in range(5):
+            assert rel_err(logits[s][i], rl[i + 1]) <= TOL
+        assert gpu.kv_len(s) == len(p) + 5
