@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   for (int st = 0; st < nstage; ++st) {
     const int buf = st & 1;
     if (st + 1 < nstage) gemm_gload(a, rs, st + 1, m0, n0, nblk);
-#pragma unroll 1
+#pragma unroll 2
     for (int kb = 0; kb < KB; ++kb) {
       v4i af[2], bf[2];
 #pragma unroll
@@ -115,22 +115,32 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
         bf[ni] = *reinterpret_cast<const v4i*>(&sB[buf][(wn * 64 + ni * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+      // the four block products first, then their scaled f64 accumulation
+      // (d_a * d_w is exact in f64 as in f32; every term S * d_a * d_w is
+      // exact in f64)
+      v16i S[2][2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const v16i zero = {};
+          S[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], zero, 0, 0, 0);
+        }
+      double dw[2];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) dw[ni] = (double)sDw[buf][kb][wn * 64 + ni * 32 + lr];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        float da[16];
+        double da[16];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const float4 d4 = *reinterpret_cast<const float4*>(&sDa[buf][kb][wm * 64 + mi * 32 + 8 * g4 + 4 * lg]);
           da[4 * g4 + 0] = d4.x, da[4 * g4 + 1] = d4.y, da[4 * g4 + 2] = d4.z, da[4 * g4 + 3] = d4.w;
         }
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const v16i zero = {};
-          const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], zero, 0, 0, 0);
-          const float dw = sDw[buf][kb][wn * 64 + ni * 32 + lr];
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (double)S[j] * (double)(da[j] * dw);
-        }
+          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (double)S[mi][ni][j] * (da[j] * dw[ni]);
       }
     }
     if (st + 1 < nstage) {
