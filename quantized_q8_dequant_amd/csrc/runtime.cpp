@@ -83,13 +83,14 @@ struct Layer {
 };
 
 // Splits of the decode attention per (batch row, KV head): about 1024
-// workgroups per launch, at most 32 by that rule, and never fewer than the
+// workgroups per launch, at most 64 by that rule (each split also keeps at
+// least 64 rows, so short caches get fewer), and never fewer than the
 // longest cache needs (a split holds at most 4096 / group rows).
 int decode_splits_needed(int max_cap, int group) { return (max_cap + 4096 / group - 1) / (4096 / group); }
 int decode_nsplit_max(int nkv, int nrows, int needed) {
   const int units = nkv * nrows;
   int n = (1024 + units - 1) / units;
-  if (n > 32) n = 32;
+  if (n > 64) n = 64;
   if (n < needed) n = needed;
   return n;
 }
