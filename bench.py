@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
-PERSISTENT_SRC = os.path.join(ROOT, "quantized_q8_dequant_amd", "csrc", "k_decode_persistent.hip")
+# the one-launch decode kernel and the headers it includes
+PERSISTENT_SRC = [os.path.join(ROOT, "quantized_q8_dequant_amd", "csrc", f)
+                  for f in ("k_decode_persistent.hip", "kernels.h", "qdevice.h")]
 INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA
 KIND_NAMES = ["qkv_gemv", "attention", "o_proj_gemv", "gate_up_swiglu_gemv", "down_gemv", "lm_head_argmax_gemv"]
 
@@ -65,11 +67,15 @@ def decode_token_bytes(shape, ctx: int) -> float:
     return shape.num_layers * per_layer + kernel_bytes(shape, 5, ctx) + 4 * shape.vocab_size
 
 
-def source_sha(path: str) -> str:
+def source_sha(paths) -> str:
+    """SHA-256 over the concatenated bytes of `paths`, in order."""
     import hashlib
 
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str):
