@@ -35,6 +35,7 @@ constexpr int kTileRows = BF16 ? 64 : 32;
 constexpr int kMaxSplit = 64;    // bound of nsplit_max
 constexpr int kScoreSlots = 4096;  // f64 scores a workgroup keeps: G heads x (4096 / G) rows
 constexpr int kLdsRow = 4;       // padding of a staged row (keeps rows 16-byte aligned)
+constexpr int kCombineRegs = 80; // f64 partial values a thread of the combine holds in flight
 
 // One tile of K or V rows staged through registers: every thread issues all
 // of its 16-byte loads for a tile at once; two tiles are in flight ahead of
@@ -82,6 +83,24 @@ QDEV void tile_store(const TileRegs<HD, BF16>& t, float (*s_t)[HD + kLdsRow]) {
     } else {
       *reinterpret_cast<v4i*>(&s_t[r][d]) = t.x[i];
     }
+  }
+}
+
+// RMSNorm (weights wa, wb) then NeoX RoPE (cos c, sin s) of one head whose
+// rotation pairs (i, i + HD/2) sit in lanes i < HD/2 of the calling wave;
+// the results go to dst[i] and dst[i + HD/2].  Same arithmetic as the
+// LDS-staged form: f64 sum of squares, one f32 rounding per output.
+template <int HD>
+QDEV void norm_rope_pair(float xa, float xb, float wa, float wb, double c, double s, float eps, float* dst) {
+#pragma clang fp contract(off)
+  constexpr int H2 = HD / 2;
+  const int lane = threadIdx.x % kWave;
+  const double sq = lane < H2 ? (double)xa * (double)xa + (double)xb * (double)xb : 0.0;
+  const double r = rms_scale(wave_total_d(sq), HD, eps);
+  const double u = (double)rms_apply(xa, r, wa), v = (double)rms_apply(xb, r, wb);
+  if (lane < H2) {
+    dst[lane] = (float)(u * c - v * s);
+    dst[lane + H2] = (float)(u * s + v * c);
   }
 }
 
@@ -148,24 +167,42 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     const bool live = t0 < cache_end;
     tile_load<HD, BF16>(r, a.kv, isv ? vbase : kbase, live ? t0 : j0, live ? min(TJ, cache_end - t0) : 1);
   };
+  // Prologue operands in registers, loaded before the first tiles so that
+  // the prologue waits for them alone: wave w takes query heads w, w + 4, ...
+  // and lane i the rotation pair (i, i + HD/2) (lanes past HD/2 repeat pair
+  // 0 and write nothing); every wave also loads the new k and v of head g,
+  // which the last wave normalises, ropes and stages.
+  constexpr int H2 = HD / 2;
+  constexpr int QH = (G + kWaves - 1) / kWaves;  // query heads per wave
+  const int pi = lane < H2 ? lane : 0;
+  const double c_rot = cs[pi], s_rot = sn[pi];
+  const float qwa = a.q_norm[pi], qwb = a.q_norm[pi + H2];
+  const float kwa = a.k_norm[pi], kwb = a.k_norm[pi + H2];
+  float qa[QH], qb[QH];
+#pragma unroll
+  for (int k = 0; k < QH; ++k) {
+    const int h = min(wave + k * kWaves, G - 1);
+    qa[k] = qkv[(int64_t)(g * G + h) * HD + pi];
+    qb[k] = qkv[(int64_t)(g * G + h) * HD + pi + H2];
+  }
+  const float* knew = qkv + (int64_t)nh * HD + (int64_t)g * HD;
+  const float* vnew = qkv + (int64_t)(nh + nkv) * HD + (int64_t)g * HD;
+  const float ka = knew[pi], kb = knew[pi + H2], va = vnew[pi], vb = vnew[pi + H2];
+
   TileRegs<HD, BF16> tA, tB;
   if (nt > 0) {  // 2 * nt >= 2 elements
     stream_load(tA, 0);
     stream_load(tB, 1);
   }
 
-  // stage raw q (G heads), and the new k / v of head g
-  for (int e = tid; e < G * HD; e += kThreads) s_qf[e / HD][e % HD] = qkv[(int64_t)(g * G) * HD + e];
   const bool has_new = j0 < j1 && j1 == ctx;  // this split holds position p
-  if (has_new) {
-    for (int d = tid; d < HD; d += kThreads) {
-      s_knew[d] = qkv[(int64_t)nh * HD + (int64_t)g * HD + d];
-      s_vnew[d] = qkv[(int64_t)(nh + nkv) * HD + (int64_t)g * HD + d];
-    }
+#pragma unroll
+  for (int k = 0; k < QH; ++k)
+    if (wave + k * kWaves < G) norm_rope_pair<HD>(qa[k], qb[k], qwa, qwb, c_rot, s_rot, a.eps, s_qf[wave + k * kWaves]);
+  if (has_new && wave == kWaves - 1) {
+    norm_rope_pair<HD>(ka, kb, kwa, kwb, c_rot, s_rot, a.eps, s_knew);
+    if (lane < H2) s_vnew[lane] = va, s_vnew[lane + H2] = vb;
   }
-  __syncthreads();
-  for (int h = wave; h < G; h += kWaves) norm_rope_wave<HD>(s_qf[h], a.q_norm, a.eps, cs, sn);
-  if (has_new && wave == kWaves - 1) norm_rope_wave<HD>(s_knew, a.k_norm, a.eps, cs, sn);
   __syncthreads();
   if (has_new) {
     // append: the cache stores post-RoPE K and raw V (bf16 caches round here,
@@ -321,61 +358,98 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  // combine the nsplit partials of the G heads (f64), round once to f32;
-  // the loads of a batch are all issued before any is used
+  // combine the nsplit partials of the G heads (f64), rounded once to f32.
+  // Every O load of a batch and the (m, l) loads are issued before any is
+  // used (one memory round trip); wave w takes heads w, w + 4, ... and lane s
+  // split s for the max and the weighted sum of l (nsplit <= 64 = lanes).
+  // Thread map: E = G*HD output dims; with E >= 256 a thread owns dims
+  // tid + 256k, otherwise dim tid % E for the splits = tid / E (mod NQ).
   const double* pb = a.part + (((int64_t)row * nkv + g) * a.nsplit_max) * pstride;
+  constexpr int E = G * HD;
+  constexpr int NQ = E >= kThreads ? 1 : kThreads / E;   // split phases
+  constexpr int EPT = E >= kThreads ? E / kThreads : 1;  // dims per thread
+  constexpr int SB = kCombineRegs / EPT < kMaxSplit / NQ ? kCombineRegs / EPT : kMaxSplit / NQ;  // splits per thread per batch
+  const int cq = tid / (kThreads / NQ);
+  const int ce = tid % (kThreads / NQ);
   __shared__ double s_w[G][kMaxSplit];
-  __shared__ double s_ls[G][kMaxSplit];
-  __shared__ double s_M[G];
   __shared__ double s_L[G];
-  for (int e = tid; e < G * nsplit; e += kThreads) {
-    const int h = e / nsplit, sidx = e % nsplit;
-    s_w[h][sidx] = ld_coherent(pb + sidx * pstride + h * (HD + 2) + HD);
-    s_ls[h][sidx] = ld_coherent(pb + sidx * pstride + h * (HD + 2) + HD + 1);
+  __shared__ double s_red[NQ > 1 ? NQ : 1][NQ > 1 ? E : 1];
+  int64_t eoff[EPT];
+  int eh[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = ce + k * kThreads;
+    eh[k] = e / HD;
+    eoff[k] = (int64_t)eh[k] * (HD + 2) + e % HD;
   }
-  __syncthreads();
-  if (tid < G) {
-    const int h = tid;
-    double M = -INFINITY;
-    for (int sidx = 0; sidx < nsplit; ++sidx) M = fmax(M, s_w[h][sidx]);
-    s_M[h] = M;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * nsplit; e += kThreads) {
-    const int h = e / nsplit, sidx = e % nsplit;
-    s_w[h][sidx] = exp(s_w[h][sidx] - s_M[h]);
-  }
-  __syncthreads();
-  if (tid < G) {
-    const int h = tid;
-    double L = 0.0;
-    for (int sidx = 0; sidx < nsplit; ++sidx) L += s_w[h][sidx] * s_ls[h][sidx];
-    s_L[h] = L;
-  }
-  __syncthreads();
-  if (out_live) {
-    constexpr int BATCH = 16 / DPT;  // splits per batch: 16 loads in flight
-    double O[DPT];
+  double O[EPT];
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) O[i] = 0.0;
-    const double* ob = pb + o_h * (HD + 2) + o_d;
-    for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
-      double v[BATCH][DPT];
+  for (int k = 0; k < EPT; ++k) O[k] = 0.0;
+  // batches of B splits per thread; B is the smallest of SB/4, SB/2, SB that
+  // covers this thread's splits, so short caches issue few clamped repeats
+  auto batches = [&](auto bsz) {
+    constexpr int B = decltype(bsz)::value;
+    for (int s0 = 0; s0 < nsplit; s0 += NQ * B) {
+      double v[B][EPT];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u)
+      for (int j = 0; j < B; ++j) {
+        const int sidx = min(s0 + cq + NQ * j, nsplit - 1);
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) v[u][i] = (s0 + u < nsplit) ? ld_coherent(ob + (s0 + u) * pstride + i) : 0.0;
+        for (int k = 0; k < EPT; ++k) v[j][k] = ld_coherent(pb + sidx * pstride + eoff[k]);
+      }
+      if (s0 == 0) {
+        const int sl = min(lane, nsplit - 1);
+        double m[QH], l[QH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        if (s0 + u < nsplit) {
-          const double wgt = s_w[o_h][s0 + u];
-#pragma unroll
-          for (int i = 0; i < DPT; ++i) O[i] += wgt * v[u][i];
+        for (int k = 0; k < QH; ++k) {
+          const int h = min(wave + k * kWaves, G - 1);
+          m[k] = ld_coherent(pb + sl * pstride + h * (HD + 2) + HD);
+          l[k] = ld_coherent(pb + sl * pstride + h * (HD + 2) + HD + 1);
         }
-    }
 #pragma unroll
-    for (int i = 0; i < DPT; ++i)
-      a.out[(int64_t)row * a.out_stride + (int64_t)(g * G + o_h) * HD + o_d + i] = (float)(O[i] / s_L[o_h]);
+        for (int k = 0; k < QH; ++k) {
+          const int h = wave + k * kWaves;
+          const bool live = lane < nsplit;
+          const double M = wave_max_all_d(live ? m[k] : -INFINITY);
+          const double w = live ? exp(m[k] - M) : 0.0;
+          const double L = wave_total_d(w * l[k]);
+          if (h < G) {
+            s_w[h][lane] = w;
+            if (lane == 0) s_L[h] = L;
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int sidx = s0 + cq + NQ * j;
+        if (sidx < nsplit) {
+#pragma unroll
+          for (int k = 0; k < EPT; ++k) O[k] += s_w[eh[k]][sidx] * v[j][k];
+        }
+      }
+    }
+  };
+  const int per_thread = (nsplit + NQ - 1) / NQ;
+  if (per_thread <= SB / 4)
+    batches(std::integral_constant<int, SB / 4>{});
+  else if (per_thread <= SB / 2)
+    batches(std::integral_constant<int, SB / 2>{});
+  else
+    batches(std::integral_constant<int, SB>{});
+  if (NQ > 1) {
+    s_red[cq][ce] = O[0];
+    __syncthreads();
+    if (cq == 0) {
+      double t = s_red[0][ce];
+      for (int q = 1; q < NQ; ++q) t += s_red[q][ce];
+      O[0] = t;
+    }
+  }
+  if (cq == 0) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      a.out[(int64_t)row * a.out_stride + (int64_t)g * E + ce + k * kThreads] = (float)(O[k] / s_L[eh[k]]);
   }
 }
 
