@@ -75,14 +75,11 @@ QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
   return false;
 }
 
-// The same for three ranges at once (one round trip per poll round).
-template <int N1, int N2, int N3>
-QDEV bool poll3(const u64* s1, const u64* s2, const u64* s3, unsigned tag, float* d1, float* d2, float* d3,
-                unsigned* err) {
-  constexpr int N = N1 + N2 + N3;
+// The same for N words at arbitrary addresses src(i); the 32-bit payload of
+// word i goes to *dst(i) (one round trip per poll round).
+template <int N, typename Src, typename Dst>
+QDEV bool poll_words(Src src, Dst dst, unsigned tag, unsigned* err) {
   constexpr int PER = (N + NT - 1) / NT;
-  auto src = [&](int i) { return i < N1 ? s1 + i : i < N1 + N2 ? s2 + (i - N1) : s3 + (i - N1 - N2); };
-  auto dst = [&](int i) { return i < N1 ? d1 + i : i < N1 + N2 ? d2 + (i - N1) : d3 + (i - N1 - N2); };
   for (int spin = 0; spin < kSpin; ++spin) {
     u64 v[PER];
     bool ok = true;
@@ -96,7 +93,7 @@ QDEV bool poll3(const u64* s1, const u64* s2, const u64* s3, unsigned tag, float
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int i = threadIdx.x + j * NT;
-        if (i < N) *dst(i) = __uint_as_float((unsigned)v[j]);
+        if (i < N) *dst(i) = (unsigned)v[j];
       }
       __syncthreads();
       return true;
@@ -107,12 +104,39 @@ QDEV bool poll3(const u64* s1, const u64* s2, const u64* s3, unsigned tag, float
   return false;
 }
 
-// Quantise the K values in LDS (optionally RMSNorm'd with w) to Q8_0 codes
+// An f64 as two tagged words (low half, then high half).
+QDEV void put_tagged_d(u64* p, double v, unsigned tag) {
+  __hip_atomic_store(p, ((u64)tag << 32) | (u64)(unsigned)__double2loint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, ((u64)tag << 32) | (u64)(unsigned)__double2hiint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A norm weight vector of K floats held in registers, one float4 per thread
+// per pass of the 256 threads (loaded before a wait, used after it).
+template <int K>
+struct NormW {
+  static constexpr int KI = (K + NT * 4 - 1) / (NT * 4);
+  float4 w[KI];
+  QDEV void load(const float* __restrict__ p) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int c = i * NT * 4 + threadIdx.x * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < K) {
+        const v4i t = ld_global<v4i>(as_global(p) + c);
+        v = make_float4(__int_as_float(t.x), __int_as_float(t.y), __int_as_float(t.z), __int_as_float(t.w));
+      }
+      w[i] = v;
+    }
+  }
+};
+
+// Quantise the K values in LDS (optionally RMSNorm'd with the weights nw) to Q8_0 codes
 // and f16-valued scales in LDS; the same arithmetic and summation order as
 // the decode GEMV's prologue.
 template <int K, bool NORM>
-QDEV void quantize_lds(const float* s_x, const float* __restrict__ w, float eps, int8_t* s_qa, float* s_da,
-                       double* s_red) {
+QDEV void quantize_lds(const float* s_x, const NormW<K>* nw, float eps, int8_t* s_qa, float* s_da, double* s_red) {
   double r = 1.0;
   if (NORM) {
     double ss = 0.0;
@@ -123,6 +147,7 @@ QDEV void quantize_lds(const float* s_x, const float* __restrict__ w, float eps,
     ss = block_sum_d<NT>(ss, s_red);
     r = rms_scale(ss, K, eps);
   }
+#pragma unroll
   for (int base = 0; base < K; base += NT * 4) {
     const int c = base + threadIdx.x * 4;
     const bool live = c < K;
@@ -131,7 +156,7 @@ QDEV void quantize_lds(const float* s_x, const float* __restrict__ w, float eps,
       const float4 t = *reinterpret_cast<const float4*>(s_x + c);
       v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
       if (NORM) {
-        const float4 w4 = *reinterpret_cast<const float4*>(w + c);
+        const float4 w4 = nw->w[base / (NT * 4)];
         v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
         v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
       }
@@ -169,13 +194,13 @@ struct Slice {
     for (int ps = 0; ps < PASSES; ++ps) {
       const int lr = ps * RPP + threadIdx.x / LPR;
       const int64_t r = row(lr < R ? lr : 0);
-      const int8_t* wr = qs + r * (int64_t)K;
-      const uint16_t* sr = sc + r * (int64_t)NB;
+      const QGLOBAL int8_t* wr = as_global(qs) + r * (int64_t)K;
+      const QGLOBAL uint16_t* sr = as_global(sc) + r * (int64_t)NB;
 #pragma unroll
       for (int j = 0; j < BPL; ++j) {
         const int b = li + j * LPR;
-        w0[ps][j] = *reinterpret_cast<const v4i*>(wr + b * 32);
-        w1[ps][j] = *reinterpret_cast<const v4i*>(wr + b * 32 + 16);
+        w0[ps][j] = ld_global<v4i>(wr + b * 32);
+        w1[ps][j] = ld_global<v4i>(wr + b * 32 + 16);
         ws[ps][j] = sr[b];
       }
     }
@@ -259,8 +284,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   constexpr int NWG = kPersistWorkgroups;
   constexpr int RA = NQKV / NWG;  // QKV rows per workgroup
   constexpr int RC = H / NWG;     // hidden rows per workgroup (o_proj, down, embedding)
-  constexpr int UD = F / NWG;     // FFN units per workgroup
-  static_assert(RA * NWG == NQKV && RC * NWG == H && UD * NWG == F, "shape does not split over the grid");
+  constexpr int NUB = F / 32;     // FFN blocks: workgroup u < NUB owns FFN outputs 32u .. 32u+31
+  static_assert(RA * NWG == NQKV && RC * NWG == H && NUB * 32 == F && NUB <= NWG,
+                "shape does not split over the grid");
   static_assert(NKV * S <= NWG, "attention units exceed the grid");
   constexpr int XMAX = (H > QW ? (H > F ? H : F) : (QW > F ? QW : F));
   // attention maps (as the decode attention kernel)
@@ -279,16 +305,23 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   __shared__ double s_red[kWavesP];
   __shared__ float s_xkeep[RC];   // this workgroup's rows of x entering o_proj
   __shared__ float s_xckeep[RC];  // ... and entering the down projection
-  __shared__ float s_gu[2 * UD];
+  __shared__ float s_gu[64];
   __shared__ float s_qf[G][HD];
   __shared__ float s_knew[HD];
   __shared__ float s_vnew[HD];
   __shared__ __align__(16) float s_t[TJ][HD + 4];
   __shared__ double s_s[G][MAXR];
-  __shared__ double s_m[G], s_l[G], s_M[G], s_L[G];
-  __shared__ double s_w[G][S], s_ls[G][S];
+  __shared__ double s_m[G], s_l[G];
+  // the combine: this workgroup's CPW outputs of its KV head's G * HD, from
+  // every split's (m, l) of that query head and its slice of o (WPS words of
+  // 32-bit halves per split)
+  constexpr int CPW = G * HD / S;
+  constexpr int WPS = 4 + 2 * CPW;
+  static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave, "combine map");
+  __shared__ unsigned s_pw[S * WPS];
+  __shared__ double s_cw[S];
+  __shared__ double s_cL;
   __shared__ ArgBest s_best[kWavesP];
-  __shared__ int s_last;
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int seq = a.seq;
@@ -343,20 +376,38 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     {
       Slice<H, RA> w;
       w.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
+      NormW<H> nw;
+      nw.load(P.attn_norm);
       if (!poll_vec<H>(a.xa, T, s_x, a.err)) goto fail;
-      quantize_lds<H, true>(s_x, P.attn_norm, eps, s_qa, s_da, s_red);
+      quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
       w.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
     }
 
     // ---- B: attention of KV head ag over rows [j0, j1) -------------------------
     if (attn_unit) {
-      const double* cs = a.rope_cos + (int64_t)p * (HD / 2);
-      const double* sn = a.rope_sin + (int64_t)p * (HD / 2);
-      if (!poll3<G * HD, HD, HD>(a.qkv + ag * G * HD, a.qkv + QW + ag * HD, a.qkv + QW + KVW + ag * HD, T,
-                                 &s_qf[0][0], s_knew, s_vnew, a.err))
-        goto fail;
-      for (int h = wave; h < G; h += kWavesP) norm_rope_wave<HD>(s_qf[h], P.q_norm, eps, cs, sn);
-      if (has_new && wave == kWavesP - 1) norm_rope_wave<HD>(s_knew, P.k_norm, eps, cs, sn);
+      // this lane's rotation pair and norm weights, loaded before the wait
+      // (waves < G rotate the query heads, the last wave the new key)
+      static_assert(G < kWavesP, "one wave per query head and one for the key");
+      constexpr int H2 = HD / 2;
+      const int rl = lane < H2 ? lane : 0;
+      const double rcos = as_global(a.rope_cos)[(int64_t)p * H2 + rl];
+      const double rsin = as_global(a.rope_sin)[(int64_t)p * H2 + rl];
+      const QGLOBAL float* nwp = as_global(wave < G ? P.q_norm : P.k_norm);
+      const float nwlo = nwp[rl], nwhi = nwp[rl + H2];
+      {
+        unsigned* qf = reinterpret_cast<unsigned*>(&s_qf[0][0]);
+        unsigned* kn = reinterpret_cast<unsigned*>(s_knew);
+        unsigned* vn = reinterpret_cast<unsigned*>(s_vnew);
+        auto src = [&](int i) {
+          return i < G * HD ? a.qkv + ag * G * HD + i
+                            : i < G * HD + HD ? a.qkv + QW + ag * HD + (i - G * HD)
+                                              : a.qkv + QW + KVW + ag * HD + (i - G * HD - HD);
+        };
+        auto dst = [&](int i) { return i < G * HD ? qf + i : i < G * HD + HD ? kn + (i - G * HD) : vn + (i - G * HD - HD); };
+        if (!poll_words<G * HD + 2 * HD>(src, dst, T, a.err)) goto fail;
+      }
+      if (wave < G) norm_rope_wave_reg<HD>(s_qf[wave], nwlo, nwhi, rcos, rsin, eps);
+      if (has_new && wave == kWavesP - 1) norm_rope_wave_reg<HD>(s_knew, nwlo, nwhi, rcos, rsin, eps);
       __syncthreads();
       if (has_new) {
         for (int d = tid; d < HD; d += NT) {
@@ -452,72 +503,50 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         process(tB, i + 1, false);
       }
       __syncthreads();
-      // partial (o, m, l) of this split, then the last arrival combines
-      const int64_t pstride = (int64_t)G * (HD + 2);
-      double* part = a.part + ((int64_t)ag * S + asplit) * pstride;
+      // partial (o, m, l) of this split as tagged words: no drain and no
+      // counter, the words are their own flags
+      constexpr int PWORDS = (HD + 2) * 2;  // words per (split, query head)
+      u64* part = a.part + ((int64_t)ag * S + asplit) * G * PWORDS;
       if (out_live) {
 #pragma unroll
-        for (int i2 = 0; i2 < DPT; ++i2) st_coherent(part + o_h * (HD + 2) + o_d + i2, o[i2]);
+        for (int i2 = 0; i2 < DPT; ++i2) put_tagged_d(part + o_h * PWORDS + 2 * (o_d + i2), o[i2], T);
       }
       if (tid < G) {
-        st_coherent(part + tid * (HD + 2) + HD, s_m[tid]);
-        st_coherent(part + tid * (HD + 2) + HD + 1, s_l[tid]);
+        put_tagged_d(part + tid * PWORDS + 2 * HD, s_m[tid], T);
+        put_tagged_d(part + tid * PWORDS + 2 * (HD + 1), s_l[tid], T);
       }
-      wait_memory();
-      __syncthreads();
-      if (tid == 0) {
-        unsigned* cnt = a.attn_cnt + (int64_t)l * NKV + ag;
-        const unsigned prev = arrive(cnt);
-        s_last = prev == (unsigned)(S - 1);
-        if (s_last) st_coherent(cnt, 0u);
+      // ---- the combine of CPW outputs (query head ch, dims cd0 ..) over the
+      // S splits: O = sum_s w_s o_s / sum_s w_s l_s, w_s = exp(m_s - max m),
+      // each sum taken in split order
+      const int ch = (asplit * CPW) / HD, cd0 = (asplit * CPW) % HD;
+      const u64* pb = a.part + (int64_t)ag * S * G * PWORDS + ch * PWORDS;
+      {
+        auto src = [&](int i) {
+          const int sp = i / WPS, k = i % WPS;
+          return pb + (int64_t)sp * G * PWORDS + (k < 4 ? 2 * HD + k : 2 * cd0 + (k - 4));
+        };
+        auto dst = [&](int i) { return s_pw + i; };
+        if (!poll_words<S * WPS>(src, dst, T, a.err)) goto fail;
+      }
+      auto pw_d = [&](int sp, int k) {  // the f64 at words k, k + 1 of split sp
+        return __hiloint2double((int)s_pw[sp * WPS + k + 1], (int)s_pw[sp * WPS + k]);
+      };
+      if (wave == 0) {
+        const bool live = lane < S;
+        const double ms = live ? pw_d(lane, 0) : -INFINITY;
+        const double M = wave_max_all_d(ms);
+        const double wgt = (live && ms != -INFINITY) ? exp(ms - M) : 0.0;
+        if (live) s_cw[lane] = wgt;
+        const double L = wave_total_d(live ? wgt * pw_d(lane, 2) : 0.0);
+        if (lane == 0) s_cL = L;
       }
       __syncthreads();
-      if (s_last) {
-        // every load of the combine is issued in one round: the O partials of
-        // this thread's outputs together with the (m, l) pairs
-        const double* pb = a.part + (int64_t)ag * S * pstride;
-        const double* ob = pb + o_h * (HD + 2) + o_d;
-        double v[S][DPT];
-#pragma unroll
-        for (int si = 0; si < S; ++si)
-#pragma unroll
-          for (int i2 = 0; i2 < DPT; ++i2) v[si][i2] = out_live ? ld_coherent(ob + si * pstride + i2) : 0.0;
-        for (int e = tid; e < G * S; e += NT) {
-          const int h = e / S, si = e % S;
-          s_w[h][si] = ld_coherent(pb + si * pstride + h * (HD + 2) + HD);
-          s_ls[h][si] = ld_coherent(pb + si * pstride + h * (HD + 2) + HD + 1);
-        }
-        __syncthreads();
-        if (tid < G) {
-          double M = -INFINITY;
-          for (int si = 0; si < S; ++si) M = fmax(M, s_w[tid][si]);
-          s_M[tid] = M;
-        }
-        __syncthreads();
-        for (int e = tid; e < G * S; e += NT) {
-          const int h = e / S, si = e % S;
-          const double ms = s_w[h][si];
-          s_w[h][si] = (ms == -INFINITY) ? 0.0 : exp(ms - s_M[h]);
-        }
-        __syncthreads();
-        if (tid < G) {
-          double L = 0.0;
-          for (int si = 0; si < S; ++si) L += s_w[tid][si] * s_ls[tid][si];
-          s_L[tid] = L;
-        }
-        __syncthreads();
-        if (out_live) {
-          double O[DPT];
-#pragma unroll
-          for (int i2 = 0; i2 < DPT; ++i2) O[i2] = 0.0;
-#pragma unroll
-          for (int si = 0; si < S; ++si)
-#pragma unroll
-            for (int i2 = 0; i2 < DPT; ++i2) O[i2] += s_w[o_h][si] * v[si][i2];
-#pragma unroll
-          for (int i2 = 0; i2 < DPT; ++i2)
-            put_tagged(a.att + (ag * G + o_h) * HD + o_d + i2, (float)(O[i2] / s_L[o_h]), T);
-        }
+      {  // thread (k, sp) takes split sp's term of output k; a group sum over the splits
+        static_assert(CPW * S <= NT, "combine threads");
+        const int sp = tid % S, k = tid / S;
+        double v = k < CPW ? s_cw[sp] * pw_d(sp, 4 + 2 * k) : 0.0;
+        v = group_sum_d<S>(v);
+        if (k < CPW && sp == S - 1) put_tagged(a.att + (ag * G + ch) * HD + cd0 + k, (float)(v / s_cL), T);
       }
     }
 
@@ -526,7 +555,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       Slice<QW, RC> w;
       w.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
       if (!poll_vec<QW>(a.att, T, s_x, a.err)) goto fail;
-      quantize_lds<QW, false>(s_x, nullptr, eps, s_qa, s_da, s_red);
+      quantize_lds<QW, false>(s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red);
       w.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xkeep[lr] + (float)acc;
         put_tagged(a.xc + b * RC + lr, xn, T);
@@ -534,26 +563,42 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       });
     }
 
-    // ---- D: gate/up + SwiGLU (rows of units u: gate (u/32)*64 + u%32, up +32) ----
-    {
-      Slice<H, 2 * UD> w;
-      w.load(P.gu_qs, P.gu_sc, [&](int lr) {
-        const int u = b * UD + (lr % UD);
-        return (u / 32) * 64 + (u % 32) + (lr < UD ? 0 : 32);
-      });
+    // ---- D: gate/up + SwiGLU + the Q8_0 quantisation of h.  Workgroup u < F/32
+    // owns FFN block u: gate rows 64u .. 64u+31 and up rows 64u+32 .. 64u+63 of
+    // the interleaved matrix.  h leaves already quantised (the down
+    // projection's prologue arithmetic): 8 words of four codes, then one word
+    // with the f16-valued block scale.
+    if (b < NUB) {
+      Slice<H, 64> w;
+      w.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
+      NormW<H> nw;
+      nw.load(P.ffn_norm);
       if (!poll_vec<H>(a.xc, T, s_x, a.err)) goto fail;
-      quantize_lds<H, true>(s_x, P.ffn_norm, eps, s_qa, s_da, s_red);
+      quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
       w.compute(s_qa, s_da, [&](int lr, double acc) { s_gu[lr] = (float)acc; });
       __syncthreads();
-      if (tid < UD) put_tagged(a.h + b * UD + tid, swiglu_f64(s_gu[tid], s_gu[UD + tid]), T);
+      if (tid < 8) {  // one 8-lane group: lane t quantises h[4t .. 4t+3]
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = swiglu_f64(s_gu[4 * tid + i], s_gu[32 + 4 * tid + i]);
+        float d;
+        const int packed = quant4_group8(v, &d);
+        put_tagged(a.h + b * 9 + tid, __int_as_float(packed), T);
+        if (tid == 0) put_tagged(a.h + b * 9 + 8, f16_round(d), T);
+      }
     }
 
     // ---- E: down + residual (x of the next layer) ----------------------------------
     {
       Slice<F, RC> w;
       w.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
-      if (!poll_vec<F>(a.h, T, s_x, a.err)) goto fail;
-      quantize_lds<F, false>(s_x, nullptr, eps, s_qa, s_da, s_red);
+      {
+        unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
+        unsigned* da = reinterpret_cast<unsigned*>(s_da);
+        auto src = [&](int i) { return a.h + i; };
+        auto dst = [&](int i) { return (i % 9) < 8 ? qa + (i / 9) * 8 + (i % 9) : da + i / 9; };
+        if (!poll_words<9 * NUB>(src, dst, T, a.err)) goto fail;
+      }
       w.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xckeep[lr] + (float)acc;
         put_tagged(a.xa + b * RC + lr, xn, T + 1u);
@@ -577,8 +622,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
     if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
     if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
+    NormW<H> nw;
+    nw.load(a.out_norm);
     if (!poll_vec<H>(a.xa, T0 + (unsigned)a.L, s_x, a.err)) goto fail;
-    quantize_lds<H, true>(s_x, a.out_norm, eps, s_qa, s_da, s_red);
+    quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
     ArgBest best{-INFINITY, 0x7FFFFFFF};
     auto run = [&](const LS& w, int ps) {
       w.compute(s_qa, s_da, [&](int lr, double acc) {

@@ -177,8 +177,9 @@ struct PersistArgs {
   float* logits;         // [V] or null
   int32_t* argmax;       // [1]
   unsigned long long *xa, *xc, *qkv, *att, *h;  // (value, epoch) words
-  double* part;          // [nkv][splits per KV head][G][hd + 2]
-  unsigned* attn_cnt;    // [L][nkv], zero between steps
+  // attention partials of every split as (32-bit half, epoch) words:
+  // [nkv][splits per KV head][G][hd + 2 (o..., m, l)][2 (low, high half)]
+  unsigned long long* part;
   unsigned long long* best_key;
   unsigned* am_cnt;
   unsigned* err;         // set on a timed-out wait

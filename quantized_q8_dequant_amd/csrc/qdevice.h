@@ -40,6 +40,21 @@ QDEV uint16_t f32_to_bf16_bits(float x) {  // round half to even on the dropped 
 QDEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 QDEV float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
 
+// ---- global address space ----------------------------------------------------------
+// A pointer read from a table in memory is generic to the compiler, which then
+// emits flat loads.  Flat loads count against the LDS wait counter as well, so
+// every later LDS wait would also drain the (slow) weight loads in flight.
+// as_global() states that the pointer addresses global memory.
+#define QGLOBAL __attribute__((address_space(1)))
+template <typename T>
+QDEV const QGLOBAL T* as_global(const T* p) {
+  return (const QGLOBAL T*)(__UINTPTR_TYPE__)p;
+}
+template <typename T, typename U>
+QDEV T ld_global(const QGLOBAL U* p) {  // a T-typed load at p
+  return *reinterpret_cast<const QGLOBAL T*>(p);
+}
+
 // ---- cross-workgroup hand-off without cache-wide fences ---------------------------
 // A device-wide fence writes back and invalidates the whole L2 of the XCD;
 // thousands of workgroups doing that stall each other.  Data handed to
@@ -238,6 +253,28 @@ QDEV void norm_rope_wave(float* x, const float* __restrict__ w, float eps, const
     const double c = cs[i], s = sn[i];
     x[i] = (float)(a * c - b * s);
     x[i + H2] = (float)(a * s + b * c);
+  }
+}
+
+// The same with this lane's operands already in registers, so they can be
+// loaded before the values arrive: weights w[lane] and w[lane + HD/2], and the
+// cos/sin of pair `lane` (lanes >= HD/2 carry no pair).  Same arithmetic and
+// summation order as norm_rope_wave.
+template <int HD>
+QDEV void norm_rope_wave_reg(float* x, float wlo, float whi, double c, double s, float eps) {
+#pragma clang fp contract(off)
+  static_assert(HD / 2 <= kWave, "one rotation pair per lane");
+  const int lane = threadIdx.x % kWave;
+  double ss = 0.0;
+  for (int d = lane; d < HD; d += kWave) ss += (double)x[d] * (double)x[d];
+  ss = wave_total_d(ss);
+  const double r = rms_scale(ss, HD, eps);
+  constexpr int H2 = HD / 2;
+  if (lane < H2) {
+    const double a = (double)rms_apply(x[lane], r, wlo);
+    const double b = (double)rms_apply(x[lane + H2], r, whi);
+    x[lane] = (float)(a * c - b * s);
+    x[lane + H2] = (float)(a * s + b * c);
   }
 }
 

@@ -130,7 +130,7 @@ struct qwen3_model {
   bool persist_capable = false, persist = false;
   PLayer* d_players = nullptr;
   unsigned long long *p_xa = nullptr, *p_xc = nullptr, *p_qkv = nullptr, *p_att = nullptr, *p_h = nullptr;
-  unsigned* p_cnt = nullptr;
+  unsigned long long* p_part = nullptr;
   unsigned* p_err = nullptr;
   unsigned pstep = 0;
   size_t bytes = 0;
@@ -143,6 +143,11 @@ struct qwen3_model {
 };
 
 namespace {
+
+// Tagged attention-partial words of the one-launch step: every workgroup of
+// its grid is at most one split, each split holds G heads of (o[hd], m, l) as
+// two words per f64.
+size_t persist_part_words(int64_t G, int64_t hd) { return (size_t)kPersistWorkgroups * G * (hd + 2) * 2; }
 
 int validate(const qwen3_config* c) {
   if (!c) return fail(QWEN3_E_INVALID_ARGUMENT, "config is null");
@@ -265,7 +270,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     m->p_qkv = cv.arr<unsigned long long>(nqkv);
     m->p_att = cv.arr<unsigned long long>(qw);
     m->p_h = cv.arr<unsigned long long>(F);
-    m->p_cnt = cv.arr<unsigned>((size_t)c.num_layers * nkv);
+    m->p_part = cv.arr<unsigned long long>(persist_part_words(G, hd));
     m->p_err = cv.arr<unsigned>(1);
   }
   if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
@@ -673,7 +678,7 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
       HIP_TRY(hipMemsetAsync(m->p_qkv, 0, (size_t)m->nqkv * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_att, 0, (size_t)m->qw * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F * 8, s));
-      HIP_TRY(hipMemsetAsync(m->p_cnt, 0, (size_t)m->L * m->nkv * 4, s));
+      HIP_TRY(hipMemsetAsync(m->p_part, 0, persist_part_words(m->G, m->hd) * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
       HIP_TRY(hipStreamSynchronize(s));  // tab is a host temporary
     }
@@ -783,8 +788,7 @@ int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_
     a.logits = d_logits;
     a.argmax = d_argmax;
     a.xa = m->p_xa, a.xc = m->p_xc, a.qkv = m->p_qkv, a.att = m->p_att, a.h = m->p_h;
-    a.part = m->attn_part;
-    a.attn_cnt = m->p_cnt;
+    a.part = m->p_part;
     a.best_key = m->am_key;
     a.am_cnt = m->am_cnt;
     a.err = m->p_err;
