@@ -45,26 +45,42 @@ QDEV void put_tagged(u64* p, float v, unsigned tag) {
 }
 QDEV unsigned ld_err(const unsigned* err) { return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-// Wait until the N words at src all carry `tag`, then copy their values to
-// dst (LDS).  False when the spin limit is reached or another workgroup has
-// reported an error.
-template <int N>
-QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
-  constexpr int PER = (N + NT - 1) / NT;
+// Polling.  A poll round re-reads every word it waits for with
+// device-coherent loads, and on this chip the cost of such a round grows with
+// the number of load instructions, not with bytes: each load here takes two
+// adjacent tagged words (16 bytes) through a buffer resource whose bounds
+// are the polled vector's.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;  // cache policy of the loads: device scope (sc1)
+
+// Wait until the 2 * NPAIR words of the pairs at word offsets off(j) (even)
+// of base[0, nwords) all carry `tag`; then the 32-bit payload of word
+// 2j + h goes to *dst(2j + h).  False when the spin limit is reached or
+// another workgroup has reported an error.
+template <int NPAIR, typename Off, typename Dst>
+QDEV bool poll_pairs(const u64* base, int nwords, Off off, Dst dst, unsigned tag, unsigned* err) {
+  constexpr int PER = (NPAIR + NT - 1) / NT;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(base), 0, nwords * 8, 0x00020000);
   for (int spin = 0; spin < kSpin; ++spin) {
-    u64 v[PER];
+    v4u v[PER];
     bool ok = true;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = threadIdx.x + j * NT;
-      v[j] = (i < N) ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_word(0.f, tag);
-      ok = ok && (unsigned)(v[j] >> 32) == tag;
+      if (i < NPAIR) {
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(i) * 8, 0, kCoherent);
+        ok = ok && v[j].y == tag && v[j].w == tag;
+      }
     }
     if (__syncthreads_and(ok)) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int i = threadIdx.x + j * NT;
-        if (i < N) dst[i] = __uint_as_float((unsigned)v[j]);
+        if (i < NPAIR) {
+          *dst(2 * i) = v[j].x;
+          *dst(2 * i + 1) = v[j].z;
+        }
       }
       __syncthreads();
       return true;
@@ -75,33 +91,12 @@ QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
   return false;
 }
 
-// The same for N words at arbitrary addresses src(i); the 32-bit payload of
-// word i goes to *dst(i) (one round trip per poll round).
-template <int N, typename Src, typename Dst>
-QDEV bool poll_words(Src src, Dst dst, unsigned tag, unsigned* err) {
-  constexpr int PER = (N + NT - 1) / NT;
-  for (int spin = 0; spin < kSpin; ++spin) {
-    u64 v[PER];
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = threadIdx.x + j * NT;
-      v[j] = (i < N) ? __hip_atomic_load(src(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_word(0.f, tag);
-      ok = ok && (unsigned)(v[j] >> 32) == tag;
-    }
-    if (__syncthreads_and(ok)) {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int i = threadIdx.x + j * NT;
-        if (i < N) *dst(i) = (unsigned)v[j];
-      }
-      __syncthreads();
-      return true;
-    }
-    if ((spin & 63) == 63 && __syncthreads_or(threadIdx.x == 0 && ld_err(err) != 0)) return false;
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return false;
+// The N (even) contiguous words at src into dst (LDS) as floats.
+template <int N>
+QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
+  static_assert(N % 2 == 0, "pairs");
+  unsigned* d = reinterpret_cast<unsigned*>(dst);
+  return poll_pairs<N / 2>(src, N, [](int j) { return 2 * j; }, [&](int i) { return d + i; }, tag, err);
 }
 
 // An f64 as two tagged words (low half, then high half).
@@ -310,6 +305,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   __shared__ float s_knew[HD];
   __shared__ float s_vnew[HD];
   __shared__ __align__(16) float s_t[TJ][HD + 4];
+  __shared__ __align__(16) float s_tv[TJ][HD + 4];  // V tile of a one-tile split
   __shared__ double s_s[G][MAXR];
   __shared__ double s_m[G], s_l[G];
   // the combine: this workgroup's CPW outputs of its KV head's G * HD, from
@@ -317,7 +313,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   // 32-bit halves per split)
   constexpr int CPW = G * HD / S;
   constexpr int WPS = 4 + 2 * CPW;
-  static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave, "combine map");
+  static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave && WPS % 2 == 0, "combine map");
   __shared__ unsigned s_pw[S * WPS];
   __shared__ double s_cw[S];
   __shared__ double s_cL;
@@ -394,36 +390,49 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       const double rsin = as_global(a.rope_sin)[(int64_t)p * H2 + rl];
       const QGLOBAL float* nwp = as_global(wave < G ? P.q_norm : P.k_norm);
       const float nwlo = nwp[rl], nwhi = nwp[rl + H2];
+      // a split of at most one tile keeps its K and V tiles in LDS, stored
+      // while the query is awaited
+      const bool one_tile = nt <= 1;
+      if (nt == 1 && j0 < cache_end) {
+        tA.store(s_t);
+        tB.store(s_tv);
+      }
       {
         unsigned* qf = reinterpret_cast<unsigned*>(&s_qf[0][0]);
         unsigned* kn = reinterpret_cast<unsigned*>(s_knew);
         unsigned* vn = reinterpret_cast<unsigned*>(s_vnew);
-        auto src = [&](int i) {
-          return i < G * HD ? a.qkv + ag * G * HD + i
-                            : i < G * HD + HD ? a.qkv + QW + ag * HD + (i - G * HD)
-                                              : a.qkv + QW + KVW + ag * HD + (i - G * HD - HD);
+        auto off = [&](int j) {  // word offset in qkv of pair j (q, then k, then v of head group ag)
+          const int i = 2 * j;
+          return i < G * HD ? ag * G * HD + i
+                            : i < G * HD + HD ? QW + ag * HD + (i - G * HD) : QW + KVW + ag * HD + (i - G * HD - HD);
         };
         auto dst = [&](int i) { return i < G * HD ? qf + i : i < G * HD + HD ? kn + (i - G * HD) : vn + (i - G * HD - HD); };
-        if (!poll_words<G * HD + 2 * HD>(src, dst, T, a.err)) goto fail;
+        if (!poll_pairs<(G * HD + 2 * HD) / 2>(a.qkv, NQKV, off, dst, T, a.err)) goto fail;
       }
       if (wave < G) norm_rope_wave_reg<HD>(s_qf[wave], nwlo, nwhi, rcos, rsin, eps);
       if (has_new && wave == kWavesP - 1) norm_rope_wave_reg<HD>(s_knew, nwlo, nwhi, rcos, rsin, eps);
-      __syncthreads();
-      if (has_new) {
-        for (int d = tid; d < HD; d += NT) {
-          const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
-          if (KVBF16) {
-            const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
-            reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
-            reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
-            s_knew[d] = bf16_bits_to_f32(kb);
-            s_vnew[d] = bf16_bits_to_f32(vb);
-          } else {
-            reinterpret_cast<float*>(a.kv)[ki] = s_knew[d];
-            reinterpret_cast<float*>(a.kv)[vi] = s_vnew[d];
+      if (one_tile) {
+        // the new row: the key wave appends k/v to the cache and to the tiles
+        if (has_new && wave == kWavesP - 1) {
+          for (int d = lane; d < HD; d += kWave) {
+            const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
+            float kf = s_knew[d], vf = s_vnew[d];
+            if (KVBF16) {
+              const uint16_t kb = f32_to_bf16_bits(kf), vb = f32_to_bf16_bits(vf);
+              reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
+              reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
+              kf = bf16_bits_to_f32(kb), vf = bf16_bits_to_f32(vb);
+            } else {
+              reinterpret_cast<float*>(a.kv)[ki] = kf;
+              reinterpret_cast<float*>(a.kv)[vi] = vf;
+            }
+            s_t[p - j0][d] = kf;
+            s_tv[p - j0][d] = vf;
           }
         }
       }
+      if (tid < G) s_m[tid] = -INFINITY, s_l[tid] = 0.0;
+      __syncthreads();  // the rotated query (and the one-tile rows) in LDS
       const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_h = tid / (NP * RG);
       double qreg[DPP];
 #pragma unroll
@@ -433,72 +442,116 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       double o[DPT];
 #pragma unroll
       for (int i = 0; i < DPT; ++i) o[i] = 0.0;
-      if (tid < G) s_m[tid] = -INFINITY, s_l[tid] = 0.0;
       const double scale = a.scale;
-
-      auto process = [&](KvTile<HD, KVBF16>& tr, int i, bool prefetch) {
-        const bool isv = i >= nt;
-        const int t0 = j0 + (isv ? i - nt : i) * TJ;
-        const int nrow = min(TJ, j1 - t0);
-        __syncthreads();
-        if (i == nt) {  // all scores written: softmax over the split, once
-          const int n = j1 - j0;
-          for (int h = wave; h < G; h += kWavesP) {
-            double m = -INFINITY;
-            for (int r = lane; r < n; r += kWave) m = fmax(m, s_s[h][r]);
-            m = wave_max_all_d(m);
-            double lsum = 0.0;
-            for (int r = lane; r < n; r += kWave) {
-              const double e = exp(s_s[h][r] - m);
-              s_s[h][r] = e;
-              lsum += e;
-            }
-            lsum = wave_total_d(lsum);
-            if (lane == 0) s_m[h] = m, s_l[h] = lsum;
-          }
-          __syncthreads();
-        }
-        if (t0 < cache_end) tr.store(s_t);
-        if (prefetch) stream_load(tr, i + 2);
-        if (t0 + nrow > p) {  // row p from this step's values (after the tile store)
-          __syncthreads();
-          const float* src = isv ? s_vnew : s_knew;
-          for (int d = tid; d < HD; d += NT) s_t[p - t0][d] = src[d];
-        }
-        __syncthreads();
-        if (!isv) {
+      // scores of tile rows [0, nrow) starting at split row t0 - j0
+      auto scores = [&](int t0, int nrow) {
 #pragma unroll
-          for (int j = 0; j < RPT; ++j) {
-            const int r = sc_rg * RPT + j;
-            const float* kr = &s_t[r][4 * sc_pt];
-            double acc = 0.0;
+        for (int j = 0; j < RPT; ++j) {
+          const int r = sc_rg * RPT + j;
+          const float* kr = &s_t[r][4 * sc_pt];
+          double ax = 0.0, ay = 0.0, az = 0.0, aw = 0.0;  // four independent FMA chains
 #pragma unroll
-            for (int d = 0; d < DPP; d += 4) {
-              const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
-              acc += qreg[d] * (double)k4.x;
-              acc += qreg[d + 1] * (double)k4.y;
-              acc += qreg[d + 2] * (double)k4.z;
-              acc += qreg[d + 3] * (double)k4.w;
-            }
-            acc = group_sum_d<NP>(acc);
-            if (sc_pt == NP - 1 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
+          for (int d = 0; d < DPP; d += 4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
+            ax += qreg[d] * (double)k4.x;
+            ay += qreg[d + 1] * (double)k4.y;
+            az += qreg[d + 2] * (double)k4.z;
+            aw += qreg[d + 3] * (double)k4.w;
           }
-        } else if (out_live) {
-          const double* pr = &s_s[o_h][t0 - j0];
-#pragma unroll 8
-          for (int r = 0; r < nrow; ++r) {
-            const double wgt = pr[r];
-#pragma unroll
-            for (int i2 = 0; i2 < DPT; ++i2) o[i2] += wgt * (double)s_t[r][o_d + i2];
-          }
+          double acc = (ax + ay) + (az + aw);
+          acc = group_sum_d<NP>(acc);
+          if (sc_pt == NP - 1 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
         }
       };
-      int i = 0;
-      for (; i + 2 < 2 * nt; i += 2) {
-        process(tA, i, true);
-        process(tB, i + 1, true);
-      }
-      if (nt > 0) {
+      // one f64 softmax over the split's n scores of each query head
+      auto softmax = [&]() {
+        const int n = j1 - j0;
+        for (int h = wave; h < G; h += kWavesP) {
+          double m = -INFINITY;
+          for (int r = lane; r < n; r += kWave) m = fmax(m, s_s[h][r]);
+          m = wave_max_all_d(m);
+          double lsum = 0.0;
+          for (int r = lane; r < n; r += kWave) {
+            const double e = exp(s_s[h][r] - m);
+            s_s[h][r] = e;
+            lsum += e;
+          }
+          lsum = wave_total_d(lsum);
+          if (lane == 0) s_m[h] = m, s_l[h] = lsum;
+        }
+      };
+      auto pv = [&](const float (*vt)[HD + 4], int t0, int nrow) {
+        if (!out_live) return;
+        const double* pr = &s_s[o_h][t0 - j0];
+        double oa[4][DPT];  // rows r % 4 in independent FMA chains
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i2 = 0; i2 < DPT; ++i2) oa[c][i2] = 0.0;
+        int r = 0;
+        for (; r + 4 <= nrow; r += 4) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i2 = 0; i2 < DPT; ++i2) oa[c][i2] += pr[r + c] * (double)vt[r + c][o_d + i2];
+        }
+        for (; r < nrow; ++r)
+#pragma unroll
+          for (int i2 = 0; i2 < DPT; ++i2) oa[0][i2] += pr[r] * (double)vt[r][o_d + i2];
+#pragma unroll
+        for (int i2 = 0; i2 < DPT; ++i2) o[i2] += (oa[0][i2] + oa[1][i2]) + (oa[2][i2] + oa[3][i2]);
+      };
+      if (one_tile) {
+        if (nt == 1) {
+          scores(j0, j1 - j0);
+          __syncthreads();
+          softmax();
+          __syncthreads();
+          pv(s_tv, j0, j1 - j0);
+        }
+      } else {
+        if (has_new) {
+          for (int d = tid; d < HD; d += NT) {
+            const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
+            if (KVBF16) {
+              const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
+              reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
+              reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
+              s_knew[d] = bf16_bits_to_f32(kb);
+              s_vnew[d] = bf16_bits_to_f32(vb);
+            } else {
+              reinterpret_cast<float*>(a.kv)[ki] = s_knew[d];
+              reinterpret_cast<float*>(a.kv)[vi] = s_vnew[d];
+            }
+          }
+        }
+        // stream element i < nt is K tile i, nt <= i < 2 nt is V tile i - nt;
+        // two tiles in flight
+        auto process = [&](KvTile<HD, KVBF16>& tr, int i, bool prefetch) {
+          const bool isv = i >= nt;
+          const int t0 = j0 + (isv ? i - nt : i) * TJ;
+          const int nrow = min(TJ, j1 - t0);
+          __syncthreads();
+          if (i == nt) {  // all scores written: softmax over the split, once
+            softmax();
+            __syncthreads();
+          }
+          if (t0 < cache_end) tr.store(s_t);
+          if (prefetch) stream_load(tr, i + 2);
+          if (t0 + nrow > p) {  // row p from this step's values (after the tile store)
+            __syncthreads();
+            const float* src = isv ? s_vnew : s_knew;
+            for (int d = tid; d < HD; d += NT) s_t[p - t0][d] = src[d];
+          }
+          __syncthreads();
+          if (!isv) scores(t0, nrow);
+          else pv(s_t, t0, nrow);
+        };
+        int i = 0;
+        for (; i + 2 < 2 * nt; i += 2) {
+          process(tA, i, true);
+          process(tB, i + 1, true);
+        }
         process(tA, i, false);
         process(tB, i + 1, false);
       }
@@ -519,14 +572,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       // S splits: O = sum_s w_s o_s / sum_s w_s l_s, w_s = exp(m_s - max m),
       // each sum taken in split order
       const int ch = (asplit * CPW) / HD, cd0 = (asplit * CPW) % HD;
-      const u64* pb = a.part + (int64_t)ag * S * G * PWORDS + ch * PWORDS;
       {
-        auto src = [&](int i) {
-          const int sp = i / WPS, k = i % WPS;
-          return pb + (int64_t)sp * G * PWORDS + (k < 4 ? 2 * HD + k : 2 * cd0 + (k - 4));
+        const int pb = ag * S * G * PWORDS + ch * PWORDS;  // word offset of (split 0, head ch)
+        auto off = [&](int j) {
+          const int sp = (2 * j) / WPS, k = (2 * j) % WPS;
+          return pb + sp * G * PWORDS + (k < 4 ? 2 * HD + k : 2 * cd0 + (k - 4));
         };
         auto dst = [&](int i) { return s_pw + i; };
-        if (!poll_words<S * WPS>(src, dst, T, a.err)) goto fail;
+        if (!poll_pairs<S * WPS / 2>(a.part, NKV * S * G * PWORDS, off, dst, T, a.err)) goto fail;
       }
       auto pw_d = [&](int sp, int k) {  // the f64 at words k, k + 1 of split sp
         return __hiloint2double((int)s_pw[sp * WPS + k + 1], (int)s_pw[sp * WPS + k]);
@@ -595,9 +648,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       {
         unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
         unsigned* da = reinterpret_cast<unsigned*>(s_da);
-        auto src = [&](int i) { return a.h + i; };
         auto dst = [&](int i) { return (i % 9) < 8 ? qa + (i / 9) * 8 + (i % 9) : da + i / 9; };
-        if (!poll_words<9 * NUB>(src, dst, T, a.err)) goto fail;
+        static_assert(NUB % 2 == 0, "pairs of h words");
+        if (!poll_pairs<9 * NUB / 2>(a.h, 9 * NUB, [](int j) { return 2 * j; }, dst, T, a.err)) goto fail;
       }
       w.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xckeep[lr] + (float)acc;
