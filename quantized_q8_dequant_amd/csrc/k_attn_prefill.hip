@@ -20,6 +20,12 @@
 // already the B operand of one O^T += V^T P^T step (keys 4*item .. +3).  The
 // workgroup's waves share one KV head, so a K/V tile staged in LDS serves all
 // of its query heads.
+//
+// Short prompts leave most CUs idle with one 32-query block per workgroup,
+// and the causal triangle makes the last blocks the longest; there (KS = 2)
+// the two waves of a query head take the two halves of every staged tile and
+// merge their (max, sum, output) through LDS at the end, which doubles the
+// workgroups and halves the longest one.  Blocks are issued longest first.
 #include "kernels.h"
 #include "qdevice.h"
 
@@ -114,26 +120,31 @@ struct KVTile {
   }
 };
 
-template <int HD, int G, bool BF16>
+template <int HD, int G, bool BF16, int KS>
 __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   constexpr int HW = G < 4 ? G : 4;  // query heads per workgroup
-  constexpr int TPW = 4 / HW;        // 16-token sub-tiles per workgroup
-  constexpr int QT = 16 * TPW;       // tokens per workgroup
+  static_assert(HW * KS <= 4, "waves");
+  constexpr int TPW = 4 / (HW * KS);  // 16-token sub-tiles per workgroup
+  constexpr int QT = 16 * TPW;        // tokens per workgroup
+  constexpr int KTW = KT / KS;        // keys of each staged tile this wave scores
   constexpr int KROW = HD + 4;       // f32 per K row in LDS (padded: the 16 x 4 lanes of
                                      // a K operand read hit 64 distinct banks)
   constexpr int VROW = HD + 16;      // f32 per V row in LDS (padded)
   constexpr int NST = HD / 4;        // k=4 steps over head_dim
   constexpr int NDT = HD / 16;       // 16-wide d tiles of the output
-  __shared__ __align__(16) float sK[KT * KROW];
-  __shared__ __align__(16) float sV[KT * VROW];
+  // K and V tiles in one array (the merge of key halves reuses all of it)
+  __shared__ __align__(16) float sKV[KT * KROW + KT * VROW];
+  float* const sK = sKV;
+  float* const sV = sKV + KT * KROW;
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int lq = lane % 16, lg = lane / 16;
   const int hb_per_g = G / HW;
   const int g = blockIdx.y / hb_per_g, hb = blockIdx.y % hb_per_g;
   const int h = g * G + hb * HW + (wave % HW);
-  const int t0 = blockIdx.x * QT;
-  const int tw0 = t0 + (wave / HW) * 16;  // first token of this wavefront
+  const int kpar = (wave / HW) % KS;  // which part of every tile this wave takes
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * QT;  // longest blocks first
+  const int tw0 = t0 + (wave / (HW * KS)) * 16;       // first token of this wavefront
   const int T = a.T;
 
   // this lane's query (clamped so padded lanes stay finite; never stored)
@@ -164,22 +175,24 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
     tile.load(a.kv, kb0, vb0, kbase + KT < kend ? kbase + KT : kbase, kend);
     __syncthreads();
 
-    // scores S^T for 4 sub-tiles of 16 keys; lane holds keys 4*item + lg
-    v4d s[KT / 16];
+    // scores S^T for the sub-tiles of 16 keys of this wave's part; lane holds
+    // keys 4*item + lg of each
+    const int kw0 = kpar * KTW;  // first key of the part within the tile
+    v4d s[KTW / 16];
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt) {
+    for (int kt = 0; kt < KTW / 16; ++kt) {
       s[kt] = v4d{0.0, 0.0, 0.0, 0.0};
-      const float* kr = &sK[(kt * 16 + lq) * KROW + lg];
+      const float* kr = &sK[(kw0 + kt * 16 + lq) * KROW + lg];
 #pragma unroll
       for (int st = 0; st < NST; ++st)
         s[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * st], qf[st], s[kt], 0, 0, 0);
     }
     double rmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt)
+    for (int kt = 0; kt < KTW / 16; ++kt)
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int key = kbase + kt * 16 + 4 * it + lg;
+        const int key = kbase + kw0 + kt * 16 + 4 * it + lg;
         const double v = (key <= qpos) ? s[kt][it] * a.scale : -INFINITY;
         s[kt][it] = v;
         rmax = fmax(rmax, v);
@@ -190,7 +203,7 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
     const double alpha = (m_run == -INFINITY) ? 0.0 : exp(m_run - m_new);
     double rsum = 0.0;
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt)
+    for (int kt = 0; kt < KTW / 16; ++kt)
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const double p = (s[kt][it] == -INFINITY) ? 0.0 : exp(s[kt][it] - m_new);
@@ -207,15 +220,44 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
     // O^T += V^T P^T: step (kt, it) covers keys kt*16 + 4*it + {0..3}; lane lg
     // supplies key kt*16 + 4*it + lg, which is exactly its score item it
 #pragma unroll
-    for (int kt = 0; kt < KT / 16; ++kt) {
+    for (int kt = 0; kt < KTW / 16; ++kt) {
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const float* vr = &sV[(kt * 16 + 4 * it + lg) * VROW + lq];
+        const float* vr = &sV[(kw0 + kt * 16 + 4 * it + lg) * VROW + lq];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           o[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * dt], s[kt][it], o[dt], 0, 0, 0);
       }
     }
+  }
+
+  if (KS == 2) {
+    // merge the two halves: the second-half wave of each (head, token tile)
+    // leaves (m, l, O) in LDS, the first-half wave rescales and adds
+    static_assert(HW * TPW * 64 * (NDT * 4 + 2) * 8 <= (int)sizeof(sKV), "merge space");
+    double* mo = reinterpret_cast<double*>(sKV);  // [HW * TPW slots][64 lanes][NDT * 4 + 2]
+    const int slot = (wave % HW) + HW * (wave / (HW * KS));
+    double* my = mo + ((int64_t)slot * 64 + lane) * (NDT * 4 + 2);
+    __syncthreads();  // every wave is done with the tiles
+    if (kpar == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) my[4 * dt + it] = o[dt][it];
+      my[NDT * 4] = m_run;
+      my[NDT * 4 + 1] = l_run;
+    }
+    __syncthreads();
+    if (kpar == 1) return;
+    const double m1 = my[NDT * 4], l1 = my[NDT * 4 + 1];
+    const double mx = fmax(m_run, m1);
+    const double a0 = (m_run == -INFINITY) ? 0.0 : exp(m_run - mx);
+    const double a1 = (m1 == -INFINITY) ? 0.0 : exp(m1 - mx);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) o[dt][it] = o[dt][it] * a0 + my[4 * dt + it] * a1;
   }
 
   // O^T layout: lane (lg, lq) holds d = 16*dt + 4*item + lg of query lq
@@ -229,16 +271,27 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   }
 }
 
+template <int HD, int G, int KS>
+hipError_t launch_attn_ks(const AttnPrefillArgs& a, bool bf16, hipStream_t s) {
+  constexpr int HW = G < 4 ? G : 4;
+  constexpr int QT = 16 * (4 / (HW * KS));
+  const dim3 grid((a.T + QT - 1) / QT, a.nkv * (G / HW));
+  if (bf16)
+    hipLaunchKernelGGL((k_attn_prefill<HD, G, true, KS>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_prefill<HD, G, false, KS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Two key halves per head when one 32-query block per workgroup would give
+// fewer than two workgroups per CU.
 template <int HD, int G>
 hipError_t launch_attn(const AttnPrefillArgs& a, bool bf16, hipStream_t s) {
   constexpr int HW = G < 4 ? G : 4;
-  constexpr int QT = 16 * (4 / HW);
-  const dim3 grid((a.T + QT - 1) / QT, a.nkv * (G / HW));
-  if (bf16)
-    hipLaunchKernelGGL((k_attn_prefill<HD, G, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_prefill<HD, G, false>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  if constexpr (HW <= 2) {
+    if ((int64_t)((a.T + 31) / 32) * a.nkv * (G / HW) < 512) return launch_attn_ks<HD, G, 2>(a, bf16, s);
+  }
+  return launch_attn_ks<HD, G, 1>(a, bf16, s);
 }
 
 }  // namespace

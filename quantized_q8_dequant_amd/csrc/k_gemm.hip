@@ -4,7 +4,8 @@
 // integer dot of 32-block b (Fucina course, "Model files and quantization",
 // section 11.9).  One 32x32x32 MFMA covers exactly one Q8_0 block, so its
 // int32 result IS S_b for a 32x32 tile; it is converted and rescaled by the
-// product of the two f16 scales (exact in f32) into an f32 accumulator.
+// product of the two f16 scales (exact in f32) into an f64 accumulator (every
+// term is exact in f64) that is rounded to f32 once.
 //
 // Tiling: a 256-thread workgroup owns a 128 (tokens) x 128 (outputs) tile;
 // its 4 wavefronts each own 64 x 64 = 2 x 2 MFMA tiles.  K advances in
@@ -15,6 +16,11 @@
 // Epilogues: store, residual add into C, and SwiGLU of the paired gate/up
 // columns (the weight stack interleaves 32 gate rows and 32 up rows, so a
 // wavefront's 64 columns are one gate tile and its up tile).
+//
+// Split K: when the tile grid alone would leave most of the 256 CUs idle
+// (short prompts, narrow outputs), blockIdx.z takes a contiguous slice of the
+// K stages and the tile's f64 sums go to a scratch plane; k_gemm_reduce adds
+// the planes in slice order, rounds once to f32 and applies the epilogue.
 #include "kernels.h"
 #include "qdevice.h"
 
@@ -74,6 +80,8 @@ QDEV void gemm_gload(const GemmArgs& a, Stage& r, int st, int m0, int n0, int nb
   }
 }
 
+constexpr int EPI_PARTIAL = 7;  // f64 sums of one K slice to the scratch plane
+
 template <int EPI>
 __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   __shared__ __align__(16) int8_t sA[2][BM * LDS_ROW];
@@ -86,7 +94,8 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   const int wm = wave / 2, wn = wave % 2;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int nblk = a.K / 32;
-  const int nstage = a.K / SK;
+  const int nslice = a.K / SK / gridDim.z;  // K stages of this workgroup's slice
+  const int st0 = blockIdx.z * nslice;
 
   Stage rs;  // global -> register staging: 4 x 16 bytes of A and of B per thread
   // block terms d_a * d_w * S are exact in f64; the sum is rounded to f32
@@ -100,12 +109,12 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
       for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0;
 
   const int lr = lane % 32, lg = lane / 32;
-  gemm_gload(a, rs, 0, m0, n0, nblk);
+  gemm_gload(a, rs, st0, m0, n0, nblk);
   gemm_lstore(rs, sA[0], sB[0], sDa[0], sDw[0]);
   __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstage) gemm_gload(a, rs, st + 1, m0, n0, nblk);
+  for (int si = 0; si < nslice; ++si) {
+    const int buf = si & 1;
+    if (si + 1 < nslice) gemm_gload(a, rs, st0 + si + 1, m0, n0, nblk);
 #pragma unroll 2
     for (int kb = 0; kb < KB; ++kb) {
       v4i af[2], bf[2];
@@ -143,7 +152,7 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
           for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (double)S[mi][ni][j] * (da[j] * dw[ni]);
       }
     }
-    if (st + 1 < nstage) {
+    if (si + 1 < nslice) {
       gemm_lstore(rs, sA[buf ^ 1], sB[buf ^ 1], sDa[buf ^ 1], sDw[buf ^ 1]);
     }
     __syncthreads();
@@ -156,7 +165,14 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
     for (int j = 0; j < 16; ++j) {
       const int m = m0 + wm * 64 + mi * 32 + 8 * (j / 4) + 4 * lg + (j % 4);
       if (m >= a.M) continue;
-      if (EPI == EPI_SWIGLU) {
+      if (EPI == EPI_PARTIAL) {
+        double* pp = a.part + (int64_t)blockIdx.z * a.M * a.N + (int64_t)m * a.N;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int n = n0 + wn * 64 + ni * 32 + lr;
+          if (n < a.N) pp[n] = acc[mi][ni][j];
+        }
+      } else if (EPI == EPI_SWIGLU) {
         if (n0 + wn * 64 >= a.N) continue;
         const int unit = ((n0 + wn * 64) / 64) * 32 + lr;
         a.out[(int64_t)m * a.ldc + unit] = swiglu_f64((float)acc[mi][0][j], (float)acc[mi][1][j]);
@@ -175,12 +191,64 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   }
 }
 
+// Sum of the split planes in split order, rounded once to f32, then the
+// epilogue; one thread per output (per hidden unit for SwiGLU).
+template <int EPI>
+__global__ void __launch_bounds__(256) k_gemm_reduce(const double* __restrict__ part, int splits, int M, int N,
+                                                     float* out, int64_t ldc) {
+  const int NO = EPI == EPI_SWIGLU ? N / 2 : N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * NO) return;
+  const int m = (int)(idx / NO), c = (int)(idx % NO);
+  const int64_t plane = (int64_t)M * N;
+  const double* p = part + (int64_t)m * N;
+  if (EPI == EPI_SWIGLU) {
+    const int ng = (c / 32) * 64 + c % 32;  // gate column; its up column is ng + 32
+    double g = 0.0, u = 0.0;
+    for (int z = 0; z < splits; ++z) {
+      g += p[z * plane + ng];
+      u += p[z * plane + ng + 32];
+    }
+    out[(int64_t)m * ldc + c] = swiglu_f64((float)g, (float)u);
+  } else {
+    double acc = 0.0;
+    for (int z = 0; z < splits; ++z) acc += p[z * plane + c];
+    float* o = out + (int64_t)m * ldc + c;
+    if (EPI == EPI_STORE) *o = (float)acc;
+    else *o = *o + (float)acc;
+  }
+}
+
 }  // namespace
 
 namespace q8k {
 
+// K slices for a grid of `tiles` workgroups: doubled while the grid is under
+// one workgroup per CU, the slices stay whole stages and the planes fit.
+int gemm_splits(int M, int N, int K, size_t part_bytes) {
+  const int tiles = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  const int nstage = K / SK;
+  int sp = 1;
+  while (tiles * sp < 256 && nstage % (2 * sp) == 0 && (size_t)2 * sp * M * N * 8 <= part_bytes) sp *= 2;
+  return sp;
+}
+
 hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  const int sp = a.part ? gemm_splits(a.M, a.N, a.K, a.part_bytes) : 1;
+  if (sp > 1) {
+    const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, sp);
+    hipLaunchKernelGGL(k_gemm_q8<EPI_PARTIAL>, grid, dim3(256), 0, s, a);
+    const int NO = epi == EPI_SWIGLU ? a.N / 2 : a.N;
+    const dim3 rg((unsigned)(((int64_t)a.M * NO + 255) / 256));
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL(k_gemm_reduce<EPI_STORE>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
+      case EPI_RESIDUAL: hipLaunchKernelGGL(k_gemm_reduce<EPI_RESIDUAL>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_reduce<EPI_SWIGLU>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL(k_gemm_q8<EPI_STORE>, grid, dim3(256), 0, s, a); break;

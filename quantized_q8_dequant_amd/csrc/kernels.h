@@ -93,6 +93,11 @@ struct GemmArgs {
   int M, N, K;
   float* out;  // STORE/RESIDUAL: [M][ldc]; SWIGLU: [M][ldc] hidden units (N/2 of them)
   int64_t ldc;
+  // split-K scratch: when the tile grid is small, K is split over `splits`
+  // slices whose f64 sums go to part[split][M][N] and are added in split
+  // order by a second kernel (0 or 1: no split)
+  double* part;
+  size_t part_bytes;
 };
 
 // Prefill per-token head work (see k_attn_prefill.hip).

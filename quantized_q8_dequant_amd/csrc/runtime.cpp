@@ -122,6 +122,8 @@ struct qwen3_model {
   float* q32 = nullptr;
   float* xn = nullptr;  // normalised rows (bf16-weight models: the norm is not fused)
   double* attn_part = nullptr;
+  double* gemm_part = nullptr;  // split-K planes of the prefill GEMM
+  size_t gemm_part_bytes = 0;
   unsigned* attn_cnt = nullptr;
   unsigned long long* am_key = nullptr;
   unsigned* am_cnt = nullptr;
@@ -148,6 +150,10 @@ namespace {
 // its grid is at most one split, each split holds G heads of (o[hd], m, l) as
 // two words per f64.
 size_t persist_part_words(int64_t G, int64_t hd) { return (size_t)kPersistWorkgroups * G * (hd + 2) * 2; }
+
+// Split-K planes of the prefill GEMM (f64 sums of K slices): enough for eight
+// slices of a 1024 x 1024 output.
+constexpr size_t kGemmPartBytes = (size_t)64 << 20;
 
 int validate(const qwen3_config* c) {
   if (!c) return fail(QWEN3_E_INVALID_ARGUMENT, "config is null");
@@ -260,6 +266,10 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   const int64_t needed = decode_splits_needed(m->max_cap, (int)G);
   const int64_t slots = std::max<int64_t>(1024 + R * nkv, R * nkv * needed);
   m->attn_part = cv.arr<double>((size_t)slots * G * (hd + 2));
+  if (!m->wbf16) {
+    m->gemm_part_bytes = kGemmPartBytes;
+    m->gemm_part = cv.arr<double>(kGemmPartBytes / 8);
+  }
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
@@ -488,6 +498,8 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     g.qa = m->qa;
     g.da = m->da;
     g.M = T;
+    g.part = m->gemm_part;
+    g.part_bytes = m->gemm_part_bytes;
     // attention input: RMSNorm + quantise, fused QKV GEMM
     if (m->wbf16) {
       HIP_TRY(q8k::rows_norm(m->x, m->H, T, m->H, ly.attn_norm, eps, m->xn, m->H, s));
