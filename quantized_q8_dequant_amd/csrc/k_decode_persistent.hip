@@ -170,10 +170,12 @@ QDEV void quantize_lds(const float* s_x, const NormW<K>* nw, float eps, int8_t* 
 // a row, each lane owns BPL whole blocks (the decode GEMV's layout for K, so
 // the per-row summation order is the same); RPP rows per pass of the 256
 // threads.
-template <int K, int R>
+// LPR0 > 0 sets the lanes per row (fewer passes and shorter lane reductions
+// for tall slices).
+template <int K, int R, int LPR0 = 0>
 struct Slice {
   static constexpr int NB = K / 32;
-  static constexpr int LPR = (NB % 64 == 0) ? 64 : (NB % 32 == 0) ? 32 : (NB % 16 == 0) ? 16 : 8;
+  static constexpr int LPR = LPR0 > 0 ? LPR0 : (NB % 64 == 0) ? 64 : (NB % 32 == 0) ? 32 : (NB % 16 == 0) ? 16 : 8;
   static constexpr int BPL = NB / LPR;
   static constexpr int RPP = NT / LPR;
   static constexpr int PASSES = (R + RPP - 1) / RPP;
@@ -370,7 +372,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 
     // ---- A: QKV projection --------------------------------------------------
     {
-      Slice<H, RA> w;
+      Slice<H, RA, (H / 32 >= 32 && RA >= 16 ? 16 : 0)> w;
       w.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
       NormW<H> nw;
       nw.load(P.attn_norm);
@@ -622,7 +624,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // projection's prologue arithmetic): 8 words of four codes, then one word
     // with the f16-valued block scale.
     if (b < NUB) {
-      Slice<H, 64> w;
+      Slice<H, 64, (H / 32 >= 32 ? 8 : 0)> w;
       w.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
       NormW<H> nw;
       nw.load(P.ffn_norm);
