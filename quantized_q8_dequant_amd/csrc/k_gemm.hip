@@ -7,8 +7,8 @@
 // product of the two f16 scales (exact in f32) into an f64 accumulator (every
 // term is exact in f64) that is rounded to f32 once.
 //
-// Tiling: a 256-thread workgroup owns a 128 (tokens) x 128 (outputs) tile;
-// its 4 wavefronts each own 64 x 64 = 2 x 2 MFMA tiles.  K advances in
+// Tiling: a 256-thread workgroup owns a 128 (tokens) x 64 (outputs) tile;
+// its 4 wavefronts each own 32 x 64 = 1 x 2 MFMA tiles.  K advances in
 // stages of 4 blocks (128 bytes); A/B stages are double-buffered in LDS
 // (rows padded by 16 bytes against bank conflicts), the next stage's global
 // loads are issued before the current stage's MFMAs.
@@ -30,60 +30,79 @@ namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128;
+// A 128 (tokens) x 64 (outputs) tile per workgroup: wavefront w owns rows
+// 32w .. 32w+31 and all 64 columns (two 32x32 MFMA tiles), so the SwiGLU
+// epilogue finds a gate tile and its up tile in one wavefront.  The small
+// per-wavefront tile keeps the kernel within 256 registers per lane and its
+// LDS within 64 KB, so two workgroups share a CU: the f64 epilogue of one
+// wavefront then runs while the other waits for LDS or memory.
+constexpr int BM = 128, BN = 64;
 constexpr int KB = 4;            // 32-blocks per stage
 constexpr int SK = KB * 32;      // bytes of K per stage
 constexpr int LDS_ROW = SK + 16; // padded row stride (bytes)
+constexpr int AL = BM * SK / 16 / 256;  // 16-byte loads of A per thread per stage (4)
+constexpr int BL = BN * SK / 16 / 256;  // ... of B (2)
 
 struct Stage {
-  v4i a[4], b[4];
-  float da[2], dw[2];
+  v4i a[AL], b[BL];
+  float da[BM * KB / 256], dw[BN * KB / 256 > 0 ? BN * KB / 256 : 1];
 };
 
 QDEV void gemm_lstore(const Stage& r, int8_t* sA, int8_t* sB, float (*sDa)[BM], float (*sDw)[BN]) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < AL; ++i) {
     const int idx = tid + 256 * i;
     const int row = idx / 8, c16 = idx % 8;
     *reinterpret_cast<v4i*>(&sA[row * LDS_ROW + c16 * 16]) = r.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / 8, c16 = idx % 8;
     *reinterpret_cast<v4i*>(&sB[row * LDS_ROW + c16 * 16]) = r.b[i];
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < BM * KB / 256; ++i) {
     const int idx = tid + 256 * i;
-    const int row = idx / KB, kb = idx % KB;
-    sDa[kb][row] = r.da[i];
-    sDw[kb][row] = r.dw[i];
+    sDa[idx % KB][idx / KB] = r.da[i];
   }
+  if (tid < BN * KB) sDw[tid % KB][tid / KB] = r.dw[0];
 }
 
 QDEV void gemm_gload(const GemmArgs& a, Stage& r, int st, int m0, int n0, int nblk) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + 256 * i;  // 0..1023
+  for (int i = 0; i < AL; ++i) {
+    const int idx = tid + 256 * i;
     const int row = idx / 8, c16 = idx % 8;
     const int gm = min(m0 + row, a.M - 1);
-    const int gn = min(n0 + row, a.N - 1);
     r.a[i] = *reinterpret_cast<const v4i*>(a.qa + (int64_t)gm * a.K + st * SK + c16 * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / 8, c16 = idx % 8;
+    const int gn = min(n0 + row, a.N - 1);
     r.b[i] = *reinterpret_cast<const v4i*>(a.qs + (int64_t)gn * a.K + st * SK + c16 * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i;  // 0..511
-    const int row = idx / KB, kb = idx % KB;
-    const int gm = min(m0 + row, a.M - 1);
-    const int gn = min(n0 + row, a.N - 1);
-    r.da[i] = a.da[(int64_t)gm * nblk + st * KB + kb];
-    r.dw[i] = f16_bits_to_f32(a.sc[(int64_t)gn * nblk + st * KB + kb]);
+  for (int i = 0; i < BM * KB / 256; ++i) {
+    const int idx = tid + 256 * i;
+    const int gm = min(m0 + idx / KB, a.M - 1);
+    r.da[i] = a.da[(int64_t)gm * nblk + st * KB + idx % KB];
+  }
+  {
+    const int idx = tid % (BN * KB);
+    const int gn = min(n0 + idx / KB, a.N - 1);
+    r.dw[0] = f16_bits_to_f32(a.sc[(int64_t)gn * nblk + st * KB + idx % KB]);
   }
 }
 
 constexpr int EPI_PARTIAL = 7;  // f64 sums of one K slice to the scratch plane
 
 template <int EPI>
-__global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
+__global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
   __shared__ __align__(16) int8_t sA[2][BM * LDS_ROW];
   __shared__ __align__(16) int8_t sB[2][BN * LDS_ROW];
   __shared__ __align__(16) float sDa[2][KB][BM];
@@ -91,22 +110,19 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int nblk = a.K / 32;
   const int nslice = a.K / SK / gridDim.z;  // K stages of this workgroup's slice
   const int st0 = blockIdx.z * nslice;
 
-  Stage rs;  // global -> register staging: 4 x 16 bytes of A and of B per thread
+  Stage rs;  // global -> register staging of the next stage
   // block terms d_a * d_w * S are exact in f64; the sum is rounded to f32
   // once, in the epilogue
-  double acc[2][2][16];
+  double acc[2][16];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0;
+    for (int j = 0; j < 16; ++j) acc[ni][j] = 0.0;
 
   const int lr = lane % 32, lg = lane / 32;
   gemm_gload(a, rs, st0, m0, n0, nblk);
@@ -115,77 +131,65 @@ __global__ void __launch_bounds__(256) k_gemm_q8(GemmArgs a) {
   for (int si = 0; si < nslice; ++si) {
     const int buf = si & 1;
     if (si + 1 < nslice) gemm_gload(a, rs, st0 + si + 1, m0, n0, nblk);
-#pragma unroll 2
+#pragma unroll 1
     for (int kb = 0; kb < KB; ++kb) {
-      v4i af[2], bf[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const v4i*>(&sA[buf][(wm * 64 + mi * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+      const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][(wave * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+      v4i bf[2];
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
-        bf[ni] = *reinterpret_cast<const v4i*>(&sB[buf][(wn * 64 + ni * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
-      // the four block products first, then their scaled f64 accumulation
-      // (d_a * d_w is exact in f64 as in f32; every term S * d_a * d_w is
-      // exact in f64)
-      v16i S[2][2];
+        bf[ni] = *reinterpret_cast<const v4i*>(&sB[buf][(ni * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
+      // the two block products (S = the exact int32 dots of 32-block kb),
+      // then their scaled f64 accumulation: d_a * d_w is exact in f64 as in
+      // f32, and every term S * d_a * d_w is exact in f64
+      v16i S[2];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const v16i zero = {};
-          S[mi][ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[ni], zero, 0, 0, 0);
-        }
+      for (int ni = 0; ni < 2; ++ni) {
+        const v16i zero = {};
+        S[ni] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf[ni], zero, 0, 0, 0);
+      }
       double dw[2];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) dw[ni] = (double)sDw[buf][kb][wn * 64 + ni * 32 + lr];
+      for (int ni = 0; ni < 2; ++ni) dw[ni] = (double)sDw[buf][kb][ni * 32 + lr];
+      double da[16];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        double da[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 d4 = *reinterpret_cast<const float4*>(&sDa[buf][kb][wm * 64 + mi * 32 + 8 * g4 + 4 * lg]);
-          da[4 * g4 + 0] = d4.x, da[4 * g4 + 1] = d4.y, da[4 * g4 + 2] = d4.z, da[4 * g4 + 3] = d4.w;
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[mi][ni][j] += (double)S[mi][ni][j] * (da[j] * dw[ni]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&sDa[buf][kb][wave * 32 + 8 * g4 + 4 * lg]);
+        da[4 * g4 + 0] = d4.x, da[4 * g4 + 1] = d4.y, da[4 * g4 + 2] = d4.z, da[4 * g4 + 3] = d4.w;
       }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[ni][j] += (double)S[ni][j] * (da[j] * dw[ni]);
     }
-    if (si + 1 < nslice) {
-      gemm_lstore(rs, sA[buf ^ 1], sB[buf ^ 1], sDa[buf ^ 1], sDw[buf ^ 1]);
-    }
+    if (si + 1 < nslice) gemm_lstore(rs, sA[buf ^ 1], sB[buf ^ 1], sDa[buf ^ 1], sDw[buf ^ 1]);
     __syncthreads();
   }
 
-  // epilogue: element j of tile (mi, ni) is row 8*(j/4) + 4*lg + j%4, column lr
+  // epilogue: element j of tile ni is row 8*(j/4) + 4*lg + j%4, column lr
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int j = 0; j < 16; ++j) {
+    const int m = m0 + wave * 32 + 8 * (j / 4) + 4 * lg + (j % 4);
+    if (m >= a.M) continue;
+    if (EPI == EPI_PARTIAL) {
+      double* pp = a.part + (int64_t)blockIdx.z * a.M * a.N + (int64_t)m * a.N;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int m = m0 + wm * 64 + mi * 32 + 8 * (j / 4) + 4 * lg + (j % 4);
-      if (m >= a.M) continue;
-      if (EPI == EPI_PARTIAL) {
-        double* pp = a.part + (int64_t)blockIdx.z * a.M * a.N + (int64_t)m * a.N;
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + ni * 32 + lr;
+        if (n < a.N) pp[n] = acc[ni][j];
+      }
+    } else if (EPI == EPI_SWIGLU) {
+      if (n0 >= a.N) continue;
+      const int unit = (n0 / 64) * 32 + lr;
+      a.out[(int64_t)m * a.ldc + unit] = swiglu_f64((float)acc[0][j], (float)acc[1][j]);
+    } else {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = n0 + wn * 64 + ni * 32 + lr;
-          if (n < a.N) pp[n] = acc[mi][ni][j];
-        }
-      } else if (EPI == EPI_SWIGLU) {
-        if (n0 + wn * 64 >= a.N) continue;
-        const int unit = ((n0 + wn * 64) / 64) * 32 + lr;
-        a.out[(int64_t)m * a.ldc + unit] = swiglu_f64((float)acc[mi][0][j], (float)acc[mi][1][j]);
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = n0 + wn * 64 + ni * 32 + lr;
-          if (n >= a.N) continue;
-          float* p = a.out + (int64_t)m * a.ldc + n;
-          const float y = (float)acc[mi][ni][j];
-          if (EPI == EPI_STORE) *p = y;
-          if (EPI == EPI_RESIDUAL) *p = *p + y;
-        }
+      for (int ni = 0; ni < 2; ++ni) {
+        const int n = n0 + ni * 32 + lr;
+        if (n >= a.N) continue;
+        float* p = a.out + (int64_t)m * a.ldc + n;
+        const float y = (float)acc[ni][j];
+        if (EPI == EPI_STORE) *p = y;
+        if (EPI == EPI_RESIDUAL) *p = *p + y;
       }
     }
   }
@@ -224,12 +228,12 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const double* __restrict__ 
 namespace q8k {
 
 // K slices for a grid of `tiles` workgroups: doubled while the grid is under
-// one workgroup per CU, the slices stay whole stages and the planes fit.
+// two workgroups per CU, the slices stay whole stages and the planes fit.
 int gemm_splits(int M, int N, int K, size_t part_bytes) {
   const int tiles = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
   const int nstage = K / SK;
   int sp = 1;
-  while (tiles * sp < 256 && nstage % (2 * sp) == 0 && (size_t)2 * sp * M * N * 8 <= part_bytes) sp *= 2;
+  while (tiles * sp < 512 && nstage % (2 * sp) == 0 && (size_t)2 * sp * M * N * 8 <= part_bytes) sp *= 2;
   return sp;
 }
 
