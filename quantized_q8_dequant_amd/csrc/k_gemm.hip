@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
   for (int si = 0; si < nslice; ++si) {
     const int buf = si & 1;
     if (si + 1 < nslice) gemm_gload(a, rs, st0 + si + 1, m0, n0, nblk);
-#pragma unroll 1
+#pragma unroll 2
     for (int kb = 0; kb < KB; ++kb) {
       const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][(wave * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
       v4i bf[2];
