@@ -259,6 +259,60 @@ def bench_batch64(args) -> int:
     return 0
 
 
+VERIFY_TOKENS = 16
+
+
+def event_ms(fn, warmup: int, reps: int) -> float:
+    """Median event-timed duration of fn() on the current stream, in ms."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return sorted(times)[len(times) // 2]
+
+
+def bench_verify(model, prompt, shape, decode_ms_per_token: float, args) -> dict:
+    """The speculative seams: an all-logits verify of VERIFY_TOKENS drafted
+    tokens after the prompt plus the rewind that drops them, set against as
+    many sequential decode steps; and the whole prompt with every row's
+    logits, set against the ordinary last-row prefill."""
+    from synthetic import gen_prompt
+
+    draft = gen_prompt(shape.vocab_size, VERIFY_TOKENS, 80)
+    P = len(prompt)
+    model.reset()
+    model.prefill(prompt, logits=False)
+
+    def verify():
+        model.prefill_all_logits(draft)
+        model.truncate(P)
+
+    v_ms = event_ms(verify, args.warmup, max(args.steps, 5))
+
+    def all_rows():
+        model.reset()
+        model.prefill_all_logits(prompt)
+
+    a_ms = event_ms(all_rows, args.warmup, args.steps)
+    return {
+        "verify_tokens": VERIFY_TOKENS,
+        "verify_ms": round(v_ms, 3),
+        "sequential_decode_ms": round(VERIFY_TOKENS * decode_ms_per_token, 3),
+        "verify_speedup_vs_sequential_decode": round(VERIFY_TOKENS * decode_ms_per_token / v_ms, 2),
+        "all_logits_prompt_tokens": P,
+        "all_logits_prefill_ms": round(a_ms, 3),
+        "all_logits_tokens_per_s": round(P / (a_ms / 1000.0), 1),
+    }
+
+
 def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
     """The CPU oracle on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_info
@@ -376,6 +430,9 @@ def main() -> int:
             "bytes_per_launch": int(nbytes),
             "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
         }
+    verify = None
+    if args.workload == "0.6b-decode":
+        verify = bench_verify(model, prompt, shape, decode_ms / wl.decode_steps, args)
     launches = model.decode_launches()
     if launches == 1:
         # the decode step is one kernel: its algorithmic bytes per launch (the
@@ -481,6 +538,7 @@ def main() -> int:
         "decode_launches_per_token": launches,
         "kernels_at_mean_ctx": kernels,
         "prefill_4096_one_call": p4,
+        "verify": verify,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -150,6 +150,25 @@ void qwen3_destroy(qwen3_t* h);
 int qwen3_prefill(qwen3_t* h, int32_t seq, const int32_t* h_tokens, int32_t n, float* d_logits,
                   int32_t* d_argmax, void* stream);
 
+/* Prefill returning every row's logits: the all-logits forward step ("A
+ * transformer from scratch", sections 12.3.7 and 12.5, forwardStepAllLogits:
+ * the same forward over the appended tokens, with the final norm and lm_head
+ * applied to every position instead of the last only), the verify pass of
+ * speculative decoding.  Appends the n tokens (host ids, validated) to `seq` at its length L
+ * exactly as qwen3_prefill does, then applies the final RMSNorm and the tied
+ * lm_head to all n rows.  d_logits [n, vocab] f32 (required, row-major);
+ * d_argmax [n] int32 greedy argmax of each row (lowest index among maxima),
+ * or NULL.  Length L -> L + n.  Errors as qwen3_prefill. */
+int qwen3_prefill_all_logits(qwen3_t* h, int32_t seq, const int32_t* h_tokens, int32_t n, float* d_logits,
+                             int32_t* d_argmax, void* stream);
+
+/* Rewind sequence `seq` to its first keep_len positions in O(1) ("The LLM
+ * stack (fucina_llm)", section 13.4, truncate; "A transformer from scratch",
+ * section 12.4): only the length changes, the next append overwrites the
+ * abandoned rows.  keep_len >= the current length is a no-op; keep_len < 0 is
+ * QWEN3_E_INVALID_ARGUMENT.  The device length is set on `stream`. */
+int qwen3_truncate(qwen3_t* h, int32_t seq, int32_t keep_len, void* stream);
+
 /* One decode step of sequence `seq`: the token id is read on the device from
  * d_token [1] (so the previous step's d_argmax can be passed straight back
  * and the step needs no host round trip).  Writes d_logits [vocab] (may be

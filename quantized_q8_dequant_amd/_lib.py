@@ -33,6 +33,8 @@ EXPORTS = (
     "qwen3_create",
     "qwen3_destroy",
     "qwen3_prefill",
+    "qwen3_prefill_all_logits",
+    "qwen3_truncate",
     "qwen3_decode_step",
     "qwen3_decode_batch",
     "qwen3_reset",
@@ -125,6 +127,8 @@ def lib() -> C.CDLL:
         "qwen3_create": (C.c_int, [C.POINTER(Config), C.POINTER(Weights), vp, sz, vp, C.POINTER(vp)]),
         "qwen3_destroy": (None, [vp]),
         "qwen3_prefill": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
+        "qwen3_prefill_all_logits": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
+        "qwen3_truncate": (C.c_int, [vp, i32, i32, vp]),
         "qwen3_decode_step": (C.c_int, [vp, i32, vp, vp, vp, vp]),
         "qwen3_decode_batch": (C.c_int, [vp, p_i32, i32, vp, vp, vp, vp]),
         "qwen3_reset": (C.c_int, [vp, i32, vp]),

@@ -215,10 +215,59 @@ hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int 
   return hipGetLastError();
 }
 
+// Greedy pick of every row of f32 logits [T, V] ("A transformer from
+// scratch", section 12.6: the argmax over the vocabulary; among equal maxima
+// the lowest index, as in the other argmax epilogues).
+// One workgroup per row; each lane scans a strided slice in ascending order,
+// then the (value, index) pairs are reduced across the lanes.
+__device__ __forceinline__ void argmax_take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) bv = v, bi = i;
+}
+
+__global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x, int V, int32_t* __restrict__ out) {
+  __shared__ float s_v[256 / kWave];
+  __shared__ int s_i[256 / kWave];
+  const float* xr = x + (int64_t)blockIdx.x * V;
+  float bv = -__builtin_inff();
+  int bi = 0x7FFFFFFF;
+  if ((V & 3) == 0) {
+    const float4* x4 = reinterpret_cast<const float4*>(xr);
+    for (int c = threadIdx.x; c < V / 4; c += 256) {
+      const float4 t = x4[c];
+      argmax_take(bv, bi, t.x, 4 * c);
+      argmax_take(bv, bi, t.y, 4 * c + 1);
+      argmax_take(bv, bi, t.z, 4 * c + 2);
+      argmax_take(bv, bi, t.w, 4 * c + 3);
+    }
+  } else {
+    for (int c = threadIdx.x; c < V; c += 256) argmax_take(bv, bi, xr[c], c);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    argmax_take(bv, bi, ov, oi);
+  }
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (lane == 0) s_v[wave] = bv, s_i[wave] = bi;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 256 / kWave; ++w) argmax_take(bv, bi, s_v[w], s_i[w]);
+    out[blockIdx.x] = bi;
+  }
+}
+
 hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
                       uint16_t* da_bits, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_rows_quant, dim3(T), dim3(256), 0, s, x, K, norm_w, eps, qa, da, da_bits);
+  return hipGetLastError();
+}
+
+hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (V <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rows_argmax, dim3(T), dim3(256), 0, s, x, V, out);
   return hipGetLastError();
 }
 

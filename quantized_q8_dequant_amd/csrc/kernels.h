@@ -79,6 +79,8 @@ bool attn_decode_supported(int hd, int group);
 int attn_decode_max_ctx(int group);  // longest context (cache capacity) the decode attention takes
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
 
+// Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T].
+hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, hipStream_t s);
 hipError_t set_len(int32_t* len, int seq, int value, hipStream_t s);
 
 }  // namespace q8k

@@ -486,8 +486,10 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
 }
 
 // One prefill chunk: T tokens (already in m->d_tok) at positions pos0.. of seq.
+// all_rows: the head runs on every row of the chunk, writing d_logits [T, V]
+// (and d_argmax [T]) from the chunk's first row; else on row T-1 of the last chunk.
 int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, float* d_logits, int32_t* d_argmax,
-                          hipStream_t s) {
+                          hipStream_t s, bool all_rows = false) {
   const float eps = m->cfg.rms_norm_eps;
   HIP_TRY(q8k::embed(m->d_tok, T, m->V, m->H, plane_rows(m->emb), m->emb.sc, m->wbf16, m->x, s));
   const int64_t head_elems = (int64_t)m->cap[seq] * m->hd;
@@ -557,7 +559,22 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     g.qs = ly.down.qs, g.sc = ly.down.sc, g.N = (int)ly.down.rows, g.K = m->F, g.out = m->x, g.ldc = m->H;
     HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
   }
-  if (last && (d_logits || d_argmax) && m->wbf16) {
+  if (all_rows) {
+    // final RMSNorm + tied lm_head on all T rows as one GEMM, then the row argmax
+    const int64_t H = m->H;
+    if (m->wbf16) {
+      HIP_TRY(q8k::rows_norm(m->x, H, T, m->H, m->out_norm, eps, m->xn, H, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args(m->emb, m->xn, H, T, d_logits, m->V), EPI_STORE, s));
+    } else {
+      HIP_TRY(q8k::rows_quant(m->x, T, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s));
+      GemmArgs g{};
+      g.qa = m->qa, g.da = m->da, g.M = T;
+      g.part = m->gemm_part, g.part_bytes = m->gemm_part_bytes;
+      g.qs = m->emb.qs, g.sc = m->emb.sc, g.N = m->V, g.K = m->H, g.out = d_logits, g.ldc = m->V;
+      HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+    }
+    if (d_argmax) HIP_TRY(q8k::rows_argmax(d_logits, T, m->V, d_argmax, s));
+  } else if (last && (d_logits || d_argmax) && m->wbf16) {
     const int64_t H = m->H;
     HIP_TRY(q8k::rows_norm(m->x + (int64_t)(T - 1) * H, H, 1, m->H, m->out_norm, eps, m->xn, H, s));
     GemmBf16Args g = bf16_args(m->emb, m->xn, H, 1, nullptr, 0);
@@ -767,6 +784,44 @@ int qwen3_prefill(qwen3_t* m, int32_t seq, const int32_t* h_tokens, int32_t n, f
     TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits, d_argmax, s));
   }
   m->h_len[seq] = len + n;
+  return QWEN3_OK;
+}
+
+int qwen3_prefill_all_logits(qwen3_t* m, int32_t seq, const int32_t* h_tokens, int32_t n, float* d_logits,
+                             int32_t* d_argmax, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (n <= 0) return fail(QWEN3_E_INVALID_SEQUENCE_LENGTH, "prefill needs n >= 1 tokens");
+  if (!h_tokens) return fail(QWEN3_E_INVALID_ARGUMENT, "h_tokens is null");
+  if (!d_logits) return fail(QWEN3_E_INVALID_ARGUMENT, "d_logits is required");
+  const int len = m->h_len[seq];
+  if ((int64_t)len + n > m->cap[seq])
+    return fail(QWEN3_E_KV_CACHE_OVERFLOW, "len " + std::to_string(len) + " + " + std::to_string(n) +
+                                               " exceeds capacity " + std::to_string(m->cap[seq]));
+  for (int i = 0; i < n; ++i)
+    if (h_tokens[i] < 0 || h_tokens[i] >= m->V)
+      return fail(QWEN3_E_TOKEN_OUT_OF_RANGE, "token " + std::to_string(i) + " = " + std::to_string(h_tokens[i]) +
+                                                  " outside [0, vocab)");
+  hipStream_t s = S(stream);
+  for (int c0 = 0; c0 < n; c0 += m->R) {
+    const int T = std::min(m->R, n - c0);
+    HIP_TRY(hipMemcpyAsync(m->d_tok, h_tokens + c0, (size_t)T * 4, hipMemcpyHostToDevice, s));
+    TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits + (int64_t)c0 * m->V,
+                              d_argmax ? d_argmax + c0 : nullptr, s, true));
+  }
+  m->h_len[seq] = len + n;
+  return QWEN3_OK;
+}
+
+int qwen3_truncate(qwen3_t* m, int32_t seq, int32_t keep_len, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (keep_len < 0) return fail(QWEN3_E_INVALID_ARGUMENT, "keep_len < 0");
+  if (keep_len >= m->h_len[seq]) return QWEN3_OK;
+  m->h_len[seq] = keep_len;
+  HIP_TRY(q8k::set_len(m->d_len, seq, keep_len, S(stream)));
   return QWEN3_OK;
 }
 

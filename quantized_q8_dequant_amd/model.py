@@ -231,6 +231,30 @@ class Qwen3Model:
         )
         return lg, am
 
+    def prefill_all_logits(self, tokens, seq: int = 0, argmax: bool = True):
+        """Append `tokens` to `seq` and return (logits [n, V] f32, argmax [n]
+        int32 or None) for every appended position (the verify pass)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        n = int(toks.shape[0])
+        lg = torch.empty((max(n, 1), self.cfg.vocab_size), dtype=torch.float32, device=self.device)
+        am = torch.empty((max(n, 1),), dtype=torch.int32, device=self.device) if argmax else None
+        check(
+            lib().qwen3_prefill_all_logits(
+                self.handle,
+                seq,
+                toks.ctypes.data_as(C.POINTER(C.c_int32)),
+                n,
+                lg.data_ptr(),
+                am.data_ptr() if argmax else None,
+                _stream(),
+            )
+        )
+        return lg[:n], (am[:n] if argmax else None)
+
+    def truncate(self, keep_len: int, seq: int = 0):
+        """Rewind `seq` to its first keep_len positions (no-op at or above its length)."""
+        check(lib().qwen3_truncate(self.handle, seq, int(keep_len), _stream()))
+
     def decode_step(self, seq: int = 0, token: torch.Tensor | None = None, logits: bool = True):
         """One decode step fed `token` (device int32 [1]); defaults to the
         sequence's own previous argmax buffer (a device-resident greedy loop)."""
