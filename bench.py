@@ -33,7 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic.json")
 # the one-launch decode kernel and the headers it includes
 PERSISTENT_SRC = [os.path.join(ROOT, "quantized_q8_dequant_amd", "csrc", f)
-                  for f in ("k_decode_persistent.hip", "kernels.h", "qdevice.h")]
+                  for f in ("k_decode_persistent.hip", "persist.h", "qdevice.h")]
 INT8_PEAK_OPS = 5.0e15  # dense int8 MFMA
 KIND_NAMES = ["qkv_gemv", "attention", "o_proj_gemv", "gate_up_swiglu_gemv", "down_gemv", "lm_head_argmax_gemv"]
 

@@ -26,8 +26,17 @@
 // the two waves of a query head take the two halves of every staged tile and
 // merge their (max, sum, output) through LDS at the end, which doubles the
 // workgroups and halves the longest one.  Blocks are issued longest first.
+//
+// Few query blocks over a long cache (a short verify pass after a long
+// prompt, the last blocks of a causal prompt) leave the launch bound by its
+// longest workgroup; there the keys of a block are also cut across
+// workgroups into runs of whole 64-key tiles, each run leaves its
+// unnormalised (O, max, sum) per (token, head), and k_attn_merge combines the
+// runs in order, in f64.
 #include "kernels.h"
 #include "qdevice.h"
+
+#include <algorithm>
 
 using namespace q8;
 
@@ -139,11 +148,18 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int lq = lane % 16, lg = lane / 16;
+  // one-dimensional grid, head groups fastest, then the runs of a query
+  // block, then the blocks from the last (longest) to the first: workgroups
+  // are dispatched in about decreasing length, whatever the head count
+  const int ny = a.nkv * (G / HW);
+  const int gy = blockIdx.x % ny;
+  const int run = (blockIdx.x / ny) % a.nz;
+  const int qrev = blockIdx.x / ny / a.nz;
   const int hb_per_g = G / HW;
-  const int g = blockIdx.y / hb_per_g, hb = blockIdx.y % hb_per_g;
+  const int g = gy / hb_per_g, hb = gy % hb_per_g;
   const int h = g * G + hb * HW + (wave % HW);
   const int kpar = (wave / HW) % KS;  // which part of every tile this wave takes
-  const int t0 = (gridDim.x - 1 - blockIdx.x) * QT;  // longest blocks first
+  const int t0 = (a.nqb - 1 - qrev) * QT;
   const int tw0 = t0 + (wave / (HW * KS)) * 16;       // first token of this wavefront
   const int T = a.T;
 
@@ -158,7 +174,13 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   const int64_t head_elems = (int64_t)a.cap * HD;
   const int64_t kb0 = a.kbase + (int64_t)g * head_elems;
   const int64_t vb0 = kb0 + (int64_t)a.nkv * head_elems;
-  const int kend = a.pos0 + min(T, t0 + QT);  // keys [0, kend) matter for this workgroup
+  const int kend = a.pos0 + min(T, t0 + QT);  // keys [0, kend) matter for this block
+  // this workgroup's run of key tiles: [k_lo, k_hi) (the whole range unsplit)
+  const int ntq = (kend + KT - 1) / KT;
+  const int ns = a.tps > 0 ? (ntq + a.tps - 1) / a.tps : 1;
+  if (run >= ns) return;  // uniform per workgroup, before any barrier
+  const int k_lo = a.tps > 0 ? run * a.tps * KT : 0;
+  const int k_hi = a.tps > 0 ? min(kend, k_lo + a.tps * KT) : kend;
 
   v4d o[NDT];
 #pragma unroll
@@ -168,11 +190,11 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   // the next tile's loads are issued right after the current tile is
   // staged, so they land while the current tile is used
   KVTile<HD, BF16> tile;
-  tile.load(a.kv, kb0, vb0, 0, kend);
-  for (int kbase = 0; kbase < kend; kbase += KT) {
+  tile.load(a.kv, kb0, vb0, k_lo, kend);
+  for (int kbase = k_lo; kbase < k_hi; kbase += KT) {
     __syncthreads();
     tile.store(sK, KROW, sV, VROW);
-    tile.load(a.kv, kb0, vb0, kbase + KT < kend ? kbase + KT : kbase, kend);
+    tile.load(a.kv, kb0, vb0, kbase + KT < k_hi ? kbase + KT : kbase, kend);
     __syncthreads();
 
     // scores S^T for the sub-tiles of 16 keys of this wave's part; lane holds
@@ -231,6 +253,9 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
     }
   }
 
+  // a query row whose keys all lie past its position (possible in a later
+  // run) keeps m = -inf, l = 0, O = 0: it contributes nothing below
+  const bool owner = KS == 1 || kpar == 0;  // the wave that holds the merged state
   if (KS == 2) {
     // merge the two halves: the second-half wave of each (head, token tile)
     // leaves (m, l, O) in LDS, the first-half wave rescales and adds
@@ -248,38 +273,133 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
       my[NDT * 4 + 1] = l_run;
     }
     __syncthreads();
-    if (kpar == 1) return;
-    const double m1 = my[NDT * 4], l1 = my[NDT * 4 + 1];
-    const double mx = fmax(m_run, m1);
-    const double a0 = (m_run == -INFINITY) ? 0.0 : exp(m_run - mx);
-    const double a1 = (m1 == -INFINITY) ? 0.0 : exp(m1 - mx);
-    l_run = l_run * a0 + l1 * a1;
+    if (owner) {
+      const double m1 = my[NDT * 4], l1 = my[NDT * 4 + 1];
+      const double mx = fmax(m_run, m1);
+      const double a0 = (m_run == -INFINITY) ? 0.0 : exp(m_run - mx);
+      const double a1 = (m1 == -INFINITY) ? 0.0 : exp(m1 - mx);
+      l_run = l_run * a0 + l1 * a1;
+      m_run = mx;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) o[dt][it] = o[dt][it] * a0 + my[4 * dt + it] * a1;
+        for (int it = 0; it < 4; ++it) o[dt][it] = o[dt][it] * a0 + my[4 * dt + it] * a1;
+    }
   }
 
   // O^T layout: lane (lg, lq) holds d = 16*dt + 4*item + lg of query lq
   const int tout = tw0 + lq;
-  if (tout < T) {
-    float* orow = a.out + (int64_t)tout * a.nh * HD + (int64_t)h * HD;
+  if (ns == 1) {
+    if (owner && tout < T) {
+      float* orow = a.out + (int64_t)tout * a.nh * HD + (int64_t)h * HD;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) orow[16 * dt + 4 * it + lg] = (float)(o[dt][it] / l_run);
+    }
+    return;
+  }
+
+  // key-split block: this run's unnormalised (O, m, l), merged by k_attn_merge
+  constexpr int PS = HD + 2;
+  if (owner && tout < T) {
+    double* pr = a.part + ((int64_t)run * T * a.nh + (int64_t)tout * a.nh + h) * PS;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int it = 0; it < 4; ++it) orow[16 * dt + 4 * it + lg] = (float)(o[dt][it] / l_run);
+      for (int it = 0; it < 4; ++it) pr[16 * dt + 4 * it + lg] = o[dt][it];
+    if (lg == 0) pr[HD] = m_run, pr[HD + 1] = l_run;
   }
 }
 
+// Merge of the key-split runs: one workgroup per (token, head), one thread
+// per output dimension.  The runs combine in run order (f64): with M the
+// largest run maximum, O = sum_r exp(m_r - M) O_r and l = sum_r exp(m_r - M)
+// l_r, and the output O / l is rounded once to f32.  Tokens of blocks that
+// were not split were written by the attention kernel itself.
+template <int HD>
+__global__ void __launch_bounds__(HD) k_attn_merge(AttnPrefillArgs a, int QT) {
+  constexpr int PS = HD + 2;
+  const int t = blockIdx.x / a.nh, h = blockIdx.x % a.nh, d = threadIdx.x;
+  const int kend = a.pos0 + min(a.T, (t / QT + 1) * QT);
+  const int ns = ((kend + KT - 1) / KT + a.tps - 1) / a.tps;
+  if (ns <= 1) return;
+  const int64_t rstride = (int64_t)a.T * a.nh * PS;
+  const double* pb = a.part + ((int64_t)t * a.nh + h) * PS;
+  double M = -INFINITY;
+  for (int r = 0; r < ns; ++r) M = fmax(M, pb[r * rstride + HD]);
+  double O = 0.0, L = 0.0;
+  for (int r = 0; r < ns; ++r) {
+    const double* pr = pb + r * rstride;
+    const double mr = pr[HD];
+    const double w = (mr == -INFINITY) ? 0.0 : exp(mr - M);
+    L += w * pr[HD + 1];
+    O += w * pr[d];
+  }
+  a.out[(int64_t)t * a.nh * HD + (int64_t)h * HD + d] = (float)(O / L);
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// Tiles per run of the key split.  Only launches whose unsplit grid leaves
+// at least half of the CUs idle are split (measured on a 512-token prompt,
+// 256 workgroups: splitting its long blocks made the launch slower).  One
+// workgroup fills a CU, so a launch takes about max(longest run, total tiles
+// / CUs) tile times; a split adds the merge (counted as one tile time).  The
+// largest power of two that minimises that estimate, within the scratch for
+// the runs' partials; 0 when not splitting is as good.
+template <int HD, int QT>
+int pick_tps(const AttnPrefillArgs& a, int ny) {
+  if (!a.part) return 0;
+  const int nqb = (a.T + QT - 1) / QT;
+  if ((int64_t)nqb * ny * 2 > cu_count()) return 0;
+  const int ntmax = (a.pos0 + a.T + KT - 1) / KT;
+  int64_t total = 0;
+  for (int q = 0; q < nqb; ++q) total += (a.pos0 + std::min(a.T, (q + 1) * QT) + KT - 1) / KT;
+  total *= ny;
+  const int cus = cu_count();
+  auto est = [&](int64_t longest) { return std::max<int64_t>(longest, (total + cus - 1) / cus); };
+  const int64_t plane = (int64_t)a.T * a.nh * (HD + 2) * 8;  // bytes of one run's partials
+  int best = 0;
+  int64_t best_t = est(ntmax);
+  for (int tps = 1; tps < ntmax; tps *= 2) {
+    const int64_t ns_max = (ntmax + tps - 1) / tps;
+    if (ns_max * plane > (int64_t)a.part_bytes) continue;
+    const int64_t t = est(tps) + 1;
+    if (t <= best_t) best = tps, best_t = t;
+  }
+  return best;
+}
+
 template <int HD, int G, int KS>
-hipError_t launch_attn_ks(const AttnPrefillArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_attn_ks(const AttnPrefillArgs& a0, bool bf16, hipStream_t s) {
   constexpr int HW = G < 4 ? G : 4;
   constexpr int QT = 16 * (4 / (HW * KS));
-  const dim3 grid((a.T + QT - 1) / QT, a.nkv * (G / HW));
+  const int ny = a0.nkv * (G / HW);
+  AttnPrefillArgs a = a0;
+  a.tps = pick_tps<HD, QT>(a0, ny);
+  const int ntmax = (a.pos0 + a.T + KT - 1) / KT;
+  a.nz = a.tps > 0 ? (ntmax + a.tps - 1) / a.tps : 1;
+  a.nqb = (a.T + QT - 1) / QT;
+  const int64_t nwg = (int64_t)a.nqb * a.nz * ny;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg);
   if (bf16)
     hipLaunchKernelGGL((k_attn_prefill<HD, G, true, KS>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((k_attn_prefill<HD, G, false, KS>), grid, dim3(256), 0, s, a);
+  if (a.tps > 0) hipLaunchKernelGGL((k_attn_merge<HD>), dim3((unsigned)(a.T * a.nh)), dim3(HD), 0, s, a, QT);
   return hipGetLastError();
 }
 

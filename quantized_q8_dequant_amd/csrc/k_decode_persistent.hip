@@ -26,7 +26,7 @@
 // Every wait is bounded: after a spin limit the workgroup sets an error word
 // and leaves, the others see the word and leave too, and the step's argmax
 // is -1.  The grid must be co-resident (the host checks occupancy).
-#include "kernels.h"
+#include "persist.h"
 #include "qdevice.h"
 
 using namespace q8;

@@ -217,22 +217,30 @@ hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int 
 
 // Greedy pick of every row of f32 logits [T, V] ("A transformer from
 // scratch", section 12.6: the argmax over the vocabulary; among equal maxima
-// the lowest index, as in the other argmax epilogues).
-// One workgroup per row; each lane scans a strided slice in ascending order,
-// then the (value, index) pairs are reduced across the lanes.
+// the lowest index, as in the other argmax epilogues).  Grid (slices, T):
+// each workgroup scans one slice of a row (lanes in ascending strided order,
+// then a (value, index) reduction), folds its best into the row's 64-bit key
+// with an atomic max (order-preserving value bits above, inverted index
+// below), and the last workgroup of the row writes the index and clears the
+// key and counter for the next launch.
+constexpr int kArgmaxSlice = 4096;  // logits per workgroup
+
 __device__ __forceinline__ void argmax_take(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) bv = v, bi = i;
 }
 
-__global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x, int V, int32_t* __restrict__ out) {
+__global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x, int V, int32_t* __restrict__ out,
+                                                     unsigned long long* key, unsigned* counter) {
   __shared__ float s_v[256 / kWave];
   __shared__ int s_i[256 / kWave];
-  const float* xr = x + (int64_t)blockIdx.x * V;
+  const int row = blockIdx.y;
+  const float* xr = x + (int64_t)row * V;
+  const int c0 = blockIdx.x * kArgmaxSlice, c1 = min(V, c0 + kArgmaxSlice);
   float bv = -__builtin_inff();
   int bi = 0x7FFFFFFF;
   if ((V & 3) == 0) {
     const float4* x4 = reinterpret_cast<const float4*>(xr);
-    for (int c = threadIdx.x; c < V / 4; c += 256) {
+    for (int c = c0 / 4 + threadIdx.x; c < c1 / 4; c += 256) {
       const float4 t = x4[c];
       argmax_take(bv, bi, t.x, 4 * c);
       argmax_take(bv, bi, t.y, 4 * c + 1);
@@ -240,7 +248,7 @@ __global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x
       argmax_take(bv, bi, t.w, 4 * c + 3);
     }
   } else {
-    for (int c = threadIdx.x; c < V; c += 256) argmax_take(bv, bi, xr[c], c);
+    for (int c = c0 + threadIdx.x; c < c1; c += 256) argmax_take(bv, bi, xr[c], c);
   }
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {
@@ -253,7 +261,19 @@ __global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < 256 / kWave; ++w) argmax_take(bv, bi, s_v[w], s_i[w]);
-    out[blockIdx.x] = bi;
+    const uint32_t u = __float_as_uint(bv + 0.0f);  // -0 -> +0
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const unsigned long long k = ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (uint32_t)bi);
+    __hip_atomic_fetch_max(key + row, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_memory();
+    const unsigned prev = arrive(counter + row);
+    if (prev == gridDim.x - 1) {  // last workgroup of this row
+      const unsigned long long best =
+          __hip_atomic_fetch_add(key + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      out[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+      st_coherent(key + row, 0ull);
+      st_coherent(counter + row, 0u);
+    }
   }
 }
 
@@ -264,10 +284,12 @@ hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float e
   return hipGetLastError();
 }
 
-hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, hipStream_t s) {
+hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, unsigned long long* key, unsigned* counter,
+                       hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (V <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_rows_argmax, dim3(T), dim3(256), 0, s, x, V, out);
+  const dim3 grid((unsigned)((V + kArgmaxSlice - 1) / kArgmaxSlice), (unsigned)T);
+  hipLaunchKernelGGL(k_rows_argmax, grid, dim3(256), 0, s, x, V, out, key, counter);
   return hipGetLastError();
 }
 

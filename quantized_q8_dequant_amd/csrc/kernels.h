@@ -79,8 +79,10 @@ bool attn_decode_supported(int hd, int group);
 int attn_decode_max_ctx(int group);  // longest context (cache capacity) the decode attention takes
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
 
-// Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T].
-hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, hipStream_t s);
+// Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T];
+// key [T] and counter [T] are zero between launches (and left so).
+hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, unsigned long long* key, unsigned* counter,
+                       hipStream_t s);
 hipError_t set_len(int32_t* len, int seq, int value, hipStream_t s);
 
 }  // namespace q8k
@@ -129,6 +131,14 @@ struct AttnPrefillArgs {
   int nh, nkv;
   double scale;  // 1/sqrt(hd)
   float* out;  // [T][nh*hd]
+  // key split across workgroups (tps = 0: none): a query block's keys are cut
+  // into runs of tps 64-key tiles, one workgroup each; every run leaves
+  // (o, m, l) per (token, head) in part [nsplit][T][nh][hd + 2], merged by a
+  // second kernel
+  int tps;
+  double* part;
+  size_t part_bytes;
+  int nz, nqb;  // set at launch: runs per block (1 unsplit), query blocks
 };
 
 // Linear with bf16 weights (see k_gemm_bf16.hip): C[M, N] = X . W^T.
@@ -159,44 +169,4 @@ hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf1
 bool attn_prefill_supported(int hd, int group);
 }  // namespace q8k
 
-// One-launch decode step (see k_decode_persistent.hip).
-constexpr int kPersistWorkgroups = 256;
-struct PLayer {  // a layer's repacked weights
-  const int8_t *qkv_qs, *o_qs, *gu_qs, *dn_qs;
-  const uint16_t *qkv_sc, *o_sc, *gu_sc, *dn_sc;
-  const float *attn_norm, *q_norm, *k_norm, *ffn_norm;
-};
-struct PersistArgs {
-  const PLayer* layers;  // device [L]
-  int L, V;
-  float eps;
-  double scale;  // 1/sqrt(hd)
-  const int8_t* emb_qs;
-  const uint16_t* emb_sc;
-  const float* out_norm;
-  const double *rope_cos, *rope_sin;
-  void* kv;
-  const int64_t* seq_base;
-  const int32_t* seq_cap;
-  int32_t* len;
-  int seq;
-  const int32_t* token;  // device [1]
-  float* logits;         // [V] or null
-  int32_t* argmax;       // [1]
-  unsigned long long *xa, *xc, *qkv, *att, *h;  // (value, epoch) words
-  // attention partials of every split as (32-bit half, epoch) words:
-  // [nkv][splits per KV head][G][hd + 2 (o..., m, l)][2 (low, high half)]
-  unsigned long long* part;
-  unsigned long long* best_key;
-  unsigned* am_cnt;
-  unsigned* err;         // set on a timed-out wait
-  unsigned pstep;        // launch counter (epochs)
-};
-struct PersistShape {
-  int H, QW, F, HD, G;
-};
-namespace q8k {
-int persist_max_ctx(const PersistShape& sh);  // 0: no persistent step for this shape
-int persist_occupancy(const PersistShape& sh, bool kv_bf16);
-hipError_t decode_persistent(const PersistShape& sh, bool kv_bf16, const PersistArgs& a, hipStream_t s);
-}  // namespace q8k
+#include "persist.h"

@@ -122,7 +122,7 @@ struct qwen3_model {
   float* q32 = nullptr;
   float* xn = nullptr;  // normalised rows (bf16-weight models: the norm is not fused)
   double* attn_part = nullptr;
-  double* gemm_part = nullptr;  // split-K planes of the prefill GEMM
+  double* gemm_part = nullptr;  // split-K planes of the prefill GEMM; key-split attention partials
   size_t gemm_part_bytes = 0;
   unsigned* attn_cnt = nullptr;
   unsigned long long* am_key = nullptr;
@@ -152,7 +152,8 @@ namespace {
 size_t persist_part_words(int64_t G, int64_t hd) { return (size_t)kPersistWorkgroups * G * (hd + 2) * 2; }
 
 // Split-K planes of the prefill GEMM (f64 sums of K slices): enough for eight
-// slices of a 1024 x 1024 output.
+// slices of a 1024 x 1024 output.  The key-split runs of prefill attention
+// use the same scratch (the two never overlap on the stream).
 constexpr size_t kGemmPartBytes = (size_t)64 << 20;
 
 int validate(const qwen3_config* c) {
@@ -266,10 +267,8 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   const int64_t needed = decode_splits_needed(m->max_cap, (int)G);
   const int64_t slots = std::max<int64_t>(1024 + R * nkv, R * nkv * needed);
   m->attn_part = cv.arr<double>((size_t)slots * G * (hd + 2));
-  if (!m->wbf16) {
-    m->gemm_part_bytes = kGemmPartBytes;
-    m->gemm_part = cv.arr<double>(kGemmPartBytes / 8);
-  }
+  m->gemm_part_bytes = kGemmPartBytes;
+  m->gemm_part = cv.arr<double>(kGemmPartBytes / 8);
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
@@ -538,6 +537,8 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     ap.nkv = m->nkv;
     ap.scale = 1.0 / std::sqrt((double)m->hd);
     ap.out = m->attn;
+    ap.part = m->gemm_part;
+    ap.part_bytes = m->gemm_part_bytes;
     HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvbf16, s));
     if (m->wbf16) {
       const int64_t H = m->H;
@@ -573,7 +574,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
       g.qs = m->emb.qs, g.sc = m->emb.sc, g.N = m->V, g.K = m->H, g.out = d_logits, g.ldc = m->V;
       HIP_TRY(q8k::gemm(g, EPI_STORE, s));
     }
-    if (d_argmax) HIP_TRY(q8k::rows_argmax(d_logits, T, m->V, d_argmax, s));
+    if (d_argmax) HIP_TRY(q8k::rows_argmax(d_logits, T, m->V, d_argmax, m->am_key, m->am_cnt, s));
   } else if (last && (d_logits || d_argmax) && m->wbf16) {
     const int64_t H = m->H;
     HIP_TRY(q8k::rows_norm(m->x + (int64_t)(T - 1) * H, H, 1, m->H, m->out_norm, eps, m->xn, H, s));

@@ -172,6 +172,37 @@ def test_tiny_truncate_edge_cases(tiny_w):
     assert gpu.kv_len() == 14
 
 
+# Long contexts on the tiny model: the attention of a block whose keys span
+# several 64-key tiles is cut into runs across workgroups and merged by the
+# last run; group sizes 1, 2 and 4 (head layouts of the three kernel shapes),
+# f32 and bf16 caches.
+LONG_SHAPES = {
+    "g2": TINY,
+    "g4": TINY.with_(name="tiny-g4", num_attention_heads=8, num_key_value_heads=2),
+    "g1": TINY.with_(name="tiny-g1", num_attention_heads=4, num_key_value_heads=4),
+    "g2-bf16kv": TINY.with_(name="tiny-bf16kv", kv_type="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(LONG_SHAPES))
+def test_tiny_long_context_all_logits_and_verify(name):
+    shape = LONG_SHAPES[name]
+    w = gen_weights(shape, 103)
+    ref_model = om.Model(shape, w)
+    prompt = gen_prompt(shape.vocab_size, 300, 81)  # 18 blocks of 16 + a ragged 12
+    draft = gen_prompt(shape.vocab_size, 12, 82)
+    gpu = make(shape, w, [340], max_batch_tokens=320)
+    lg_p, am_p = gpu.prefill_all_logits(prompt)
+    lg_v, am_v = gpu.prefill_all_logits(draft)
+    cache = ref_model.new_cache(340)
+    check_rows(lg_p.cpu().numpy(), am_p.cpu().numpy(), ref_model.forward(prompt, cache, all_logits=True))
+    check_rows(lg_v.cpu().numpy(), am_v.cpu().numpy(), ref_model.forward(draft, cache, all_logits=True))
+    # the same prompt in 48-row chunks: later chunks attend 64-key tiles of earlier ones
+    chunked = make(shape, w, [340], max_batch_tokens=48)
+    lg_c, _ = chunked.prefill(prompt)
+    assert row_errs(lg_c.cpu().numpy()[None], lg_p[-1:].cpu().numpy()).max() <= TOL
+
+
 TINY_BF16 = TINY.with_(name="tiny-bf16", weight_type="bf16", kv_type="bf16")
 
 
