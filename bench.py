@@ -313,6 +313,43 @@ def bench_verify(model, prompt, shape, decode_ms_per_token: float, args) -> dict
     }
 
 
+BATCH_SIZES = (16, 64)
+
+
+def bench_batched(shape, weights, prompt, args) -> dict:
+    """Lockstep batched greedy decode (one token for each of n streams per
+    step) at KV length len(prompt), every stream prefilled with the prompt."""
+    import torch
+
+    from quantized_q8_dequant_amd import Qwen3Config, Qwen3Model
+
+    nmax = max(BATCH_SIZES)
+    P = len(prompt)
+    steps = 8
+    model = Qwen3Model(Qwen3Config.from_shape(shape), weights, [P + steps * (args.warmup + args.steps + 1) + 1] * nmax)
+    for s in range(nmax):
+        model.prefill(prompt, seq=s, logits=False)
+    out = {}
+    for n in BATCH_SIZES:
+        seqs = list(range(n))
+        am = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+
+        def run():
+            for _ in range(steps):
+                model.decode_batch(seqs, am, None, am)
+
+        ms = event_ms(run, args.warmup, args.steps) / steps
+        for s in seqs:
+            model.truncate(P, seq=s)
+        out[str(n)] = {
+            "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(n * 1000.0 / ms, 1),
+            "weight_GBps": round(weight_bytes(shape) / (ms / 1000.0) / 1e9, 1),
+        }
+    model.close()
+    return out
+
+
 def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
     """The CPU oracle on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_info
@@ -494,6 +531,11 @@ def main() -> int:
         del model
         torch.cuda.empty_cache()
 
+    batched = None
+    if args.workload == "0.6b-decode":
+        batched = bench_batched(shape, weights, prompt, args)
+        torch.cuda.empty_cache()
+
     if args.pmc_calibrate:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
@@ -539,6 +581,7 @@ def main() -> int:
         "kernels_at_mean_ctx": kernels,
         "prefill_4096_one_call": p4,
         "verify": verify,
+        "batched_decode": batched,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -230,7 +230,8 @@ __device__ __forceinline__ void argmax_take(float& bv, int& bi, float v, int i) 
 }
 
 __global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x, int V, int32_t* __restrict__ out,
-                                                     unsigned long long* key, unsigned* counter) {
+                                                     unsigned long long* key, unsigned* counter, int32_t* len,
+                                                     const int32_t* row_seq, int len_add) {
   __shared__ float s_v[256 / kWave];
   __shared__ int s_i[256 / kWave];
   const int row = blockIdx.y;
@@ -273,6 +274,7 @@ __global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x
       out[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
       st_coherent(key + row, 0ull);
       st_coherent(counter + row, 0u);
+      if (len) len[row_seq ? row_seq[row] : row] += len_add;  // the step's row is in the cache
     }
   }
 }
@@ -285,11 +287,11 @@ hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float e
 }
 
 hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, unsigned long long* key, unsigned* counter,
-                       hipStream_t s) {
+                       hipStream_t s, int32_t* len, const int32_t* row_seq, int len_add) {
   if (T == 0) return hipSuccess;
   if (V <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((V + kArgmaxSlice - 1) / kArgmaxSlice), (unsigned)T);
-  hipLaunchKernelGGL(k_rows_argmax, grid, dim3(256), 0, s, x, V, out, key, counter);
+  hipLaunchKernelGGL(k_rows_argmax, grid, dim3(256), 0, s, x, V, out, key, counter, len, row_seq, len_add);
   return hipGetLastError();
 }
 

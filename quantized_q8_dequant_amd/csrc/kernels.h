@@ -80,9 +80,10 @@ int attn_decode_max_ctx(int group);  // longest context (cache capacity) the dec
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
 
 // Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T];
-// key [T] and counter [T] are zero between launches (and left so).
+// key [T] and counter [T] are zero between launches (and left so).  With
+// len: len[row_seq[r]] (row_seq null: len[r]) += len_add once row r is done.
 hipError_t rows_argmax(const float* x, int T, int V, int32_t* out, unsigned long long* key, unsigned* counter,
-                       hipStream_t s);
+                       hipStream_t s, int32_t* len = nullptr, const int32_t* row_seq = nullptr, int len_add = 0);
 hipError_t set_len(int32_t* len, int seq, int value, hipStream_t s);
 
 }  // namespace q8k
@@ -161,6 +162,11 @@ struct GemmBf16Args {
 
 namespace q8k {
 hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s);
+// Small-M form (see k_gemm_skinny.hip): M <= kSkinnyMaxRows, K % 128 == 0;
+// STORE, RESIDUAL, SWIGLU; no scratch.
+constexpr int kSkinnyMaxRows = 64;
+bool gemm_skinny_supported(int M, int K);
+hipError_t gemm_skinny(const GemmArgs& a, int epi, hipStream_t s);
 hipError_t gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 hipError_t rows_norm(const float* x, int64_t ldx, int T, int K, const float* w, float eps, float* y, int64_t ldy,
                      hipStream_t s);

@@ -123,6 +123,7 @@ struct qwen3_model {
   float* xn = nullptr;  // normalised rows (bf16-weight models: the norm is not fused)
   double* attn_part = nullptr;
   double* gemm_part = nullptr;  // split-K planes of the prefill GEMM; key-split attention partials
+  float* blogits = nullptr;     // [kSkinnyMaxRows][V] logits of a batched step called without a logits buffer
   size_t gemm_part_bytes = 0;
   unsigned* attn_cnt = nullptr;
   unsigned long long* am_key = nullptr;
@@ -269,6 +270,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->attn_part = cv.arr<double>((size_t)slots * G * (hd + 2));
   m->gemm_part_bytes = kGemmPartBytes;
   m->gemm_part = cv.arr<double>(kGemmPartBytes / 8);
+  if (!m->wbf16) m->blogits = cv.arr<float>((size_t)std::min<int64_t>(R, q8k::kSkinnyMaxRows) * V);
   m->attn_cnt = cv.arr<unsigned>(R * nkv);
   m->am_key = cv.arr<unsigned long long>(R);
   m->am_cnt = cv.arr<unsigned>(R);
@@ -392,6 +394,18 @@ AttnDecodeArgs attn_args(const qwen3_model* m, const int32_t* d_row_seq, int nro
   return at;
 }
 
+// Batched decode steps of at least this many rows take the small-M GEMM
+// (measured on the 0.6B shape at KV length 512: from 16 rows on it beats
+// the per-row GEMV, which re-reads the weights for every row).
+constexpr int kSkinnyMinBatch = 16;
+
+// Q8_0 weights and rows the small-M GEMM takes (every K of the model a
+// multiple of 128).
+bool skinny_rows(const qwen3_model* m, int rows) {
+  return !m->wbf16 && rows <= q8k::kSkinnyMaxRows && q8k::gemm_skinny_supported(rows, m->H) &&
+         q8k::gemm_skinny_supported(rows, m->qw) && q8k::gemm_skinny_supported(rows, m->F);
+}
+
 // Kernels of one decode step.  kind: 0 QKV GEMV, 1 attention, 2 o_proj,
 // 3 gate/up SwiGLU, 4 down, 5 lm_head + argmax (len_add advances lengths).
 int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32_t* d_row_seq, float* d_logits,
@@ -433,6 +447,50 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
         return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind");
     }
     return QWEN3_OK;
+  }
+  if (nrows >= kSkinnyMinBatch && skinny_rows(m, nrows)) {
+    // a batch of streams: quantise the rows once, one small-M GEMM pass over
+    // each weight matrix for all of them (smaller batches: the per-row GEMV,
+    // whose fused norm/quantise prologue saves the separate launches)
+    const int64_t H = m->H;
+    GemmArgs g{};
+    g.qa = m->qa, g.da = m->da, g.M = nrows;
+    auto run = [&](const QPlane& p, int K, float* out, int64_t ldc, int epi) {
+      g.qs = p.qs, g.sc = p.sc, g.N = (int)p.rows, g.K = K, g.out = out, g.ldc = ldc;
+      return q8k::gemm_skinny(g, epi, s);
+    };
+    if (kind == 5) {
+      float* lg = d_logits ? d_logits : m->blogits;
+      HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s));
+      HIP_TRY(run(m->emb, m->H, lg, m->V, EPI_STORE));
+      HIP_TRY(q8k::rows_argmax(lg, nrows, m->V, d_argmax, m->am_key, m->am_cnt, s, len_add ? m->d_len : nullptr,
+                               d_row_seq, len_add));
+      return QWEN3_OK;
+    }
+    if (kind != 1) {
+      const Layer& ly = m->layers[l];
+      switch (kind) {
+        case 0:
+          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(run(ly.qkv, m->H, m->qkv, m->nqkv, EPI_STORE));
+          break;
+        case 2:
+          HIP_TRY(q8k::rows_quant(m->attn, nrows, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(run(ly.o, m->qw, m->x, H, EPI_RESIDUAL));
+          break;
+        case 3:
+          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(run(ly.gateup, m->H, m->h, m->F, EPI_SWIGLU));
+          break;
+        case 4:
+          HIP_TRY(q8k::rows_quant(m->h, nrows, m->F, nullptr, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(run(ly.down, m->F, m->x, H, EPI_RESIDUAL));
+          break;
+        default:
+          return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind");
+      }
+      return QWEN3_OK;
+    }
   }
   if (kind == 5) {
     GemvArgs a = gemv_args(m->emb, m->x, m->H, m->out_norm, eps, nullptr, 0);
@@ -490,6 +548,11 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
 int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, float* d_logits, int32_t* d_argmax,
                           hipStream_t s, bool all_rows = false) {
   const float eps = m->cfg.rms_norm_eps;
+  // projections: the small-M GEMM for short chunks (no split-K pass), else the tiled one
+  const bool small = skinny_rows(m, T);
+  auto gemm = [&](const GemmArgs& g, int epi, hipStream_t st) {
+    return small ? q8k::gemm_skinny(g, epi, st) : q8k::gemm(g, epi, st);
+  };
   HIP_TRY(q8k::embed(m->d_tok, T, m->V, m->H, plane_rows(m->emb), m->emb.sc, m->wbf16, m->x, s));
   const int64_t head_elems = (int64_t)m->cap[seq] * m->hd;
   for (int l = 0; l < m->L; ++l) {
@@ -508,7 +571,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     } else {
       HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
       g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
-      HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+      HIP_TRY(gemm(g, EPI_STORE, s));
     }
     QkRopeArgs qr{};
     qr.qkv = m->qkv;
@@ -551,14 +614,14 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     // o_proj + residual
     HIP_TRY(q8k::rows_quant(m->attn, T, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
     g.qs = ly.o.qs, g.sc = ly.o.sc, g.N = (int)ly.o.rows, g.K = m->qw, g.out = m->x, g.ldc = m->H;
-    HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
+    HIP_TRY(gemm(g, EPI_RESIDUAL, s));
     // FFN: RMSNorm + quantise, gate/up with SwiGLU, quantise, down + residual
     HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s));
     g.qs = ly.gateup.qs, g.sc = ly.gateup.sc, g.N = (int)ly.gateup.rows, g.K = m->H, g.out = m->h, g.ldc = m->F;
-    HIP_TRY(q8k::gemm(g, EPI_SWIGLU, s));
+    HIP_TRY(gemm(g, EPI_SWIGLU, s));
     HIP_TRY(q8k::rows_quant(m->h, T, m->F, nullptr, eps, m->qa, m->da, nullptr, s));
     g.qs = ly.down.qs, g.sc = ly.down.sc, g.N = (int)ly.down.rows, g.K = m->F, g.out = m->x, g.ldc = m->H;
-    HIP_TRY(q8k::gemm(g, EPI_RESIDUAL, s));
+    HIP_TRY(gemm(g, EPI_RESIDUAL, s));
   }
   if (all_rows) {
     // final RMSNorm + tied lm_head on all T rows as one GEMM, then the row argmax
@@ -572,7 +635,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
       g.qa = m->qa, g.da = m->da, g.M = T;
       g.part = m->gemm_part, g.part_bytes = m->gemm_part_bytes;
       g.qs = m->emb.qs, g.sc = m->emb.sc, g.N = m->V, g.K = m->H, g.out = d_logits, g.ldc = m->V;
-      HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+      HIP_TRY(skinny_rows(m, T) ? q8k::gemm_skinny(g, EPI_STORE, s) : q8k::gemm(g, EPI_STORE, s));
     }
     if (d_argmax) HIP_TRY(q8k::rows_argmax(d_logits, T, m->V, d_argmax, m->am_key, m->am_cnt, s));
   } else if (last && (d_logits || d_argmax) && m->wbf16) {
