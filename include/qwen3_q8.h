@@ -240,10 +240,10 @@ int qwen3_q8_0_repack(const void* d_blocks, int64_t rows, int64_t k, int8_t* d_q
                       uint16_t* d_scale, void* stream);
 
 /* The Q8_0 linear on repacked planes: y[t, :] = linear(x[t, :]) for t < m,
- * x f32 [m, k], y f32 [m, n].  m == 1 runs the decode GEMV kernel, m > 1 the
- * prefill GEMM kernel (the same kernels the model uses).  k % 128 == 0;
- * for m > 1 also n % 128 == 0.  d_work: scratch of qwen3_linear_work_bytes
- * (m, k) bytes. */
+ * x f32 [m, k], y f32 [m, n].  m == 1 runs the decode GEMV kernel, 2..64
+ * rows the small-M GEMM, more rows the prefill GEMM (the same kernels the
+ * model uses).  k % 128 == 0; for m > 64 also n % 128 == 0.  d_work:
+ * scratch of qwen3_linear_work_bytes(m, k) bytes. */
 size_t qwen3_linear_work_bytes(int64_t m, int64_t k);
 int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs,
                       const uint16_t* d_scale, int64_t n, float* d_y, void* d_work, void* stream);

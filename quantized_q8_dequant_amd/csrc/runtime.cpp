@@ -1059,6 +1059,7 @@ int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs
   int8_t* qa = static_cast<int8_t*>(d_work);
   float* da = reinterpret_cast<float*>(static_cast<uint8_t*>(d_work) + align_up((size_t)(m * k)));
   HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, qa, da, nullptr, s));
+  const bool small = q8k::gemm_skinny_supported((int)m, (int)k);
   GemmArgs g{};
   g.qa = qa;
   g.da = da;
@@ -1069,7 +1070,7 @@ int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs
   g.K = (int)k;
   g.out = d_y;
   g.ldc = n;
-  HIP_TRY(q8k::gemm(g, EPI_STORE, s));
+  HIP_TRY(small ? q8k::gemm_skinny(g, EPI_STORE, s) : q8k::gemm(g, EPI_STORE, s));
   return QWEN3_OK;
 }
 

@@ -92,7 +92,10 @@ def _linear_bound(x, ow):
     "m,k,n",
     [(1, 1024, 4096), (1, 3072, 1024), (1, 2048, 1024), (1, 256, 512), (1, 768, 256), (1, 4096, 384),
      (1, 12288, 256), (1, 4096, 4100), (1, 12288, 1400), (2, 1024, 256), (7, 1024, 256), (128, 1024, 512),
-     (300, 3072, 384), (129, 256, 128)],
+     (300, 3072, 384), (129, 256, 128),
+     # small-M GEMM: 16/32/64-row tilings, K slices of 4/8/16, ragged N, 64-row units
+     (16, 1024, 4096), (17, 2048, 1024), (33, 3072, 1000), (64, 4096, 520), (20, 12288, 256), (5, 768, 4100),
+     (32, 256, 65600), (64, 256, 96)],
 )
 def test_linear_matches_oracle(m, k, n):
     from quantized_q8_dequant_amd import q8_0_linear
