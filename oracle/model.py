@@ -44,10 +44,15 @@ class KVCache:
     section 13.4): every layer appends at the same base `len`; `advance(m)`
     runs once after all layers; `truncate(keep)` rewinds by lowering `len`;
     `reset()` sets len = 0.  kv_type "bf16" rounds rows to bf16 on store
-    (widened on read); "f32" stores them as they are.
+    (widened on read); "f32" stores them as they are; "q8_0" stores each
+    (position, head) row as head_dim/32 Q8_0 blocks ("A transformer from
+    scratch", section 12.4, the q8_0 option; "The LLM stack (fucina_llm)",
+    section 13.4), kept here as their exact dequantised values.
     """
 
     def __init__(self, num_layers: int, kv_heads: int, head_dim: int, capacity: int, kv_type: str = "f32"):
+        if kv_type == "q8_0" and head_dim % q8_0.QK:
+            raise ValueError("a q8_0 KV cache needs head_dim % 32 == 0")
         self.k = [np.zeros((capacity, kv_heads, head_dim), dtype=np.float32) for _ in range(num_layers)]
         self.v = [np.zeros((capacity, kv_heads, head_dim), dtype=np.float32) for _ in range(num_layers)]
         self.capacity = capacity
@@ -55,8 +60,7 @@ class KVCache:
         self.len = 0
 
     def _store(self, rows: np.ndarray) -> np.ndarray:
-        rows = np.asarray(rows, dtype=np.float32)
-        return ops.bf16_round(rows) if self.kv_type == "bf16" else rows
+        return kv_store(rows, self.kv_type)
 
     def append_layer(self, layer: int, k_rows: np.ndarray, v_rows: np.ndarray) -> None:
         T = k_rows.shape[0]
@@ -82,6 +86,32 @@ class KVCache:
 
     def v_slice(self, layer: int, n: int) -> np.ndarray:
         return self.v[layer][:n]
+
+
+def kv_store(rows: np.ndarray, kv_type: str) -> np.ndarray:
+    """K or V rows [..., head_dim] as the cache holds them (f32 values)."""
+    rows = np.asarray(rows, dtype=np.float32)
+    if kv_type == "bf16":
+        return ops.bf16_round(rows)
+    if kv_type == "q8_0":
+        return q8_0.decode(*q8_0.encode(rows))
+    return rows
+
+
+def attention_query(q: np.ndarray, kv_type: str) -> np.ndarray:
+    """The query as the attention scores use it.  With a q8_0 cache a
+    single-token step takes the integer score path: each head's query is
+    quantised per 32-block like an activation and dotted with the cached K
+    codes block by block, V dequantised as it is accumulated; a step of
+    several tokens (prefill, the all-logits verify) keeps the dequantising
+    path, its f32 query against the dequantised cache ("The LLM stack
+    (fucina_llm)", section 13.4, the q8_0 option).  Since sum_b d_q,b d_k,b
+    S_b is the dot of the two dequantised rows, the oracle uses the
+    dequantised query (exact in f32) with the dequantised keys.  q is
+    [T, heads, head_dim]; T == 1 is the single-token step."""
+    if kv_type == "q8_0" and q.shape[0] == 1:
+        return q8_0.decode(*q8_0.encode(q))
+    return q
 
 
 class Model:
@@ -187,6 +217,7 @@ class Model:
             q, k, v = self.qkv(layer, x, positions)
             cache.append_layer(layer, k, v)
             n = base + T
+            q = attention_query(q, cache.kv_type)
             o = ops.attention(q, cache.k_slice(layer, n), cache.v_slice(layer, n), positions)
             x = self.finish_layer(layer, x, o)
         cache.advance(T)
@@ -202,8 +233,8 @@ class Model:
         x = self.embed(tokens)
         for layer in range(self.shape.num_layers):
             q, k, v = self.qkv(layer, x, positions)
-            if self.shape.kv_type == "bf16":
-                k, v = ops.bf16_round(k), ops.bf16_round(v)
+            kvt = self.shape.kv_type
+            k, v, q = kv_store(k, kvt), kv_store(v, kvt), attention_query(q, kvt)
             o = ops.attention(q, k, v, positions, positions)
             x = self.finish_layer(layer, x, o)
         rows = x if all_logits else x[-1:]

@@ -198,3 +198,105 @@ def test_bf16_model_cached_equals_recompute():
     # bf16 cache rows really are bf16 values
     k = c.k[0][: c.len]
     assert np.all((k.view(np.uint32) & 0xFFFF) == 0)
+
+
+# ---- q8_0 KV cache ("The LLM stack (fucina_llm)", section 13.4; "A transformer
+# from scratch", section 12.4) ------------------------------------------------------
+
+TINY_Q8KV = TINY.with_(name="tiny-q8kv", kv_type="q8_0")
+
+
+def _q8_exact_rows(shape, seed):
+    """Rows that Q8_0 holds without loss: per 32-block an f16 scale d and int
+    codes in [-127, 127] with one code at +-127 (so max|x| / 127 == d)."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(-127, 128, size=shape).astype(np.int64)
+    codes.reshape(-1, 32)[:, 0] = 127
+    d = rng.uniform(0.01, 0.05, size=shape[:-1] + (shape[-1] // 32,)).astype(np.float16).astype(np.float32)
+    return (codes.reshape(shape[:-1] + (shape[-1] // 32, 32)) * d[..., None]).reshape(shape).astype(np.float32)
+
+
+def test_q8_kv_store_rounds_per_block():
+    c = om.KVCache(1, 2, 64, 8, "q8_0")
+    exact = _q8_exact_rows((3, 2, 64), 1)
+    c.append_layer(0, exact, exact)
+    assert np.array_equal(c.k[0][:3], exact)  # nothing lost for Q8_0-exact rows
+    rng = np.random.default_rng(2)
+    rows = rng.standard_normal((2, 2, 64)).astype(np.float32)
+    c.append_layer(0, rows, rows)  # overwrites rows 0..1 (len is still 0)
+    got = c.k[0][:2].reshape(-1, 32).astype(np.float64)
+    blocks = rows.reshape(-1, 32).astype(np.float64)
+    d = np.max(np.abs(blocks), axis=1) / 127.0
+    # per element within half a code step (plus the f16 rounding of d)
+    assert np.all(np.abs(got - blocks) <= (0.5 + 127 * 2.0**-11) * d[:, None] * (1 + 1e-6))
+    assert not np.array_equal(got, blocks)
+    with pytest.raises(ValueError):
+        om.KVCache(1, 2, 48, 8, "q8_0")  # head_dim must be whole 32-blocks
+
+
+def test_q8_kv_integer_scores_are_the_dequantised_dot():
+    """The integer score path (query quantised per 32-block, q8 x q8 block dots
+    scaled by d_q * d_k) equals the dot of the dequantised rows."""
+    from oracle import q8_0 as oq
+
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 128)).astype(np.float32)
+    keys = rng.standard_normal((40, 128)).astype(np.float32)
+    qa, dq = oq.encode(q)
+    kq, dk = oq.encode(keys)
+    S = oq.block_dots(qa, kq)[0].astype(np.float64)  # [40, 4]
+    integer = np.sum(S * dq.astype(np.float64)[0][None, :] * dk.astype(np.float64), axis=1)
+    deq = oq.decode(kq, dk).astype(np.float64) @ oq.decode(qa, dq).astype(np.float64)[0]
+    assert np.allclose(integer, deq, rtol=1e-13, atol=1e-13)
+    # and the quantised query is what attention_query hands to the scores
+    assert np.array_equal(om.attention_query(q.reshape(1, 1, 128), "q8_0").reshape(1, 128), oq.decode(qa, dq))
+
+
+def test_q8_kv_attention_equals_f32_on_lossless_rows():
+    """With queries, keys and values that Q8_0 holds exactly, a decode step over
+    a q8_0 cache is the f32 cache's step, and a multi-token step keeps its f32
+    query (the dequantising prefill path)."""
+    from oracle import ops
+
+    k = _q8_exact_rows((9, 2, 64), 4)
+    v = _q8_exact_rows((9, 2, 64), 5)
+    q1 = _q8_exact_rows((1, 4, 64), 6)
+    for kvt in ("f32", "q8_0"):
+        assert np.array_equal(om.kv_store(k, kvt), k)
+    assert np.array_equal(om.attention_query(q1, "q8_0"), q1)
+    qn = np.random.default_rng(7).standard_normal((3, 4, 64)).astype(np.float32)
+    assert np.array_equal(om.attention_query(qn, "q8_0"), qn)  # T > 1: unquantised
+    a = ops.attention(om.attention_query(q1, "q8_0"), om.kv_store(k, "q8_0"), om.kv_store(v, "q8_0"), [8])
+    b = ops.attention(q1, k, v, [8])
+    assert np.array_equal(a, b)
+
+
+def test_q8_kv_model_decode_steps_quantise_the_query():
+    """Model level: a q8_0-KV decode step equals attention over the dequantised
+    cache with the quantised query, and prefill logits stay within the Q8_0
+    loss of the f32-KV model (the cache differs, the tokens mostly do not)."""
+    w = gen_weights(TINY_Q8KV, 101)
+    m8 = om.Model(TINY_Q8KV, w)
+    m32 = om.Model(TINY, w)
+    toks = gen_prompt(TINY.vocab_size, 24, seed=9)
+    c8, c32 = m8.new_cache(32), m32.new_cache(32)
+    p8, p32 = m8.forward(toks, c8)[0], m32.forward(toks, c32)[0]
+    assert 0 < _rel(p8, p32) <= 0.03
+    # a single-token step: same as a step whose query is explicitly quantised
+    # and whose attention reads the stored (dequantised) rows
+    import copy
+
+    c8b = copy.deepcopy(c8)
+    tok = int(np.argmax(p8))
+    d8 = m8.forward([tok], c8)[0]
+    assert c8.len == 25 and np.all(np.isfinite(d8))
+    orig = om.attention_query
+    try:  # the same step with the query left unquantised differs
+        om.attention_query = lambda q, kvt: q
+        d8_plain = m8.forward([tok], c8b)[0]
+    finally:
+        om.attention_query = orig
+    assert 0 < _rel(d8, d8_plain) <= 0.03
+    # the cached K rows are Q8_0 round trips of the f32 model's K rows
+    k32 = c32.k[0][:24]
+    assert np.array_equal(c8.k[0][:24], om.kv_store(k32, "q8_0"))
