@@ -53,6 +53,15 @@ extern "C" {
 #define QWEN3_W_BF16 1 /* projections and embedding in bf16 */
 #define QWEN3_KV_F32 0
 #define QWEN3_KV_BF16 1
+/* Q8_0 KV cache ("The LLM stack (fucina_llm)", section 13.4, the q8_0 option;
+ * "A transformer from scratch", section 12.4): every (position, KV head) row
+ * is head_dim/32 Q8_0 blocks, held as an int8 code plane plus an f16 scale
+ * plane (1.0625 bytes per element).  A single-token step (decode, batched
+ * decode, a one-token prefill) scores with the query quantised per head (the
+ * integer score path); multi-token steps keep the f32 query against the
+ * dequantised cache.  Needs head_dim % 32 == 0; decode runs the per-kernel
+ * step (qwen3_decode_launches > 1). */
+#define QWEN3_KV_Q8_0 2
 
 /* Q8_0 block on the wire (Fucina course, "Model files and quantization",
  * section 11.7): the f16 bits of the scale d, then 32 signed bytes; 34 bytes,

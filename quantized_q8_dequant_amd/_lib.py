@@ -26,7 +26,7 @@ ERRORS = {
     -9: "QWEN3_E_DEVICE",
 }
 W_Q8_0, W_BF16 = 0, 1
-KV_F32, KV_BF16 = 0, 1
+KV_F32, KV_BF16, KV_Q8_0 = 0, 1, 2
 
 EXPORTS = (
     "qwen3_workspace_bytes",

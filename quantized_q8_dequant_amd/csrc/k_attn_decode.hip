@@ -29,9 +29,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-// cache rows per staged tile: 16 KB of K or V either way
-template <bool BF16>
-constexpr int kTileRows = BF16 ? 64 : 32;
+// cache rows per staged tile: 16 KB of f32 K or V, 16 KB of bf16, 8 KB of
+// Q8_0 codes
+template <int KVT>
+constexpr int kTileRows = KVT == KV_F32 ? 32 : 64;
 constexpr int kMaxSplit = 64;    // bound of nsplit_max
 constexpr int kScoreSlots = 4096;  // f64 scores a workgroup keeps: G heads x (4096 / G) rows
 constexpr int kLdsRow = 4;       // padding of a staged row (keeps rows 16-byte aligned)
@@ -40,38 +41,53 @@ constexpr int kCombineRegs = 80; // f64 partial values a thread of the combine h
 // One tile of K or V rows staged through registers: every thread issues all
 // of its 16-byte loads for a tile at once; two tiles are in flight ahead of
 // the one being used.
-template <int HD, bool BF16>
+template <int HD, int KVT>
 struct TileRegs {
-  static constexpr int TJ = kTileRows<BF16>;
-  static constexpr int PER_LOAD = BF16 ? 8 : 4;                   // elements per 16 bytes
-  static constexpr int LOADS = TJ * HD / PER_LOAD / kThreads;    // per thread
+  static constexpr int TJ = kTileRows<KVT>;
+  static constexpr int PER_LOAD = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 8 : 16);  // elements per 16 bytes
+  static constexpr int LOADS = TJ * HD / PER_LOAD / kThreads;                    // per thread
+  static_assert(LOADS >= 1 && LOADS * PER_LOAD * kThreads == TJ * HD, "tile map");
   v4i x[LOADS];
+  uint16_t sc[KVT == KV_Q8_0 ? LOADS : 1];  // Q8_0: the block scale of each 16-code load
 };
 
 // Every thread issues the same loads whatever the tile (rows past the end
 // re-read the tile's last row and are never used), so the compiler can keep
 // the older tile's loads in flight while waiting for the newer one.
-template <int HD, bool BF16>
-QDEV void tile_load(TileRegs<HD, BF16>& t, const void* kv, int64_t base, int row0, int nrow) {
-  constexpr int PER = TileRegs<HD, BF16>::PER_LOAD;
-  constexpr int ESZ = BF16 ? 2 : 4;
+template <int HD, int KVT>
+QDEV void tile_load(TileRegs<HD, KVT>& t, const void* kv, const uint16_t* kvs, int64_t base, int row0, int nrow) {
+  constexpr int PER = TileRegs<HD, KVT>::PER_LOAD;
+  constexpr int ESZ = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
 #pragma unroll
-  for (int i = 0; i < TileRegs<HD, BF16>::LOADS; ++i) {
+  for (int i = 0; i < TileRegs<HD, KVT>::LOADS; ++i) {
     const int e = (threadIdx.x + i * kThreads) * PER;  // element index in the tile
     const int r = min(e / HD, nrow - 1);
     const int64_t off = (int64_t)(row0 + r) * HD + (e % HD);
     t.x[i] = *reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(kv) + (base + off) * ESZ);
+    if (KVT == KV_Q8_0) t.sc[i] = kvs[(base + off) / 32];
   }
 }
 
-template <int HD, bool BF16>
-QDEV void tile_store(const TileRegs<HD, BF16>& t, float (*s_t)[HD + kLdsRow]) {
-  constexpr int PER = TileRegs<HD, BF16>::PER_LOAD;
+template <int HD, int KVT>
+QDEV void tile_store(const TileRegs<HD, KVT>& t, float (*s_t)[HD + kLdsRow]) {
+  constexpr int PER = TileRegs<HD, KVT>::PER_LOAD;
 #pragma unroll
-  for (int i = 0; i < TileRegs<HD, BF16>::LOADS; ++i) {
+  for (int i = 0; i < TileRegs<HD, KVT>::LOADS; ++i) {
     const int e = (threadIdx.x + i * kThreads) * PER;
     const int r = e / HD, d = e % HD;
-    if (BF16) {
+    if (KVT == KV_Q8_0) {  // 16 codes widened exactly: code times the block scale
+      const float sc = f16_bits_to_f32(t.sc[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t.x[i][j];
+        float4 f;
+        f.x = (float)(int8_t)(c & 0xFF) * sc;
+        f.y = (float)(int8_t)((c >> 8) & 0xFF) * sc;
+        f.z = (float)(int8_t)((c >> 16) & 0xFF) * sc;
+        f.w = (float)(int8_t)((c >> 24) & 0xFF) * sc;
+        *reinterpret_cast<float4*>(&s_t[r][d + 4 * j]) = f;
+      }
+    } else if (KVT == KV_BF16) {
       const uint32_t w[4] = {(uint32_t)t.x[i][0], (uint32_t)t.x[i][1], (uint32_t)t.x[i][2], (uint32_t)t.x[i][3]};
       float4 lo, hi;
       lo.x = __uint_as_float(w[0] << 16), lo.y = __uint_as_float(w[0] & 0xFFFF0000u);
@@ -104,9 +120,9 @@ QDEV void norm_rope_pair(float xa, float xb, float wa, float wb, double c, doubl
   }
 }
 
-template <int HD, int G, bool BF16>
+template <int HD, int G, int KVT>
 __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
-  constexpr int TJ = kTileRows<BF16>;
+  constexpr int TJ = kTileRows<KVT>;
   // scores: thread -> (head h, d-part pt, row group rg of RPT rows); part pt
   // holds dims 4*pt + 4*NP*i + c (c < 4), interleaved so that the float4
   // reads of 16 lanes (4 rows x 4 parts, rows 132 or 68 floats apart) fall
@@ -161,11 +177,11 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   const int cache_end = min(j1, p);
   // loads of stream element i < 2 * nt; an element without cache rows (one
   // that holds only row p) reads its first row's slot instead, unused
-  auto stream_load = [&](TileRegs<HD, BF16>& r, int i) {
+  auto stream_load = [&](TileRegs<HD, KVT>& r, int i) {
     const bool isv = i >= nt;
     const int t0 = j0 + (isv ? i - nt : i) * TJ;
     const bool live = t0 < cache_end;
-    tile_load<HD, BF16>(r, a.kv, isv ? vbase : kbase, live ? t0 : j0, live ? min(TJ, cache_end - t0) : 1);
+    tile_load<HD, KVT>(r, a.kv, a.kvs, isv ? vbase : kbase, live ? t0 : j0, live ? min(TJ, cache_end - t0) : 1);
   };
   // Prologue operands in registers, loaded before the first tiles so that
   // the prologue waits for them alone: wave w takes query heads w, w + 4, ...
@@ -189,7 +205,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   const float* vnew = qkv + (int64_t)(nh + nkv) * HD + (int64_t)g * HD;
   const float ka = knew[pi], kb = knew[pi + H2], va = vnew[pi], vb = vnew[pi + H2];
 
-  TileRegs<HD, BF16> tA, tB;
+  TileRegs<HD, KVT> tA, tB;
   if (nt > 0) {  // 2 * nt >= 2 elements
     stream_load(tA, 0);
     stream_load(tB, 1);
@@ -204,12 +220,52 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     if (lane < H2) s_vnew[lane] = va, s_vnew[lane + H2] = vb;
   }
   __syncthreads();
-  if (has_new) {
+  if (KVT == KV_Q8_0) {
+    // the integer score path of a decode step ("The LLM stack (fucina_llm)",
+    // section 13.4, the q8_0 option): each head's query is quantised per
+    // 32-block like an activation; the dot of its exact dequantised values
+    // with the widened K codes is sum_b d_q d_k S_b, as the integer dots give
+    // it.  Every thread takes part in every pass (groups of 8 lanes = one
+    // block of one head).
+    for (int base = 0; base < G * HD; base += 4 * kThreads) {
+      const int idx = base + 4 * tid;
+      const bool live = idx < G * HD;
+      float* q = &s_qf[live ? idx / HD : 0][live ? idx % HD : 0];
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live) v[0] = q[0], v[1] = q[1], v[2] = q[2], v[3] = q[3];
+      float d;
+      const int packed = quant4_group8(v, &d);
+      if (live) {
+        const float df = f16_round(d);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = (float)(int8_t)((packed >> (8 * c)) & 0xFF) * df;
+      }
+    }
+    if (has_new && wave < 2) {
+      // append: wave 0 encodes the new K row, wave 1 the new V row, into
+      // codes and scales; the dequantised values are the ones attended below
+      float* row = wave == 0 ? s_knew : s_vnew;
+      const int64_t e0 = (wave == 0 ? kbase : vbase) + (int64_t)p * HD;
+      const bool live = lane < HD / 4;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (live) v[0] = row[4 * lane], v[1] = row[4 * lane + 1], v[2] = row[4 * lane + 2], v[3] = row[4 * lane + 3];
+      float d;
+      const int packed = quant4_group8(v, &d);
+      if (live) {
+        *reinterpret_cast<int*>(reinterpret_cast<int8_t*>(a.kv) + e0 + 4 * lane) = packed;
+        if ((lane & 7) == 0) a.kvs[e0 / 32 + lane / 8] = f32_to_f16_bits(d);
+        const float df = f16_round(d);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) row[4 * lane + c] = (float)(int8_t)((packed >> (8 * c)) & 0xFF) * df;
+      }
+    }
+    __syncthreads();
+  } else if (has_new) {
     // append: the cache stores post-RoPE K and raw V (bf16 caches round here,
     // and the rounded values are the ones attended below)
     for (int d = tid; d < HD; d += kThreads) {
       const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
-      if (BF16) {
+      if (KVT == KV_BF16) {
         const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
         reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
         reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
@@ -255,7 +311,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
 
   // stream element i: stage it in LDS, start the load of element i + 2 into
   // the freed registers, then scores (K) or P.V (V)
-  auto process = [&](TileRegs<HD, BF16>& tr, int i, auto prefetch) {
+  auto process = [&](TileRegs<HD, KVT>& tr, int i, auto prefetch) {
     constexpr bool PREFETCH = decltype(prefetch)::value;
     const bool isv = i >= nt;
     const int t0 = j0 + (isv ? i - nt : i) * TJ;
@@ -265,7 +321,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
       softmax();
       __syncthreads();
     }
-    if (t0 < cache_end) tile_store<HD, BF16>(tr, s_t);
+    if (t0 < cache_end) tile_store<HD, KVT>(tr, s_t);
     if (PREFETCH) stream_load(tr, i + 2);
     if (t0 + nrow > p) {  // the tile holds row p: take it from this step's values
       __syncthreads();    // (after the tile store, which zero-fills that row)
@@ -454,12 +510,14 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
 }
 
 template <int HD, int G>
-hipError_t launch(const AttnDecodeArgs& a, bool bf16, int nrows, hipStream_t s) {
+hipError_t launch(const AttnDecodeArgs& a, int kvt, int nrows, hipStream_t s) {
   const dim3 grid(a.nsplit_max, a.nkv, nrows);
-  if (bf16)
-    hipLaunchKernelGGL((k_attn_decode<HD, G, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_decode<HD, G, false>), grid, dim3(kThreads), 0, s, a);
+  switch (kvt) {
+    case KV_F32: hipLaunchKernelGGL((k_attn_decode<HD, G, KV_F32>), grid, dim3(kThreads), 0, s, a); break;
+    case KV_BF16: hipLaunchKernelGGL((k_attn_decode<HD, G, KV_BF16>), grid, dim3(kThreads), 0, s, a); break;
+    case KV_Q8_0: hipLaunchKernelGGL((k_attn_decode<HD, G, KV_Q8_0>), grid, dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -475,9 +533,9 @@ bool attn_decode_supported(int hd, int group) {
 
 int attn_decode_max_ctx(int group) { return kMaxSplit * (kScoreSlots / group); }
 
-hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s) {
+hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, int kvt, int nrows, hipStream_t s) {
 #define Q8_ATT(HD_, G_) \
-  if (hd == HD_ && group == G_) return launch<HD_, G_>(a, kv_bf16, nrows, s);
+  if (hd == HD_ && group == G_) return launch<HD_, G_>(a, kvt, nrows, s);
   Q8_ATT(64, 1)
   Q8_ATT(64, 2)
   Q8_ATT(64, 4)

@@ -44,9 +44,35 @@ namespace {
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-template <int HD, bool BF16>
+// Q8_0 round trip of one head row in LDS, by all 64 threads of the
+// workgroup: per 32-block the activation encoder (scale max|x|/127, codes
+// rounded to nearest even), the codes and f16 scale bits to `codes` /
+// `scales` when given, the dequantised values (exact in f32) back into x.
+// Each thread touches only its own four values.
+template <int HD>
+QDEV void q8_row(float* x, int8_t* codes, uint16_t* scales) {
+  const int t = threadIdx.x;
+  const bool live = t < HD / 4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = x[4 * t + i];
+  }
+  float d;
+  const int packed = quant4_group8(v, &d);  // groups of 8 lanes: one block each
+  if (live) {
+    const float df = f16_round(d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * t + i] = (float)(int8_t)((packed >> (8 * i)) & 0xFF) * df;
+    if (codes) *reinterpret_cast<int*>(codes + 4 * t) = packed;
+    if (scales && (t & 7) == 0) scales[t / 8] = f32_to_f16_bits(d);
+  }
+}
+
+template <int HD, int KVT>
 __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
   __shared__ float x[HD];
+  __shared__ float xv[HD];
   const int t = blockIdx.x, h = blockIdx.y;
   const int pos = a.pos0 + t;
   const float* row = a.qkv + (int64_t)t * a.qkv_stride;
@@ -57,6 +83,10 @@ __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
     __syncthreads();
     norm_rope_wave<HD>(x, a.q_norm, a.eps, cs, sn);
     __syncthreads();
+    if (KVT == KV_Q8_0 && a.quant_q) {  // the integer score path of a single-token step
+      q8_row<HD>(x, nullptr, nullptr);
+      __syncthreads();
+    }
     for (int d = threadIdx.x; d < HD; d += 64) a.q32[((int64_t)t * a.nh + h) * HD + d] = x[d];
   } else {
     const int g = h - a.nh;
@@ -67,9 +97,17 @@ __global__ void __launch_bounds__(64) k_qk_rope_append(QkRopeArgs a) {
     const int64_t head_elems = (int64_t)a.cap * HD;
     const int64_t kb = a.kbase + g * head_elems + (int64_t)pos * HD;
     const int64_t vb = kb + (int64_t)a.nkv * head_elems;
+    if (KVT == KV_Q8_0) {
+      for (int d = threadIdx.x; d < HD; d += 64) xv[d] = row[(int64_t)(a.nh + a.nkv + g) * HD + d];
+      __syncthreads();
+      int8_t* codes = reinterpret_cast<int8_t*>(a.kv);
+      q8_row<HD>(x, codes + kb, a.kvs + kb / 32);
+      q8_row<HD>(xv, codes + vb, a.kvs + vb / 32);
+      return;
+    }
     for (int d = threadIdx.x; d < HD; d += 64) {
       const float v = row[(int64_t)(a.nh + a.nkv + g) * HD + d];
-      if (BF16) {
+      if (KVT == KV_BF16) {
         reinterpret_cast<uint16_t*>(a.kv)[kb + d] = f32_to_bf16_bits(x[d]);
         reinterpret_cast<uint16_t*>(a.kv)[vb + d] = f32_to_bf16_bits(v);
       } else {
@@ -84,14 +122,18 @@ constexpr int KT = 64;  // keys per LDS tile
 
 // One K/V tile (KT rows of HD) in registers: 16-byte loads, the same count
 // for every tile (rows past `kend` re-read row kend - 1: finite values whose
-// scores are masked and whose probabilities are 0).
-template <int HD, bool BF16>
+// scores are masked and whose probabilities are 0).  KV_Q8_0: a load is 16
+// codes of one row (half a block) plus that block's f16 scale; the codes are
+// widened exactly (code times scale) when the tile is staged.
+template <int HD, int KVT>
 struct KVTile {
-  static constexpr int PER = BF16 ? 8 : 4;  // elements per 16-byte load
+  static constexpr int ESZ = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
+  static constexpr int PER = 16 / ESZ;  // elements per 16-byte load
   static constexpr int LOADS = KT * HD / PER / 256;
+  static_assert(LOADS >= 1 && LOADS * PER * 256 == KT * HD, "tile map");
   v4i k[LOADS], v[LOADS];
-  QDEV void load(const void* kv, int64_t kb0, int64_t vb0, int kbase, int kend) {
-    constexpr int ESZ = BF16 ? 2 : 4;
+  uint16_t ks[KVT == KV_Q8_0 ? LOADS : 1], vs[KVT == KV_Q8_0 ? LOADS : 1];
+  QDEV void load(const void* kv, const uint16_t* kvs, int64_t kb0, int64_t vb0, int kbase, int kend) {
     const uint8_t* base = static_cast<const uint8_t*>(kv);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -100,6 +142,22 @@ struct KVTile {
       const int64_t off = (int64_t)key * HD + (e % HD);
       k[i] = *reinterpret_cast<const v4i*>(base + (kb0 + off) * ESZ);
       v[i] = *reinterpret_cast<const v4i*>(base + (vb0 + off) * ESZ);
+      if (KVT == KV_Q8_0) {
+        ks[i] = kvs[(kb0 + off) / 32];
+        vs[i] = kvs[(vb0 + off) / 32];
+      }
+    }
+  }
+  QDEV static void widen_q8(v4i w, float sc, float* dst) {  // 16 codes -> 16 floats
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = w[j];
+      float4 f;
+      f.x = (float)(int8_t)(c & 0xFF) * sc;
+      f.y = (float)(int8_t)((c >> 8) & 0xFF) * sc;
+      f.z = (float)(int8_t)((c >> 16) & 0xFF) * sc;
+      f.w = (float)(int8_t)((c >> 24) & 0xFF) * sc;
+      *reinterpret_cast<float4*>(dst + 4 * j) = f;
     }
   }
   QDEV void store(float* sK, int krow, float* sV, int vrow) const {
@@ -107,7 +165,10 @@ struct KVTile {
     for (int i = 0; i < LOADS; ++i) {
       const int e = (threadIdx.x + i * 256) * PER;
       const int r = e / HD, d = e % HD;
-      if (BF16) {
+      if (KVT == KV_Q8_0) {
+        widen_q8(k[i], f16_bits_to_f32(ks[i]), sK + r * krow + d);
+        widen_q8(v[i], f16_bits_to_f32(vs[i]), sV + r * vrow + d);
+      } else if (KVT == KV_BF16) {
         float4 a0, a1, b0, b1;
         a0.x = __uint_as_float((uint32_t)k[i][0] << 16), a0.y = __uint_as_float((uint32_t)k[i][0] & 0xFFFF0000u);
         a0.z = __uint_as_float((uint32_t)k[i][1] << 16), a0.w = __uint_as_float((uint32_t)k[i][1] & 0xFFFF0000u);
@@ -129,7 +190,7 @@ struct KVTile {
   }
 };
 
-template <int HD, int G, bool BF16, int KS>
+template <int HD, int G, int KVT, int KS>
 __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   constexpr int HW = G < 4 ? G : 4;  // query heads per workgroup
   static_assert(HW * KS <= 4, "waves");
@@ -189,12 +250,12 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
 
   // the next tile's loads are issued right after the current tile is
   // staged, so they land while the current tile is used
-  KVTile<HD, BF16> tile;
-  tile.load(a.kv, kb0, vb0, k_lo, kend);
+  KVTile<HD, KVT> tile;
+  tile.load(a.kv, a.kvs, kb0, vb0, k_lo, kend);
   for (int kbase = k_lo; kbase < k_hi; kbase += KT) {
     __syncthreads();
     tile.store(sK, KROW, sV, VROW);
-    tile.load(a.kv, kb0, vb0, kbase + KT < k_hi ? kbase + KT : kbase, kend);
+    tile.load(a.kv, a.kvs, kb0, vb0, kbase + KT < k_hi ? kbase + KT : kbase, kend);
     __syncthreads();
 
     // scores S^T for the sub-tiles of 16 keys of this wave's part; lane holds
@@ -383,7 +444,7 @@ int pick_tps(const AttnPrefillArgs& a, int ny) {
 }
 
 template <int HD, int G, int KS>
-hipError_t launch_attn_ks(const AttnPrefillArgs& a0, bool bf16, hipStream_t s) {
+hipError_t launch_attn_ks(const AttnPrefillArgs& a0, int kvt, hipStream_t s) {
   constexpr int HW = G < 4 ? G : 4;
   constexpr int QT = 16 * (4 / (HW * KS));
   const int ny = a0.nkv * (G / HW);
@@ -395,10 +456,12 @@ hipError_t launch_attn_ks(const AttnPrefillArgs& a0, bool bf16, hipStream_t s) {
   const int64_t nwg = (int64_t)a.nqb * a.nz * ny;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg);
-  if (bf16)
-    hipLaunchKernelGGL((k_attn_prefill<HD, G, true, KS>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_prefill<HD, G, false, KS>), grid, dim3(256), 0, s, a);
+  switch (kvt) {
+    case KV_F32: hipLaunchKernelGGL((k_attn_prefill<HD, G, KV_F32, KS>), grid, dim3(256), 0, s, a); break;
+    case KV_BF16: hipLaunchKernelGGL((k_attn_prefill<HD, G, KV_BF16, KS>), grid, dim3(256), 0, s, a); break;
+    case KV_Q8_0: hipLaunchKernelGGL((k_attn_prefill<HD, G, KV_Q8_0, KS>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   if (a.tps > 0) hipLaunchKernelGGL((k_attn_merge<HD>), dim3((unsigned)(a.T * a.nh)), dim3(HD), 0, s, a, QT);
   return hipGetLastError();
 }
@@ -406,41 +469,45 @@ hipError_t launch_attn_ks(const AttnPrefillArgs& a0, bool bf16, hipStream_t s) {
 // Two key halves per head when one 32-query block per workgroup would give
 // fewer than two workgroups per CU.
 template <int HD, int G>
-hipError_t launch_attn(const AttnPrefillArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_attn(const AttnPrefillArgs& a, int kvt, hipStream_t s) {
   constexpr int HW = G < 4 ? G : 4;
   if constexpr (HW <= 2) {
-    if ((int64_t)((a.T + 31) / 32) * a.nkv * (G / HW) < 512) return launch_attn_ks<HD, G, 2>(a, bf16, s);
+    if ((int64_t)((a.T + 31) / 32) * a.nkv * (G / HW) < 512) return launch_attn_ks<HD, G, 2>(a, kvt, s);
   }
-  return launch_attn_ks<HD, G, 1>(a, bf16, s);
+  return launch_attn_ks<HD, G, 1>(a, kvt, s);
 }
 
 }  // namespace
 
 namespace q8k {
 
-hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, bool kv_bf16, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const dim3 grid(T, a.nh + a.nkv);
-  if (hd == 64) {
-    if (kv_bf16) hipLaunchKernelGGL((k_qk_rope_append<64, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((k_qk_rope_append<64, false>), grid, dim3(64), 0, s, a);
-  } else if (hd == 128) {
-    if (kv_bf16) hipLaunchKernelGGL((k_qk_rope_append<128, true>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((k_qk_rope_append<128, false>), grid, dim3(64), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+template <int HD>
+hipError_t launch_qk(const QkRopeArgs& a, dim3 grid, int kvt, hipStream_t s) {
+  switch (kvt) {
+    case KV_F32: hipLaunchKernelGGL((k_qk_rope_append<HD, KV_F32>), grid, dim3(64), 0, s, a); break;
+    case KV_BF16: hipLaunchKernelGGL((k_qk_rope_append<HD, KV_BF16>), grid, dim3(64), 0, s, a); break;
+    case KV_Q8_0: hipLaunchKernelGGL((k_qk_rope_append<HD, KV_Q8_0>), grid, dim3(64), 0, s, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, int kvt, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid(T, a.nh + a.nkv);
+  if (hd == 64) return launch_qk<64>(a, grid, kvt, s);
+  if (hd == 128) return launch_qk<128>(a, grid, kvt, s);
+  return hipErrorInvalidValue;
 }
 
 bool attn_prefill_supported(int hd, int group) {
   return (hd == 64 || hd == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf16, hipStream_t s) {
+hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, int kvt, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
 #define Q8_AP(HD_, G_) \
-  if (hd == HD_ && group == G_) return launch_attn<HD_, G_>(a, kv_bf16, s);
+  if (hd == HD_ && group == G_) return launch_attn<HD_, G_>(a, kvt, s);
   Q8_AP(64, 1)
   Q8_AP(64, 2)
   Q8_AP(64, 4)

@@ -145,12 +145,21 @@ __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x,
 }
 
 // KV slab export: [nkv][cap][hd] (f32 or bf16) rows [0, len) -> f32 [nkv][len][hd].
-__global__ void k_kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* __restrict__ dst) {
+// (KV_Q8_0: code times its block's f16 scale, exact in f32.)
+__global__ void k_kv_export(const void* src, const uint16_t* __restrict__ srcs, int kvt, int nkv, int cap, int len,
+                            int hd, float* __restrict__ dst) {
   const int64_t total = (int64_t)nkv * len * hd;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t g = i / ((int64_t)len * hd), rem = i % ((int64_t)len * hd);
     const int64_t si = g * (int64_t)cap * hd + rem;
-    dst[i] = bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[si]) : reinterpret_cast<const float*>(src)[si];
+    float v;
+    if (kvt == KV_BF16)
+      v = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(src)[si]);
+    else if (kvt == KV_Q8_0)
+      v = (float)reinterpret_cast<const int8_t*>(src)[si] * f16_bits_to_f32(srcs[si / 32]);
+    else
+      v = reinterpret_cast<const float*>(src)[si];
+    dst[i] = v;
   }
 }
 
@@ -206,12 +215,13 @@ hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, con
   return hipGetLastError();
 }
 
-hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* dst, hipStream_t s) {
+hipError_t kv_export(const void* src, const uint16_t* srcs, int kvt, int nkv, int cap, int len, int hd, float* dst,
+                     hipStream_t s) {
   const int64_t total = (int64_t)nkv * len * hd;
   if (total == 0) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   if (grid > 65536) grid = 65536;
-  hipLaunchKernelGGL(k_kv_export, dim3((unsigned)grid), dim3(256), 0, s, src, bf16, nkv, cap, len, hd, dst);
+  hipLaunchKernelGGL(k_kv_export, dim3((unsigned)grid), dim3(256), 0, s, src, srcs, kvt, nkv, cap, len, hd, dst);
   return hipGetLastError();
 }
 

@@ -7,6 +7,11 @@
 
 enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 
+// KV cache element types.  KV_Q8_0: int8 codes at the element offsets (one
+// byte each) and one f16 scale per 32 elements in a second plane (scale of
+// element e at kvs[e / 32]); a (position, head) row is head_dim/32 blocks.
+enum { KV_F32 = 0, KV_BF16 = 1, KV_Q8_0 = 2 };
+
 // Arguments of the decode GEMV family (see k_gemv.hip).
 struct GemvArgs {
   const float* src;  // activation rows f32 [grid_y][K] (row stride src_stride)
@@ -42,6 +47,7 @@ struct AttnDecodeArgs {
   const double* rope_cos;  // [max_pos][hd/2]
   const double* rope_sin;
   void* kv;                  // cache base
+  uint16_t* kvs;             // KV_Q8_0: the scale plane
   const int64_t* seq_base;   // [max_seqs] element offset of each sequence
   const int32_t* seq_cap;    // [max_seqs] capacity (rows) of each sequence
   const int32_t* len;        // [max_seqs] KV lengths (position of the new token)
@@ -66,7 +72,9 @@ hipError_t repack_bf16(const void* src, int64_t rows, int64_t k, uint16_t* dst, 
                        hipStream_t s);
 hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, const uint16_t* sc, bool bf16, float* x,
                  hipStream_t s);
-hipError_t kv_export(const void* src, bool bf16, int nkv, int cap, int len, int hd, float* dst, hipStream_t s);
+// src: the (sequence, layer) K or V block; srcs: its scales (KV_Q8_0)
+hipError_t kv_export(const void* src, const uint16_t* srcs, int kvt, int nkv, int cap, int len, int hd, float* dst,
+                     hipStream_t s);
 hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
                       uint16_t* da_bits, hipStream_t s);
 
@@ -77,7 +85,7 @@ hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, i
 
 bool attn_decode_supported(int hd, int group);
 int attn_decode_max_ctx(int group);  // longest context (cache capacity) the decode attention takes
-hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, bool kv_bf16, int nrows, hipStream_t s);
+hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, int kvt, int nrows, hipStream_t s);
 
 // Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T];
 // key [T] and counter [T] are zero between launches (and left so).  With
@@ -116,15 +124,18 @@ struct QkRopeArgs {
   const double* rope_sin;
   float* q32;  // [T][nh][hd] normalised + roped queries
   void* kv;
+  uint16_t* kvs;  // KV_Q8_0: the scale plane
   int64_t kbase;  // element offset of this (sequence, layer) K block; V follows at + nkv*cap*hd
   int cap;
   int pos0;       // position of token 0
   int nh, nkv;
+  int quant_q;    // KV_Q8_0 single-token step: q32 gets the Q8_0 round trip of each head's query
 };
 
 struct AttnPrefillArgs {
   const float* q32;  // [T][nh][hd]
   const void* kv;
+  const uint16_t* kvs;  // KV_Q8_0 scale plane
   int64_t kbase;
   int cap;
   int pos0;  // position of query token 0 (cache rows [0, pos0 + T) are valid)
@@ -170,8 +181,8 @@ hipError_t gemm_skinny(const GemmArgs& a, int epi, hipStream_t s);
 hipError_t gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 hipError_t rows_norm(const float* x, int64_t ldx, int T, int K, const float* w, float eps, float* y, int64_t ldy,
                      hipStream_t s);
-hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, bool kv_bf16, hipStream_t s);
-hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, bool kv_bf16, hipStream_t s);
+hipError_t qk_rope_append(const QkRopeArgs& a, int T, int hd, int kvt, hipStream_t s);
+hipError_t attn_prefill(const AttnPrefillArgs& a, int hd, int group, int kvt, hipStream_t s);
 bool attn_prefill_supported(int hd, int group);
 }  // namespace q8k
 

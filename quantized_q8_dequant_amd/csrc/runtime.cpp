@@ -103,6 +103,8 @@ struct qwen3_model {
   int R = 0;  // max_batch_tokens
   int nh = 0, nkv = 0, hd = 0, H = 0, F = 0, V = 0, L = 0, G = 0, qw = 0, kvw = 0, nqkv = 0, kmax = 0;
   bool wbf16 = false, kvbf16 = false;
+  int kvt = KV_F32;  // KV_F32 / KV_BF16 / KV_Q8_0
+  uint16_t* kvs = nullptr;  // KV_Q8_0 scale plane (scale of element e at kvs[e / 32])
   int max_cap = 0;
   // device
   std::vector<Layer> layers;
@@ -171,8 +173,10 @@ int validate(const qwen3_config* c) {
     return fail(QWEN3_E_INVALID_CONFIG, "rope_theta must be > 1");
   if (c->weight_type != QWEN3_W_Q8_0 && c->weight_type != QWEN3_W_BF16)
     return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown weight_type");
-  if (c->kv_type != QWEN3_KV_F32 && c->kv_type != QWEN3_KV_BF16)
+  if (c->kv_type != QWEN3_KV_F32 && c->kv_type != QWEN3_KV_BF16 && c->kv_type != QWEN3_KV_Q8_0)
     return fail(QWEN3_E_UNSUPPORTED_WEIGHT_TYPE, "unknown kv_type");
+  if (c->kv_type == QWEN3_KV_Q8_0 && c->head_dim % 32 != 0)
+    return fail(QWEN3_E_INVALID_CONFIG, "a q8_0 KV cache needs head_dim % 32 == 0");
   const int qw = c->num_attention_heads * c->head_dim;
   if (c->hidden_size % 128 || qw % 128 || c->intermediate_size % 128)
     return fail(QWEN3_E_INVALID_CONFIG, "hidden_size, heads*head_dim and intermediate_size must be multiples of 128");
@@ -235,7 +239,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   m->rope_cos = cv.arr<double>((size_t)m->max_cap * (hd / 2));
   m->rope_sin = cv.arr<double>((size_t)m->max_cap * (hd / 2));
   // KV cache: sequence s holds [layers][K, V][nkv][cap_s][hd]
-  const size_t esz = m->kvbf16 ? 2 : 4;
+  const size_t esz = m->kvt == KV_F32 ? 4 : (m->kvt == KV_BF16 ? 2 : 1);
   m->seq_base.assign(c.max_seqs, 0);
   size_t kv_elems = 0;
   for (int s = 0; s < c.max_seqs; ++s) {
@@ -248,6 +252,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
   size_t kv_bytes;
   if (!mul_ok(kv_elems, esz, &kv_bytes)) cv.overflow = true;
   m->kv = cv.take(kv_bytes);
+  if (m->kvt == KV_Q8_0) m->kvs = cv.arr<uint16_t>(kv_elems / 32);
   m->d_seq_base = cv.arr<int64_t>(c.max_seqs);
   m->d_seq_cap = cv.arr<int32_t>(c.max_seqs);
   m->d_len = cv.arr<int32_t>(c.max_seqs);
@@ -308,10 +313,11 @@ int fill_model_shape(qwen3_model* m, const qwen3_config* cfg) {
   m->kmax = std::max(m->H, std::max(m->qw, m->F));
   m->wbf16 = cfg->weight_type == QWEN3_W_BF16;
   m->kvbf16 = cfg->kv_type == QWEN3_KV_BF16;
+  m->kvt = cfg->kv_type == QWEN3_KV_BF16 ? KV_BF16 : (cfg->kv_type == QWEN3_KV_Q8_0 ? KV_Q8_0 : KV_F32);
   m->max_cap = 0;
   for (int c : m->cap) m->max_cap = std::max(m->max_cap, c);
   m->psh = PersistShape{m->H, m->qw, m->F, m->hd, m->G};
-  m->persist_capable = !m->wbf16 && q8k::persist_max_ctx(m->psh) > 0;
+  m->persist_capable = !m->wbf16 && m->kvt != KV_Q8_0 && q8k::persist_max_ctx(m->psh) > 0;
   return QWEN3_OK;
 }
 
@@ -379,6 +385,7 @@ AttnDecodeArgs attn_args(const qwen3_model* m, const int32_t* d_row_seq, int nro
   at.rope_cos = m->rope_cos;
   at.rope_sin = m->rope_sin;
   at.kv = m->kv;
+  at.kvs = m->kvs;
   at.seq_base = m->d_seq_base;
   at.seq_cap = m->d_seq_cap;
   at.len = m->d_len;
@@ -514,7 +521,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
       at.q_norm = ly.q_norm;
       at.k_norm = ly.k_norm;
       at.layer = l;
-      HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvbf16, nrows, s));
+      HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvt, nrows, s));
       break;
     }
     case 2:
@@ -545,8 +552,10 @@ int enqueue_decode(qwen3_model* m, int nrows, const int32_t* d_tok, const int32_
 // One prefill chunk: T tokens (already in m->d_tok) at positions pos0.. of seq.
 // all_rows: the head runs on every row of the chunk, writing d_logits [T, V]
 // (and d_argmax [T]) from the chunk's first row; else on row T-1 of the last chunk.
+// quant_q: the call is a single-token step (a q8_0 cache then scores with the
+// quantised query).
 int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, float* d_logits, int32_t* d_argmax,
-                          hipStream_t s, bool all_rows = false) {
+                          hipStream_t s, bool all_rows = false, bool quant_q = false) {
   const float eps = m->cfg.rms_norm_eps;
   // projections: the small-M GEMM for short chunks (no split-K pass), else the tiled one
   const bool small = skinny_rows(m, T);
@@ -583,15 +592,18 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     qr.rope_sin = m->rope_sin;
     qr.q32 = m->q32;
     qr.kv = m->kv;
+    qr.kvs = m->kvs;
+    qr.quant_q = quant_q;
     qr.kbase = kbase;
     qr.cap = m->cap[seq];
     qr.pos0 = pos0;
     qr.nh = m->nh;
     qr.nkv = m->nkv;
-    HIP_TRY(q8k::qk_rope_append(qr, T, m->hd, m->kvbf16, s));
+    HIP_TRY(q8k::qk_rope_append(qr, T, m->hd, m->kvt, s));
     AttnPrefillArgs ap{};
     ap.q32 = m->q32;
     ap.kv = m->kv;
+    ap.kvs = m->kvs;
     ap.kbase = kbase;
     ap.cap = m->cap[seq];
     ap.pos0 = pos0;
@@ -602,7 +614,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     ap.out = m->attn;
     ap.part = m->gemm_part;
     ap.part_bytes = m->gemm_part_bytes;
-    HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvbf16, s));
+    HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvt, s));
     if (m->wbf16) {
       const int64_t H = m->H;
       HIP_TRY(q8k::gemm_bf16(bf16_args(ly.o, m->attn, m->qw, T, m->x, H), EPI_RESIDUAL, s));
@@ -845,7 +857,7 @@ int qwen3_prefill(qwen3_t* m, int32_t seq, const int32_t* h_tokens, int32_t n, f
   for (int c0 = 0; c0 < n; c0 += m->R) {
     const int T = std::min(m->R, n - c0);
     HIP_TRY(hipMemcpyAsync(m->d_tok, h_tokens + c0, (size_t)T * 4, hipMemcpyHostToDevice, s));
-    TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits, d_argmax, s));
+    TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits, d_argmax, s, false, n == 1));
   }
   m->h_len[seq] = len + n;
   return QWEN3_OK;
@@ -872,7 +884,7 @@ int qwen3_prefill_all_logits(qwen3_t* m, int32_t seq, const int32_t* h_tokens, i
     const int T = std::min(m->R, n - c0);
     HIP_TRY(hipMemcpyAsync(m->d_tok, h_tokens + c0, (size_t)T * 4, hipMemcpyHostToDevice, s));
     TRY(enqueue_prefill_chunk(m, seq, len + c0, T, c0 + T == n, d_logits + (int64_t)c0 * m->V,
-                              d_argmax ? d_argmax + c0 : nullptr, s, true));
+                              d_argmax ? d_argmax + c0 : nullptr, s, true, n == 1));
   }
   m->h_len[seq] = len + n;
   return QWEN3_OK;
@@ -1000,10 +1012,12 @@ int qwen3_kv_export(const qwen3_t* m, int32_t seq, int32_t layer, float* d_k, fl
   const int64_t head_elems = (int64_t)cap * m->hd;
   const int64_t kbase = m->seq_base[seq] + (int64_t)layer * 2 * m->nkv * head_elems;
   const int64_t vbase = kbase + (int64_t)m->nkv * head_elems;
-  const size_t esz = m->kvbf16 ? 2 : 4;
+  const size_t esz = m->kvt == KV_F32 ? 4 : (m->kvt == KV_BF16 ? 2 : 1);
   const uint8_t* base = static_cast<const uint8_t*>(m->kv);
-  HIP_TRY(q8k::kv_export(base + kbase * esz, m->kvbf16, m->nkv, cap, len, m->hd, d_k, S(stream)));
-  HIP_TRY(q8k::kv_export(base + vbase * esz, m->kvbf16, m->nkv, cap, len, m->hd, d_v, S(stream)));
+  const uint16_t* ks = m->kvs ? m->kvs + kbase / 32 : nullptr;
+  const uint16_t* vs = m->kvs ? m->kvs + vbase / 32 : nullptr;
+  HIP_TRY(q8k::kv_export(base + kbase * esz, ks, m->kvt, m->nkv, cap, len, m->hd, d_k, S(stream)));
+  HIP_TRY(q8k::kv_export(base + vbase * esz, vs, m->kvt, m->nkv, cap, len, m->hd, d_v, S(stream)));
   return QWEN3_OK;
 }
 

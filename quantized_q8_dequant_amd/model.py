@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import KV_BF16, KV_F32, W_BF16, W_Q8_0, check, lib
+from ._lib import KV_BF16, KV_F32, KV_Q8_0, W_BF16, W_Q8_0, check, lib
 
 
 def _stream() -> int:
@@ -69,7 +69,7 @@ class Qwen3Config:
             float(self.rms_norm_eps),
             float(self.rope_theta),
             W_Q8_0 if self.weight_type == "q8_0" else W_BF16 if self.weight_type == "bf16" else 99,
-            KV_F32 if self.kv_type == "f32" else KV_BF16 if self.kv_type == "bf16" else 99,
+            {"f32": KV_F32, "bf16": KV_BF16, "q8_0": KV_Q8_0}.get(self.kv_type, 99),
             len(capacities),
             caps,
             int(max_batch_tokens),

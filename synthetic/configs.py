@@ -25,7 +25,7 @@ class ModelShape:
     rms_norm_eps: float = 1e-6
     rope_theta: float = 1e6
     weight_type: str = "q8_0"  # "q8_0" or "bf16"
-    kv_type: str = "f32"  # "f32" or "bf16"
+    kv_type: str = "f32"  # "f32", "bf16" or "q8_0"
 
     @property
     def q_width(self) -> int:
