@@ -14,9 +14,10 @@ algorithmic bytes per launch over its event-timed average duration), the
 prefill-dominated variant (4096 tokens in one call, same weights) and the
 CPU oracle timed on a bounded sample of the same workload.
 
-Other workloads (`--workload`): `8b-longctx` (Qwen3-8B shape, bf16 KV,
-decode at KV lengths 2048/16384/32768) and `0.6b-bf16-batch64` (bf16
-weights, 64 ragged sequences, batched decode)."""
+Other workloads (`--workload`): `8b-longctx` (Qwen3-8B shape, bf16 KV --
+`--kv q8_0` for the Q8_0 cache -- decode at KV lengths 2048/16384/32768)
+and `0.6b-bf16-batch64` (bf16 weights, 64 ragged sequences, batched
+decode)."""
 
 from __future__ import annotations
 
@@ -109,8 +110,9 @@ def weight_bytes(shape) -> float:
     return q8_bytes(n) if shape.weight_type == "q8_0" else 2.0 * n
 
 
-def kv_bytes_per_position(shape) -> int:
-    return shape.num_layers * 2 * shape.kv_width * (4 if shape.kv_type == "f32" else 2)
+def kv_bytes_per_position(shape) -> float:
+    per = {"f32": 4.0, "bf16": 2.0, "q8_0": 34.0 / 32.0}[shape.kv_type]  # q8_0: codes + f16 scale per 32
+    return shape.num_layers * 2 * shape.kv_width * per
 
 
 def timed(fn, reps: int) -> float:
@@ -136,7 +138,7 @@ def bench_8b(args) -> int:
     from synthetic import WORKLOADS, gen_prompt, gen_weights
 
     wl = WORKLOADS["8b-longctx"]
-    shape = wl.shape
+    shape = wl.shape if args.kv is None else wl.shape.with_(kv_type=args.kv)
     weights = gen_weights(shape, wl.weight_seed)
     model = Qwen3Model(Qwen3Config.from_shape(shape), weights, [wl.kv_capacity], max_batch_tokens=2048)
     del weights
@@ -180,10 +182,10 @@ def bench_8b(args) -> int:
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": "Qwen3-8B shape, Q8_0 weights, bf16 KV cache: a prompt of L random tokens in "
+            "workload": f"Qwen3-8B shape, Q8_0 weights, {shape.kv_type} KV cache: a prompt of L random tokens in "
             "2048-row chunks, then greedy decode steps at KV length L, L = 2048, 16384, 32768, batch 1",
             "weights": "q8_0",
-            "kv_cache": "bf16",
+            "kv_cache": shape.kv_type,
             "parallelism": "single GPU",
         },
         "contexts": out,
@@ -347,6 +349,22 @@ def bench_batched(shape, weights, prompt, args) -> dict:
             "weight_GBps": round(weight_bytes(shape) / (ms / 1000.0) / 1e9, 1),
         }
     model.close()
+    # the same 64-stream step over a q8_0 KV cache (a quarter of the f32
+    # cache's bytes), the per-step KV reads being the largest part at 64
+    qshape = shape.with_(kv_type="q8_0")
+    model = Qwen3Model(Qwen3Config.from_shape(qshape), weights, [P + steps * (args.warmup + args.steps + 1) + 1] * nmax)
+    for s in range(nmax):
+        model.prefill(prompt, seq=s, logits=False)
+    seqs = list(range(nmax))
+    am = torch.zeros(nmax, dtype=torch.int32, device="cuda:0")
+
+    def runq():
+        for _ in range(steps):
+            model.decode_batch(seqs, am, None, am)
+
+    ms = event_ms(runq, args.warmup, args.steps) / steps
+    out[f"{nmax}_q8_0_kv"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(nmax * 1000.0 / ms, 1)}
+    model.close()
     return out
 
 
@@ -385,6 +403,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-steps", type=int, default=8)
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument(
+        "--kv",
+        choices=["f32", "bf16", "q8_0"],
+        default=None,
+        help="KV cache type of the 8b-longctx workload (default: its bf16)",
+    )
     ap.add_argument(
         "--pmc-calibrate",
         action="store_true",
