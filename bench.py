@@ -368,6 +368,35 @@ def bench_batched(shape, weights, prompt, args) -> dict:
     return out
 
 
+def bench_sampling(V: int, args) -> dict:
+    """The device sampling pipeline on rows of V logits: a Qwen3-style
+    setting (temperature 0.7, top-k 20, top-p 0.95, repetition penalty over
+    64 tokens) and the exact nucleus (top-k 0, top-p 0.9, its window grown to
+    1024 candidates on these logits), for 1 and 64 rows."""
+    import torch
+
+    from quantized_q8_dequant_amd import sample
+
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    out = {}
+    for rows in (1, 64):
+        base = torch.randn((rows, V), device="cuda:0", generator=g) * 4.0
+        uni = torch.rand(rows, device="cuda:0", generator=g)
+        hist = torch.randint(0, V, (rows, 64), device="cuda:0", dtype=torch.int32, generator=g)
+        hlen = torch.full((rows,), 64, device="cuda:0", dtype=torch.int32)
+        for name, kw in (
+            ("top_k20_top_p0.95", dict(temperature=0.7, top_k=20, top_p=0.95, repeat_penalty=1.1)),
+            ("nucleus_top_p0.9", dict(temperature=1.0, top_k=0, top_p=0.9)),
+        ):
+            lg = base.clone()
+
+            def run():
+                sample(lg, uni, history=hist, history_len=hlen, **kw)
+
+            out[f"{name}_rows{rows}_us"] = round(event_ms(run, args.warmup, max(args.steps, 5)) * 1000.0, 1)
+    return out
+
+
 def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
     """The CPU oracle on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_info
@@ -555,10 +584,11 @@ def main() -> int:
         del model
         torch.cuda.empty_cache()
 
-    batched = None
+    batched = sampling = None
     if args.workload == "0.6b-decode":
         batched = bench_batched(shape, weights, prompt, args)
         torch.cuda.empty_cache()
+        sampling = bench_sampling(shape.vocab_size, args)
 
     if args.pmc_calibrate:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
@@ -606,6 +636,7 @@ def main() -> int:
         "prefill_4096_one_call": p4,
         "verify": verify,
         "batched_decode": batched,
+        "sampling": sampling,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -272,6 +272,41 @@ int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* 
 int qwen3_bf16_linear(const float* d_x, int64_t m, int64_t k, const uint16_t* d_w, int64_t n,
                       float* d_y, void* stream);
 
+/* ---- sampling ----------------------------------------------------------------
+ * The sampling pipeline of Fucina course, "A transformer from scratch",
+ * section 12.6 and Fucina reference, "The LLM stack (fucina_llm)", section
+ * 13.6, on the device, in its fixed order: repetition / frequency / presence
+ * penalties over the last repeat_last_n history tokens (each distinct token
+ * once, with its count), the greedy shortcut (temperature <= 0: the argmax,
+ * lowest id among equal maxima), top-k (at most 256 candidates), the
+ * temperature softmax, top-p, min-p and one draw.  top_k == 0 is the exact
+ * nucleus: probabilities carry the whole-vocabulary denominator and the
+ * candidate window grows 256 -> 1024 -> 4096 until it holds the top_p mass;
+ * this implementation stops the window at 4096 candidates (a nucleus that
+ * needs more is cut there).  Candidates are ordered by logit, ties by lower
+ * id; the softmax and every sum are f64; the draw takes the first candidate
+ * whose cumulative probability exceeds u times the kept total. */
+typedef struct qwen3_sampler_config {
+  float temperature;      /* <= 0: greedy */
+  int32_t top_k;          /* 0: the exact nucleus; otherwise min(top_k, 256) candidates */
+  float top_p;            /* (0, 1]; 1 disables */
+  float min_p;            /* [0, 1]; 0 disables */
+  float repeat_penalty;   /* > 0; 1 disables */
+  float freq_penalty;     /* per-count subtraction */
+  float presence_penalty; /* flat subtraction for a token present in the window */
+  int32_t repeat_last_n;  /* penalty window, [0, 4096] */
+} qwen3_sampler_config;
+
+/* One token per row: d_logits f32 [n, vocab] (penalised in place, as the
+ * pages' sampler does), d_history int32 [n, history_stride] with the first
+ * d_history_len[r] entries of row r valid, most recent last (NULL: no
+ * penalties), d_uniform f32 [n] one uniform in [0, 1) per row (the draw's
+ * random number; unused when greedy, may then be NULL), d_tokens int32 [n]
+ * out.  QWEN3_E_INVALID_ARGUMENT for a null or out-of-range argument. */
+int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_config* cfg,
+                 const int32_t* d_history, int32_t history_stride, const int32_t* d_history_len,
+                 const float* d_uniform, int32_t* d_tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

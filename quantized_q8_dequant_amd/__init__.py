@@ -14,5 +14,6 @@ from .model import (  # noqa: F401
     q8_0_block_dots,
     q8_0_linear,
     repack_q8_0,
+    sample,
     workspace_bytes,
 )

@@ -35,6 +35,7 @@ EXPORTS = (
     "qwen3_prefill",
     "qwen3_prefill_all_logits",
     "qwen3_truncate",
+    "qwen3_sample",
     "qwen3_decode_step",
     "qwen3_decode_batch",
     "qwen3_reset",
@@ -94,6 +95,21 @@ LAYER_FIELDS = (
 )
 
 
+class SamplerConfig(C.Structure):
+    """qwen3_sampler_config."""
+
+    _fields_ = [
+        ("temperature", C.c_float),
+        ("top_k", C.c_int32),
+        ("top_p", C.c_float),
+        ("min_p", C.c_float),
+        ("repeat_penalty", C.c_float),
+        ("freq_penalty", C.c_float),
+        ("presence_penalty", C.c_float),
+        ("repeat_last_n", C.c_int32),
+    ]
+
+
 class LayerWeights(C.Structure):
     _fields_ = [(f, C.c_void_p) for f in LAYER_FIELDS]
 
@@ -129,6 +145,7 @@ def lib() -> C.CDLL:
         "qwen3_prefill": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
         "qwen3_prefill_all_logits": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
         "qwen3_truncate": (C.c_int, [vp, i32, i32, vp]),
+        "qwen3_sample": (C.c_int, [vp, i32, i32, C.POINTER(SamplerConfig), vp, i32, vp, vp, vp, vp]),
         "qwen3_decode_step": (C.c_int, [vp, i32, vp, vp, vp, vp]),
         "qwen3_decode_batch": (C.c_int, [vp, p_i32, i32, vp, vp, vp, vp]),
         "qwen3_reset": (C.c_int, [vp, i32, vp]),

@@ -61,6 +61,15 @@ struct AttnDecodeArgs {
   double scale;  // 1/sqrt(hd)
 };
 
+// Sampling pipeline (see k_sample.hip).
+struct SampleArgs {
+  float temperature;  // <= 0: greedy
+  int top_k;          // 0: the exact nucleus (window capped at 4096 candidates)
+  float top_p, min_p;
+  float repeat_penalty, freq_penalty, presence_penalty;
+  int repeat_last_n;
+};
+
 namespace q8k {
 
 hipError_t encode_q8_0(const float* x, int64_t n, void* out, hipStream_t s);
@@ -86,6 +95,11 @@ hipError_t block_dots(const int8_t* qa, const int8_t* qs, int M, int K, int N, i
 bool attn_decode_supported(int hd, int group);
 int attn_decode_max_ctx(int group);  // longest context (cache capacity) the decode attention takes
 hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, int kvt, int nrows, hipStream_t s);
+
+// Sampling: penalties in place (when any is active and a history is given),
+// then one token per row.
+hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_t* hist, int hstride,
+                  const int32_t* hlen, const float* uni, int32_t* out, hipStream_t s);
 
 // Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T];
 // key [T] and counter [T] are zero between launches (and left so).  With

@@ -1100,6 +1100,38 @@ int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* 
   return QWEN3_OK;
 }
 
+int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_config* cfg, const int32_t* d_history,
+                 int32_t history_stride, const int32_t* d_history_len, const float* d_uniform, int32_t* d_tokens,
+                 void* stream) {
+  g_err.clear();
+  if (!d_logits || !cfg || !d_tokens) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  if (n <= 0 || vocab <= 0) return fail(QWEN3_E_INVALID_ARGUMENT, "n and vocab must be positive");
+  const qwen3_sampler_config& c = *cfg;
+  if (!std::isfinite(c.temperature)) return fail(QWEN3_E_INVALID_ARGUMENT, "temperature is not finite");
+  if (c.top_k < 0) return fail(QWEN3_E_INVALID_ARGUMENT, "top_k < 0");
+  if (!(c.top_p > 0.f && c.top_p <= 1.f)) return fail(QWEN3_E_INVALID_ARGUMENT, "top_p outside (0, 1]");
+  if (!(c.min_p >= 0.f && c.min_p <= 1.f)) return fail(QWEN3_E_INVALID_ARGUMENT, "min_p outside [0, 1]");
+  if (!(c.repeat_penalty > 0.f) || !std::isfinite(c.repeat_penalty) || !std::isfinite(c.freq_penalty) ||
+      !std::isfinite(c.presence_penalty))
+    return fail(QWEN3_E_INVALID_ARGUMENT, "penalties must be finite and repeat_penalty > 0");
+  if (c.repeat_last_n < 0 || c.repeat_last_n > 4096) return fail(QWEN3_E_INVALID_ARGUMENT, "repeat_last_n outside [0, 4096]");
+  if (d_history && (!d_history_len || history_stride <= 0))
+    return fail(QWEN3_E_INVALID_ARGUMENT, "a history needs its lengths and a positive stride");
+  if (c.temperature > 0.f && !d_uniform) return fail(QWEN3_E_INVALID_ARGUMENT, "d_uniform is required when sampling");
+  SampleArgs a{};
+  a.temperature = c.temperature;
+  a.top_k = c.top_k;
+  a.top_p = c.top_p;
+  a.min_p = c.min_p;
+  a.repeat_penalty = c.repeat_penalty;
+  a.freq_penalty = c.freq_penalty;
+  a.presence_penalty = c.presence_penalty;
+  a.repeat_last_n = c.repeat_last_n;
+  HIP_TRY(q8k::sample(d_logits, n, vocab, a, d_history, history_stride, d_history_len, d_uniform, d_tokens,
+                      S(stream)));
+  return QWEN3_OK;
+}
+
 int qwen3_bf16_linear(const float* d_x, int64_t m, int64_t k, const uint16_t* d_w, int64_t n, float* d_y,
                       void* stream) {
   g_err.clear();

@@ -122,6 +122,44 @@ def q8_0_linear(x: torch.Tensor, qs: torch.Tensor, sc: torch.Tensor) -> torch.Te
     return y
 
 
+def sample(
+    logits: torch.Tensor,
+    uniform: torch.Tensor | None,
+    temperature: float = 0.0,
+    top_k: int = 0,
+    top_p: float = 1.0,
+    min_p: float = 0.0,
+    repeat_penalty: float = 1.0,
+    freq_penalty: float = 0.0,
+    presence_penalty: float = 0.0,
+    repeat_last_n: int = 64,
+    history: torch.Tensor | None = None,
+    history_len: torch.Tensor | None = None,
+) -> torch.Tensor:
+    """One token per row of f32 logits [n, V] (penalised in place); uniform
+    f32 [n] in [0, 1); history int32 [n, stride] with history_len int32 [n]."""
+    from ._lib import SamplerConfig
+
+    n, V = logits.shape
+    cfg = SamplerConfig(temperature, top_k, top_p, min_p, repeat_penalty, freq_penalty, presence_penalty, repeat_last_n)
+    out = torch.empty(n, dtype=torch.int32, device=logits.device)
+    check(
+        lib().qwen3_sample(
+            logits.data_ptr(),
+            n,
+            V,
+            C.byref(cfg),
+            _ptr(history),
+            int(history.shape[1]) if history is not None else 0,
+            _ptr(history_len),
+            _ptr(uniform),
+            out.data_ptr(),
+            _stream(),
+        )
+    )
+    return out
+
+
 def bf16_linear(x: torch.Tensor, w_bits: torch.Tensor) -> torch.Tensor:
     """x f32 [m, k] times bf16 weights (int16 bits [n, k]) transposed -> f32 [m, n]."""
     m, k = x.shape
