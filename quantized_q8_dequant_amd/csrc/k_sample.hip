@@ -34,6 +34,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxCand = 256;      // top_k cap (the pages' candidate limit)
 constexpr int kMaxWindow = 4096;   // exact-nucleus window cap (LDS)
+constexpr int kHists = kWaves / 2; // radix histograms (fewer same-bin atomics per copy)
 
 QDEV uint32_t okey(float v) {  // order-preserving bits; -0 and +0 tie
   const uint32_t u = __float_as_uint(v + 0.0f);
@@ -117,7 +118,8 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
                                                      const float* __restrict__ uni, int32_t* __restrict__ out) {
   __shared__ unsigned long long s_cand[kMaxWindow];  // (key << 32) | ~id; after the sort, the f64 cumulative p
   __shared__ int s_id[kMaxWindow];
-  __shared__ unsigned s_hist[256];
+  __shared__ unsigned s_hist[kHists][256];  // one histogram per pair of wavefronts
+  __shared__ int s_cnt[2];
   __shared__ int s_iw[kWaves + 1];
   __shared__ double s_dw[kWaves + 1];
   __shared__ float s_bv[kWaves];
@@ -171,27 +173,35 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   int W = a.top_k > 0 ? min(min(a.top_k, kMaxCand), V) : min(kMaxCand, V);
   const int C = (V + kThreads - 1) / kThreads;  // contiguous chunk per thread (keeps ids in order)
   for (;;) {
-    // radix select: the key of the W-th best candidate
+    // radix select: the key of the W-th best candidate (pairs of wavefronts
+    // count into their own histogram; the bins are then summed in order)
     if (tid == 0) s_sel[0] = 0u, s_sel[1] = (unsigned)W;
     unsigned mask = 0u;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += kThreads) s_hist[b] = 0u;
+      for (int b = tid; b < kHists * 256; b += kThreads) s_hist[b / 256][b % 256] = 0u;
       __syncthreads();
       const unsigned prefix = s_sel[0];
       for (int j = tid; j < V; j += kThreads) {
         const uint32_t k = okey(l[j]);
-        if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+        if ((k & mask) == prefix) atomicAdd(&s_hist[wave / 2][(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 256) {
+        unsigned t = 0u;
+        for (int w = 0; w < kHists; ++w) t += s_hist[w][tid];
+        s_hist[0][tid] = t;
       }
       __syncthreads();
       if (tid == 0) {
         unsigned rem = s_sel[1], acc = 0u;
         int b = 255;
         for (; b > 0; --b) {
-          if (acc + s_hist[b] >= rem) break;
-          acc += s_hist[b];
+          if (acc + s_hist[0][b] >= rem) break;
+          acc += s_hist[0][b];
         }
         s_sel[0] = prefix | ((unsigned)b << shift);
         s_sel[1] = rem - acc;
+        s_sel[2] = s_hist[0][b];  // after the last pass: the count of keys equal to the threshold
       }
       mask |= 255u << shift;
       __syncthreads();
@@ -199,31 +209,48 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
     const uint32_t thr = s_sel[0];
     const int need_eq = (int)s_sel[1];  // >= 1 candidates with key == thr, in id order
     const int cnt_gt = W - need_eq;
+    const int all_eq = (int)s_sel[2];
 
-    // gather
-    int ngt = 0, neq = 0;
-    const int j0 = tid * C, j1 = min(V, j0 + C);
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t k = okey(l[j]);
-      ngt += k > thr;
-      neq += k == thr;
-    }
-    int tot;
-    int ogt = block_exclusive_scan(ngt, s_iw, &tot);
-    int oeq = block_exclusive_scan(neq, s_iw, &tot);
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t k = okey(l[j]);
-      const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
-      if (k > thr) {
-        s_cand[ogt++] = c;
-      } else if (k == thr) {
-        if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
-        ++oeq;
+    // gather.  Usually every key equal to the threshold fits in the window:
+    // then all of them are taken with strided (coalesced) reads into slots
+    // from a counter, the sort orders them (ties by id) and the first W are
+    // kept.  Otherwise each thread scans its own contiguous chunk, so equal
+    // keys are taken in id order.
+    int NC = W;  // candidates gathered
+    if (cnt_gt + all_eq <= kMaxWindow) {
+      NC = cnt_gt + all_eq;
+      if (tid == 0) s_cnt[0] = 0;
+      __syncthreads();
+      for (int j = tid; j < V; j += kThreads) {
+        const uint32_t k = okey(l[j]);
+        if (k >= thr) s_cand[atomicAdd(&s_cnt[0], 1)] = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+      }
+    } else {
+      int ngt = 0, neq = 0;
+      const int j0 = tid * C, j1 = min(V, j0 + C);
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t k = okey(l[j]);
+        ngt += k > thr;
+        neq += k == thr;
+      }
+      int tot;
+      int ogt = block_exclusive_scan(ngt, s_iw, &tot);
+      int oeq = block_exclusive_scan(neq, s_iw, &tot);
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t k = okey(l[j]);
+        const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+        if (k > thr) {
+          s_cand[ogt++] = c;
+        } else if (k == thr) {
+          if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
+          ++oeq;
+        }
       }
     }
     int W2 = 1;
-    while (W2 < W) W2 <<= 1;
-    for (int i = W + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
+    while (W2 < NC) W2 <<= 1;
+    __syncthreads();
+    for (int i = NC + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
     __syncthreads();
 
     // bitonic sort, descending
