@@ -302,10 +302,13 @@ typedef struct qwen3_sampler_config {
  * d_history_len[r] entries of row r valid, most recent last (NULL: no
  * penalties), d_uniform f32 [n] one uniform in [0, 1) per row (the draw's
  * random number; unused when greedy, may then be NULL), d_tokens int32 [n]
- * out.  QWEN3_E_INVALID_ARGUMENT for a null or out-of-range argument. */
+ * out, d_work device scratch of qwen3_sample_work_bytes(n, vocab) bytes
+ * (caller-owned, 256-byte aligned; each row's candidates per slice of 4096
+ * logits).  QWEN3_E_INVALID_ARGUMENT for a null or out-of-range argument. */
+size_t qwen3_sample_work_bytes(int32_t n, int32_t vocab);
 int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_config* cfg,
                  const int32_t* d_history, int32_t history_stride, const int32_t* d_history_len,
-                 const float* d_uniform, int32_t* d_tokens, void* stream);
+                 const float* d_uniform, int32_t* d_tokens, void* d_work, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,7 @@ EXPORTS = (
     "qwen3_prefill",
     "qwen3_prefill_all_logits",
     "qwen3_truncate",
+    "qwen3_sample_work_bytes",
     "qwen3_sample",
     "qwen3_decode_step",
     "qwen3_decode_batch",
@@ -145,7 +146,8 @@ def lib() -> C.CDLL:
         "qwen3_prefill": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
         "qwen3_prefill_all_logits": (C.c_int, [vp, i32, p_i32, i32, vp, vp, vp]),
         "qwen3_truncate": (C.c_int, [vp, i32, i32, vp]),
-        "qwen3_sample": (C.c_int, [vp, i32, i32, C.POINTER(SamplerConfig), vp, i32, vp, vp, vp, vp]),
+        "qwen3_sample_work_bytes": (C.c_size_t, [i32, i32]),
+        "qwen3_sample": (C.c_int, [vp, i32, i32, C.POINTER(SamplerConfig), vp, i32, vp, vp, vp, vp, vp]),
         "qwen3_decode_step": (C.c_int, [vp, i32, vp, vp, vp, vp]),
         "qwen3_decode_batch": (C.c_int, [vp, p_i32, i32, vp, vp, vp, vp]),
         "qwen3_reset": (C.c_int, [vp, i32, vp]),

@@ -9,14 +9,22 @@
 // (positive) or multiplied (negative) by repeat_penalty, then c * freq +
 // presence subtracted, in f64, rounded back to f32 once.
 //
+// k_sample_slices: one workgroup per (4096-logit slice, row): the slice's
+// max (lowest index on ties), its partial softmax denominator (exact
+// nucleus) and its list of keys at or above its W1-th best, by a radix
+// select on order-preserving 32-bit keys (four 8-bit passes of LDS
+// histograms: the counts are exact, so the cut is too).
+//
 // k_sample: one 1024-thread workgroup per row.
-//   - max and argmax (lowest index): the greedy answer when temperature <= 0;
+//   - max and argmax from the slices': the greedy answer when temperature <= 0;
 //   - the W best candidates (W = min(top_k, 256), or the exact-nucleus window
-//     256, 1024, 4096 when top_k == 0) by a radix select on order-preserving
-//     32-bit keys (four 8-bit passes of LDS histograms; counts are exact, so
-//     the threshold is too), then a gather that keeps equal keys in token
-//     order, then a bitonic sort of (key, inverted id) in LDS: descending
-//     logit, ties by lower id;
+//     256, 1024, 4096 when top_k == 0), descending logit, ties by lower id.
+//     The union of the slices' lists holds every key at or above the highest
+//     cut T* of a partial list.  A union that fits the LDS window is copied
+//     and bitonic-sorted once; its prefix of keys >= T* serves every window
+//     it covers.  Otherwise a radix select over the union (checked against
+//     T*) or over the whole row gives the W-th key, a gather takes the keys
+//     at or above it (ties in id order) and a bitonic sort orders them;
 //   - p_i = exp((l_i - l_max) / T) / Z in f64, Z over the W candidates
 //     (top_k > 0) or over the whole row (top_k == 0), an inclusive f64 scan,
 //     the top-p prefix, the min-p prefix, and the inverse-CDF draw of the
@@ -35,6 +43,18 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxCand = 256;      // top_k cap (the pages' candidate limit)
 constexpr int kMaxWindow = 4096;   // exact-nucleus window cap (LDS)
 constexpr int kHists = kWaves / 2; // radix histograms (fewer same-bin atomics per copy)
+
+// Stage-1 results: per (row, slice) the max, its lowest index, the partial
+// denominator and the candidate list (kSlice slots, cnt used).
+struct SliceScratch {
+  unsigned long long* cand;
+  double* z;
+  float* m;
+  int* am;
+  int* cnt;
+  unsigned* thr;  // the list's cut (its W1-th best key), 0 when it holds the whole slice
+  int S;
+};
 
 QDEV uint32_t okey(float v) {  // order-preserving bits; -0 and +0 tie
   const uint32_t u = __float_as_uint(v + 0.0f);
@@ -69,6 +89,114 @@ __global__ void __launch_bounds__(256) k_penalties(float* __restrict__ logits, i
     v = v > 0 ? v / (double)a.repeat_penalty : v * (double)a.repeat_penalty;
     v = v - ((double)c * (double)a.freq_penalty + (double)a.presence_penalty);
     *p = (float)v;
+  }
+}
+
+// f(j, l[j]) for every j < V, by all threads of the workgroup.  With V a
+// multiple of 4 (rows 16-byte aligned) each thread keeps four float4 loads in
+// flight per step: one load at a time would leave every pass waiting out the
+// memory latency once per element group.
+template <typename F>
+QDEV void for_row(const float* __restrict__ l, int V, F&& f) {
+  const int tid = threadIdx.x;
+  if ((V & 3) == 0) {
+    const float4* l4 = reinterpret_cast<const float4*>(l);
+    const int V4 = V / 4;
+    for (int base = 0; base < V4; base += 4 * kThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kThreads + tid;
+        v[u] = i < V4 ? l4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kThreads + tid;
+        if (i < V4) {
+          f(4 * i, v[u].x);
+          f(4 * i + 1, v[u].y);
+          f(4 * i + 2, v[u].z);
+          f(4 * i + 3, v[u].w);
+        }
+      }
+    }
+  } else {
+    for (int j = tid; j < V; j += kThreads) f(j, l[j]);
+  }
+}
+
+// A slot in an LDS list for each lane whose `take` is set: one atomic per
+// wavefront (its lanes' count), each lane offset by the taking lanes below it.
+QDEV int claim_slot(bool take, int* counter) {
+  const int lane = threadIdx.x % kWave;
+  const unsigned long long m = __ballot(take);
+  if (m == 0ull) return -1;
+  const int leader = __ffsll((long long)m) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, leader);
+  return take ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+}
+
+// The bin (8 bits at `shift`) of the rem-th largest counted key, for radix
+// select: every thread of the workgroup calls it; thread t < 256 takes bin
+// 255 - t, so a prefix scan over t counts the keys in the bins above.  One
+// bin satisfies above < rem <= above + count; it writes the prefix, the rank
+// left within it and its count to s_sel.
+template <int NW>
+QDEV void pick_bin(const unsigned* hist, unsigned* s_w, unsigned* s_sel, int shift) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const unsigned rem = s_sel[1], prefix = s_sel[0];
+  const unsigned c = tid < 256 ? hist[255 - tid] : 0u;
+  unsigned inc = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned n = __shfl_up(inc, o);
+    if (lane >= o) inc += n;
+  }
+  if (lane == kWave - 1) s_w[wave] = inc;
+  __syncthreads();
+  unsigned before = 0u;
+  for (int w = 0; w < wave && w < NW; ++w) before += s_w[w];
+  const unsigned above = before + inc - c;
+  __syncthreads();  // every thread has read s_sel and s_w
+  if (tid < 256 && above < rem && above + c >= rem) {
+    s_sel[0] = prefix | ((unsigned)(255 - tid) << shift);
+    s_sel[1] = rem - above;
+    s_sel[2] = c;
+  }
+}
+
+// As for_row, but every thread calls f(j, v, valid) the same number of
+// times (valid == false past the row), for callers that ballot.
+template <typename F>
+QDEV void for_row_all(const float* __restrict__ l, int V, F&& f) {
+  const int tid = threadIdx.x;
+  if ((V & 3) == 0) {
+    const float4* l4 = reinterpret_cast<const float4*>(l);
+    const int V4 = V / 4;
+    for (int base = 0; base < V4; base += 4 * kThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kThreads + tid;
+        v[u] = i < V4 ? l4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kThreads + tid;
+        const bool ok = i < V4;
+        f(4 * i, v[u].x, ok);
+        f(4 * i + 1, v[u].y, ok);
+        f(4 * i + 2, v[u].z, ok);
+        f(4 * i + 3, v[u].w, ok);
+      }
+    }
+  } else {
+    for (int base = 0; base < V; base += kThreads) {
+      const int j = base + tid;
+      f(j, j < V ? l[j] : 0.f, j < V);
+    }
   }
 }
 
@@ -114,31 +242,42 @@ QDEV T block_sum(T v, T* s_w) {  // fixed order: lanes by halving, then waves in
   return t;
 }
 
-__global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ logits, int V, SampleArgs a,
-                                                     const float* __restrict__ uni, int32_t* __restrict__ out) {
-  __shared__ unsigned long long s_cand[kMaxWindow];  // (key << 32) | ~id; after the sort, the f64 cumulative p
-  __shared__ int s_id[kMaxWindow];
-  __shared__ unsigned s_hist[kHists][256];  // one histogram per pair of wavefronts
-  __shared__ int s_cnt[2];
-  __shared__ int s_iw[kWaves + 1];
-  __shared__ double s_dw[kWaves + 1];
-  __shared__ float s_bv[kWaves];
-  __shared__ int s_bi[kWaves];
-  __shared__ unsigned s_sel[3];  // prefix, remaining, found bin
-  __shared__ int s_pos[2];       // top-p and min-p prefix lengths, then the pick
-  __shared__ double s_z[1];      // the softmax denominator of the candidates
-  double* s_cum = reinterpret_cast<double*>(s_cand);
+// Stage 1: one 256-thread workgroup per (slice of kSlice logits, row): the
+// slice's max and its lowest index, its partial denominator relative to its
+// own max (exact nucleus), and every logit at or above the slice's W1-th
+// best (radix select on 16 keys per thread), written as (key << 32) | ~id.
+// The union of the slices' lists holds the row's best W1.
+constexpr int kSlice = 4096;
+constexpr int kSliceThreads = 256;
+constexpr int kSliceWaves = kSliceThreads / kWave;
 
-  const int row = blockIdx.x, tid = threadIdx.x;
+__global__ void __launch_bounds__(kSliceThreads) k_sample_slices(const float* __restrict__ logits, int V, SampleArgs a,
+                                                                 int W1, SliceScratch ss) {
+  __shared__ unsigned s_hist[kSliceWaves][256];
+  __shared__ float s_bv[kSliceWaves];
+  __shared__ int s_bi[kSliceWaves];
+  __shared__ double s_dz[kSliceWaves];
+  __shared__ unsigned s_sel[3];
+  __shared__ unsigned s_uw[kSliceWaves];
+  __shared__ int s_n;
+  const int sl = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
-  const float* l = logits + (int64_t)row * V;
-
-  // max and the lowest index of it
+  const int j0 = sl * kSlice;
+  const int n = min(kSlice, V - j0);
+  const float* l = logits + (int64_t)row * V + j0;
+  constexpr int PER = kSlice / kSliceThreads;  // 16
+  float v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * kSliceThreads;
+    v[k] = i < n ? l[i] : -__builtin_inff();
+  }
   float bv = -__builtin_inff();
   int bi = 0x7FFFFFFF;
-  for (int j = tid; j < V; j += kThreads) {
-    const float v = l[j];
-    if (v > bv || (v == bv && j < bi)) bv = v, bi = j;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * kSliceThreads;
+    if (i < n && (v[k] > bv || (v[k] == bv && j0 + i < bi))) bv = v[k], bi = j0 + i;
   }
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {
@@ -149,9 +288,124 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   if (lane == 0) s_bv[wave] = bv, s_bi[wave] = bi;
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kWaves; ++w)
+    for (int w = 1; w < kSliceWaves; ++w)
       if (s_bv[w] > bv || (s_bv[w] == bv && s_bi[w] < bi)) bv = s_bv[w], bi = s_bi[w];
-    s_bv[0] = bv, s_bi[0] = bi;
+    const int64_t o = (int64_t)row * ss.S + sl;
+    ss.m[o] = bv;
+    ss.am[o] = bi;
+    s_bv[0] = bv;
+  }
+  __syncthreads();
+  if (!(a.temperature > 0.f)) return;  // greedy: the maxima are all stage 2 needs
+  const float ms = s_bv[0];
+  if (a.top_k == 0) {
+    double z = 0.0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if (tid + k * kSliceThreads < n) z += exp(((double)v[k] - (double)ms) / (double)a.temperature);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    if (lane == 0) s_dz[wave] = z;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+      for (int w = 0; w < kSliceWaves; ++w) t += s_dz[w];
+      ss.z[(int64_t)row * ss.S + sl] = t;
+    }
+  }
+  // the slice's W1-th best key
+  const int w1 = min(W1, n);
+  uint32_t key[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) key[k] = tid + k * kSliceThreads < n ? okey(v[k]) : 0u;
+  if (tid == 0) s_sel[0] = 0u, s_sel[1] = (unsigned)w1, s_n = 0;
+  unsigned mask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < kSliceWaves * 256; b += kSliceThreads) s_hist[b / 256][b % 256] = 0u;
+    __syncthreads();
+    const unsigned prefix = s_sel[0];
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if (tid + k * kSliceThreads < n && (key[k] & mask) == prefix) atomicAdd(&s_hist[wave][(key[k] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 256) {
+      unsigned t = 0u;
+      for (int w = 0; w < kSliceWaves; ++w) t += s_hist[w][tid];
+      s_hist[0][tid] = t;
+    }
+    __syncthreads();
+    pick_bin<kSliceWaves>(s_hist[0], s_uw, s_sel, shift);
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = s_sel[0];
+  unsigned long long* dst = ss.cand + ((int64_t)row * ss.S + sl) * kSlice;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * kSliceThreads;
+    const bool take = i < n && key[k] >= thr;
+    const int slot = claim_slot(take, &s_n);
+    if (take) dst[slot] = ((unsigned long long)key[k] << 32) | (0xFFFFFFFFu - (uint32_t)(j0 + i));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ss.cnt[(int64_t)row * ss.S + sl] = s_n;
+    ss.thr[(int64_t)row * ss.S + sl] = n > W1 ? thr : 0u;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ logits, int V, SampleArgs a,
+                                                     const float* __restrict__ uni, int32_t* __restrict__ out,
+                                                     SliceScratch ss) {
+  __shared__ unsigned long long s_cand[kMaxWindow];  // (key << 32) | ~id, sorted descending
+  __shared__ double s_cum[kMaxWindow];               // inclusive cumulative p of the window
+  __shared__ int s_id[kMaxWindow];
+  __shared__ unsigned s_hist[kHists][256];  // one histogram per pair of wavefronts
+  __shared__ int s_cnt[2];
+  __shared__ int s_iw[kWaves + 1];
+  __shared__ double s_dw[kWaves + 1];
+  __shared__ float s_bv[kWaves];
+  __shared__ int s_bi[kWaves];
+  __shared__ unsigned s_sel[3];  // prefix, remaining rank, the bin's count
+  __shared__ unsigned s_uw[kWaves];
+  __shared__ unsigned s_ut[kWaves];
+  __shared__ int s_pos[2];       // top-p and min-p prefix lengths, then the pick
+  __shared__ double s_z[1];      // the softmax denominator of the candidates
+
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
+  const float* l = logits + (int64_t)row * V;
+  const int64_t r0 = (int64_t)row * ss.S;
+
+  // max and the lowest index of it, from the slices' maxima; the union's
+  // size U and the highest cut T* among the slices whose list is partial
+  float bv = -__builtin_inff();
+  int bi = 0x7FFFFFFF, U = 0;
+  unsigned tstar = 0u;
+  for (int sl = tid; sl < ss.S; sl += kThreads) {
+    const float v = ss.m[r0 + sl];
+    const int j = ss.am[r0 + sl];
+    if (v > bv || (v == bv && j < bi)) bv = v, bi = j;
+    U += ss.cnt[r0 + sl];
+    tstar = max(tstar, ss.thr[r0 + sl]);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) bv = ov, bi = oi;
+    U += __shfl_xor(U, o);
+    tstar = max(tstar, (unsigned)__shfl_xor((int)tstar, o));
+  }
+  if (lane == 0) s_bv[wave] = bv, s_bi[wave] = bi, s_iw[wave] = U, s_ut[wave] = tstar;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kWaves; ++w) {
+      if (s_bv[w] > bv || (s_bv[w] == bv && s_bi[w] < bi)) bv = s_bv[w], bi = s_bi[w];
+      U += s_iw[w];
+      tstar = max(tstar, s_ut[w]);
+    }
+    s_bv[0] = bv, s_bi[0] = bi, s_iw[kWaves] = U, s_ut[0] = tstar;
   }
   __syncthreads();
   const float fmax = s_bv[0];
@@ -159,104 +413,31 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
     if (tid == 0) out[row] = s_bi[0];
     return;
   }
+  U = s_iw[kWaves];
+  tstar = s_ut[0];
   const double lmax = (double)fmax, T = (double)a.temperature;
   const double top_p = (double)a.top_p;
 
-  // the whole-row denominator of the exact nucleus
+  // the whole-row denominator of the exact nucleus: the slices' partials,
+  // each rescaled from its own max to the row's, added in slice order
   double zfull = 0.0;
-  if (a.top_k == 0) {
-    double z = 0.0;
-    for (int j = tid; j < V; j += kThreads) z += exp(((double)l[j] - lmax) / T);
-    zfull = block_sum(z, s_dw);
+  if (a.top_k == 0 && tid == 0) {
+    for (int sl = 0; sl < ss.S; ++sl) zfull += ss.z[r0 + sl] * exp(((double)ss.m[r0 + sl] - lmax) / T);
+    s_z[0] = zfull;
   }
+  __syncthreads();
+  zfull = s_z[0];
+  __syncthreads();
 
-  int W = a.top_k > 0 ? min(min(a.top_k, kMaxCand), V) : min(kMaxCand, V);
-  const int C = (V + kThreads - 1) / kThreads;  // contiguous chunk per thread (keeps ids in order)
-  for (;;) {
-    // radix select: the key of the W-th best candidate (pairs of wavefronts
-    // count into their own histogram; the bins are then summed in order)
-    if (tid == 0) s_sel[0] = 0u, s_sel[1] = (unsigned)W;
-    unsigned mask = 0u;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < kHists * 256; b += kThreads) s_hist[b / 256][b % 256] = 0u;
-      __syncthreads();
-      const unsigned prefix = s_sel[0];
-      for (int j = tid; j < V; j += kThreads) {
-        const uint32_t k = okey(l[j]);
-        if ((k & mask) == prefix) atomicAdd(&s_hist[wave / 2][(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 256) {
-        unsigned t = 0u;
-        for (int w = 0; w < kHists; ++w) t += s_hist[w][tid];
-        s_hist[0][tid] = t;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        unsigned rem = s_sel[1], acc = 0u;
-        int b = 255;
-        for (; b > 0; --b) {
-          if (acc + s_hist[0][b] >= rem) break;
-          acc += s_hist[0][b];
-        }
-        s_sel[0] = prefix | ((unsigned)b << shift);
-        s_sel[1] = rem - acc;
-        s_sel[2] = s_hist[0][b];  // after the last pass: the count of keys equal to the threshold
-      }
-      mask |= 255u << shift;
-      __syncthreads();
-    }
-    const uint32_t thr = s_sel[0];
-    const int need_eq = (int)s_sel[1];  // >= 1 candidates with key == thr, in id order
-    const int cnt_gt = W - need_eq;
-    const int all_eq = (int)s_sel[2];
-
-    // gather.  Usually every key equal to the threshold fits in the window:
-    // then all of them are taken with strided (coalesced) reads into slots
-    // from a counter, the sort orders them (ties by id) and the first W are
-    // kept.  Otherwise each thread scans its own contiguous chunk, so equal
-    // keys are taken in id order.
-    int NC = W;  // candidates gathered
-    if (cnt_gt + all_eq <= kMaxWindow) {
-      NC = cnt_gt + all_eq;
-      if (tid == 0) s_cnt[0] = 0;
-      __syncthreads();
-      for (int j = tid; j < V; j += kThreads) {
-        const uint32_t k = okey(l[j]);
-        if (k >= thr) s_cand[atomicAdd(&s_cnt[0], 1)] = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
-      }
-    } else {
-      int ngt = 0, neq = 0;
-      const int j0 = tid * C, j1 = min(V, j0 + C);
-      for (int j = j0; j < j1; ++j) {
-        const uint32_t k = okey(l[j]);
-        ngt += k > thr;
-        neq += k == thr;
-      }
-      int tot;
-      int ogt = block_exclusive_scan(ngt, s_iw, &tot);
-      int oeq = block_exclusive_scan(neq, s_iw, &tot);
-      for (int j = j0; j < j1; ++j) {
-        const uint32_t k = okey(l[j]);
-        const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
-        if (k > thr) {
-          s_cand[ogt++] = c;
-        } else if (k == thr) {
-          if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
-          ++oeq;
-        }
-      }
-    }
-    int W2 = 1;
-    while (W2 < NC) W2 <<= 1;
-    __syncthreads();
-    for (int i = NC + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
-    __syncthreads();
-
-    // bitonic sort, descending
-    for (int k = 2; k <= W2; k <<= 1) {
+  // The union of the slices' lists holds every key >= T* of the row (a
+  // partial list holds all of its slice's keys >= its cut).  So the top W of
+  // the union are the row's top W whenever the W-th of them is >= T*.
+  const unsigned long long* crow = ss.cand + r0 * kSlice;
+  const int* nrow = ss.cnt + r0;
+  auto sort_desc = [&](int n2) {  // bitonic sort of s_cand[0, n2), n2 a power of two
+    for (int k = 2; k <= n2; k <<= 1) {
       for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < W2; i += kThreads) {
+        for (int i = tid; i < n2; i += kThreads) {
           const int p = i ^ jj;
           if (p > i) {
             const unsigned long long x = s_cand[i], y = s_cand[p];
@@ -266,6 +447,152 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
         }
         __syncthreads();
       }
+    }
+  };
+  auto pow2_at_least = [](int n) {
+    int w = 1;
+    while (w < n) w <<= 1;
+    return w;
+  };
+
+  // A small union is copied whole into LDS and sorted once: its prefix of
+  // keys >= T* (NV entries) serves every window up to NV.
+  int NV = 0;
+  bool sorted_union = U <= kMaxWindow;
+  if (sorted_union) {
+    if (tid == 0) s_cnt[0] = 0, s_cnt[1] = 0;
+    __syncthreads();
+    for (int sl = wave; sl < ss.S; sl += kWaves) {
+      const int c = nrow[sl];
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_cnt[0], c);
+      base = __shfl(base, 0);
+      for (int i = lane; i < c; i += kWave) s_cand[base + i] = crow[(int64_t)sl * kSlice + i];
+    }
+    const int W2 = pow2_at_least(U);
+    __syncthreads();
+    for (int i = U + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
+    __syncthreads();
+    sort_desc(W2);
+    for (int i = tid; i < U; i += kThreads)
+      if ((uint32_t)(s_cand[i] >> 32) >= tstar && (i + 1 == U || (uint32_t)(s_cand[i + 1] >> 32) < tstar))
+        s_cnt[1] = i + 1;
+    __syncthreads();
+    NV = s_cnt[1];
+    __syncthreads();
+  }
+
+  // element sources for a radix select: the union (wavefront by slice) or
+  // the whole row.  f(key, id, valid) is called by every lane of a wavefront
+  // the same number of times (valid == false past the end), so it can ballot.
+  bool from_union = true;
+  auto for_elems = [&](auto&& f) {
+    if (from_union) {
+      for (int sl = wave; sl < ss.S; sl += kWaves) {
+        const int c = nrow[sl];
+        const unsigned long long* src = crow + (int64_t)sl * kSlice;
+        for (int base = 0; base < c; base += 4 * kWave) {
+          unsigned long long e[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = base + u * kWave + lane;
+            e[u] = i < c ? src[i] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            f((uint32_t)(e[u] >> 32), (int)(0xFFFFFFFFu - (uint32_t)(e[u] & 0xFFFFFFFFull)),
+              base + u * kWave + lane < c);
+        }
+      }
+    } else {
+      for_row_all(l, V, [&](int j, float v, bool valid) { f(okey(v), j, valid); });
+    }
+  };
+
+  int W = a.top_k > 0 ? min(min(a.top_k, kMaxCand), V) : min(kMaxCand, V);
+  const int C = (V + kThreads - 1) / kThreads;  // contiguous chunk per thread (keeps ids in order)
+  for (;;) {
+    if (sorted_union && W > NV) {
+      sorted_union = false;  // past the union's valid prefix: select over the row
+      from_union = false;
+    }
+    if (!sorted_union) {
+      // radix select: the key of the W-th best candidate (pairs of
+      // wavefronts count into their own histogram; the bins are then summed)
+      if (tid == 0) s_sel[0] = 0u, s_sel[1] = (unsigned)W;
+      unsigned mask = 0u;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int b = tid; b < kHists * 256; b += kThreads) s_hist[b / 256][b % 256] = 0u;
+        __syncthreads();
+        const unsigned prefix = s_sel[0];
+        for_elems([&](uint32_t k, int, bool valid) {
+          if (valid && (k & mask) == prefix) atomicAdd(&s_hist[wave / 2][(k >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        if (tid < 256) {
+          unsigned t = 0u;
+          for (int w = 0; w < kHists; ++w) t += s_hist[w][tid];
+          s_hist[0][tid] = t;
+        }
+        __syncthreads();
+        pick_bin<kWaves>(s_hist[0], s_uw, s_sel, shift);  // s_sel[2]: after the last pass, the ties
+        mask |= 255u << shift;
+        __syncthreads();
+      }
+      const uint32_t thr = s_sel[0];
+      const int need_eq = (int)s_sel[1];  // >= 1 candidates with key == thr, in id order
+      const int cnt_gt = W - need_eq;
+      const int all_eq = (int)s_sel[2];
+      if (from_union && (thr < tstar || cnt_gt + all_eq > kMaxWindow)) {
+        // the union may miss keys of the window, or too many ties for the
+        // window: redo over the row
+        from_union = false;
+        __syncthreads();
+        continue;
+      }
+
+      // gather.  Usually every key equal to the threshold fits in the
+      // window: then all of them are taken into slots from a counter, the
+      // sort orders them (ties by id) and the first W are kept.  Otherwise
+      // each thread scans its own contiguous chunk of the row, so equal keys
+      // are taken in id order.
+      int NC = W;  // candidates gathered
+      if (cnt_gt + all_eq <= kMaxWindow) {
+        NC = cnt_gt + all_eq;
+        if (tid == 0) s_cnt[0] = 0;
+        __syncthreads();
+        for_elems([&](uint32_t k, int j, bool valid) {
+          const bool take = valid && k >= thr;
+          const int slot = claim_slot(take, &s_cnt[0]);
+          if (take) s_cand[slot] = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+        });
+      } else {
+        int ngt = 0, neq = 0;
+        const int j0 = tid * C, j1 = min(V, j0 + C);
+        for (int j = j0; j < j1; ++j) {
+          const uint32_t k = okey(l[j]);
+          ngt += k > thr;
+          neq += k == thr;
+        }
+        int tot;
+        int ogt = block_exclusive_scan(ngt, s_iw, &tot);
+        int oeq = block_exclusive_scan(neq, s_iw, &tot);
+        for (int j = j0; j < j1; ++j) {
+          const uint32_t k = okey(l[j]);
+          const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+          if (k > thr) {
+            s_cand[ogt++] = c;
+          } else if (k == thr) {
+            if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
+            ++oeq;
+          }
+        }
+      }
+      const int W2 = pow2_at_least(NC);
+      __syncthreads();
+      for (int i = NC + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
+      __syncthreads();
+      sort_desc(W2);
     }
 
     // p_i in f64, then the inclusive scan (4 consecutive candidates per thread)
@@ -297,7 +624,6 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
     }
     double dtot;
     const double off = block_exclusive_scan(loc, s_dw, &dtot);
-    __syncthreads();  // every s_cand read above is done before s_cum overwrites it
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * tid + q;
@@ -321,10 +647,10 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
       if (s_cum[i] >= top_p && (i == 0 || s_cum[i - 1] < top_p)) s_pos[0] = i + 1;
   }
   if (a.min_p > 0.f) {
-    // p_i recomputed exactly as above; p descends, so p_i < min_p * p_0
-    // first holds at one index
+    // p_i recomputed exactly as above from the sorted keys; p descends, so
+    // p_i < min_p * p_0 first holds at one index
     const double z = s_z[0];
-    auto p_of = [&](int i) { return exp(((double)l[s_id[i]] - lmax) / T) / z; };
+    auto p_of = [&](int i) { return exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) / z; };
     const double thr = (double)a.min_p * p_of(0);
     for (int i = tid; i < W; i += kThreads)
       if (p_of(i) < thr && (i == 0 || !(p_of(i - 1) < thr))) s_pos[1] = i;
@@ -344,13 +670,35 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
 
 namespace q8k {
 
+size_t sample_work_bytes(int n, int V) {
+  const size_t S = (size_t)((V + kSlice - 1) / kSlice);
+  return (size_t)n * S * ((size_t)kSlice * 8 + 8 + 4 + 4 + 4 + 4) + 256;
+}
+
 hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_t* hist, int hstride,
-                  const int32_t* hlen, const float* uni, int32_t* out, hipStream_t s) {
+                  const int32_t* hlen, const float* uni, int32_t* out, void* work, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const bool penalise = hist && hlen && a.repeat_last_n > 0 &&
                         (a.repeat_penalty != 1.f || a.freq_penalty != 0.f || a.presence_penalty != 0.f);
   if (penalise) hipLaunchKernelGGL(k_penalties, dim3(n), dim3(256), 0, s, logits, V, hist, hstride, hlen, a);
-  hipLaunchKernelGGL(k_sample, dim3(n), dim3(kThreads), 0, s, logits, V, a, uni, out);
+  const int S = (V + kSlice - 1) / kSlice;
+  SliceScratch ss{};
+  ss.S = S;
+  uint8_t* w = static_cast<uint8_t*>(work);
+  const size_t rs = (size_t)n * S;
+  ss.cand = reinterpret_cast<unsigned long long*>(w);
+  ss.z = reinterpret_cast<double*>(w + rs * kSlice * 8);
+  ss.m = reinterpret_cast<float*>(w + rs * (kSlice * 8 + 8));
+  ss.am = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 12));
+  ss.cnt = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 16));
+  ss.thr = reinterpret_cast<unsigned*>(w + rs * (kSlice * 8 + 20));
+  // slice lists hold each slice's best W1: min(top_k, 256) for top-k (the
+  // union then holds the row's top k); for the exact nucleus, as many as
+  // keep the union within one LDS window (its valid prefix serves the
+  // windows it covers)
+  const int W1 = a.top_k > 0 ? min(a.top_k, kMaxCand) : max(1, kMaxWindow / S);
+  hipLaunchKernelGGL(k_sample_slices, dim3(S, n), dim3(kSliceThreads), 0, s, logits, V, a, W1, ss);
+  hipLaunchKernelGGL(k_sample, dim3(n), dim3(kThreads), 0, s, logits, V, a, uni, out, ss);
   return hipGetLastError();
 }
 

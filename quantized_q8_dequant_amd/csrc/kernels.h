@@ -98,8 +98,9 @@ hipError_t attn_decode(const AttnDecodeArgs& a, int hd, int group, int kvt, int 
 
 // Sampling: penalties in place (when any is active and a history is given),
 // then one token per row.
+size_t sample_work_bytes(int n, int V);
 hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_t* hist, int hstride,
-                  const int32_t* hlen, const float* uni, int32_t* out, hipStream_t s);
+                  const int32_t* hlen, const float* uni, int32_t* out, void* work, hipStream_t s);
 
 // Row argmax of f32 [T, V] (lowest index among equal maxima) -> out [T];
 // key [T] and counter [T] are zero between launches (and left so).  With

@@ -1100,11 +1100,17 @@ int qwen3_q8_0_block_dots(const float* d_x, int64_t m, int64_t k, const int8_t* 
   return QWEN3_OK;
 }
 
+size_t qwen3_sample_work_bytes(int32_t n, int32_t vocab) {
+  if (n <= 0 || vocab <= 0) return 0;
+  return q8k::sample_work_bytes(n, vocab);
+}
+
 int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_config* cfg, const int32_t* d_history,
                  int32_t history_stride, const int32_t* d_history_len, const float* d_uniform, int32_t* d_tokens,
-                 void* stream) {
+                 void* d_work, void* stream) {
   g_err.clear();
-  if (!d_logits || !cfg || !d_tokens) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  if (!d_logits || !cfg || !d_tokens || !d_work) return fail(QWEN3_E_INVALID_ARGUMENT, "null argument");
+  if (reinterpret_cast<uintptr_t>(d_work) % 256) return fail(QWEN3_E_INVALID_ARGUMENT, "d_work must be 256-byte aligned");
   if (n <= 0 || vocab <= 0) return fail(QWEN3_E_INVALID_ARGUMENT, "n and vocab must be positive");
   const qwen3_sampler_config& c = *cfg;
   if (!std::isfinite(c.temperature)) return fail(QWEN3_E_INVALID_ARGUMENT, "temperature is not finite");
@@ -1127,7 +1133,7 @@ int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_
   a.freq_penalty = c.freq_penalty;
   a.presence_penalty = c.presence_penalty;
   a.repeat_last_n = c.repeat_last_n;
-  HIP_TRY(q8k::sample(d_logits, n, vocab, a, d_history, history_stride, d_history_len, d_uniform, d_tokens,
+  HIP_TRY(q8k::sample(d_logits, n, vocab, a, d_history, history_stride, d_history_len, d_uniform, d_tokens, d_work,
                       S(stream)));
   return QWEN3_OK;
 }

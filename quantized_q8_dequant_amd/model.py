@@ -143,6 +143,7 @@ def sample(
     n, V = logits.shape
     cfg = SamplerConfig(temperature, top_k, top_p, min_p, repeat_penalty, freq_penalty, presence_penalty, repeat_last_n)
     out = torch.empty(n, dtype=torch.int32, device=logits.device)
+    work = torch.empty(lib().qwen3_sample_work_bytes(n, V), dtype=torch.uint8, device=logits.device)
     check(
         lib().qwen3_sample(
             logits.data_ptr(),
@@ -154,6 +155,7 @@ def sample(
             _ptr(history_len),
             _ptr(uniform),
             out.data_ptr(),
+            work.data_ptr(),
             _stream(),
         )
     )
