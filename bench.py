@@ -371,8 +371,8 @@ def bench_batched(shape, weights, prompt, args) -> dict:
 def bench_sampling(V: int, args) -> dict:
     """The device sampling pipeline on rows of V logits: a Qwen3-style
     setting (temperature 0.7, top-k 20, top-p 0.95, repetition penalty over
-    64 tokens) and the exact nucleus (top-k 0, top-p 0.9, its window grown to
-    1024 candidates on these logits), for 1 and 64 rows."""
+    64 tokens) and the exact nucleus (top-k 0, top-p 0.9: on these N(0, 4^2)
+    logits its window grows past 256 candidates), for 1 and 64 rows."""
     import torch
 
     from quantized_q8_dequant_amd import sample

@@ -20,11 +20,11 @@
 //   - the W best candidates (W = min(top_k, 256), or the exact-nucleus window
 //     256, 1024, 4096 when top_k == 0), descending logit, ties by lower id.
 //     The union of the slices' lists holds every key at or above the highest
-//     cut T* of a partial list.  A union that fits the LDS window is copied
-//     and bitonic-sorted once; its prefix of keys >= T* serves every window
-//     it covers.  Otherwise a radix select over the union (checked against
-//     T*) or over the whole row gives the W-th key, a gather takes the keys
-//     at or above it (ties in id order) and a bitonic sort orders them;
+//     cut T* of a partial list; a union of up to 8192 keys is copied to LDS.
+//     Per window a radix select over that copy (else over the union in
+//     memory; over the whole row when the union may miss keys of the
+//     window) gives the W-th key, a gather takes the keys at or above it
+//     (ties in id order) and a bitonic sort held in registers orders them;
 //   - p_i = exp((l_i - l_max) / T) / Z in f64, Z over the W candidates
 //     (top_k > 0) or over the whole row (top_k == 0), an inclusive f64 scan,
 //     the top-p prefix, the min-p prefix, and the inverse-CDF draw of the
@@ -42,6 +42,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxCand = 256;      // top_k cap (the pages' candidate limit)
 constexpr int kMaxWindow = 4096;   // exact-nucleus window cap (LDS)
+constexpr int kUnionCap = 8192;    // slice-list union copied to LDS
 constexpr int kHists = kWaves / 2; // radix histograms (fewer same-bin atomics per copy)
 
 // Stage-1 results: per (row, slice) the max, its lowest index, the partial
@@ -92,85 +93,13 @@ __global__ void __launch_bounds__(256) k_penalties(float* __restrict__ logits, i
   }
 }
 
-// f(j, l[j]) for every j < V, by all threads of the workgroup.  With V a
-// multiple of 4 (rows 16-byte aligned) each thread keeps four float4 loads in
-// flight per step: one load at a time would leave every pass waiting out the
-// memory latency once per element group.
+// f(j, l[j], valid) for every j < V, by all threads of the workgroup; every
+// thread calls f the same number of times (valid == false past the row), so
+// f may ballot.  With V a multiple of 4 (rows 16-byte aligned) each thread
+// keeps four float4 loads in flight per step: one load at a time would leave
+// every pass waiting out the memory latency once per element group.
 template <typename F>
 QDEV void for_row(const float* __restrict__ l, int V, F&& f) {
-  const int tid = threadIdx.x;
-  if ((V & 3) == 0) {
-    const float4* l4 = reinterpret_cast<const float4*>(l);
-    const int V4 = V / 4;
-    for (int base = 0; base < V4; base += 4 * kThreads) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = base + u * kThreads + tid;
-        v[u] = i < V4 ? l4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = base + u * kThreads + tid;
-        if (i < V4) {
-          f(4 * i, v[u].x);
-          f(4 * i + 1, v[u].y);
-          f(4 * i + 2, v[u].z);
-          f(4 * i + 3, v[u].w);
-        }
-      }
-    }
-  } else {
-    for (int j = tid; j < V; j += kThreads) f(j, l[j]);
-  }
-}
-
-// A slot in an LDS list for each lane whose `take` is set: one atomic per
-// wavefront (its lanes' count), each lane offset by the taking lanes below it.
-QDEV int claim_slot(bool take, int* counter) {
-  const int lane = threadIdx.x % kWave;
-  const unsigned long long m = __ballot(take);
-  if (m == 0ull) return -1;
-  const int leader = __ffsll((long long)m) - 1;
-  int base = 0;
-  if (lane == leader) base = atomicAdd(counter, __popcll(m));
-  base = __shfl(base, leader);
-  return take ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
-}
-
-// The bin (8 bits at `shift`) of the rem-th largest counted key, for radix
-// select: every thread of the workgroup calls it; thread t < 256 takes bin
-// 255 - t, so a prefix scan over t counts the keys in the bins above.  One
-// bin satisfies above < rem <= above + count; it writes the prefix, the rank
-// left within it and its count to s_sel.
-template <int NW>
-QDEV void pick_bin(const unsigned* hist, unsigned* s_w, unsigned* s_sel, int shift) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const unsigned rem = s_sel[1], prefix = s_sel[0];
-  const unsigned c = tid < 256 ? hist[255 - tid] : 0u;
-  unsigned inc = c;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const unsigned n = __shfl_up(inc, o);
-    if (lane >= o) inc += n;
-  }
-  if (lane == kWave - 1) s_w[wave] = inc;
-  __syncthreads();
-  unsigned before = 0u;
-  for (int w = 0; w < wave && w < NW; ++w) before += s_w[w];
-  const unsigned above = before + inc - c;
-  __syncthreads();  // every thread has read s_sel and s_w
-  if (tid < 256 && above < rem && above + c >= rem) {
-    s_sel[0] = prefix | ((unsigned)(255 - tid) << shift);
-    s_sel[1] = rem - above;
-    s_sel[2] = c;
-  }
-}
-
-// As for_row, but every thread calls f(j, v, valid) the same number of
-// times (valid == false past the row), for callers that ballot.
-template <typename F>
-QDEV void for_row_all(const float* __restrict__ l, int V, F&& f) {
   const int tid = threadIdx.x;
   if ((V & 3) == 0) {
     const float4* l4 = reinterpret_cast<const float4*>(l);
@@ -197,6 +126,69 @@ QDEV void for_row_all(const float* __restrict__ l, int V, F&& f) {
       const int j = base + tid;
       f(j, j < V ? l[j] : 0.f, j < V);
     }
+  }
+}
+
+// A slot in an LDS list for each lane whose `take` is set: one atomic per
+// wavefront (its lanes' count), each lane offset by the taking lanes below it.
+QDEV int claim_slot(bool take, int* counter) {
+  const int lane = threadIdx.x % kWave;
+  const unsigned long long m = __ballot(take);
+  if (m == 0ull) return -1;
+  const int leader = __ffsll((long long)m) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, leader);
+  return take ? base + __popcll(m & ((1ull << lane) - 1ull)) : -1;
+}
+
+// Counts one key into bin `bin` of an LDS histogram for each lane whose
+// `take` is set.  The keys of a radix pass crowd into few bins (the best
+// logits share their sign and exponent), and lanes adding to one address
+// are served one at a time: so the lanes of the two most common bins of the
+// wavefront are counted with one atomic each, the rest lane by lane.
+QDEV void hist_add(unsigned* h, unsigned bin, bool take) {
+  const int lane = threadIdx.x % kWave;
+  unsigned long long rem = __ballot(take);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (rem == 0ull) return;
+    const int leader = __ffsll((long long)rem) - 1;
+    const unsigned b0 = __shfl(bin, leader);
+    const unsigned long long same = __ballot(bin == b0) & rem;
+    if (lane == leader) atomicAdd(&h[b0], (unsigned)__popcll(same));
+    rem &= ~same;
+  }
+  if ((rem >> lane) & 1ull) atomicAdd(&h[bin], 1u);
+}
+
+// The bin (8 bits at `shift`) of the rem-th largest counted key, for radix
+// select: every thread of the workgroup calls it; thread t < 256 takes bin
+// 255 - t, so a prefix scan over t counts the keys in the bins above.  One
+// bin satisfies above < rem <= above + count; it writes the prefix, the rank
+// left within it and its count to s_sel.
+template <int NW>
+QDEV void pick_bin(const unsigned* hist, unsigned* s_w, unsigned* s_sel, int shift) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const unsigned rem = s_sel[1], prefix = s_sel[0];
+  const unsigned c = tid < 256 ? hist[255 - tid] : 0u;
+  unsigned inc = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned n = __shfl_up(inc, o);
+    if (lane >= o) inc += n;
+  }
+  if (lane == kWave - 1) s_w[wave] = inc;
+  __syncthreads();
+  unsigned before = 0u;  // bins live in the first 256 threads (four wavefronts)
+  if (tid < 256)
+    for (int w = 0; w < wave && w < NW; ++w) before += s_w[w];
+  const unsigned above = before + inc - c;
+  __syncthreads();  // every thread has read s_sel and s_w
+  if (tid < 256 && above < rem && above + c >= rem) {
+    s_sel[0] = prefix | ((unsigned)(255 - tid) << shift);
+    s_sel[1] = rem - above;
+    s_sel[2] = c;
   }
 }
 
@@ -242,11 +234,74 @@ QDEV T block_sum(T v, T* s_w) {  // fixed order: lanes by halving, then waves in
   return t;
 }
 
+// Bitonic sort, descending, of s[0, n) padded with zeros (below every key)
+// to n2, a power of two of at most E * kThreads, by the whole workgroup.  Thread t holds the E consecutive
+// elements from E t in registers: compare distances below E stay in the
+// thread, those below E * 64 are lane exchanges within the wavefront, and
+// only the wider ones go through LDS (two barriers each).  At distance jj
+// in a merge of size k, element i keeps the larger of itself and i ^ jj
+// when (i & jj == 0) equals (i & k == 0).
+template <int E>
+QDEV void sort_desc(unsigned long long* s, int n, int n2) {
+  const int i0 = threadIdx.x * E;
+  unsigned long long v[E];
+#pragma unroll
+  for (int q = 0; q < E; ++q) v[q] = i0 + q < n ? s[i0 + q] : 0ull;
+  auto settle = [&](int q, unsigned long long y, int jj, int k) {
+    const int i = i0 + q;
+    const bool keep_max = ((i & jj) == 0) == ((i & k) == 0);
+    v[q] = keep_max ? (v[q] > y ? v[q] : y) : (v[q] < y ? v[q] : y);
+  };
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= E * kWave) {
+        __syncthreads();  // earlier reads of s are done
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+          if (i0 + q < n2) s[i0 + q] = v[q];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+          if (i0 + q < n2) settle(q, s[(i0 + q) ^ jj], jj, k);
+      } else if (jj >= E) {
+        const int lm = jj / E;
+#pragma unroll
+        for (int q = 0; q < E; ++q) settle(q, __shfl_xor(v[q], lm), jj, k);
+      } else {
+        // jj < E: partners in this thread's registers (indices fixed at
+        // compile time, so the array stays in registers)
+        unsigned long long w[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q) w[q] = v[q];
+#pragma unroll
+        for (int d = 1; d < E; d <<= 1)
+          if (d == jj) {
+#pragma unroll
+            for (int q = 0; q < E; ++q) settle(q, w[q ^ d], jj, k);
+          }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < E; ++q)
+    if (i0 + q < n2) s[i0 + q] = v[q];
+  __syncthreads();
+}
+
+QDEV void sort_window(unsigned long long* s, int n) {
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  if (n2 > 2 * kThreads) sort_desc<4>(s, n, n2);
+  else if (n2 > kThreads) sort_desc<2>(s, n, n2);
+  else sort_desc<1>(s, n, n2);
+}
+
 // Stage 1: one 256-thread workgroup per (slice of kSlice logits, row): the
 // slice's max and its lowest index, its partial denominator relative to its
 // own max (exact nucleus), and every logit at or above the slice's W1-th
-// best (radix select on 16 keys per thread), written as (key << 32) | ~id.
-// The union of the slices' lists holds the row's best W1.
+// best (radix select on 16 keys per thread), written as (key << 32) | ~id,
+// with that cut (0 when the list holds the whole slice).
 constexpr int kSlice = 4096;
 constexpr int kSliceThreads = 256;
 constexpr int kSliceWaves = kSliceThreads / kWave;
@@ -354,13 +409,14 @@ __global__ void __launch_bounds__(kSliceThreads) k_sample_slices(const float* __
   }
 }
 
+// Stage 2: one 1024-thread workgroup per row.
 __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ logits, int V, SampleArgs a,
                                                      const float* __restrict__ uni, int32_t* __restrict__ out,
                                                      SliceScratch ss) {
-  __shared__ unsigned long long s_cand[kMaxWindow];  // (key << 32) | ~id, sorted descending
+  __shared__ unsigned long long s_u[kUnionCap];      // the union of the slices' lists
+  __shared__ unsigned long long s_cand[kMaxWindow];  // (key << 32) | ~id of the window, sorted descending
   __shared__ double s_cum[kMaxWindow];               // inclusive cumulative p of the window
-  __shared__ int s_id[kMaxWindow];
-  __shared__ unsigned s_hist[kHists][256];  // one histogram per pair of wavefronts
+  __shared__ unsigned s_hist[kHists][256];           // one histogram per pair of wavefronts
   __shared__ int s_cnt[2];
   __shared__ int s_iw[kWaves + 1];
   __shared__ double s_dw[kWaves + 1];
@@ -369,8 +425,9 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   __shared__ unsigned s_sel[3];  // prefix, remaining rank, the bin's count
   __shared__ unsigned s_uw[kWaves];
   __shared__ unsigned s_ut[kWaves];
-  __shared__ int s_pos[2];       // top-p and min-p prefix lengths, then the pick
-  __shared__ double s_z[1];      // the softmax denominator of the candidates
+  __shared__ unsigned s_lo;
+  __shared__ int s_pos[2];  // top-p and min-p prefix lengths, then the pick
+  __shared__ double s_z[1];  // the softmax denominator of the candidates
 
   const int row = blockIdx.x, tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
@@ -419,84 +476,79 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   const double top_p = (double)a.top_p;
 
   // the whole-row denominator of the exact nucleus: the slices' partials,
-  // each rescaled from its own max to the row's, added in slice order
+  // each rescaled from its own max to the row's
   double zfull = 0.0;
-  if (a.top_k == 0 && tid == 0) {
-    for (int sl = 0; sl < ss.S; ++sl) zfull += ss.z[r0 + sl] * exp(((double)ss.m[r0 + sl] - lmax) / T);
-    s_z[0] = zfull;
+  if (a.top_k == 0) {
+    double zt = 0.0;
+    for (int sl = tid; sl < ss.S; sl += kThreads) zt += ss.z[r0 + sl] * exp(((double)ss.m[r0 + sl] - lmax) / T);
+    zfull = block_sum(zt, s_dw);
   }
-  __syncthreads();
-  zfull = s_z[0];
-  __syncthreads();
 
   // The union of the slices' lists holds every key >= T* of the row (a
-  // partial list holds all of its slice's keys >= its cut).  So the top W of
-  // the union are the row's top W whenever the W-th of them is >= T*.
+  // partial list holds all of its slice's keys >= its cut), so the union's
+  // best W are the row's best W when W <= NV, the union's count of keys
+  // >= T*.  A union that fits LDS is copied there once.
   const unsigned long long* crow = ss.cand + r0 * kSlice;
   const int* nrow = ss.cnt + r0;
-  auto sort_desc = [&](int n2) {  // bitonic sort of s_cand[0, n2), n2 a power of two
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = tid; i < n2; i += kThreads) {
-          const int p = i ^ jj;
-          if (p > i) {
-            const unsigned long long x = s_cand[i], y = s_cand[p];
-            const bool up = (i & k) == 0;
-            if ((x < y) == up) s_cand[i] = y, s_cand[p] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
-  };
-  auto pow2_at_least = [](int n) {
-    int w = 1;
-    while (w < n) w <<= 1;
-    return w;
-  };
-
-  // A small union is copied whole into LDS and sorted once: its prefix of
-  // keys >= T* (NV entries) serves every window up to NV.
+  enum { kFromLds, kFromUnion, kFromRow };
+  int src = U <= kUnionCap ? kFromLds : kFromUnion;
   int NV = 0;
-  bool sorted_union = U <= kMaxWindow;
-  if (sorted_union) {
-    if (tid == 0) s_cnt[0] = 0, s_cnt[1] = 0;
+  unsigned ulo = 0u;  // the union's lowest key
+  if (src == kFromLds) {
+    if (tid == 0) s_cnt[0] = 0, s_cnt[1] = 0, s_lo = 0xFFFFFFFFu;
     __syncthreads();
     for (int sl = wave; sl < ss.S; sl += kWaves) {
       const int c = nrow[sl];
       int base = 0;
       if (lane == 0) base = atomicAdd(&s_cnt[0], c);
       base = __shfl(base, 0);
-      for (int i = lane; i < c; i += kWave) s_cand[base + i] = crow[(int64_t)sl * kSlice + i];
+      for (int i = lane; i < c; i += kWave) s_u[base + i] = crow[(int64_t)sl * kSlice + i];
     }
-    const int W2 = pow2_at_least(U);
     __syncthreads();
-    for (int i = U + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
-    __syncthreads();
-    sort_desc(W2);
-    for (int i = tid; i < U; i += kThreads)
-      if ((uint32_t)(s_cand[i] >> 32) >= tstar && (i + 1 == U || (uint32_t)(s_cand[i + 1] >> 32) < tstar))
-        s_cnt[1] = i + 1;
+    int nv = 0;
+    unsigned lo = 0xFFFFFFFFu;
+    for (int i = tid; i < U; i += kThreads) {
+      const uint32_t k = (uint32_t)(s_u[i] >> 32);
+      nv += k >= tstar;
+      lo = min(lo, k);
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      nv += __shfl_xor(nv, o);
+      lo = min(lo, (unsigned)__shfl_xor((int)lo, o));
+    }
+    if (lane == 0) atomicAdd(&s_cnt[1], nv), atomicMin(&s_lo, lo);
     __syncthreads();
     NV = s_cnt[1];
+    ulo = s_lo;
     __syncthreads();
   }
 
-  // element sources for a radix select: the union (wavefront by slice) or
-  // the whole row.  f(key, id, valid) is called by every lane of a wavefront
-  // the same number of times (valid == false past the end), so it can ballot.
-  bool from_union = true;
+  // f(key, id, valid) over the source's elements; every lane of a wavefront
+  // calls f the same number of times (valid == false past the end)
   auto for_elems = [&](auto&& f) {
-    if (from_union) {
+    if (src == kFromLds) {
+      for (int base = 0; base < U; base += 2 * kThreads) {
+        unsigned long long e[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = base + u * kThreads + tid;
+          e[u] = i < U ? s_u[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          f((uint32_t)(e[u] >> 32), (int)(0xFFFFFFFFu - (uint32_t)(e[u] & 0xFFFFFFFFull)),
+            base + u * kThreads + tid < U);
+      }
+    } else if (src == kFromUnion) {
       for (int sl = wave; sl < ss.S; sl += kWaves) {
         const int c = nrow[sl];
-        const unsigned long long* src = crow + (int64_t)sl * kSlice;
+        const unsigned long long* p = crow + (int64_t)sl * kSlice;
         for (int base = 0; base < c; base += 4 * kWave) {
           unsigned long long e[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int i = base + u * kWave + lane;
-            e[u] = i < c ? src[i] : 0ull;
+            e[u] = i < c ? p[i] : 0ull;
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -505,95 +557,96 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
         }
       }
     } else {
-      for_row_all(l, V, [&](int j, float v, bool valid) { f(okey(v), j, valid); });
+      for_row(l, V, [&](int j, float v, bool valid) { f(okey(v), j, valid); });
     }
   };
 
   int W = a.top_k > 0 ? min(min(a.top_k, kMaxCand), V) : min(kMaxCand, V);
   const int C = (V + kThreads - 1) / kThreads;  // contiguous chunk per thread (keeps ids in order)
   for (;;) {
-    if (sorted_union && W > NV) {
-      sorted_union = false;  // past the union's valid prefix: select over the row
-      from_union = false;
+    if (src == kFromLds && W > NV) src = kFromRow;  // past what the union is sure to hold
+    // radix select: the key of the W-th best candidate (pairs of wavefronts
+    // count into their own histogram; the bins are then summed).  The
+    // union's keys lie in [ulo, okey(max)]: the leading bytes those share
+    // are every key's, so the passes start at the first byte that differs
+    // (the last pass always runs: it counts the ties).
+    int start = 24;
+    unsigned mask = 0u;
+    if (src == kFromLds) {
+      const unsigned d = ulo ^ okey(fmax);
+      start = d >= (1u << 24) ? 24 : d >= (1u << 16) ? 16 : d >= (1u << 8) ? 8 : 0;
+      mask = start == 24 ? 0u : 0xFFFFFFFFu << (start + 8);
     }
-    if (!sorted_union) {
-      // radix select: the key of the W-th best candidate (pairs of
-      // wavefronts count into their own histogram; the bins are then summed)
-      if (tid == 0) s_sel[0] = 0u, s_sel[1] = (unsigned)W;
-      unsigned mask = 0u;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int b = tid; b < kHists * 256; b += kThreads) s_hist[b / 256][b % 256] = 0u;
-        __syncthreads();
-        const unsigned prefix = s_sel[0];
-        for_elems([&](uint32_t k, int, bool valid) {
-          if (valid && (k & mask) == prefix) atomicAdd(&s_hist[wave / 2][(k >> shift) & 255u], 1u);
-        });
-        __syncthreads();
-        if (tid < 256) {
-          unsigned t = 0u;
-          for (int w = 0; w < kHists; ++w) t += s_hist[w][tid];
-          s_hist[0][tid] = t;
-        }
-        __syncthreads();
-        pick_bin<kWaves>(s_hist[0], s_uw, s_sel, shift);  // s_sel[2]: after the last pass, the ties
-        mask |= 255u << shift;
-        __syncthreads();
+    if (tid == 0) s_sel[0] = okey(fmax) & mask, s_sel[1] = (unsigned)W;
+    for (int shift = start; shift >= 0; shift -= 8) {
+      for (int b = tid; b < kHists * 256; b += kThreads) s_hist[b / 256][b % 256] = 0u;
+      __syncthreads();
+      const unsigned prefix = s_sel[0];
+      for_elems([&](uint32_t k, int, bool valid) {
+        hist_add(s_hist[wave / 2], (k >> shift) & 255u, valid && (k & mask) == prefix);
+      });
+      __syncthreads();
+      if (tid < 256) {
+        unsigned t = 0u;
+        for (int w = 0; w < kHists; ++w) t += s_hist[w][tid];
+        s_hist[0][tid] = t;
       }
-      const uint32_t thr = s_sel[0];
-      const int need_eq = (int)s_sel[1];  // >= 1 candidates with key == thr, in id order
-      const int cnt_gt = W - need_eq;
-      const int all_eq = (int)s_sel[2];
-      if (from_union && (thr < tstar || cnt_gt + all_eq > kMaxWindow)) {
-        // the union may miss keys of the window, or too many ties for the
-        // window: redo over the row
-        from_union = false;
-        __syncthreads();
-        continue;
-      }
+      __syncthreads();
+      pick_bin<kWaves>(s_hist[0], s_uw, s_sel, shift);  // s_sel[2]: after the last pass, the ties
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+    const uint32_t thr = s_sel[0];
+    const int need_eq = (int)s_sel[1];  // >= 1 candidates with key == thr, in id order
+    const int cnt_gt = W - need_eq;
+    const int all_eq = (int)s_sel[2];
+    if (src != kFromRow && (thr < tstar || cnt_gt + all_eq > kMaxWindow)) {
+      // the union may miss keys of the window, or too many ties for the
+      // window: redo over the row
+      src = kFromRow;
+      __syncthreads();
+      continue;
+    }
 
-      // gather.  Usually every key equal to the threshold fits in the
-      // window: then all of them are taken into slots from a counter, the
-      // sort orders them (ties by id) and the first W are kept.  Otherwise
-      // each thread scans its own contiguous chunk of the row, so equal keys
-      // are taken in id order.
-      int NC = W;  // candidates gathered
-      if (cnt_gt + all_eq <= kMaxWindow) {
-        NC = cnt_gt + all_eq;
-        if (tid == 0) s_cnt[0] = 0;
-        __syncthreads();
-        for_elems([&](uint32_t k, int j, bool valid) {
-          const bool take = valid && k >= thr;
-          const int slot = claim_slot(take, &s_cnt[0]);
-          if (take) s_cand[slot] = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
-        });
-      } else {
-        int ngt = 0, neq = 0;
-        const int j0 = tid * C, j1 = min(V, j0 + C);
-        for (int j = j0; j < j1; ++j) {
-          const uint32_t k = okey(l[j]);
-          ngt += k > thr;
-          neq += k == thr;
-        }
-        int tot;
-        int ogt = block_exclusive_scan(ngt, s_iw, &tot);
-        int oeq = block_exclusive_scan(neq, s_iw, &tot);
-        for (int j = j0; j < j1; ++j) {
-          const uint32_t k = okey(l[j]);
-          const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
-          if (k > thr) {
-            s_cand[ogt++] = c;
-          } else if (k == thr) {
-            if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
-            ++oeq;
-          }
+    // gather.  Usually every key equal to the threshold fits in the window:
+    // then all of them are taken into slots from a counter, the sort orders
+    // them (ties by id) and the first W are kept.  Otherwise each thread
+    // scans its own contiguous chunk of the row, so equal keys are taken in
+    // id order.
+    int NC = W;  // candidates gathered
+    if (cnt_gt + all_eq <= kMaxWindow) {
+      NC = cnt_gt + all_eq;
+      if (tid == 0) s_cnt[0] = 0;
+      __syncthreads();
+      for_elems([&](uint32_t k, int j, bool valid) {
+        const bool take = valid && k >= thr;
+        const int slot = claim_slot(take, &s_cnt[0]);
+        if (take) s_cand[slot] = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+      });
+    } else {
+      int ngt = 0, neq = 0;
+      const int j0 = tid * C, j1 = min(V, j0 + C);
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t k = okey(l[j]);
+        ngt += k > thr;
+        neq += k == thr;
+      }
+      int tot;
+      int ogt = block_exclusive_scan(ngt, s_iw, &tot);
+      int oeq = block_exclusive_scan(neq, s_iw, &tot);
+      for (int j = j0; j < j1; ++j) {
+        const uint32_t k = okey(l[j]);
+        const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
+        if (k > thr) {
+          s_cand[ogt++] = c;
+        } else if (k == thr) {
+          if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
+          ++oeq;
         }
       }
-      const int W2 = pow2_at_least(NC);
-      __syncthreads();
-      for (int i = NC + tid; i < W2; i += kThreads) s_cand[i] = 0ull;
-      __syncthreads();
-      sort_desc(W2);
     }
+    __syncthreads();
+    sort_window(s_cand, NC);
 
     // p_i in f64, then the inclusive scan (4 consecutive candidates per thread)
     double pv[4];
@@ -601,12 +654,7 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * tid + q;
-      pv[q] = 0.0;
-      if (i < W) {
-        const unsigned long long c = s_cand[i];
-        s_id[i] = (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
-        pv[q] = exp(((double)okey_value((uint32_t)(c >> 32)) - lmax) / T);
-      }
+      pv[q] = i < W ? exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) : 0.0;
     }
     double z = zfull;
     if (a.top_k > 0) {
@@ -647,8 +695,8 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
       if (s_cum[i] >= top_p && (i == 0 || s_cum[i - 1] < top_p)) s_pos[0] = i + 1;
   }
   if (a.min_p > 0.f) {
-    // p_i recomputed exactly as above from the sorted keys; p descends, so
-    // p_i < min_p * p_0 first holds at one index
+    // p_i recomputed exactly as above; p descends, so p_i < min_p * p_0
+    // first holds at one index
     const double z = s_z[0];
     auto p_of = [&](int i) { return exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) / z; };
     const double thr = (double)a.min_p * p_of(0);
@@ -663,7 +711,7 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   for (int i = tid; i < keep; i += kThreads)
     if (s_cum[i] > r && (i == 0 || !(s_cum[i - 1] > r))) s_pos[0] = i;
   __syncthreads();
-  if (tid == 0) out[row] = s_id[s_pos[0]];
+  if (tid == 0) out[row] = (int)(0xFFFFFFFFu - (uint32_t)(s_cand[s_pos[0]] & 0xFFFFFFFFull));
 }
 
 }  // namespace
@@ -692,11 +740,9 @@ hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_
   ss.am = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 12));
   ss.cnt = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 16));
   ss.thr = reinterpret_cast<unsigned*>(w + rs * (kSlice * 8 + 20));
-  // slice lists hold each slice's best W1: min(top_k, 256) for top-k (the
-  // union then holds the row's top k); for the exact nucleus, as many as
-  // keep the union within one LDS window (its valid prefix serves the
-  // windows it covers)
-  const int W1 = a.top_k > 0 ? min(a.top_k, kMaxCand) : max(1, kMaxWindow / S);
+  // Each slice lists its best W1, sized so the union fits the LDS copy
+  // (W1 <= kUnionCap / S); for top-k no more than min(top_k, 256) are needed
+  const int W1 = max(1, min(a.top_k > 0 ? min(a.top_k, kMaxCand) : kUnionCap, kUnionCap / S));
   hipLaunchKernelGGL(k_sample_slices, dim3(S, n), dim3(kSliceThreads), 0, s, logits, V, a, W1, ss);
   hipLaunchKernelGGL(k_sample, dim3(n), dim3(kThreads), 0, s, logits, V, a, uni, out, ss);
   return hipGetLastError();

@@ -109,6 +109,52 @@ def test_tokens_match_the_oracle(ci):
     assert checked >= n - 3
 
 
+def _rows(kind, n, V, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "best_in_one_slice":  # every top logit in ids [0, 4096)
+        x = rng.standard_normal((n, V)) * 3.0
+        x[:, :4096] += 12.0
+    elif kind == "integer_logits":  # heavy ties at every cut
+        x = np.round(rng.standard_normal((n, V)) * 1.5)
+    else:  # "clipped": about 31% of the row tied at the maximum
+        x = np.minimum(rng.standard_normal((n, V)), 0.5)
+    return x.astype(np.float32)
+
+
+SPECIAL = [
+    # the window passes what the slices' lists are sure to hold: the whole row
+    ("best_in_one_slice", sp.SamplerConfig(temperature=1.0, top_k=256)),
+    ("best_in_one_slice", sp.SamplerConfig(temperature=1.0, top_k=200)),  # exactly what the lists hold
+    ("best_in_one_slice", sp.SamplerConfig(temperature=1.0, top_p=0.9)),
+    # the union overflows its LDS copy; ties at the cut, kept in id order
+    ("integer_logits", sp.SamplerConfig(temperature=1.0, top_k=256)),
+    ("integer_logits", sp.SamplerConfig(temperature=1.0, top_p=0.05)),
+    ("integer_logits", sp.SamplerConfig(temperature=0.8, top_k=30, min_p=0.2)),
+    # more equal keys than the window: gathered from the row in id order
+    ("clipped", sp.SamplerConfig(temperature=1.0, top_k=256)),
+    ("clipped", sp.SamplerConfig(temperature=1.0, top_p=0.01)),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SPECIAL)))
+def test_tokens_match_the_oracle_on_skewed_and_tied_rows(ci):
+    kind, cfg = SPECIAL[ci]
+    n, V = 6, 151936
+    logits = _rows(kind, n, V, 300 + ci)
+    u = np.random.default_rng(400 + ci).random(n).astype(np.float32)
+    tok, _ = gpu_sample(logits, cfg, u)
+    checked = 0
+    for r in range(n):
+        want, info = sp.sample(logits[r], [], cfg, float(u[r]))
+        assert len(info["cand"]) <= 4096
+        if near_boundary(info, cfg.top_p):
+            assert tok[r] in info["cand"]
+            continue
+        assert tok[r] == want, (r, tok[r], want)
+        checked += 1
+    assert checked >= n - 2
+
+
 def test_window_cap_keeps_a_valid_candidate():
     """The exact nucleus that needs more than 4096 candidates: the device
     draws from the 4096 best (ordered by logit, ties by id)."""
