@@ -95,7 +95,9 @@ def _linear_bound(x, ow):
      (300, 3072, 384), (129, 256, 128),
      # small-M GEMM: 16/32/64-row tilings, K slices of 4/8/16, ragged N, 64-row units
      (16, 1024, 4096), (17, 2048, 1024), (33, 3072, 1000), (64, 4096, 520), (20, 12288, 256), (5, 768, 4100),
-     (32, 256, 65600), (64, 256, 96)],
+     (32, 256, 65600), (64, 256, 96),
+     # 33..64 rows on narrow matrices (64 workgroups; two and three chunks per K slice, a ragged M)
+     (64, 2048, 1024), (40, 3072, 1024), (64, 3072, 1000)],
 )
 def test_linear_matches_oracle(m, k, n):
     from quantized_q8_dequant_amd import q8_0_linear
