@@ -397,6 +397,42 @@ def bench_sampling(V: int, args) -> dict:
     return out
 
 
+def measure_peaks(args) -> dict:
+    """Achievable peaks on this GPU, measured with the library's own probes:
+    a streaming copy of 1 GiB (read plus write bytes over its event-timed
+    duration), a streaming read of 1 GiB and a loop of int8 MFMAs (2048
+    workgroups, operands in registers)."""
+    import torch
+
+    from quantized_q8_dequant_amd import peak_copy, peak_mfma_i8, peak_read, peak_read_partials
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    copy_ms = event_ms(lambda: peak_copy(src, dst), max(args.warmup, 1), 10)
+    parts = torch.zeros(peak_read_partials(), dtype=torch.int32, device="cuda:0")
+    read_ms = event_ms(lambda: peak_read(src, parts), max(args.warmup, 1), 10)
+    del src, dst, parts
+    torch.cuda.empty_cache()
+    wgs, iters = 2048, 4000
+    out = torch.empty(256 * wgs, dtype=torch.int32, device="cuda:0")
+    ops = [0.0]
+
+    def run():
+        ops[0] = peak_mfma_i8(out, wgs, iters)
+
+    mfma_ms = event_ms(run, 1, 5)
+    return {
+        "copy_GBps": round(2 * n / (copy_ms / 1000.0) / 1e9, 1),
+        "copy_frac_of_vendor_peak": round(2 * n / (copy_ms / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "read_GBps": round(n / (read_ms / 1000.0) / 1e9, 1),
+        "read_frac_of_vendor_peak": round(n / (read_ms / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "mfma_int8_TOPS": round(ops[0] / (mfma_ms / 1000.0) / 1e12, 1),
+        "mfma_int8_frac_of_vendor_peak": round(ops[0] / (mfma_ms / 1000.0) / INT8_PEAK_OPS, 4),
+    }
+
+
 def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
     """The CPU oracle on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_info
@@ -589,6 +625,7 @@ def main() -> int:
         batched = bench_batched(shape, weights, prompt, args)
         torch.cuda.empty_cache()
         sampling = bench_sampling(shape.vocab_size, args)
+    peaks = measure_peaks(args)
 
     if args.pmc_calibrate:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
@@ -629,6 +666,7 @@ def main() -> int:
         "decode_tokens_per_s": round(decode_tps, 2),
         "decode_hbm_GBps": round(decode_gbps, 1),
         "decode_hbm_frac": round(decode_gbps / HBM_PEAK_GBPS, 4),
+        "decode_frac_of_measured_read_peak": round(decode_gbps / peaks["read_GBps"], 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(prefill_tps, 1),
         "decode_launches_per_token": launches,
@@ -637,6 +675,7 @@ def main() -> int:
         "verify": verify,
         "batched_decode": batched,
         "sampling": sampling,
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

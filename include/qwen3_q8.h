@@ -220,6 +220,28 @@ int qwen3_kv_export(const qwen3_t* h, int32_t seq, int32_t layer, float* d_k, fl
  * advanced.  Enqueue after at least one decode step of `seq`. */
 int qwen3_replay_kernel(qwen3_t* h, int32_t seq, int32_t kind, int32_t layer, int32_t reps, void* stream);
 
+/* Achievable-peak probes, the measured figures the roofline fractions are
+ * also given against (the vendor's peaks are the other).  qwen3_peak_copy:
+ * copies `bytes` (a multiple of 16) from d_src to d_dst (device buffers that
+ * do not overlap), a streaming kernel whose HBM traffic is 2 * bytes.
+ * qwen3_peak_read: reads `bytes` (a multiple of 16) at d_src and writes
+ * wrapping sums of its 32-bit words, one per wavefront, into d_out, which
+ * holds qwen3_peak_read_partials() uint32 (entries past the launch's
+ * wavefronts are left as they were; the partials' wrapping total is the
+ * buffer's).  qwen3_peak_mfma_i8: `workgroups` workgroups of four wavefronts, each
+ * wavefront `iters` rounds of four independent int8 MFMAs (32x32x32) on
+ * operands every byte of which is the low byte of `fill` (b, read as a
+ * signed 8-bit value); every lane writes 2048 * b * b * iters (wrapping as
+ * int32) to d_out, which holds
+ * 256 * workgroups int32.  qwen3_peak_mfma_i8_ops gives the int8 operations
+ * of such a launch (two per multiply-add), 0 for invalid counts.  Both
+ * launches are enqueued on `stream` to be timed with events there. */
+int qwen3_peak_copy(const void* d_src, void* d_dst, size_t bytes, void* stream);
+int qwen3_peak_read(const void* d_src, size_t bytes, uint32_t* d_out, void* stream);
+int32_t qwen3_peak_read_partials(void);
+int qwen3_peak_mfma_i8(int32_t* d_out, int32_t workgroups, int32_t iters, int32_t fill, void* stream);
+double qwen3_peak_mfma_i8_ops(int32_t workgroups, int32_t iters);
+
 /* Thread-local description of the last error ("" if none). */
 const char* qwen3_last_error(void);
 

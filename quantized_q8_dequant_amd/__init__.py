@@ -11,6 +11,10 @@ from .model import (  # noqa: F401
     bf16_linear,
     encode_bf16,
     encode_q8_0,
+    peak_copy,
+    peak_mfma_i8,
+    peak_read,
+    peak_read_partials,
     q8_0_block_dots,
     q8_0_linear,
     repack_q8_0,

@@ -52,6 +52,11 @@ EXPORTS = (
     "qwen3_replay_kernel",
     "qwen3_bf16_linear",
     "qwen3_decode_launches",
+    "qwen3_peak_copy",
+    "qwen3_peak_read",
+    "qwen3_peak_read_partials",
+    "qwen3_peak_mfma_i8",
+    "qwen3_peak_mfma_i8_ops",
 )
 
 
@@ -163,6 +168,11 @@ def lib() -> C.CDLL:
         "qwen3_replay_kernel": (C.c_int, [vp, i32, i32, i32, i32, vp]),
         "qwen3_bf16_linear": (C.c_int, [vp, i64, i64, vp, i64, vp, vp]),
         "qwen3_decode_launches": (i32, [vp]),
+        "qwen3_peak_copy": (C.c_int, [vp, vp, sz, vp]),
+        "qwen3_peak_read": (C.c_int, [vp, sz, vp, vp]),
+        "qwen3_peak_read_partials": (i32, []),
+        "qwen3_peak_mfma_i8": (C.c_int, [vp, i32, i32, i32, vp]),
+        "qwen3_peak_mfma_i8_ops": (C.c_double, [i32, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -193,6 +193,13 @@ hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s);
 constexpr int kSkinnyMaxRows = 64;
 bool gemm_skinny_supported(int M, int K);
 hipError_t gemm_skinny(const GemmArgs& a, int epi, hipStream_t s);
+
+// Achievable-peak probes (see k_peak.hip).
+hipError_t copy_peak(const void* src, void* dst, size_t bytes, hipStream_t s);
+int read_peak_partials();
+hipError_t read_peak(const void* src, size_t bytes, uint32_t* out, hipStream_t s);
+double mfma_peak_ops(int workgroups, int iters);
+hipError_t mfma_peak(int32_t* out, int workgroups, int iters, int fill, hipStream_t s);
 hipError_t gemm_bf16(const GemmBf16Args& a, int epi, hipStream_t s);
 hipError_t rows_norm(const float* x, int64_t ldx, int T, int K, const float* w, float eps, float* y, int64_t ldy,
                      hipStream_t s);

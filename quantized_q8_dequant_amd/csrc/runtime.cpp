@@ -1023,6 +1023,38 @@ int qwen3_kv_export(const qwen3_t* m, int32_t seq, int32_t layer, float* d_k, fl
 
 // ---- op-level entry points ---------------------------------------------------------------
 
+int qwen3_peak_copy(const void* d_src, void* d_dst, size_t bytes, void* stream) {
+  g_err.clear();
+  if (bytes % 16) return fail(QWEN3_E_INVALID_ARGUMENT, "bytes must be a multiple of 16");
+  if (bytes && (!d_src || !d_dst)) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  HIP_TRY(q8k::copy_peak(d_src, d_dst, bytes, S(stream)));
+  return QWEN3_OK;
+}
+
+int qwen3_peak_read(const void* d_src, size_t bytes, uint32_t* d_out, void* stream) {
+  g_err.clear();
+  if (bytes % 16) return fail(QWEN3_E_INVALID_ARGUMENT, "bytes must be a multiple of 16");
+  if (bytes && (!d_src || !d_out)) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  HIP_TRY(q8k::read_peak(d_src, bytes, d_out, S(stream)));
+  return QWEN3_OK;
+}
+
+int32_t qwen3_peak_read_partials(void) { return q8k::read_peak_partials(); }
+
+double qwen3_peak_mfma_i8_ops(int32_t workgroups, int32_t iters) {
+  if (workgroups < 1 || iters < 1) return 0.0;
+  return q8k::mfma_peak_ops(workgroups, iters);
+}
+
+int qwen3_peak_mfma_i8(int32_t* d_out, int32_t workgroups, int32_t iters, int32_t fill, void* stream) {
+  g_err.clear();
+  if (!d_out) return fail(QWEN3_E_INVALID_ARGUMENT, "null pointer");
+  if (workgroups < 1 || workgroups > 65536 || iters < 1)
+    return fail(QWEN3_E_INVALID_ARGUMENT, "workgroups must be in [1, 65536], iters >= 1");
+  HIP_TRY(q8k::mfma_peak(d_out, workgroups, iters, fill, S(stream)));
+  return QWEN3_OK;
+}
+
 int qwen3_q8_0_encode(const float* d_x, int64_t n, void* d_blocks, void* stream) {
   g_err.clear();
   if (n < 0 || n % 32) return fail(QWEN3_E_INVALID_ARGUMENT, "n must be a non-negative multiple of 32");

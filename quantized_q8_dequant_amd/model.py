@@ -184,6 +184,37 @@ def q8_0_block_dots(x: torch.Tensor, qs: torch.Tensor):
     return qa, da, S
 
 
+def peak_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Enqueue the library's streaming copy of src into dst (same byte size,
+    a multiple of 16, no overlap) on the current stream."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    check(lib().qwen3_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream()))
+
+
+def peak_read(src: torch.Tensor, partials: torch.Tensor) -> None:
+    """Enqueue the library's streaming read of src (a multiple of 16 bytes)
+    on the current stream; partials (int32, peak_read_partials() entries)
+    receive per-wavefront wrapping sums of its 32-bit words."""
+    if partials.dtype != torch.int32 or partials.numel() < lib().qwen3_peak_read_partials():
+        raise ValueError("partials must be int32 with qwen3_peak_read_partials() elements")
+    check(lib().qwen3_peak_read(src.data_ptr(), src.numel() * src.element_size(), partials.data_ptr(), _stream()))
+
+
+def peak_read_partials() -> int:
+    return int(lib().qwen3_peak_read_partials())
+
+
+def peak_mfma_i8(out: torch.Tensor, workgroups: int, iters: int, fill: int = 1) -> float:
+    """Enqueue the int8 MFMA loop on the current stream; out is int32 with
+    256 * workgroups elements.  Returns the launch's int8 operation count."""
+    if out.dtype != torch.int32 or out.numel() < 256 * workgroups:
+        raise ValueError("out must be int32 with 256 * workgroups elements")
+    check(lib().qwen3_peak_mfma_i8(out.data_ptr(), workgroups, iters, fill, _stream()))
+    return float(lib().qwen3_peak_mfma_i8_ops(workgroups, iters))
+
+
 # ---- the model ------------------------------------------------------------------------
 
 

@@ -137,3 +137,19 @@ def test_null_handle_and_op_argument_errors():
     assert lib.qwen3_decode_launches(None) == -1
     # encoding zero values enqueues nothing
     assert lib.qwen3_q8_0_encode(None, 0, None, None) == 0
+
+
+def test_peak_probes_validate_on_the_host():
+    L = _lib.lib()
+    assert L.qwen3_peak_copy(C.c_void_p(16), C.c_void_p(4096), 24, None) == -1  # not a multiple of 16
+    assert L.qwen3_peak_copy(None, None, 32, None) == -1
+    assert L.qwen3_peak_copy(None, None, 0, None) == 0  # nothing to copy, no launch
+    assert L.qwen3_peak_read(C.c_void_p(16), 40, C.c_void_p(4096), None) == -1
+    assert L.qwen3_peak_read(None, 32, None, None) == -1
+    assert L.qwen3_peak_read_partials() == 8192 * 4
+    assert L.qwen3_peak_mfma_i8(None, 1, 1, 1, None) == -1
+    assert L.qwen3_peak_mfma_i8(C.c_void_p(4096), 0, 1, 1, None) == -1
+    assert L.qwen3_peak_mfma_i8(C.c_void_p(4096), 1, 0, 1, None) == -1
+    # four wavefronts x four 32x32x32 MFMAs (65,536 int8 ops each) per round
+    assert L.qwen3_peak_mfma_i8_ops(2048, 4000) == 2048 * 4 * 4 * 4000 * 65536.0
+    assert L.qwen3_peak_mfma_i8_ops(0, 5) == 0.0

@@ -130,3 +130,27 @@ def test_bf16_linear_matches_oracle(m, k, n):
     ulps = np.abs(y.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
     assert ulps.max() <= 1, f"max {ulps.max()} ulps"
     assert (ulps == 0).mean() >= 0.999
+
+
+def test_peak_probes_compute_what_they_claim():
+    """The copy probe copies and the read probe sums (a ragged multiple of 16
+    bytes included); the MFMA probe's accumulators hold 32 * b * b per MFMA
+    element."""
+    from quantized_q8_dequant_amd import peak_copy, peak_mfma_i8, peak_read, peak_read_partials
+
+    for nbytes in (1 << 20, 16 * 1_000_003):
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+        dst = torch.zeros_like(src)
+        peak_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        parts = torch.zeros(peak_read_partials(), dtype=torch.int32, device=DEV)
+        peak_read(src, parts)
+        words = src.cpu().numpy().view(np.uint32)
+        assert int(parts.cpu().numpy().view(np.uint32).sum(dtype=np.uint64)) % 2**32 == int(
+            words.sum(dtype=np.uint64)) % 2**32
+    out = torch.zeros(256 * 3, dtype=torch.int32, device=DEV)
+    ops = peak_mfma_i8(out, 3, 7, fill=0x1FD)  # low byte 0xFD = -3
+    torch.cuda.synchronize()
+    assert ops == 3 * 4 * 4 * 7 * 65536
+    assert bool((out == 2048 * 9 * 7).all())
