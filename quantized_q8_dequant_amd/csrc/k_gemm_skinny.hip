@@ -1,12 +1,13 @@
 // Small-M Q8_0 GEMM for gfx950 on int8 MFMA (v_mfma_i32_16x16x32_i8): the
 // projections of a batched decode step (one row per stream) and of short
-// prefill chunks, where M <= 64 rows share one pass over the weights.
+// prefill chunks (M <= 64 rows), in M tiles of 16 or 32 rows per workgroup.
 //
 // C[m, n] = sum_b d_a[m, b] * d_w[n, b] * S_b[m, n], S_b the exact integer dot
 // of 32-block b (Fucina course, "Model files and quantization", section
 // 11.9); one 16x16x32 MFMA is exactly one block for a 16 x 16 tile, every
 // term S_b * d_a * d_w is exact in f64 and the sum is rounded to f32 once.
-// Reading the weights once for all rows is what makes a batch of streams
+// Reading the weights from HBM once for all rows (the M tiles of a weight
+// unit run on one XCD and share its L2) is what makes a batch of streams
 // cheaper than the streams one by one (the same page, section 11.6, and "A
 // transformer from scratch", section 12.5: decode is weight-bandwidth-bound,
 // and the batched decode step reads the weights once for all of its streams).
@@ -16,7 +17,8 @@
 // wavefronts take KW equal slices of K and add their f64 sums in slice order
 // at the end (through LDS), so the sum order is fixed for a given matrix.
 // The small units spread even narrow matrices (1024 outputs) over 64
-// workgroups; the vocabulary projection gets 64-row units.  KW is chosen so
+// workgroups, times the 16-row M tiles (grid.y); the vocabulary projection
+// gets 64-row units and all M rows per workgroup.  KW is chosen so
 // that a slice is at most eight blocks: a wavefront then issues every load
 // of its slice at once and waits one memory round trip (longer slices take
 // their chunks of eight in turn).  Operands come straight from global memory
@@ -33,7 +35,7 @@ namespace {
 
 typedef int v4i_acc __attribute__((ext_vector_type(4)));
 
-// MT: 16-row M tiles (1, 2 or 4); NT: 16-row weight tiles per workgroup (for
+// MT: 16-row M tiles per workgroup (1 or 2); NT: 16-row weight tiles per workgroup (for
 // SwiGLU the gate tile and its up tile); KW: wavefronts (slices of K).
 template <int MT, int NT, int KW, int EPI>
 __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
@@ -44,6 +46,8 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
   __shared__ __align__(16) float s_da[KW][UG][MR];  // per wavefront: scales of its chunk
   __shared__ double s_red[KW - 1][RV][kWave];
 
+  const int units = EPI == EPI_SWIGLU ? a.N / 32 : (a.N + 16 * NT - 1) / (16 * NT);
+  if ((int)blockIdx.x >= units) return;  // the grid rounded up to whole XCD rounds
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int lc = lane % 16, lk = lane / 16;
   const int K = a.K, nblk = K / 32;
@@ -64,10 +68,11 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) wrow[nt] = min(n0 + 16 * nt + lc, a.N - 1);
   }
+  const int m0 = blockIdx.y * MR;  // first row of this workgroup's M tile
   int64_t arow[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) arow[mt] = min(mt * 16 + lc, a.M - 1);
-  const int64_t drow = min(lane, a.M - 1);  // the scale row this lane stages (lane < MR)
+  for (int mt = 0; mt < MT; ++mt) arow[mt] = min(m0 + mt * 16 + lc, a.M - 1);
+  const int64_t drow = min(m0 + lane, a.M - 1);  // the scale row this lane stages (lane < MR)
 
   struct Chunk {
     long b[NT][UG];
@@ -174,7 +179,7 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int m = mt * 16 + 4 * lk + q;
+      const int m = m0 + mt * 16 + 4 * lk + q;
       if (m >= a.M) continue;
       if (EPI == EPI_SWIGLU) {
         const int unit = (n0 / 64) * 32 + (n0 % 64) + lc;  // hidden unit of gate row n0 + lc
@@ -193,10 +198,16 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
     }
 }
 
+// grid.y: M tiles of 16 * MT rows.  With a grid.x that is a multiple of
+// eight, the M tiles of one weight unit land on one XCD (workgroups are
+// dealt to the XCDs in turn), whose L2 then serves the unit's weights to
+// all of them.
 template <int MT, int NT, int KW, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
-  const unsigned grid = EPI == EPI_SWIGLU ? (unsigned)(a.N / 32) : (unsigned)((a.N + 16 * NT - 1) / (16 * NT));
-  hipLaunchKernelGGL((k_gemm_skinny<MT, NT, KW, EPI>), dim3(grid), dim3(64 * KW), 0, s, a);
+  const unsigned mtiles = (unsigned)((a.M + 16 * MT - 1) / (16 * MT));
+  unsigned grid = EPI == EPI_SWIGLU ? (unsigned)(a.N / 32) : (unsigned)((a.N + 16 * NT - 1) / (16 * NT));
+  if (mtiles > 1) grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_gemm_skinny<MT, NT, KW, EPI>), dim3(grid, mtiles), dim3(64 * KW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -245,9 +256,14 @@ hipError_t gemm_skinny(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (!gemm_skinny_supported(a.M, a.K) || a.N <= 0 || (epi == EPI_SWIGLU && a.N % 64 != 0))
     return hipErrorInvalidValue;
-  if (a.M <= 16) return launch_mt<1>(a, epi, s);
-  if (a.M <= 32) return launch_mt<2>(a, epi, s);
-  return launch_mt<4>(a, epi, s);
+  // M goes over workgroups in tiles (grid.y): a workgroup's loads bound
+  // these launches, and every workgroup reads all of its rows' activations,
+  // so fewer rows per workgroup and more workgroups win.  Narrow matrices
+  // (fewer than 1024 16-row weight units) take 16-row tiles; the vocabulary
+  // projection takes 32-row tiles of 64-row weight units (at most two tiles
+  // reading each unit, on one XCD).
+  if (a.M <= 16 || (a.N + 15) / 16 < 1024) return launch_mt<1>(a, epi, s);
+  return launch_mt<2>(a, epi, s);
 }
 
 }  // namespace q8k
