@@ -23,7 +23,11 @@
 // of its slice at once and waits one memory round trip (longer slices take
 // their chunks of eight in turn).  Operands come straight from global memory
 // in the MFMA's lane layout (lane (r, g) holds bytes 8g..8g+7 of a block of
-// row r): the weights once, the activation rows from L2.  The activation
+// row r): the weights once, the activation rows from L2.  The activations
+// may be stored block-major (the 32 codes of block b of every row together),
+// so that a load instruction's 16 rows are 512 contiguous bytes: row-major,
+// they are 16 pieces of 32 bytes K apart, and a workgroup's loads were
+// measured a third slower.  The activation
 // scales of a chunk are staged in the wavefront's own LDS, where each lane
 // reads those of the four rows it accumulates.
 #include "kernels.h"
@@ -93,8 +97,9 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
         c.dw[nt][i] = a.sc[wrow[nt] * nblk + kb];
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) c.x[mt][i] = *reinterpret_cast<const long*>(a.qa + arow[mt] * K + kb * 32 + 8 * lk);
-      c.d[i] = a.da[drow * nblk + kb];
+      for (int mt = 0; mt < MT; ++mt)
+        c.x[mt][i] = *reinterpret_cast<const long*>(a.qa + (a.a_blocked ? ((int64_t)kb * a.M + arow[mt]) * 32 : arow[mt] * K + kb * 32) + 8 * lk);
+      c.d[i] = a.da[a.a_blocked ? (int64_t)kb * a.M + drow : drow * nblk + kb];
     }
   };
 

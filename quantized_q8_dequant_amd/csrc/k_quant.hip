@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) k_embed_bf16(const int32_t* __restrict__ 
 // norm_w == nullptr skips the norm.  K % 32 == 0.
 __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x, int K, const float* __restrict__ norm_w,
                                                     float eps, int8_t* __restrict__ qa, float* __restrict__ da,
-                                                    uint16_t* __restrict__ da_bits) {
+                                                    uint16_t* __restrict__ da_bits, int blocked) {
   __shared__ double s_red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * K;
@@ -134,9 +134,10 @@ __global__ void __launch_bounds__(256) k_rows_quant(const float* __restrict__ x,
     float d;
     const int packed = quant4_group8(v, &d);
     if (live) {
-      *reinterpret_cast<int*>(qa + t * K + c) = packed;
+      const int64_t T = gridDim.x, b = c / 32;
+      *reinterpret_cast<int*>(qa + (blocked ? (b * T + t) * 32 + c % 32 : t * K + c)) = packed;
       if ((threadIdx.x & 7) == 0) {
-        const int64_t bi = t * (K / 32) + c / 32;
+        const int64_t bi = blocked ? b * T + t : t * (K / 32) + b;
         if (da) da[bi] = f16_round(d);
         if (da_bits) da_bits[bi] = f32_to_f16_bits(d);
       }
@@ -290,9 +291,9 @@ __global__ void __launch_bounds__(256) k_rows_argmax(const float* __restrict__ x
 }
 
 hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
-                      uint16_t* da_bits, hipStream_t s) {
+                      uint16_t* da_bits, hipStream_t s, bool blocked) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rows_quant, dim3(T), dim3(256), 0, s, x, K, norm_w, eps, qa, da, da_bits);
+  hipLaunchKernelGGL(k_rows_quant, dim3(T), dim3(256), 0, s, x, K, norm_w, eps, qa, da, da_bits, blocked ? 1 : 0);
   return hipGetLastError();
 }
 

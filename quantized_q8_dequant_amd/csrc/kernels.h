@@ -84,8 +84,10 @@ hipError_t embed(const int32_t* tok, int T, int vocab, int H, const void* w, con
 // src: the (sequence, layer) K or V block; srcs: its scales (KV_Q8_0)
 hipError_t kv_export(const void* src, const uint16_t* srcs, int kvt, int nkv, int cap, int len, int hd, float* dst,
                      hipStream_t s);
+// blocked: codes and scales block-major (qa[(b * T + t) * 32 + j], da[b * T + t]),
+// the small-M GEMM's activation layout; else row-major ([T][K], [T][K/32]).
 hipError_t rows_quant(const float* x, int T, int K, const float* norm_w, float eps, int8_t* qa, float* da,
-                      uint16_t* da_bits, hipStream_t s);
+                      uint16_t* da_bits, hipStream_t s, bool blocked = false);
 
 bool gemv_supported_k(int K);
 int gemv_argmax_grid(int N, int K);
@@ -126,6 +128,8 @@ struct GemmArgs {
   // order by a second kernel (0 or 1: no split)
   double* part;
   size_t part_bytes;
+  // small-M form: qa/da block-major (qa[(b * M + m) * 32 + j], da[b * M + m])
+  int a_blocked;
 };
 
 // Prefill per-token head work (see k_attn_prefill.hip).

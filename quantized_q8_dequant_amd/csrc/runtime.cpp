@@ -461,14 +461,14 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
     // whose fused norm/quantise prologue saves the separate launches)
     const int64_t H = m->H;
     GemmArgs g{};
-    g.qa = m->qa, g.da = m->da, g.M = nrows;
+    g.qa = m->qa, g.da = m->da, g.M = nrows, g.a_blocked = 1;  // rows quantised block-major
     auto run = [&](const QPlane& p, int K, float* out, int64_t ldc, int epi) {
       g.qs = p.qs, g.sc = p.sc, g.N = (int)p.rows, g.K = K, g.out = out, g.ldc = ldc;
       return q8k::gemm_skinny(g, epi, s);
     };
     if (kind == 5) {
       float* lg = d_logits ? d_logits : m->blogits;
-      HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s));
+      HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s, true));
       HIP_TRY(run(m->emb, m->H, lg, m->V, EPI_STORE));
       HIP_TRY(q8k::rows_argmax(lg, nrows, m->V, d_argmax, m->am_key, m->am_cnt, s, len_add ? m->d_len : nullptr,
                                d_row_seq, len_add));
@@ -478,19 +478,19 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
       const Layer& ly = m->layers[l];
       switch (kind) {
         case 0:
-          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s, true));
           HIP_TRY(run(ly.qkv, m->H, m->qkv, m->nqkv, EPI_STORE));
           break;
         case 2:
-          HIP_TRY(q8k::rows_quant(m->attn, nrows, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(q8k::rows_quant(m->attn, nrows, m->qw, nullptr, eps, m->qa, m->da, nullptr, s, true));
           HIP_TRY(run(ly.o, m->qw, m->x, H, EPI_RESIDUAL));
           break;
         case 3:
-          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s, true));
           HIP_TRY(run(ly.gateup, m->H, m->h, m->F, EPI_SWIGLU));
           break;
         case 4:
-          HIP_TRY(q8k::rows_quant(m->h, nrows, m->F, nullptr, eps, m->qa, m->da, nullptr, s));
+          HIP_TRY(q8k::rows_quant(m->h, nrows, m->F, nullptr, eps, m->qa, m->da, nullptr, s, true));
           HIP_TRY(run(ly.down, m->F, m->x, H, EPI_RESIDUAL));
           break;
         default:
@@ -573,12 +573,13 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     g.M = T;
     g.part = m->gemm_part;
     g.part_bytes = m->gemm_part_bytes;
+    g.a_blocked = small ? 1 : 0;  // the small-M GEMM reads the rows block-major
     // attention input: RMSNorm + quantise, fused QKV GEMM
     if (m->wbf16) {
       HIP_TRY(q8k::rows_norm(m->x, m->H, T, m->H, ly.attn_norm, eps, m->xn, m->H, s));
       HIP_TRY(q8k::gemm_bf16(bf16_args(ly.qkv, m->xn, m->H, T, m->qkv, m->nqkv), EPI_STORE, s));
     } else {
-      HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s));
+      HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s, small));
       g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
       HIP_TRY(gemm(g, EPI_STORE, s));
     }
@@ -624,14 +625,14 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
       continue;
     }
     // o_proj + residual
-    HIP_TRY(q8k::rows_quant(m->attn, T, m->qw, nullptr, eps, m->qa, m->da, nullptr, s));
+    HIP_TRY(q8k::rows_quant(m->attn, T, m->qw, nullptr, eps, m->qa, m->da, nullptr, s, small));
     g.qs = ly.o.qs, g.sc = ly.o.sc, g.N = (int)ly.o.rows, g.K = m->qw, g.out = m->x, g.ldc = m->H;
     HIP_TRY(gemm(g, EPI_RESIDUAL, s));
     // FFN: RMSNorm + quantise, gate/up with SwiGLU, quantise, down + residual
-    HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s));
+    HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.ffn_norm, eps, m->qa, m->da, nullptr, s, small));
     g.qs = ly.gateup.qs, g.sc = ly.gateup.sc, g.N = (int)ly.gateup.rows, g.K = m->H, g.out = m->h, g.ldc = m->F;
     HIP_TRY(gemm(g, EPI_SWIGLU, s));
-    HIP_TRY(q8k::rows_quant(m->h, T, m->F, nullptr, eps, m->qa, m->da, nullptr, s));
+    HIP_TRY(q8k::rows_quant(m->h, T, m->F, nullptr, eps, m->qa, m->da, nullptr, s, small));
     g.qs = ly.down.qs, g.sc = ly.down.sc, g.N = (int)ly.down.rows, g.K = m->F, g.out = m->x, g.ldc = m->H;
     HIP_TRY(gemm(g, EPI_RESIDUAL, s));
   }
@@ -642,12 +643,13 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
       HIP_TRY(q8k::rows_norm(m->x, H, T, m->H, m->out_norm, eps, m->xn, H, s));
       HIP_TRY(q8k::gemm_bf16(bf16_args(m->emb, m->xn, H, T, d_logits, m->V), EPI_STORE, s));
     } else {
-      HIP_TRY(q8k::rows_quant(m->x, T, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s));
+      const bool head_small = skinny_rows(m, T);
+      HIP_TRY(q8k::rows_quant(m->x, T, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s, head_small));
       GemmArgs g{};
-      g.qa = m->qa, g.da = m->da, g.M = T;
+      g.qa = m->qa, g.da = m->da, g.M = T, g.a_blocked = head_small ? 1 : 0;
       g.part = m->gemm_part, g.part_bytes = m->gemm_part_bytes;
       g.qs = m->emb.qs, g.sc = m->emb.sc, g.N = m->V, g.K = m->H, g.out = d_logits, g.ldc = m->V;
-      HIP_TRY(skinny_rows(m, T) ? q8k::gemm_skinny(g, EPI_STORE, s) : q8k::gemm(g, EPI_STORE, s));
+      HIP_TRY(head_small ? q8k::gemm_skinny(g, EPI_STORE, s) : q8k::gemm(g, EPI_STORE, s));
     }
     if (d_argmax) HIP_TRY(q8k::rows_argmax(d_logits, T, m->V, d_argmax, m->am_key, m->am_cnt, s));
   } else if (last && (d_logits || d_argmax) && m->wbf16) {
@@ -1104,9 +1106,10 @@ int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs
   }
   int8_t* qa = static_cast<int8_t*>(d_work);
   float* da = reinterpret_cast<float*>(static_cast<uint8_t*>(d_work) + align_up((size_t)(m * k)));
-  HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, qa, da, nullptr, s));
   const bool small = q8k::gemm_skinny_supported((int)m, (int)k);
+  HIP_TRY(q8k::rows_quant(d_x, (int)m, (int)k, nullptr, 1e-6f, qa, da, nullptr, s, small));
   GemmArgs g{};
+  g.a_blocked = small ? 1 : 0;
   g.qa = qa;
   g.da = da;
   g.qs = d_qs;
