@@ -17,7 +17,7 @@
 // wavefronts take KW equal slices of K and add their f64 sums in slice order
 // at the end (through LDS), so the sum order is fixed for a given matrix.
 // The small units spread even narrow matrices (1024 outputs) over 64
-// workgroups, times the 16-row M tiles (grid.y); the vocabulary projection
+// workgroups, times the 16-row M tiles; the vocabulary projection
 // gets 64-row units and all M rows per workgroup.  KW is chosen so
 // that a slice is at most eight blocks: a wavefront then issues every load
 // of its slice at once and waits one memory round trip (longer slices take
@@ -51,7 +51,13 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
   __shared__ double s_red[KW - 1][RV][kWave];
 
   const int units = EPI == EPI_SWIGLU ? a.N / 32 : (a.N + 16 * NT - 1) / (16 * NT);
-  if ((int)blockIdx.x >= units) return;  // the grid rounded up to whole XCD rounds
+  // workgroup -> (weight unit, M tile): workgroups are dealt to the eight
+  // XCDs in turn, so id % 8 is the XCD; on each XCD the M tiles of a unit
+  // are consecutive, run together and share the unit's weights in its L2
+  const int mtiles = (a.M + MR - 1) / MR;
+  const int wid = blockIdx.x / 8;
+  const int unit = (wid / mtiles) * 8 + blockIdx.x % 8, mtile = wid % mtiles;
+  if (unit >= units) return;  // units rounded up to a multiple of eight
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int lc = lane % 16, lk = lane / 16;
   const int K = a.K, nblk = K / 32;
@@ -63,16 +69,16 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
   int64_t wrow[NT];
   int n0;
   if (EPI == EPI_SWIGLU) {
-    const int g = blockIdx.x / 2, h = blockIdx.x % 2;
+    const int g = unit / 2, h = unit % 2;
     n0 = 64 * g + 16 * h;
     wrow[0] = min(n0 + lc, a.N - 1);
     wrow[NT - 1] = min(n0 + 32 + lc, a.N - 1);
   } else {
-    n0 = blockIdx.x * 16 * NT;
+    n0 = unit * 16 * NT;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) wrow[nt] = min(n0 + 16 * nt + lc, a.N - 1);
   }
-  const int m0 = blockIdx.y * MR;  // first row of this workgroup's M tile
+  const int m0 = mtile * MR;  // first row of this workgroup's M tile
   int64_t arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) arow[mt] = min(m0 + mt * 16 + lc, a.M - 1);
@@ -203,16 +209,14 @@ __global__ void __launch_bounds__(64 * KW) k_gemm_skinny(GemmArgs a) {
     }
 }
 
-// grid.y: M tiles of 16 * MT rows.  With a grid.x that is a multiple of
-// eight, the M tiles of one weight unit land on one XCD (workgroups are
-// dealt to the XCDs in turn), whose L2 then serves the unit's weights to
-// all of them.
+// One workgroup per (weight unit, M tile of 16 * MT rows), the units
+// rounded up to a multiple of eight (see the kernel's mapping).
 template <int MT, int NT, int KW, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t s) {
   const unsigned mtiles = (unsigned)((a.M + 16 * MT - 1) / (16 * MT));
-  unsigned grid = EPI == EPI_SWIGLU ? (unsigned)(a.N / 32) : (unsigned)((a.N + 16 * NT - 1) / (16 * NT));
-  if (mtiles > 1) grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm_skinny<MT, NT, KW, EPI>), dim3(grid, mtiles), dim3(64 * KW), 0, s, a);
+  const unsigned units = EPI == EPI_SWIGLU ? (unsigned)(a.N / 32) : (unsigned)((a.N + 16 * NT - 1) / (16 * NT));
+  const unsigned grid = (units + 7) / 8 * 8 * mtiles;
+  hipLaunchKernelGGL((k_gemm_skinny<MT, NT, KW, EPI>), dim3(grid), dim3(64 * KW), 0, s, a);
   return hipGetLastError();
 }
 
