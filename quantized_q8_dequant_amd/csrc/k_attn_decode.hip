@@ -504,8 +504,26 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   }
   if (cq == 0) {
 #pragma unroll
-    for (int k = 0; k < EPT; ++k)
-      a.out[(int64_t)row * a.out_stride + (int64_t)g * E + ce + k * kThreads] = (float)(O[k] / s_L[eh[k]]);
+    for (int k = 0; k < EPT; ++k) {
+      const float y = (float)(O[k] / s_L[eh[k]]);
+      const int col = g * E + ce + k * kThreads;
+      a.out[(int64_t)row * a.out_stride + col] = y;
+      if (a.q_out) {
+        // Q8_0 of the output row, block by block: a block's 32 values sit
+        // in 32 consecutive lanes (E and g * E are multiples of 32); the
+        // arithmetic is k_rows_quant's (max over the block, d = amax / 127,
+        // codes rint(v / d) clamped, scale rounded to f16)
+        float am = fabsf(y);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        const float d = am / 127.0f;
+        const float inv = d == 0.f ? 0.f : 1.0f / d;
+        const float q = fminf(fmaxf(rintf(y * inv), -127.f), 127.f);
+        const int64_t bi = (int64_t)(col / 32) * gridDim.z + row;
+        a.q_out[bi * 32 + col % 32] = (int8_t)(int)q;
+        if (col % 32 == 0) a.q_scale[bi] = f16_round(d);
+      }
+    }
   }
 }
 

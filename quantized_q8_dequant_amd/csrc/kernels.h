@@ -57,6 +57,11 @@ struct AttnDecodeArgs {
   unsigned* counter;  // [nrows][nkv], zero between launches
   float* out;         // attention output [nrows][out_stride], head h at h*hd
   int64_t out_stride;
+  // optional (null: off): the output rows quantised to Q8_0 block-major for
+  // the small-M GEMM, codes q_out[(b * nrows + row) * 32 + j], scales
+  // q_scale[b * nrows + row] (f16-rounded), exactly as k_rows_quant does
+  int8_t* q_out;
+  float* q_scale;
   int nkv, nsplit_max, min_rows;
   double scale;  // 1/sqrt(hd)
 };

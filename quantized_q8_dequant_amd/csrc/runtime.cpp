@@ -413,6 +413,9 @@ bool skinny_rows(const qwen3_model* m, int rows) {
          q8k::gemm_skinny_supported(rows, m->qw) && q8k::gemm_skinny_supported(rows, m->F);
 }
 
+// A batched decode step of nrows rows runs its projections on the small-M GEMM.
+bool batched_small_m(const qwen3_model* m, int nrows) { return nrows >= kSkinnyMinBatch && skinny_rows(m, nrows); }
+
 // Kernels of one decode step.  kind: 0 QKV GEMV, 1 attention, 2 o_proj,
 // 3 gate/up SwiGLU, 4 down, 5 lm_head + argmax (len_add advances lengths).
 int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32_t* d_row_seq, float* d_logits,
@@ -455,7 +458,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
     }
     return QWEN3_OK;
   }
-  if (nrows >= kSkinnyMinBatch && skinny_rows(m, nrows)) {
+  if (batched_small_m(m, nrows)) {
     // a batch of streams: quantise the rows once, one small-M GEMM pass over
     // each weight matrix for all of them (smaller batches: the per-row GEMV,
     // whose fused norm/quantise prologue saves the separate launches)
@@ -481,8 +484,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
           HIP_TRY(q8k::rows_quant(m->x, nrows, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s, true));
           HIP_TRY(run(ly.qkv, m->H, m->qkv, m->nqkv, EPI_STORE));
           break;
-        case 2:
-          HIP_TRY(q8k::rows_quant(m->attn, nrows, m->qw, nullptr, eps, m->qa, m->da, nullptr, s, true));
+        case 2:  // the attention kernel wrote its output rows quantised to qa/da
           HIP_TRY(run(ly.o, m->qw, m->x, H, EPI_RESIDUAL));
           break;
         case 3:
@@ -521,6 +523,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
       at.q_norm = ly.q_norm;
       at.k_norm = ly.k_norm;
       at.layer = l;
+      if (batched_small_m(m, nrows)) at.q_out = m->qa, at.q_scale = m->da;  // o_proj's input rows
       HIP_TRY(q8k::attn_decode(at, m->hd, m->G, m->kvt, nrows, s));
       break;
     }
