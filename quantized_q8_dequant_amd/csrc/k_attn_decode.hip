@@ -38,6 +38,9 @@ constexpr int kScoreSlots = 4096;  // f64 scores a workgroup keeps: G heads x (4
 constexpr int kLdsRow = 4;       // padding of a staged row (keeps rows 16-byte aligned)
 constexpr int kCombineRegs = 80; // f64 partial values a thread of the combine holds in flight
 
+template <int G, int HD>
+constexpr int direct_slots() { return G * HD; }
+
 // One tile of K or V rows staged through registers: every thread issues all
 // of its 16-byte loads for a tile at once; two tiles are in flight ahead of
 // the one being used.
@@ -393,20 +396,35 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   }
   __syncthreads();
 
+  // one split: its own o and l are the result (the combine below would
+  // weigh it by exp(0) = 1 and divide by l, so the output is the same); o
+  // goes through LDS to the combine's thread map, no memory round trip
+  const bool direct = nsplit == 1;
+  __shared__ double s_o[direct_slots<G, HD>()];
+  if (direct) {
+    if (out_live) {
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) s_o[o_h * HD + o_d + i] = o[i];
+    }
+    __syncthreads();
+  }
+
   // write this split's partial: [row][g][split][h][0..HD-1] = o, [HD] = m, [HD+1] = l
   const int64_t pstride = (int64_t)G * (HD + 2);
   double* part = a.part + (((int64_t)row * nkv + g) * a.nsplit_max + split) * pstride;
-  if (out_live) {
+  if (!direct && out_live) {
 #pragma unroll
     for (int i = 0; i < DPT; ++i) st_coherent(part + o_h * (HD + 2) + o_d + i, o[i]);
   }
-  if (tid < G) {
+  if (!direct && tid < G) {
     st_coherent(part + tid * (HD + 2) + HD, s_m[tid]);
     st_coherent(part + tid * (HD + 2) + HD + 1, s_l[tid]);
   }
   wait_memory();
   __syncthreads();
-  if (tid == 0) {
+  if (direct) {
+    if (tid == 0) s_last = 1;
+  } else if (tid == 0) {
     unsigned* cnt = a.counter + (int64_t)row * nkv + g;
     const unsigned prev = arrive(cnt);
     s_last = prev == (unsigned)(nsplit - 1);
@@ -487,13 +505,20 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     }
   };
   const int per_thread = (nsplit + NQ - 1) / NQ;
-  if (per_thread <= SB / 4)
+  if (direct) {
+    if (cq == 0) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) O[k] = s_o[ce + k * kThreads];
+    }
+    if (tid < G) s_L[tid] = s_l[tid];
+    __syncthreads();
+  } else if (per_thread <= SB / 4)
     batches(std::integral_constant<int, SB / 4>{});
   else if (per_thread <= SB / 2)
     batches(std::integral_constant<int, SB / 2>{});
   else
     batches(std::integral_constant<int, SB>{});
-  if (NQ > 1) {
+  if (NQ > 1 && !direct) {
     s_red[cq][ce] = O[0];
     __syncthreads();
     if (cq == 0) {

@@ -82,14 +82,17 @@ struct Layer {
   float *attn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr, *ffn_norm = nullptr;
 };
 
-// Splits of the decode attention per (batch row, KV head): about 1024
-// workgroups per launch, at most 64 by that rule (each split also keeps at
-// least 64 rows, so short caches get fewer), and never fewer than the
-// longest cache needs (a split holds at most 4096 / group rows).
+// Splits of the decode attention per (batch row, KV head): about 512
+// workgroups per launch (two per CU at its register use; 1024 and 2048 were
+// measured slower on the 64-stream step, whose 512 (row, KV head) pairs then
+// take one split each and skip the partial round trip), at most 64 by that
+// rule (each split also keeps at least 64 rows, so short caches get fewer),
+// and never fewer than the longest cache needs (a split holds at most
+// 4096 / group rows).
 int decode_splits_needed(int max_cap, int group) { return (max_cap + 4096 / group - 1) / (4096 / group); }
 int decode_nsplit_max(int nkv, int nrows, int needed) {
   const int units = nkv * nrows;
-  int n = (1024 + units - 1) / units;
+  int n = (512 + units - 1) / units;
   if (n > 64) n = 64;
   if (n < needed) n = needed;
   return n;
