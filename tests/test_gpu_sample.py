@@ -191,3 +191,26 @@ def test_sampling_model_logits_with_a_history():
     want, info = sp.sample(logits[0], prompt, cfg, 0.123)
     assert np.array_equal(pen[0], info["row"])
     assert tok[0] == want
+
+
+@pytest.mark.parametrize("V", [1, 7, 255, 4097, 8195])
+@pytest.mark.parametrize("cfg", [
+    sp.SamplerConfig(temperature=1.0, top_p=0.9),
+    sp.SamplerConfig(temperature=0.8, top_k=300),  # more than the 256 cap, more than some rows
+    sp.SamplerConfig(temperature=0.6, top_k=40, min_p=0.05, top_p=0.8),
+    sp.SamplerConfig(temperature=0.0),
+], ids=["nucleus", "top_k300", "mixed", "greedy"])
+def test_odd_vocabulary_sizes(V, cfg):
+    """Rows shorter than a slice, one logit past a slice (a one-element
+    slice), lengths that are not multiples of four (scalar row passes)."""
+    rng = np.random.default_rng(V)
+    n = 5
+    logits = (rng.standard_normal((n, V)) * 2.0).astype(np.float32)
+    u = rng.random(n).astype(np.float32)
+    tok, _ = gpu_sample(logits, cfg, u)
+    for r in range(n):
+        want, info = sp.sample(logits[r], [], cfg, float(u[r]))
+        if near_boundary(info, cfg.top_p):
+            assert tok[r] in info["cand"]
+            continue
+        assert tok[r] == want, (r, tok[r], want)
