@@ -193,7 +193,10 @@ int qwen3_decode_step(qwen3_t* h, int32_t seq, const int32_t* d_token, float* d_
  * [n] (host) in one pass: weights are read once for all n rows, while RoPE
  * positions, KV appends and attention are per sequence ("A transformer from
  * scratch", section 12.5, batch decode).  d_tokens [n] (device),
- * d_logits [n, vocab] (may be NULL), d_argmax [n].  n <= max_batch_tokens. */
+ * d_logits [n, vocab] (may be NULL), d_argmax [n].  n <= max_batch_tokens.
+ * The step is replayed from a captured HIP graph keyed by (n, d_tokens,
+ * d_logits, d_argmax), h_seqs being uploaded before each replay; a handle
+ * keeps at most 32 such graphs (then waits on `stream` and starts over). */
 int qwen3_decode_batch(qwen3_t* h, const int32_t* h_seqs, int32_t n, const int32_t* d_tokens,
                        float* d_logits, int32_t* d_argmax, void* stream);
 

@@ -148,6 +148,9 @@ struct qwen3_model {
   hipStream_t cap_stream = nullptr;
   bool use_graphs = true;
   std::map<std::tuple<int, const void*, const void*, const void*>, hipGraphExec_t> graphs;
+  // batched steps, keyed by (n, d_tokens, d_logits, d_argmax); the row -> sequence
+  // map is uploaded to d_row_seq before each replay
+  std::map<std::tuple<int, const void*, const void*, const void*>, hipGraphExec_t> bgraphs;
 };
 
 namespace {
@@ -825,6 +828,7 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
 void qwen3_destroy(qwen3_t* m) {
   if (!m) return;
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : m->bgraphs) (void)hipGraphExecDestroy(kv.second);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   delete m;
 }
@@ -909,6 +913,40 @@ int qwen3_truncate(qwen3_t* m, int32_t seq, int32_t keep_len, void* stream) {
   return QWEN3_OK;
 }
 
+// Launch the decode step of nrows rows from the graph cached under `key`,
+// capturing it on the model's capture stream the first time.
+constexpr size_t kMaxCachedGraphs = 32;  // per cache; beyond it the cache starts over
+
+static int replay_decode(qwen3_model* m, std::map<std::tuple<int, const void*, const void*, const void*>, hipGraphExec_t>& cache,
+                         const std::tuple<int, const void*, const void*, const void*>& key, int nrows, const int32_t* d_tok,
+                         const int32_t* d_row_seq, float* d_logits, int32_t* d_argmax, hipStream_t s) {
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    hipGraph_t graph = nullptr;
+    HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue_decode(m, nrows, d_tok, d_row_seq, d_logits, d_argmax, m->cap_stream);
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
+    if (rc != QWEN3_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph capture: ") + hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
+    if (cache.size() >= kMaxCachedGraphs) {  // callers that pass fresh buffers every step
+      // a graph launched earlier on the stream may still run: wait for it first
+      HIP_TRY(hipStreamSynchronize(s));
+      for (auto& kv : cache) (void)hipGraphExecDestroy(kv.second);
+      cache.clear();
+    }
+    it = cache.emplace(key, exec).first;
+  }
+  HIP_TRY(hipGraphLaunch(it->second, s));
+  return QWEN3_OK;
+}
+
 int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_logits, int32_t* d_argmax,
                       void* stream) {
   g_err.clear();
@@ -955,24 +993,7 @@ int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_
     return QWEN3_OK;
   }
   auto key = std::make_tuple((int)seq, (const void*)d_token, (const void*)d_logits, (const void*)d_argmax);
-  auto it = m->graphs.find(key);
-  if (it == m->graphs.end()) {
-    hipGraph_t graph = nullptr;
-    HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-    int rc = enqueue_decode(m, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, m->cap_stream);
-    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
-    if (rc != QWEN3_OK) {
-      if (graph) (void)hipGraphDestroy(graph);
-      return rc;
-    }
-    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph capture: ") + hipGetErrorString(e));
-    hipGraphExec_t exec = nullptr;
-    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (e != hipSuccess) return fail(QWEN3_E_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(e));
-    it = m->graphs.emplace(key, exec).first;
-  }
-  HIP_TRY(hipGraphLaunch(it->second, s));
+  TRY(replay_decode(m, m->graphs, key, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, s));
   m->h_len[seq] += 1;
   return QWEN3_OK;
 }
@@ -994,7 +1015,14 @@ int qwen3_decode_batch(qwen3_t* m, const int32_t* h_seqs, int32_t n, const int32
   }
   hipStream_t s = S(stream);
   HIP_TRY(hipMemcpyAsync(m->d_row_seq, h_seqs, (size_t)n * 4, hipMemcpyHostToDevice, s));
-  TRY(enqueue_decode(m, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
+  if (m->use_graphs) {
+    // a step is a few hundred small launches: replayed from a graph the host
+    // no longer paces them
+    auto key = std::make_tuple((int)n, (const void*)d_tokens, (const void*)d_logits, (const void*)d_argmax);
+    TRY(replay_decode(m, m->bgraphs, key, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
+  } else {
+    TRY(enqueue_decode(m, n, d_tokens, m->d_row_seq, d_logits, d_argmax, s));
+  }
   for (int i = 0; i < n; ++i) m->h_len[h_seqs[i]] += 1;
   return QWEN3_OK;
 }
