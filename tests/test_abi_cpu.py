@@ -153,3 +153,42 @@ def test_peak_probes_validate_on_the_host():
     # four wavefronts x four 32x32x32 MFMAs (65,536 int8 ops each) per round
     assert L.qwen3_peak_mfma_i8_ops(2048, 4000) == 2048 * 4 * 4 * 4000 * 65536.0
     assert L.qwen3_peak_mfma_i8_ops(0, 5) == 0.0
+
+
+def test_sample_arguments_validated_on_the_host():
+    """qwen3_sample rejects bad arguments before any launch (the pointers
+    here are never dereferenced)."""
+    L = _lib.lib()
+    good = dict(temperature=0.7, top_k=20, top_p=0.9, min_p=0.0, repeat_penalty=1.1, freq_penalty=0.0,
+                presence_penalty=0.0, repeat_last_n=64)
+    dev, work = C.c_void_p(1 << 20), C.c_void_p(1 << 24)  # aligned stand-ins
+
+    def call(cfg=None, n=2, vocab=1000, logits=dev, hist=None, stride=0, hlen=None, uni=dev, toks=dev, wk=work):
+        c = _lib.SamplerConfig(**{**good, **(cfg or {})})
+        return L.qwen3_sample(logits, n, vocab, C.byref(c), hist, stride, hlen, uni, toks, wk, None)
+
+    assert call(logits=None) == -1
+    assert call(toks=None) == -1
+    assert call(wk=None) == -1
+    assert call(wk=C.c_void_p((1 << 24) + 8)) == -1  # scratch not 256-byte aligned
+    assert call(n=0) == -1 and call(vocab=0) == -1
+    assert call(cfg=dict(top_k=-1)) == -1
+    assert call(cfg=dict(top_p=0.0)) == -1 and call(cfg=dict(top_p=1.5)) == -1
+    assert call(cfg=dict(min_p=-0.1)) == -1 and call(cfg=dict(min_p=1.1)) == -1
+    assert call(cfg=dict(repeat_penalty=0.0)) == -1
+    assert call(cfg=dict(freq_penalty=float("inf"))) == -1
+    assert call(cfg=dict(temperature=float("nan"))) == -1
+    assert call(cfg=dict(repeat_last_n=-1)) == -1 and call(cfg=dict(repeat_last_n=4097)) == -1
+    assert call(hist=dev, stride=64, hlen=None) == -1  # a history needs its lengths
+    assert call(hist=dev, stride=0, hlen=dev) == -1
+    assert call(uni=None) == -1  # sampling needs the uniforms
+    assert _lib.last_error()
+
+
+def test_sample_work_bytes():
+    """The scratch holds each (row, 4096-logit slice) list and its stats."""
+    L = _lib.lib()
+    for n, V in ((1, 151936), (64, 151936), (3, 4097), (1, 1)):
+        S = (V + 4095) // 4096
+        assert L.qwen3_sample_work_bytes(n, V) >= n * S * 4096 * 8
+        assert L.qwen3_sample_work_bytes(n, V) <= n * S * (4096 * 8 + 64) + 4096
