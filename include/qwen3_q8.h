@@ -131,13 +131,20 @@ typedef struct qwen3_weights {
 typedef struct qwen3_model qwen3_t;
 
 /* Bytes of device workspace a handle needs for `cfg` (weights repacked into
- * the library's layout, KV caches, RoPE table and activations).  Returns 0
- * if cfg is invalid (qwen3_last_error says why).  Host-only. */
+ * the library's layout, KV caches, RoPE table and activations).  The KV part
+ * is layers * 2 * kv_heads * head_dim * element bytes per cached position of
+ * every sequence ("A transformer from scratch", section 12.4, the cache's
+ * bytes per position; "The LLM stack (fucina_llm)", section 13.4: the caller
+ * sizes and owns the cache).  Returns 0 if cfg is invalid (qwen3_last_error
+ * says why).  Host-only. */
 size_t qwen3_workspace_bytes(const qwen3_config* cfg);
 
-/* Build a handle.  Copies and repacks the weights (device pointers in the
- * layout above) into `d_workspace`, builds the RoPE table, and sets every
- * sequence's KV length to 0.  The weight buffers are only read during this
+/* Build a handle ("The LLM stack (fucina_llm)", section 13.2: loaded weights
+ * are copied into the engine's own layout, so the source may be freed;
+ * section 13.4: a new cache has length 0; "A transformer from scratch",
+ * section 12.3.4: the RoPE table is built once).  Copies and repacks the
+ * weights (device pointers in the layout above) into `d_workspace`, builds
+ * the RoPE table, and sets every sequence's KV length to 0.  The weight buffers are only read during this
  * call (enqueued on `stream`; the call synchronises the stream before
  * returning, so the caller may free them afterwards).  The workspace is owned
  * by the caller, must be at least qwen3_workspace_bytes(cfg) bytes, 256-byte
@@ -178,14 +185,18 @@ int qwen3_prefill_all_logits(qwen3_t* h, int32_t seq, const int32_t* h_tokens, i
  * QWEN3_E_INVALID_ARGUMENT.  The device length is set on `stream`. */
 int qwen3_truncate(qwen3_t* h, int32_t seq, int32_t keep_len, void* stream);
 
-/* One decode step of sequence `seq`: the token id is read on the device from
+/* One decode step of sequence `seq` ("A transformer from scratch", sections
+ * 12.3-12.5: the cached forward of one token at position L, greedy argmax as
+ * in section 12.6): the token id is read on the device from
  * d_token [1] (so the previous step's d_argmax can be passed straight back
  * and the step needs no host round trip).  Writes d_logits [vocab] (may be
  * NULL) and d_argmax [1] (required).  Length L -> L + 1; L + 1 > capacity is
  * QWEN3_E_KV_CACHE_OVERFLOW.  A device token outside [0, vocab) is clamped
  * into range (the host cannot check it without a synchronisation).  The
- * step is replayed from a captured HIP graph keyed by (seq, d_token,
- * d_logits, d_argmax); it allocates nothing. */
+ * step is either one cooperative launch (qwen3_decode_launches == 1; its
+ * device-side failure is reported by qwen3_step_status) or replayed from a
+ * captured HIP graph keyed by (seq, d_token, d_logits, d_argmax); it
+ * allocates nothing. */
 int qwen3_decode_step(qwen3_t* h, int32_t seq, const int32_t* d_token, float* d_logits,
                       int32_t* d_argmax, void* stream);
 
@@ -204,7 +215,30 @@ int qwen3_decode_batch(qwen3_t* h, const int32_t* h_seqs, int32_t n, const int32
  * section 13.4, reset).  Enqueued on `stream`. */
 int qwen3_reset(qwen3_t* h, int32_t seq, void* stream);
 
-/* Host-side KV length of `seq` (counts every enqueued append). */
+/* Outcome of the one-launch decode steps enqueued so far ("A transformer from
+ * scratch", section 12.6 and "The LLM stack", section 13.4: a failing step
+ * leaves the state it found valid).  The one-launch step (qwen3_decode_launches
+ * == 1) hands activations between workgroups through bounded waits; a wait
+ * that gives up (about 2 s) sets an error word on the device, and that step
+ * and every later one-launch step of the handle write -1 to d_argmax and
+ * advance no length, while qwen3_decode_step, which cannot see the device,
+ * has already counted them.  This call waits for `stream`, reads the word,
+ * and returns QWEN3_OK if it is clear; otherwise it sets every host length
+ * back to the device's (the length before the first failed step), clears
+ * the word, and returns QWEN3_E_DEVICE, after which steps run again.
+ * QWEN3_OK at once for handles without the one-launch step. */
+int qwen3_step_status(qwen3_t* h, void* stream);
+
+/* Test hook for the failure path above: sets the error word on `stream`,
+ * exactly as a wait that gave up would, so that the next one-launch step
+ * fails without waiting.  QWEN3_E_INVALID_ARGUMENT for handles without the
+ * one-launch step. */
+int qwen3_inject_step_error(qwen3_t* h, void* stream);
+
+/* Host-side KV length of `seq` ("The LLM stack (fucina_llm)", section 13.4:
+ * the cache's len, the next append position); it counts every enqueued
+ * append, so after a failed one-launch step it is right again only once
+ * qwen3_step_status has reported the failure. */
 int qwen3_kv_len(const qwen3_t* h, int32_t seq, int32_t* out);
 
 /* Copy layer `layer` of sequence `seq`'s KV cache, positions [0, len), to

@@ -14,8 +14,9 @@ def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
 
     ("A transformer from scratch", section 12.3.2; the same form serves the
     per-head Q/K norm over head_dim, minfer "Qwen3 Support Plan" section 2.2.)
-    eps is a config field stored as f32 (section 12.1), so its f32 value is
-    used.  Parity: pinned (mean(y^2) closed form, grouping equivalence).
+    eps is a config field read from the model file's metadata (section
+    12.1), whose float keys are read as f32 ("The LLM stack (fucina_llm)",
+    section 13.3), so its f32 value is used.  Parity: pinned (mean(y^2) closed form, grouping equivalence).
     """
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     ms = np.mean(x64 * x64, axis=-1, keepdims=True)
@@ -131,8 +132,12 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 def bf16_linear(x: np.ndarray, w_bf16_as_f32: np.ndarray, chunk: int = 16384) -> np.ndarray:
     """y = x @ W^T with f32 activations and bf16 weights (exactly widened),
-    summed in f64, rounded once to f32 (reading of the pages' bf16 weight
-    arm: in-register widening, no activation rounding)."""
+    summed in f64, rounded once to f32 (reading of the bf16 weight arm of
+    "The LLM stack (fucina_llm)", section 13.2.1: a mixed f32 x bf16 kernel
+    with exact in-register widening, no activation rounding).  Every product
+    of an f32 and a bf16 value is exact in f64.  Parity: pinned (the exact
+    rational sum rounded once, a cancellation an f32 running sum loses,
+    unit columns returning activations and weights unrounded)."""
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
     if x64.ndim == 1:
         x64 = x64[None, :]

@@ -40,6 +40,8 @@ EXPORTS = (
     "qwen3_decode_step",
     "qwen3_decode_batch",
     "qwen3_reset",
+    "qwen3_step_status",
+    "qwen3_inject_step_error",
     "qwen3_kv_len",
     "qwen3_last_error",
     "qwen3_q8_0_encode",
@@ -156,6 +158,8 @@ def lib() -> C.CDLL:
         "qwen3_decode_step": (C.c_int, [vp, i32, vp, vp, vp, vp]),
         "qwen3_decode_batch": (C.c_int, [vp, p_i32, i32, vp, vp, vp, vp]),
         "qwen3_reset": (C.c_int, [vp, i32, vp]),
+        "qwen3_step_status": (C.c_int, [vp, vp]),
+        "qwen3_inject_step_error": (C.c_int, [vp, vp]),
         "qwen3_kv_len": (C.c_int, [vp, i32, p_i32]),
         "qwen3_last_error": (C.c_char_p, []),
         "qwen3_q8_0_encode": (C.c_int, [vp, i64, vp, vp]),

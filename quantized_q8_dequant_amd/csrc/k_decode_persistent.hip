@@ -24,8 +24,11 @@
 // that every reader of one epoch has finished before the next is written.
 //
 // Every wait is bounded: after a spin limit the workgroup sets an error word
-// and leaves, the others see the word and leave too, and the step's argmax
-// is -1.  The grid must be co-resident (the host checks occupancy).
+// and leaves, the others see the word and leave too, the step's argmax is -1
+// and the sequence length is not advanced.  The word is sticky: a step that
+// starts with it set does nothing but write -1, until the host reads and
+// clears it.  The grid must be co-resident: it is launched cooperatively, so
+// a grid that cannot be resident fails to launch instead of waiting forever.
 #include "persist.h"
 #include "qdevice.h"
 
@@ -328,9 +331,16 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   const unsigned T0 = a.pstep * (unsigned)(a.L + 1) + 1u;  // epoch of layer 0
   const float eps = a.eps;
 
+  // a failed earlier step leaves the error word set: do nothing
+  if (ld_err(a.err) != 0) {
+    if (b == 0 && tid == 0) a.argmax[0] = -1;
+    return;
+  }
+
   // ---- embedding rows of this workgroup (exact f16(d) * q) ------------------
   {
-    const int tok = a.token[0];
+    // a device token cannot be checked by the host: clamp it into [0, V)
+    const int tok = min(max(a.token[0], 0), a.V - 1);
     if (tid < RC) {
       const int n = b * RC + tid;
       const float x = f16_bits_to_f32(a.emb_sc[(int64_t)tok * (H / 32) + n / 32]) * (float)a.emb_qs[(int64_t)tok * H + n];
@@ -731,10 +741,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       const unsigned prev = arrive(a.am_cnt);
       if (prev == gridDim.x - 1) {
         const unsigned long long k = __hip_atomic_fetch_add(a.best_key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.argmax[0] = ld_err(a.err) ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        const bool failed = ld_err(a.err) != 0;
+        a.argmax[0] = failed ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
         st_coherent(a.best_key, 0ull);
         st_coherent(a.am_cnt, 0u);
-        a.len[seq] = p + 1;
+        if (!failed) a.len[seq] = p + 1;
       }
     }
   }
@@ -757,13 +768,13 @@ bool persist_try(const PersistShape& sh, bool kvbf16, const PersistArgs* a, hipS
   if (sh.H != H || sh.QW != QW || sh.F != F || sh.HD != HD || sh.G != G) return false;
   if (max_ctx) *max_ctx = S * MAXR;
   if (!a) return true;
-  if (kvbf16)
-    hipLaunchKernelGGL((k_decode_persistent<H, QW, F, HD, G, true, S, MAXR>), dim3(kPersistWorkgroups), dim3(NT), 0,
-                       s, *a);
-  else
-    hipLaunchKernelGGL((k_decode_persistent<H, QW, F, HD, G, false, S, MAXR>), dim3(kPersistWorkgroups), dim3(NT), 0,
-                       s, *a);
-  *err = hipGetLastError();
+  // a cooperative launch is refused unless the whole grid can be resident
+  // at once, which every hand-off between workgroups relies on
+  PersistArgs arg = *a;
+  void* params[] = {&arg};
+  const void* fn = kvbf16 ? reinterpret_cast<const void*>(&k_decode_persistent<H, QW, F, HD, G, true, S, MAXR>)
+                          : reinterpret_cast<const void*>(&k_decode_persistent<H, QW, F, HD, G, false, S, MAXR>);
+  *err = hipLaunchCooperativeKernel(fn, dim3(kPersistWorkgroups), dim3(NT), params, 0, s);
   return true;
 }
 

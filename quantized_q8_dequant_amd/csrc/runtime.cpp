@@ -845,8 +845,38 @@ int qwen3_reset(qwen3_t* m, int32_t seq, void* stream) {
   if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
   if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
   HIP_TRY(q8k::set_len(m->d_len, seq, 0, S(stream)));
-  if (m->p_err) HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, S(stream)));
   m->h_len[seq] = 0;
+  return QWEN3_OK;
+}
+
+int qwen3_step_status(qwen3_t* m, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (!m->p_err) return QWEN3_OK;  // no one-launch step on this handle
+  hipStream_t s = S(stream);
+  unsigned word = 0;
+  HIP_TRY(hipMemcpyAsync(&word, m->p_err, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (word == 0) return QWEN3_OK;
+  // the failed steps advanced no device length: the host lengths follow them
+  std::vector<int32_t> dl(m->h_len.size());
+  HIP_TRY(hipMemcpyAsync(dl.data(), m->d_len, dl.size() * 4, hipMemcpyDeviceToHost, s));
+  // a failed step leaves the argmax key and arrival counter part-way
+  HIP_TRY(hipMemsetAsync(m->am_key, 0, 8, s));
+  HIP_TRY(hipMemsetAsync(m->am_cnt, 0, 4, s));
+  HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  m->h_len = dl;
+  return fail(QWEN3_E_DEVICE,
+              "a one-launch decode step gave up waiting on another workgroup: it and every later one-launch step "
+              "wrote token -1 and advanced no length");
+}
+
+int qwen3_inject_step_error(qwen3_t* m, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (!m->p_err) return fail(QWEN3_E_INVALID_ARGUMENT, "this handle has no one-launch decode step");
+  HIP_TRY(hipMemsetAsync(m->p_err, 0xFF, 4, S(stream)));
   return QWEN3_OK;
 }
 

@@ -351,6 +351,16 @@ class Qwen3Model:
     def reset(self, seq: int = 0):
         check(lib().qwen3_reset(self.handle, seq, _stream()))
 
+    def step_status(self) -> None:
+        """Wait for the stream and raise Qwen3Error (QWEN3_E_DEVICE) if a
+        one-launch decode step failed since the last check; the host lengths
+        are then those of the device again."""
+        check(lib().qwen3_step_status(self.handle, _stream()))
+
+    def inject_step_error(self) -> None:
+        """Test hook: set the one-launch step's error word from the host."""
+        check(lib().qwen3_inject_step_error(self.handle, _stream()))
+
     def kv_export(self, seq: int, layer: int):
         """(K, V) of one layer as f32 tensors [kv_heads, len, head_dim]."""
         n = self.kv_len(seq)

@@ -123,6 +123,8 @@ def test_null_handle_and_op_argument_errors():
     assert lib.qwen3_prefill(None, 0, toks, 2, None, None, None) == -1
     assert lib.qwen3_decode_step(None, 0, None, None, None, None) == -1
     assert lib.qwen3_reset(None, 0, None) == -1
+    assert lib.qwen3_step_status(None, None) == -1
+    assert lib.qwen3_inject_step_error(None, None) == -1
     out = C.c_int32()
     assert lib.qwen3_kv_len(None, 0, C.byref(out)) == -1
     assert lib.qwen3_q8_0_encode(0x1000, 33, 0x2000, None) == -1

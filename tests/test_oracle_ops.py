@@ -204,3 +204,57 @@ def test_bf16_round_matches_torch():
     for arr in (x, ties, -ties):
         ref = torch.from_numpy(arr.copy()).to(torch.bfloat16).to(torch.float32).numpy()
         assert np.array_equal(ops.bf16_round(arr), ref)
+
+
+# -- bf16-weight linear ("The LLM stack (fucina_llm)", section 13.2.1: bf16
+# weights widened exactly in registers, activations kept in f32) -------------
+def _round_f32(fr):
+    """The f32 nearest to the rational fr (ties to even), by exact compare."""
+    from fractions import Fraction
+
+    f = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (c.view(np.uint32) & 1) == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_bf16_linear_is_the_exact_sum_rounded_once():
+    from fractions import Fraction
+
+    x = gen_normal_rows((3, 96), seed=41)
+    w = ops.bf16_round(gen_normal_rows((8, 96), seed=42, scale=0.02))
+    y = ops.bf16_linear(x, w)
+    assert y.dtype == np.float32 and y.shape == (3, 8)
+    exact = np.empty((3, 8), np.float32)
+    for t in range(3):
+        for n in range(8):
+            acc = sum((Fraction(float(x[t, k])) * Fraction(float(w[n, k])) for k in range(96)), Fraction(0))
+            exact[t, n] = _round_f32(acc)
+    assert np.array_equal(y, exact)
+
+
+def test_bf16_linear_keeps_what_an_f32_sum_loses():
+    # x . w with w = 1: 2^24 + 1 - 2^24 is 0 in an f32 running sum, 1 exactly
+    x = np.zeros((2, 32), np.float32)
+    x[0, :3] = [2.0**24, 1.0, -(2.0**24)]
+    x[1, :4] = [1.0, 2.0**-30, 2.0**-30, -1.0]
+    w = np.ones((1, 32), np.float32)
+    y = ops.bf16_linear(x, w)
+    assert y[0, 0] == 1.0
+    assert y[1, 0] == np.float32(2.0**-29)
+
+
+def test_bf16_linear_activations_are_not_rounded():
+    # a unit weight column picks out the activation itself, all 24 bits of it
+    x = gen_normal_rows((4, 64), seed=43)
+    w = np.zeros((64, 64), np.float32)
+    w[np.arange(64), np.arange(64)] = 1.0
+    assert np.array_equal(ops.bf16_linear(x, w), x)
+    # and a weight row is used as the bf16 value it holds (no re-rounding)
+    wb = ops.bf16_round(gen_normal_rows((5, 64), seed=44, scale=0.02))
+    e = np.zeros((64, 64), np.float32)
+    e[np.arange(64), np.arange(64)] = 1.0
+    assert np.array_equal(ops.bf16_linear(e, wb), wb.T)
