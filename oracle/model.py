@@ -121,9 +121,11 @@ class Model:
     encoder; bf16 models round them to bf16.  Norm weights stay f32.
     """
 
-    def __init__(self, shape, weights: dict, threads: int = 1):
+    def __init__(self, shape, weights: dict, threads: int = 1, keep_f64: bool = False):
         """threads > 1 encodes the tensors in a thread pool (same results;
-        the encoder is independent per tensor)."""
+        the encoder is independent per tensor).  keep_f64 keeps every matrix
+        also widened to f64 (8 bytes per weight), so that many decode steps
+        do not widen the weights on every call; results are the same."""
         self.shape = shape
         if shape.weight_type not in ("q8_0", "bf16"):
             raise ValueError(shape.weight_type)
@@ -143,6 +145,12 @@ class Model:
                 self.w = {name: f.result() for name, f in futs.items()}
         else:
             self.w = {name: prep(arr) for name, arr in weights.items()}
+        if keep_f64:
+            for name, w in self.w.items():
+                if isinstance(w, q8_0.Q8Weight):
+                    w.keep_f64()
+                elif w.ndim == 2:
+                    self.w[name] = w.astype(np.float64)
 
     # -- building blocks -------------------------------------------------
     def linear(self, x: np.ndarray, name: str) -> np.ndarray:

@@ -145,5 +145,6 @@ def bf16_linear(x: np.ndarray, w_bf16_as_f32: np.ndarray, chunk: int = 16384) ->
     out = np.empty((x64.shape[0], N), dtype=np.float32)
     for n0 in range(0, N, chunk):
         n1 = min(N, n0 + chunk)
-        out[:, n0:n1] = (x64 @ w_bf16_as_f32[n0:n1].astype(np.float64).T).astype(np.float32)
+        wt = np.asarray(w_bf16_as_f32[n0:n1], dtype=np.float64)  # no copy if already f64
+        out[:, n0:n1] = (x64 @ wt.T).astype(np.float32)
     return out

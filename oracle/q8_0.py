@@ -133,6 +133,12 @@ class Q8Weight:
         obj.deq = decode(obj.qs, obj.d)
         return obj
 
+    def keep_f64(self) -> None:
+        """Keep an f64 copy of the dequantised values (exact widening), so
+        that repeated linears do not widen the matrix on every call.  Same
+        values, same products and sums: a speed option only."""
+        self.deq64 = self.deq.astype(np.float64)
+
     def rows(self, ids) -> np.ndarray:
         """Dequantised rows (the embedding gather; exact in f32)."""
         return self.deq[np.asarray(ids)]
@@ -151,7 +157,9 @@ def linear(x: np.ndarray, w: Q8Weight, chunk: int = 16384) -> np.ndarray:
     qa, da = encode(x)
     a = decode(qa, da).astype(np.float64)
     out = np.empty((x.shape[0], w.N), dtype=np.float32)
+    wide = getattr(w, "deq64", None)  # the same values already widened, if kept
     for n0 in range(0, w.N, chunk):
         n1 = min(w.N, n0 + chunk)
-        out[:, n0:n1] = (a @ w.deq[n0:n1].astype(np.float64).T).astype(np.float32)
+        wt = wide[n0:n1] if wide is not None else w.deq[n0:n1].astype(np.float64)
+        out[:, n0:n1] = (a @ wt.T).astype(np.float32)
     return out

@@ -182,16 +182,23 @@ def test_tiny_batched_decode_matches_single(tiny_w, tiny_ref):
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_qwen3_0_6b_prefill_and_decode_matches_oracle():
+    """The decode workload as timed: the 512-token prompt, then all 256 greedy
+    decode steps (the one-launch step), every step's logits and token against
+    the oracle's."""
     wl = WORKLOADS["0.6b-decode"]
     w = gen_weights(QWEN3_0_6B, wl.weight_seed)
     prompt = gen_prompt(QWEN3_0_6B.vocab_size, wl.prompt_len, wl.prompt_seed)
-    steps = 4
+    steps = wl.decode_steps
     gpu = make(QWEN3_0_6B, w, [wl.kv_capacity])
+    assert gpu.decode_launches() == 1
     toks, logits = gpu_generate(gpu, prompt, steps)
+    gpu.step_status()
     gpu.close()
     del gpu
     torch.cuda.empty_cache()
-    ref = om.Model(QWEN3_0_6B, w)
+    for lg, t in zip(logits, toks):
+        assert int(np.argmax(lg)) == t
+    ref = om.Model(QWEN3_0_6B, w, keep_f64=True)
     del w
     rtoks, rlogits = ref.generate(prompt, steps, ref.new_cache(wl.kv_capacity))
     check_against_oracle(toks, logits, rtoks, rlogits)
@@ -273,19 +280,6 @@ def test_tiny_bf16_batched_decode_matches_oracle(tiny_bf16_w, tiny_bf16_ref):
             assert outs[i][1][s] == rt[i + 1]
 
 
-def oracle_cache_from_gpu(ref, gpu, seq, capacity):
-    """An oracle KV cache holding the GPU's cache of one sequence."""
-    s = ref.shape
-    cache = ref.new_cache(capacity)
-    n = gpu.kv_len(seq)
-    for layer in range(s.num_layers):
-        k, v = gpu.kv_export(seq, layer)
-        cache.k[layer][:n] = k.cpu().numpy().transpose(1, 0, 2)
-        cache.v[layer][:n] = v.cpu().numpy().transpose(1, 0, 2)
-    cache.len = n
-    return cache
-
-
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_qwen3_0_6b_bf16_ragged_batch_matches_oracle():
@@ -320,99 +314,197 @@ def test_qwen3_0_6b_bf16_ragged_batch_matches_oracle():
             assert outs[i][1][s] == rt[i + 1], (s, i)
 
 
+def oracle_cache_from_rows(ref, ks, vs, rows, capacity):
+    """An oracle cache holding rows [0, rows) of exported GPU K/V rows."""
+    c = ref.new_cache(capacity)
+    for layer in range(ref.shape.num_layers):
+        c.k[layer][:rows] = ks[layer][:rows]
+        c.v[layer][:rows] = vs[layer][:rows]
+    c.len = rows
+    return c
+
+
+def export_rows(gpu, seq):
+    """Every layer's cached K and V rows of one sequence, as f32 [n, kv_heads, hd]."""
+    ks, vs = [], []
+    for layer in range(gpu.cfg.num_layers):
+        k, v = gpu.kv_export(seq, layer)
+        ks.append(k.cpu().numpy().transpose(1, 0, 2).copy())
+        vs.append(v.cpu().numpy().transpose(1, 0, 2).copy())
+    return ks, vs
+
+
+def check_prompt_blocks(ref, prompt, ks, vs, starts, B, what):
+    """Oracle forward of each block prompt[p0 : p0 + B] over the GPU's rows
+    [0, p0) (p0 = 0: the oracle's own prefill); the block's cached rows of
+    every layer against the oracle's.  Returns the last block's logits."""
+    lg = None
+    for p0 in starts:
+        c = oracle_cache_from_rows(ref, ks, vs, p0, p0 + B)
+        lg = ref.forward(prompt[p0 : p0 + B], c)[0]
+        for layer in range(ref.shape.num_layers):
+            check_cache_rows(ks[layer][p0 : p0 + B], c.k[layer][p0 : p0 + B], f"{what} K rows {p0}+{B} layer {layer}")
+            check_cache_rows(vs[layer][p0 : p0 + B], c.v[layer][p0 : p0 + B], f"{what} V rows {p0}+{B} layer {layer}")
+        del c
+    return lg
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(1200)
 def test_bf16_batch64_ragged_workload():
     """The batched bf16 workload at full size: 64 sequences with lengths drawn
-    from 1024..16384, each filled by prefill, then 128 lockstep greedy steps.
+    from 1024..16384, each filled by prefill, then 128 lockstep greedy steps
+    ("A transformer from scratch", section 12.5: a batched step is each
+    sequence's own step).
 
-    Checked: every step's token is the argmax of its own logits; for the
-    shortest and the longest sequence, the first 32 cache rows of every layer
-    equal the oracle's (rows of early positions do not depend on later
-    tokens), and the oracle, started from the GPU's cache, reproduces the
-    logits and tokens of the first two batched steps and of the last one."""
+    Checked against the oracle, for the shortest, the longest and six
+    sequences drawn with a fixed seed: the shortest in full (the oracle's own
+    prefill, every cached row, its first two decode steps); for the others,
+    64-row blocks of the prompt (the first from an empty cache, one in the
+    middle and the last over the GPU's earlier rows: every layer's rows and
+    the prefill's logits and token), and the first and last batched steps
+    over the GPU's cache.  For all 64: every step's token is the argmax of
+    its logits, and the first and last batched steps equal each sequence's
+    own decode step (rewound with truncate and stepped alone)."""
     from synthetic import QWEN3_0_6B_BF16, gen_lengths, gen_prompts
 
     wl = WORKLOADS["0.6b-bf16-batch64"]
     shape = QWEN3_0_6B_BF16
+    B = 64
     lengths = gen_lengths(wl.n_seqs, wl.min_len, wl.max_len, wl.length_seed)
     prompts = gen_prompts(shape.vocab_size, lengths, wl.prompt_seed)
-    w = gen_weights(shape, wl.weight_seed)
-    caps = [int(n) + wl.decode_steps for n in lengths]
-    gpu = make(shape, w, caps)
-    first = []
-    for s, p in enumerate(prompts):
-        first.append(int(gpu.prefill(p, seq=s, logits=False)[1].item()))
     n = wl.n_seqs
+    order = np.argsort(lengths, kind="stable")
+    short, longest = int(order[0]), int(order[-1])
+    rest = [i for i in range(n) if i not in (short, longest)]
+    drawn = np.random.Generator(np.random.PCG64(504)).choice(len(rest), 6, replace=False)
+    picks = [short, longest] + sorted(rest[i] for i in drawn)
+    w = gen_weights(shape, wl.weight_seed)
+    caps = [int(L) + wl.decode_steps for L in lengths]
+    gpu = make(shape, w, caps)
+    ref = om.Model(shape, w, keep_f64=True)
+    del w
+    first, pre_logits = [], {}
+    for s, p in enumerate(prompts):
+        lg, am = gpu.prefill(p, seq=s, logits=s in picks)
+        first.append(int(am.item()))
+        if s in picks:
+            pre_logits[s] = lg.cpu().numpy().copy()
+    progress("GPU: 64 prompts prefilled")
+
+    # oracle checks of the prefills, and the oracle's first step of each pick
+    want0, want1 = {}, None
+    for s in picks:
+        L = int(lengths[s])
+        ks, vs = export_rows(gpu, s)
+        if s == short:
+            rc = ref.new_cache(L + 2)
+            lr = ref.forward(prompts[s], rc)[0]
+            for layer in range(shape.num_layers):
+                check_cache_rows(ks[layer], rc.k[layer][:L], f"seq {s} K layer {layer}")
+                check_cache_rows(vs[layer], rc.v[layer][:L], f"seq {s} V layer {layer}")
+            want0[s] = ref.forward([first[s]], rc)[0]
+            want1 = (ref, rc)  # the oracle's own cache, one step on
+        else:
+            mid = (L // 2 // B) * B
+            lr = check_prompt_blocks(ref, prompts[s], ks, vs, [0, mid, L - B], B, f"seq {s}")
+            c = oracle_cache_from_rows(ref, ks, vs, L, L + 1)
+            want0[s] = ref.forward([first[s]], c)[0]
+            del c
+        assert rel_err(pre_logits[s], lr) <= TOL, s
+        assert first[s] == int(np.argmax(lr)), s
+        del ks, vs
+        progress(f"oracle: sequence {s} (length {L}) checked")
+
     seqs = list(range(n))
-    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
     logits = torch.empty((n, shape.vocab_size), dtype=torch.float32, device="cuda:0")
     am = torch.empty(n, dtype=torch.int32, device="cuda:0")
-    picks = [int(np.argmin(lengths)), int(np.argmax(lengths))]
-    kept = {}
-    ref = om.Model(shape, w)
-    del w
-    caches = {}
+
+    def batched_equals_single(step_toks, lg_b, am_b):
+        """Rewind every sequence by the batched step's row and redo it alone."""
+        for s in seqs:
+            L = gpu.kv_len(s)
+            gpu.truncate(L - 1, seq=s)
+            t = torch.tensor([step_toks[s]], dtype=torch.int32, device="cuda:0")
+            lg1, am1 = gpu.decode_step(seq=s, token=t)
+            lg1 = lg1.cpu().numpy()
+            assert int(am1.item()) == int(am_b[s]), s
+            assert rel_err(lg1, lg_b[s]) <= TOL, s
+            assert gpu.kv_len(s) == L
+
+    toks_h = list(first)
+    toks = torch.tensor(first, dtype=torch.int32, device="cuda:0")
     for step in range(wl.decode_steps):
-        if step == wl.decode_steps - 1:  # oracle caches just before the last step
-            caches_last = {s: oracle_cache_from_gpu(ref, gpu, s, caps[s]) for s in picks}
-            tok_last = {s: int(toks[s].item()) for s in picks}
-        if step == 0:
-            caches = {s: oracle_cache_from_gpu(ref, gpu, s, caps[s]) for s in picks}
+        last = step == wl.decode_steps - 1
+        if last:  # the oracle's last step of each pick, over the GPU's cache
+            wantN = {}
+            for s in picks:
+                ks, vs = export_rows(gpu, s)
+                c = oracle_cache_from_rows(ref, ks, vs, gpu.kv_len(s), gpu.kv_len(s) + 1)
+                del ks, vs
+                wantN[s] = ref.forward([toks_h[s]], c)[0]
+                del c
+            progress("oracle: last-step references done")
         gpu.decode_batch(seqs, toks, logits, am)
         lg = logits.cpu().numpy()
         amh = am.cpu().numpy()
         assert np.array_equal(np.argmax(lg, axis=1), amh), f"step {step}"
-        if step in (0, 1, wl.decode_steps - 1):
-            kept[step] = (lg[picks].copy(), amh[picks].copy())
+        if step == 0:
+            for s in picks:
+                assert rel_err(lg[s], want0[s]) <= TOL, (s, step)
+                assert int(amh[s]) == int(np.argmax(want0[s])), (s, step)
+            batched_equals_single(toks_h, lg, amh)
+        if step == 1:
+            r, rc = want1
+            lr = r.forward([toks_h[short]], rc)[0]
+            assert rel_err(lg[short], lr) <= TOL
+            assert int(amh[short]) == int(np.argmax(lr))
+            want1 = None
+        if last:
+            for s in picks:
+                assert rel_err(lg[s], wantN[s]) <= TOL, (s, step)
+                assert int(amh[s]) == int(np.argmax(wantN[s])), (s, step)
+            batched_equals_single(toks_h, lg, amh)
+        toks_h = [int(t) for t in amh]
         toks = am.clone()
-    for s in picks:
+    for s in seqs:
         assert gpu.kv_len(s) == lengths[s] + wl.decode_steps
-    # early cache rows against the oracle's own prefill of the first 32 tokens
-    for i, s in enumerate(picks):
-        rc = ref.new_cache(32)
-        ref.forward(prompts[s][:32], rc)
-        for layer in (0, shape.num_layers // 2, shape.num_layers - 1):
-            k, v = gpu.kv_export(s, layer)
-            for g, o in ((k, rc.k[layer][:32]), (v, rc.v[layer][:32])):
-                g = g.cpu().numpy()[:, :32].transpose(1, 0, 2)
-                # both sides round to bf16 on store: at most one bf16 ulp apart
-                assert np.all(np.abs(g - o) <= 2.0**-8 * np.abs(o)), (s, layer)
-                assert np.mean(g == o) >= 0.99, (s, layer)
     gpu.close()
-    del gpu
-    torch.cuda.empty_cache()
-    for i, s in enumerate(picks):
-        cache = caches[s]
-        tok = first[s]
-        for step in (0, 1):
-            lr = ref.forward([tok], cache)[0]
-            assert rel_err(kept[step][0][i], lr) <= TOL, (s, step)
-            assert kept[step][1][i] == int(np.argmax(lr)), (s, step)
-            tok = int(kept[step][1][i])
-        lr = ref.forward([tok_last[s]], caches_last[s])[0]
-        last = wl.decode_steps - 1
-        assert rel_err(kept[last][0][i], lr) <= TOL, (s, last)
-        assert kept[last][1][i] == int(np.argmax(lr)), (s, last)
+
+
+def check_cache_rows(gpu_rows, ref_rows, what):
+    """Cached K or V rows [n, kv_heads, hd] of the GPU against the oracle's.
+    Both round the same f32 values to the cache type, so nearly all are
+    bitwise equal; a row may differ where an upstream Q8_0 code flipped, by
+    at most one bf16 step of the row's largest element (the logits' own bar
+    is 1e-3 of their range)."""
+    g = np.asarray(gpu_rows, np.float64)
+    o = np.asarray(ref_rows, np.float64)
+    assert g.shape == o.shape, what
+    scale = np.max(np.abs(o), axis=-1, keepdims=True) + 1e-30
+    worst = float(np.max(np.abs(g - o) / scale))
+    same = float(np.mean(g == o))
+    assert worst <= 2.0**-8, f"{what}: worst row error {worst:.2e} of the row's largest element"
+    assert same >= 0.99, f"{what}: {same:.4f} bitwise equal"
 
 
 @pytest.mark.slow
 @pytest.mark.timeout(2400)
 def test_qwen3_8b_long_context_matches_oracle():
-    """Qwen3-8B shape, Q8_0 weights, bf16 KV cache: the 2048-token prompt, one
-    decode step, then decode steps at KV lengths 16384 and 32768 (each cache
-    filled by prefilling a seeded random prompt of that length).
+    """Qwen3-8B shape, Q8_0 weights, bf16 KV cache.
 
-    The oracle cannot redo a 2048..32768-token prefill of an 8B model on the
-    host, so it starts from the GPU's cache: rows of the first 16 positions
-    are checked against the oracle's own 16-token prefill (one bf16 ulp),
-    the prefill's last-row logits against the oracle's forward of the last
-    prompt token over the GPU's first 2047 rows, and each decode step's
-    logits and token against the oracle's step over the GPU's cache."""
+    The 2048-token prompt and 8 greedy decode steps against the oracle's own
+    prefill and steps: every step's logits and token, and every cached row
+    (all 2056 positions, all 36 layers) against the oracle's cache.  Then
+    decode steps at KV lengths 16384 and 32768 (each cache filled by
+    prefilling a seeded random prompt of that length): there the oracle,
+    which cannot redo an 8B prefill of that length on the host, takes the
+    GPU's cache and checks the step's logits and token."""
     from synthetic import QWEN3_8B
 
     wl = WORKLOADS["8b-longctx"]
     shape = QWEN3_8B
+    steps = 8
     w = gen_weights(shape, wl.weight_seed)
     progress("8B weights drawn")
     prompt = gen_prompt(shape.vocab_size, wl.prompt_len, wl.prompt_seed)
@@ -429,11 +521,9 @@ def test_qwen3_8b_long_context_matches_oracle():
             vs.append(v.cpu().numpy().transpose(1, 0, 2).copy())
         return n, ks, vs
 
-    lg, am = gpu.prefill(prompt)
-    pre_logits, pre_tok = lg.cpu().numpy().copy(), int(am.item())
-    n2048, ks2048, vs2048 = export_all()
-    lg, am = gpu.decode_step()
-    step_logits, step_tok = lg.cpu().numpy().copy(), int(am.item())
+    toks, logits = gpu_generate(gpu, prompt, steps)
+    n_short, ks_short, vs_short = export_all()
+    assert n_short == wl.prompt_len + steps
     long = {}
     for L in wl.decode_contexts[1:]:
         gpu.reset()
@@ -447,9 +537,20 @@ def test_qwen3_8b_long_context_matches_oracle():
     gpu.close()
     del gpu
     torch.cuda.empty_cache()
-    ref = om.Model(shape, w, threads=16)
+    for lg, t in zip(logits, toks):
+        assert int(np.argmax(lg)) == t
+    ref = om.Model(shape, w, threads=16, keep_f64=True)
     del w
     progress("oracle model built")
+
+    rc = ref.new_cache(n_short + 1)
+    rtoks, rlogits = ref.generate(prompt, steps, rc)
+    progress("oracle: 2048-token prefill and 8 steps done")
+    check_against_oracle(toks, logits, rtoks, rlogits)
+    for layer in range(L_):
+        check_cache_rows(ks_short[layer], rc.k[layer][:n_short], f"K layer {layer}")
+        check_cache_rows(vs_short[layer], rc.v[layer][:n_short], f"V layer {layer}")
+    del rc, ks_short, vs_short
 
     def cache_of(n, ks, vs, rows):
         c = ref.new_cache(n + 1)
@@ -459,24 +560,6 @@ def test_qwen3_8b_long_context_matches_oracle():
         c.len = rows
         return c
 
-    # early rows
-    rc = ref.new_cache(16)
-    ref.forward(prompt[:16], rc)
-    for layer in (0, L_ // 2, L_ - 1):
-        for g, o in ((ks2048[layer][:16], rc.k[layer][:16]), (vs2048[layer][:16], rc.v[layer][:16])):
-            assert np.all(np.abs(g - o) <= 2.0**-8 * np.abs(o)), layer
-            assert np.mean(g == o) >= 0.99, layer
-    # the prefill's last row, then the decode step at len 2048
-    assert n2048 == wl.prompt_len
-    c = cache_of(n2048, ks2048, vs2048, n2048 - 1)
-    lr = ref.forward(prompt[-1:], c)[0]
-    assert rel_err(pre_logits, lr) <= TOL
-    assert pre_tok == int(np.argmax(lr))
-    progress("oracle: prefill last row checked")
-    lr = ref.forward([pre_tok], c)[0]
-    assert rel_err(step_logits, lr) <= TOL
-    assert step_tok == int(np.argmax(lr))
-    del c, ks2048, vs2048
     for L, (t0, n, ks, vs, lg, tok) in long.items():
         assert n == L
         c = cache_of(n, ks, vs, n)
