@@ -316,6 +316,20 @@ size_t qwen3_linear_work_bytes(int64_t m, int64_t k);
 int qwen3_q8_0_linear(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs,
                       const uint16_t* d_scale, int64_t n, float* d_y, void* d_work, void* stream);
 
+/* The same Q8_0 linear for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no d_work argument; the scratch is a fixed array of
+ * QWEN3_LINEAR_NOALLOC_SCRATCH_BYTES in device memory that each GPU holds
+ * until the process ends.  Arguments, layouts and results are those of
+ * qwen3_q8_0_linear (the same kernels run).  m > 1 with
+ * qwen3_linear_work_bytes(m, k) above the limit is
+ * QWEN3_E_INVALID_ARGUMENT, before any launch.  It calls no allocator.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (two streams, two threads) race; calls in one stream do not. */
+#define QWEN3_LINEAR_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int qwen3_q8_0_linear_noalloc(const float* d_x, int64_t m, int64_t k, const int8_t* d_qs,
+                              const uint16_t* d_scale, int64_t n, float* d_y, void* stream);
+
 /* Test hook for the integer path: quantise x [m, k] the way the linears do
  * (d_qa int8 [m, k], d_da f16 bits [m, k/32]) and write every integer block
  * dot S[t, j, b] = sum_i qa[t, 32b+i] * qw[j, 32b+i] to d_s int32 [m, n, k/32],

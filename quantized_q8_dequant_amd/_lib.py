@@ -49,6 +49,7 @@ EXPORTS = (
     "qwen3_q8_0_repack",
     "qwen3_linear_work_bytes",
     "qwen3_q8_0_linear",
+    "qwen3_q8_0_linear_noalloc",
     "qwen3_q8_0_block_dots",
     "qwen3_kv_export",
     "qwen3_replay_kernel",
@@ -167,6 +168,7 @@ def lib() -> C.CDLL:
         "qwen3_q8_0_repack": (C.c_int, [vp, i64, i64, vp, vp, vp]),
         "qwen3_linear_work_bytes": (sz, [i64, i64]),
         "qwen3_q8_0_linear": (C.c_int, [vp, i64, i64, vp, vp, i64, vp, vp, vp]),
+        "qwen3_q8_0_linear_noalloc": (C.c_int, [vp, i64, i64, vp, vp, i64, vp, vp]),
         "qwen3_q8_0_block_dots": (C.c_int, [vp, i64, i64, vp, i64, vp, vp, vp, vp]),
         "qwen3_kv_export": (C.c_int, [vp, i32, i32, vp, vp, vp]),
         "qwen3_replay_kernel": (C.c_int, [vp, i32, i32, i32, i32, vp]),

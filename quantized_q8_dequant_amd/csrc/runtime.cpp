@@ -19,6 +19,7 @@
 #include <vector>
 
 #include "../../include/qwen3_q8.h"
+#include "errors.h"
 #include "kernels.h"
 
 namespace {
@@ -29,6 +30,12 @@ int fail(int code, const std::string& msg) {
   g_err = msg;
   return code;
 }
+
+}  // namespace
+
+int q8rt::set_error(int code, const char* msg) { return fail(code, msg); }
+
+namespace {
 
 #define HIP_TRY(expr)                                                                                   \
   do {                                                                                                  \

@@ -137,6 +137,11 @@ def test_null_handle_and_op_argument_errors():
     assert lib.qwen3_bf16_linear(0x1000, 0, 64, 0x2000, 8, 0x3000, None) == -1
     assert lib.qwen3_bf16_linear(None, 2, 64, 0x2000, 8, 0x3000, None) == -1
     assert lib.qwen3_decode_launches(None) == -1
+    # the allocation-free linear refuses an over-limit m x k on the host,
+    # before resolving any device address
+    assert lib.qwen3_q8_0_linear_noalloc(0x1000, 8192, 2048, 0x2000, 0x3000, 64, 0x4000, None) == -1
+    assert "scratch" in _lib.last_error()
+    assert lib.qwen3_q8_0_linear_noalloc(0x1000, 1 << 40, 2048, 0x2000, 0x3000, 64, 0x4000, None) == -1
     # encoding zero values enqueues nothing
     assert lib.qwen3_q8_0_encode(None, 0, None, None) == 0
 
