@@ -372,7 +372,9 @@ def bench_sampling(V: int, args) -> dict:
     """The device sampling pipeline on rows of V logits: a Qwen3-style
     setting (temperature 0.7, top-k 20, top-p 0.95, repetition penalty over
     64 tokens) and the exact nucleus (top-k 0, top-p 0.9: on these N(0, 4^2)
-    logits its window grows past 256 candidates), for 1 and 64 rows."""
+    logits its window grows past 256 candidates), for 1 and 64 rows; and the
+    exact nucleus on flat N(0, 1) rows, whose window grows to the whole
+    vocabulary (the wide window sorted in scratch), for 1 and 8 rows."""
     import torch
 
     from quantized_q8_dequant_amd import sample
@@ -394,6 +396,17 @@ def bench_sampling(V: int, args) -> dict:
                 sample(lg, uni, history=hist, history_len=hlen, **kw)
 
             out[f"{name}_rows{rows}_us"] = round(event_ms(run, args.warmup, max(args.steps, 5)) * 1000.0, 1)
+    for rows in (1, 8):
+        base = torch.randn((rows, V), device="cuda:0", generator=g)
+        uni = torch.rand(rows, device="cuda:0", generator=g)
+        lg = base.clone()
+
+        def run_wide():
+            sample(lg, uni, temperature=1.0, top_k=0, top_p=0.9)
+
+        out[f"nucleus_whole_vocab_top_p0.9_rows{rows}_us"] = round(
+            event_ms(run_wide, args.warmup, max(args.steps, 5)) * 1000.0, 1
+        )
     return out
 
 

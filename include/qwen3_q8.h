@@ -354,9 +354,9 @@ int qwen3_bf16_linear(const float* d_x, int64_t m, int64_t k, const uint16_t* d_
  * lowest id among equal maxima), top-k (at most 256 candidates), the
  * temperature softmax, top-p, min-p and one draw.  top_k == 0 is the exact
  * nucleus: probabilities carry the whole-vocabulary denominator and the
- * candidate window grows 256 -> 1024 -> 4096 until it holds the top_p mass;
- * this implementation stops the window at 4096 candidates (a nucleus that
- * needs more is cut there).  Candidates are ordered by logit, ties by lower
+ * candidate window grows four-fold (256, 1024, 4096, 16384, 65536, ...) up
+ * to the whole vocabulary until it holds the top_p mass, so no tail is cut.
+ * Candidates are ordered by logit, ties by lower
  * id; the softmax and every sum are f64; the draw takes the first candidate
  * whose cumulative probability exceeds u times the kept total. */
 typedef struct qwen3_sampler_config {
@@ -377,7 +377,9 @@ typedef struct qwen3_sampler_config {
  * random number; unused when greedy, may then be NULL), d_tokens int32 [n]
  * out, d_work device scratch of qwen3_sample_work_bytes(n, vocab) bytes
  * (caller-owned, 256-byte aligned; each row's candidates per slice of 4096
- * logits).  QWEN3_E_INVALID_ARGUMENT for a null or out-of-range argument. */
+ * logits, and 8 * vocab bytes per row for an exact-nucleus window wider than
+ * 4096 candidates).  QWEN3_E_INVALID_ARGUMENT for a null or out-of-range
+ * argument. */
 size_t qwen3_sample_work_bytes(int32_t n, int32_t vocab);
 int qwen3_sample(float* d_logits, int32_t n, int32_t vocab, const qwen3_sampler_config* cfg,
                  const int32_t* d_history, int32_t history_stride, const int32_t* d_history_len,

@@ -18,13 +18,18 @@
 // k_sample: one 1024-thread workgroup per row.
 //   - max and argmax from the slices': the greedy answer when temperature <= 0;
 //   - the W best candidates (W = min(top_k, 256), or the exact-nucleus window
-//     256, 1024, 4096 when top_k == 0), descending logit, ties by lower id.
+//     256, 1024, 4096, 16384, 65536, ... up to the vocabulary when top_k == 0),
+//     descending logit, ties by lower id.
 //     The union of the slices' lists holds every key at or above the highest
 //     cut T* of a partial list; a union of up to 8192 keys is copied to LDS.
 //     Per window a radix select over that copy (else over the union in
 //     memory; over the whole row when the union may miss keys of the
 //     window) gives the W-th key, a gather takes the keys at or above it
-//     (ties in id order) and a bitonic sort held in registers orders them;
+//     (ties in id order) and a bitonic sort held in registers orders them.
+//     A window of more than 4096 candidates lives in the caller's scratch:
+//     the row's keys at or above the W-th are gathered in id order and put
+//     in descending order by a stable radix sort (4-bit digits), so ties
+//     stay in id order, and the cumulative p go to the scratch too;
 //   - p_i = exp((l_i - l_max) / T) / Z in f64, Z over the W candidates
 //     (top_k > 0) or over the whole row (top_k == 0), an inclusive f64 scan,
 //     the top-p prefix, the min-p prefix, and the inverse-CDF draw of the
@@ -41,7 +46,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxCand = 256;      // top_k cap (the pages' candidate limit)
-constexpr int kMaxWindow = 4096;   // exact-nucleus window cap (LDS)
+constexpr int kMaxWindow = 4096;   // windows up to this size live in LDS
 constexpr int kUnionCap = 8192;    // slice-list union copied to LDS
 constexpr int kHists = kWaves / 2; // radix histograms (fewer same-bin atomics per copy)
 
@@ -49,6 +54,7 @@ constexpr int kHists = kWaves / 2; // radix histograms (fewer same-bin atomics p
 // denominator and the candidate list (kSlice slots, cnt used).
 struct SliceScratch {
   unsigned long long* cand;
+  unsigned long long* wide;  // per row V more slots: the exact nucleus's wide window
   double* z;
   float* m;
   int* am;
@@ -295,6 +301,57 @@ QDEV void sort_window(unsigned long long* s, int n) {
   if (n2 > 2 * kThreads) sort_desc<4>(s, n, n2);
   else if (n2 > kThreads) sort_desc<2>(s, n, n2);
   else sort_desc<1>(s, n, n2);
+}
+
+// Stable sort, descending by key (the high 32 bits), of the n elements at a,
+// with b (n slots) as the other buffer: one pass per 4-bit digit from bit 0
+// up to the digit at top_shift (the keys agree above it; top_shift < 0: all
+// keys are equal and a is already in order).  Each thread takes a contiguous
+// chunk, counts its digits into its own column of s_cnt (16 x kThreads),
+// the counts are scanned in (digit, thread) order, and the chunk is
+// scattered in its order, so equal digits keep their order.  Returns the
+// buffer that holds the result.
+QDEV unsigned long long* radix_sort_desc(unsigned long long* a, unsigned long long* b, int n, int top_shift,
+                                         unsigned* s_cnt, int* s_iw) {
+  const int tid = threadIdx.x;
+  const int C = (n + kThreads - 1) / kThreads;
+  const int j0 = min(n, tid * C), j1 = min(n, j0 + C);
+  for (int shift = 0; shift <= top_shift; shift += 4) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) s_cnt[d * kThreads + tid] = 0u;
+    for (int j = j0; j < j1; ++j) {
+      const unsigned d = 15u - (unsigned)((a[j] >> (32 + shift)) & 15ull);
+      s_cnt[d * kThreads + tid] += 1u;
+    }
+    __syncthreads();
+    unsigned loc[16];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      loc[q] = s_cnt[16 * tid + q];
+      sum += (int)loc[q];
+    }
+    int total;
+    unsigned run = (unsigned)block_exclusive_scan(sum, s_iw, &total);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      s_cnt[16 * tid + q] = run;
+      run += loc[q];
+    }
+    __syncthreads();
+    for (int j = j0; j < j1; ++j) {
+      const unsigned long long e = a[j];
+      const unsigned d = 15u - (unsigned)((e >> (32 + shift)) & 15ull);
+      const unsigned pos = s_cnt[d * kThreads + tid];
+      s_cnt[d * kThreads + tid] = pos + 1u;
+      b[pos] = e;
+    }
+    __syncthreads();  // b is whole before the next pass reads it
+    unsigned long long* t = a;
+    a = b;
+    b = t;
+  }
+  return a;
 }
 
 // Stage 1: one 256-thread workgroup per (slice of kSlice logits, row): the
@@ -563,7 +620,15 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
 
   int W = a.top_k > 0 ? min(min(a.top_k, kMaxCand), V) : min(kMaxCand, V);
   const int C = (V + kThreads - 1) / kThreads;  // contiguous chunk per thread (keeps ids in order)
+  // the window and its cumulative p: in LDS, or for a wide exact-nucleus
+  // window in the caller's scratch (the row's list slots and V more)
+  unsigned long long* cand = s_cand;
+  double* cum = s_cum;
+  unsigned long long* const gA = ss.cand + r0 * kSlice;  // S * kSlice >= V slots
+  unsigned long long* const gB = ss.wide + (int64_t)row * V;
   for (;;) {
+    const bool wide = W > kMaxWindow;
+    if (wide) src = kFromRow;
     if (src == kFromLds && W > NV) src = kFromRow;  // past what the union is sure to hold
     // radix select: the key of the W-th best candidate (pairs of wavefronts
     // count into their own histogram; the bins are then summed).  The
@@ -610,11 +675,13 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
 
     // gather.  Usually every key equal to the threshold fits in the window:
     // then all of them are taken into slots from a counter, the sort orders
-    // them (ties by id) and the first W are kept.  Otherwise each thread
-    // scans its own contiguous chunk of the row, so equal keys are taken in
-    // id order.
+    // them (ties by id) and the first W are kept.  Otherwise (and always for
+    // a wide window) each thread scans its own contiguous chunk of the row,
+    // so equal keys are taken in id order.
+    cand = wide ? gA : s_cand;
+    cum = s_cum;
     int NC = W;  // candidates gathered
-    if (cnt_gt + all_eq <= kMaxWindow) {
+    if (!wide && cnt_gt + all_eq <= kMaxWindow) {
       NC = cnt_gt + all_eq;
       if (tid == 0) s_cnt[0] = 0;
       __syncthreads();
@@ -638,49 +705,68 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
         const uint32_t k = okey(l[j]);
         const unsigned long long c = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)j);
         if (k > thr) {
-          s_cand[ogt++] = c;
+          cand[ogt++] = c;
         } else if (k == thr) {
-          if (oeq < need_eq) s_cand[cnt_gt + oeq] = c;
+          if (oeq < need_eq) cand[cnt_gt + oeq] = c;
           ++oeq;
         }
       }
     }
     __syncthreads();
-    sort_window(s_cand, NC);
 
-    // p_i in f64, then the inclusive scan (4 consecutive candidates per thread)
-    double pv[4];
-    double loc = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = 4 * tid + q;
-      pv[q] = i < W ? exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) : 0.0;
-    }
     double z = zfull;
-    if (a.top_k > 0) {
-      double zs = 0.0;
+    if (!wide) {
+      sort_window(s_cand, NC);
+      // p_i in f64, then the inclusive scan (4 consecutive candidates per thread)
+      double pv[4];
+      double loc = 0.0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) zs += pv[q];
-      z = block_sum(zs, s_dw);
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * tid + q;
+        pv[q] = i < W ? exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) : 0.0;
+      }
+      if (a.top_k > 0) {
+        double zs = 0.0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) zs += pv[q];
+        z = block_sum(zs, s_dw);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pv[q] = pv[q] / z;
+        loc += pv[q];
+        pv[q] = loc;  // running local sum
+      }
+      double dtot;
+      const double off = block_exclusive_scan(loc, s_dw, &dtot);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * tid + q;
+        if (i < W) s_cum[i] = off + pv[q];
+      }
+    } else {
+      // the keys of the window agree above the highest bit where the W-th
+      // key and the maximum differ: the sort needs only the digits below
+      const unsigned dk = thr ^ okey(fmax);
+      const int top_shift = dk == 0u ? -4 : ((31 - __builtin_clz(dk)) / 4) * 4;
+      cand = radix_sort_desc(gA, gB, W, top_shift, reinterpret_cast<unsigned*>(s_u), s_iw);
+      cum = reinterpret_cast<double*>(cand == gA ? gB : gA);
+      // p_i in f64 and the inclusive scan, a contiguous chunk per thread
+      const int C2 = (W + kThreads - 1) / kThreads;
+      const int j0 = min(W, tid * C2), j1 = min(W, j0 + C2);
+      double loc = 0.0;
+      for (int j = j0; j < j1; ++j) loc += exp(((double)okey_value((uint32_t)(cand[j] >> 32)) - lmax) / T) / z;
+      double dtot;
+      double run = block_exclusive_scan(loc, s_dw, &dtot);
+      for (int j = j0; j < j1; ++j) {
+        run += exp(((double)okey_value((uint32_t)(cand[j] >> 32)) - lmax) / T) / z;
+        cum[j] = run;
+      }
     }
     if (tid == 0) s_z[0] = z;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      pv[q] = pv[q] / z;
-      loc += pv[q];
-      pv[q] = loc;  // running local sum
-    }
-    double dtot;
-    const double off = block_exclusive_scan(loc, s_dw, &dtot);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = 4 * tid + q;
-      if (i < W) s_cum[i] = off + pv[q];
-    }
     __syncthreads();
-    const int cap = min(V, kMaxWindow);
-    if (a.top_k == 0 && top_p < 1.0 && s_cum[W - 1] < top_p && W < cap) {
-      W = min(4 * W, cap);
+    if (a.top_k == 0 && top_p < 1.0 && cum[W - 1] < top_p && W < V) {
+      W = min(4 * W, V);
       __syncthreads();
       continue;
     }
@@ -692,26 +778,26 @@ __global__ void __launch_bounds__(kThreads) k_sample(const float* __restrict__ l
   __syncthreads();
   if (top_p < 1.0) {
     for (int i = tid; i < W; i += kThreads)
-      if (s_cum[i] >= top_p && (i == 0 || s_cum[i - 1] < top_p)) s_pos[0] = i + 1;
+      if (cum[i] >= top_p && (i == 0 || cum[i - 1] < top_p)) s_pos[0] = i + 1;
   }
   if (a.min_p > 0.f) {
     // p_i recomputed exactly as above; p descends, so p_i < min_p * p_0
     // first holds at one index
     const double z = s_z[0];
-    auto p_of = [&](int i) { return exp(((double)okey_value((uint32_t)(s_cand[i] >> 32)) - lmax) / T) / z; };
+    auto p_of = [&](int i) { return exp(((double)okey_value((uint32_t)(cand[i] >> 32)) - lmax) / T) / z; };
     const double thr = (double)a.min_p * p_of(0);
     for (int i = tid; i < W; i += kThreads)
       if (p_of(i) < thr && (i == 0 || !(p_of(i - 1) < thr))) s_pos[1] = i;
   }
   __syncthreads();
   const int keep = max(1, min(s_pos[0], s_pos[1]));
-  const double r = (double)uni[row] * s_cum[keep - 1];
+  const double r = (double)uni[row] * cum[keep - 1];
   if (tid == 0) s_pos[0] = keep - 1;
   __syncthreads();
   for (int i = tid; i < keep; i += kThreads)
-    if (s_cum[i] > r && (i == 0 || !(s_cum[i - 1] > r))) s_pos[0] = i;
+    if (cum[i] > r && (i == 0 || !(cum[i - 1] > r))) s_pos[0] = i;
   __syncthreads();
-  if (tid == 0) out[row] = (int)(0xFFFFFFFFu - (uint32_t)(s_cand[s_pos[0]] & 0xFFFFFFFFull));
+  if (tid == 0) out[row] = (int)(0xFFFFFFFFu - (uint32_t)(cand[s_pos[0]] & 0xFFFFFFFFull));
 }
 
 }  // namespace
@@ -720,7 +806,7 @@ namespace q8k {
 
 size_t sample_work_bytes(int n, int V) {
   const size_t S = (size_t)((V + kSlice - 1) / kSlice);
-  return (size_t)n * S * ((size_t)kSlice * 8 + 8 + 4 + 4 + 4 + 4) + 256;
+  return (size_t)n * S * ((size_t)kSlice * 8 + 8 + 4 + 4 + 4 + 4) + (size_t)n * V * 8 + 256;
 }
 
 hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_t* hist, int hstride,
@@ -735,11 +821,14 @@ hipError_t sample(float* logits, int n, int V, const SampleArgs& a, const int32_
   uint8_t* w = static_cast<uint8_t*>(work);
   const size_t rs = (size_t)n * S;
   ss.cand = reinterpret_cast<unsigned long long*>(w);
-  ss.z = reinterpret_cast<double*>(w + rs * kSlice * 8);
-  ss.m = reinterpret_cast<float*>(w + rs * (kSlice * 8 + 8));
-  ss.am = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 12));
-  ss.cnt = reinterpret_cast<int*>(w + rs * (kSlice * 8 + 16));
-  ss.thr = reinterpret_cast<unsigned*>(w + rs * (kSlice * 8 + 20));
+  w += rs * kSlice * 8;
+  ss.wide = reinterpret_cast<unsigned long long*>(w);
+  w += (size_t)n * V * 8;
+  ss.z = reinterpret_cast<double*>(w);
+  ss.m = reinterpret_cast<float*>(w + rs * 8);
+  ss.am = reinterpret_cast<int*>(w + rs * 12);
+  ss.cnt = reinterpret_cast<int*>(w + rs * 16);
+  ss.thr = reinterpret_cast<unsigned*>(w + rs * 20);
   // Each slice lists its best W1, sized so the union fits the LDS copy
   // (W1 <= kUnionCap / S); for top-k no more than min(top_k, 256) are needed
   const int W1 = max(1, min(a.top_k > 0 ? min(a.top_k, kMaxCand) : kUnionCap, kUnionCap / S));

@@ -69,7 +69,7 @@ struct AttnDecodeArgs {
 // Sampling pipeline (see k_sample.hip).
 struct SampleArgs {
   float temperature;  // <= 0: greedy
-  int top_k;          // 0: the exact nucleus (window capped at 4096 candidates)
+  int top_k;          // 0: the exact nucleus (window grows up to the vocabulary)
   float top_p, min_p;
   float repeat_penalty, freq_penalty, presence_penalty;
   int repeat_last_n;

@@ -193,9 +193,11 @@ def test_sample_arguments_validated_on_the_host():
 
 
 def test_sample_work_bytes():
-    """The scratch holds each (row, 4096-logit slice) list and its stats."""
+    """The scratch holds each (row, 4096-logit slice) list and its stats,
+    and per row one more vocabulary of 8-byte slots (a wide exact-nucleus
+    window is sorted between the row's list slots and these)."""
     L = _lib.lib()
     for n, V in ((1, 151936), (64, 151936), (3, 4097), (1, 1)):
         S = (V + 4095) // 4096
-        assert L.qwen3_sample_work_bytes(n, V) >= n * S * 4096 * 8
-        assert L.qwen3_sample_work_bytes(n, V) <= n * S * (4096 * 8 + 64) + 4096
+        assert L.qwen3_sample_work_bytes(n, V) >= n * S * 4096 * 8 + n * V * 8
+        assert L.qwen3_sample_work_bytes(n, V) <= n * S * (4096 * 8 + 64) + n * V * 8 + 4096
