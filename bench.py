@@ -141,6 +141,15 @@ def bench_8b(args) -> int:
     shape = wl.shape if args.kv is None else wl.shape.with_(kv_type=args.kv)
     weights = gen_weights(shape, wl.weight_seed)
     model = Qwen3Model(Qwen3Config.from_shape(shape), weights, [wl.kv_capacity], max_batch_tokens=2048)
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        p0 = gen_prompt(shape.vocab_size, wl.prompt_len, wl.prompt_seed)[:16]
+        cpu = cpu_baseline(
+            shape, weights, p0, 2,
+            "prefill of the first 16 prompt tokens then 2 greedy decode steps (KV length 16-18; at 8B the "
+            "weights, not the KV length, set the oracle's time per token)",
+        )
     del weights
     steps = max(args.steps, 1) * 4
     out = {}
@@ -189,6 +198,7 @@ def bench_8b(args) -> int:
             "parallelism": "single GPU",
         },
         "contexts": out,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -209,6 +219,15 @@ def bench_batch64(args) -> int:
     weights = gen_weights(shape, wl.weight_seed)
     caps = [int(n) + wl.decode_steps for n in lengths]
     model = Qwen3Model(Qwen3Config.from_shape(shape), weights, caps)
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        s0 = int(np.argmin(lengths))
+        cpu = cpu_baseline(
+            shape, weights, prompts[s0][:32], 4,
+            "one sequence: prefill of 32 prompt tokens then 4 greedy decode steps; the oracle steps sequences "
+            "one at a time, so its tokens/s is that of a batched step of any size (at this short KV length)",
+        )
     del weights
     n = wl.n_seqs
     t0 = time.perf_counter()
@@ -256,6 +275,7 @@ def bench_batch64(args) -> int:
         "bytes_per_step": int(nbytes),
         "cache_fill_s": round(fill_s, 2),
         "mean_kv_length": float(np.mean(ctx0)),
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -446,13 +466,39 @@ def measure_peaks(args) -> dict:
     }
 
 
-def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
-    """The CPU oracle on a bounded sample of the same workload."""
+def host_info() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs, and the
+    BLAS library numpy calls (its threads are the cores the oracle uses)."""
     from threadpoolctl import threadpool_info
 
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [
+        {
+            "api": i.get("internal_api"),
+            "version": i.get("version"),
+            "threads": i.get("num_threads"),
+            "library": os.path.basename(i.get("filepath", "")),
+        }
+        for i in threadpool_info()
+        if i.get("user_api") == "blas"
+    ]
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas": blas}
+
+
+def cpu_baseline(shape, weights, prompt, decode_steps: int, sample: str | None = None) -> dict:
+    """The CPU oracle (as it stands, not tuned) on a bounded sample of the
+    same workload: a prefill of `prompt`, then `decode_steps` greedy steps."""
     from oracle import model as om
 
-    ref = om.Model(shape, weights)
+    ref = om.Model(shape, weights, threads=min(16, os.cpu_count() or 1))
     cache = ref.new_cache(len(prompt) + decode_steps + 1)
     t0 = time.perf_counter()
     logits = ref.forward(prompt, cache)[0]
@@ -461,14 +507,16 @@ def cpu_baseline(shape, weights, prompt, decode_steps: int) -> dict:
     for _ in range(decode_steps):
         tok = int(ref.forward([tok], cache)[0].argmax())
     t2 = time.perf_counter()
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = host_info()
+    threads = max([b["threads"] or 1 for b in info["blas"]] or [1])
     return {
         "value": decode_steps / (t2 - t1),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"prefill of the {len(prompt)}-token prompt then {decode_steps} greedy decode steps",
+        "sample": sample or f"prefill of the {len(prompt)}-token prompt then {decode_steps} greedy decode steps",
         "prefill_tokens_per_s": len(prompt) / (t1 - t0),
+        "host": info,
     }
 
 
