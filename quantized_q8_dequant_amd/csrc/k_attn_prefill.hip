@@ -190,16 +190,26 @@ struct KVTile {
   }
 };
 
+// An LDS pointer for the global-to-LDS loads.
+QDEV __attribute__((address_space(3))) void* lds_ptr(float* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
+// Two workgroups per CU (eight waves, two per SIMD): while one waits for a
+// tile or runs its softmax, the other's MFMAs keep the SIMD busy.
 template <int HD, int G, int KVT, int KS>
-__global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
+__global__ void __launch_bounds__(256, 2) k_attn_prefill(AttnPrefillArgs a) {
   constexpr int HW = G < 4 ? G : 4;  // query heads per workgroup
   static_assert(HW * KS <= 4, "waves");
   constexpr int TPW = 4 / (HW * KS);  // 16-token sub-tiles per workgroup
   constexpr int QT = 16 * TPW;        // tokens per workgroup
   constexpr int KTW = KT / KS;        // keys of each staged tile this wave scores
-  constexpr int KROW = HD + 4;       // f32 per K row in LDS (padded: the 16 x 4 lanes of
-                                     // a K operand read hit 64 distinct banks)
-  constexpr int VROW = HD + 16;      // f32 per V row in LDS (padded)
+  // An f32 cache goes to LDS as it is, straight from memory (no staging
+  // registers); other caches are widened in registers first.
+  constexpr bool DMA = KVT == KV_F32;
+  constexpr int KROW = HD + 4;   // f32 per K row in LDS (padded: the 16 x 4 lanes of
+                                 // a K operand read hit 64 distinct banks)
+  constexpr int VROW = HD + 16;  // f32 per V row in LDS (padded)
   constexpr int NST = HD / 4;        // k=4 steps over head_dim
   constexpr int NDT = HD / 16;       // 16-wide d tiles of the output
   // K and V tiles in one array (the merge of key halves reuses all of it)
@@ -227,10 +237,12 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   // this lane's query (clamped so padded lanes stay finite; never stored)
   const int tq = min(tw0 + lq, T - 1);
   const int qpos = a.pos0 + tq;
-  double qf[NST];
+  // the query stays f32 in registers and is widened at each use (an f64
+  // copy would cost NST more registers than two waves per SIMD leave)
+  float qf[NST];
   const float* qrow = a.q32 + ((int64_t)tq * a.nh + h) * HD;
 #pragma unroll
-  for (int st = 0; st < NST; ++st) qf[st] = (double)qrow[4 * st + lg];
+  for (int st = 0; st < NST; ++st) qf[st] = qrow[4 * st + lg];
 
   const int64_t head_elems = (int64_t)a.cap * HD;
   const int64_t kb0 = a.kbase + (int64_t)g * head_elems;
@@ -248,14 +260,39 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   for (int dt = 0; dt < NDT; ++dt) o[dt] = v4d{0.0, 0.0, 0.0, 0.0};
   double m_run = -INFINITY, l_run = 0.0;
 
-  // the next tile's loads are issued right after the current tile is
-  // staged, so they land while the current tile is used
-  KVTile<HD, KVT> tile;
-  tile.load(a.kv, a.kvs, kb0, vb0, k_lo, kend);
+  // widened caches: the next tile's loads are issued right after the current
+  // tile is staged, so they land while the current tile is used
+  KVTile<HD, DMA ? KV_BF16 : KVT> tile;
+  if (!DMA) tile.load(a.kv, a.kvs, kb0, vb0, k_lo, kend);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   for (int kbase = k_lo; kbase < k_hi; kbase += KT) {
     __syncthreads();
-    tile.store(sK, KROW, sV, VROW);
-    tile.load(a.kv, a.kvs, kb0, vb0, kbase + KT < k_hi ? kbase + KT : kbase, kend);
+    if constexpr (DMA) {
+      // rows [kbase, kbase + KT) of K and V (rows past kend re-read row
+      // kend - 1: finite, masked, probability 0).  One load of a wave writes
+      // 64 consecutive 16-byte chunks of LDS, one per lane, so each lane
+      // fetches the chunk that belongs at its place in the padded rows (a
+      // padding chunk fetches the row's first chunk, never read)
+      const float* kvf = static_cast<const float*>(a.kv);
+      auto fill = [&](float* dst, int64_t base, int rowf) {
+        const int cpr = rowf / 4;      // chunks per padded row
+        const int nld = KT * cpr / kWave;  // loads for the whole tile
+        for (int j = wv; j < nld; j += 4) {
+          const int L = j * kWave + lane;
+          const int r = L / cpr, pc = L % cpr;
+          const int64_t key = min(kbase + r, kend - 1);
+          __builtin_amdgcn_global_load_lds(kvf + base + key * HD + (pc < HD / 4 ? 4 * pc : 0),
+                                           lds_ptr(dst + j * kWave * 4), 16, 0, 0);
+        }
+      };
+      static_assert(KT * (KROW / 4) % kWave == 0 && KT * (VROW / 4) % kWave == 0, "whole loads");
+      fill(sK, kb0, KROW);
+      fill(sV, vb0, VROW);
+      __builtin_amdgcn_s_waitcnt(0);  // the loads have written LDS
+    } else {
+      tile.store(sK, KROW, sV, VROW);
+      tile.load(a.kv, a.kvs, kb0, vb0, kbase + KT < k_hi ? kbase + KT : kbase, kend);
+    }
     __syncthreads();
 
     // scores S^T for the sub-tiles of 16 keys of this wave's part; lane holds
@@ -263,12 +300,14 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
     const int kw0 = kpar * KTW;  // first key of the part within the tile
     v4d s[KTW / 16];
 #pragma unroll
+    for (int st = 0; st < NST; ++st) asm volatile("" : "+v"(qf[st]));  // widened per tile, not kept in f64
+#pragma unroll
     for (int kt = 0; kt < KTW / 16; ++kt) {
       s[kt] = v4d{0.0, 0.0, 0.0, 0.0};
       const float* kr = &sK[(kw0 + kt * 16 + lq) * KROW + lg];
 #pragma unroll
       for (int st = 0; st < NST; ++st)
-        s[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * st], qf[st], s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * st], (double)qf[st], s[kt], 0, 0, 0);
     }
     double rmax = -INFINITY;
 #pragma unroll
@@ -317,7 +356,7 @@ __global__ void __launch_bounds__(256) k_attn_prefill(AttnPrefillArgs a) {
   // a query row whose keys all lie past its position (possible in a later
   // run) keeps m = -inf, l = 0, O = 0: it contributes nothing below
   const bool owner = KS == 1 || kpar == 0;  // the wave that holds the merged state
-  if (KS == 2) {
+  if constexpr (KS == 2) {
     // merge the two halves: the second-half wave of each (head, token tile)
     // leaves (m, l, O) in LDS, the first-half wave rescales and adds
     static_assert(HW * TPW * 64 * (NDT * 4 + 2) * 8 <= (int)sizeof(sKV), "merge space");
