@@ -56,6 +56,23 @@ QDEV unsigned ld_err(const unsigned* err) { return __hip_atomic_load(err, __ATOM
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kCoherent = 16;  // cache policy of the loads: device scope (sc1)
 
+// Each wavefront polls its own words, without a barrier per round: a round
+// is its loads, one wait and a wavefront-wide check.  A wavefront stops when
+// its words are all there, when the error word is set (checked every 64
+// rounds) or at the spin limit (it then sets the error word, so the others
+// stop too); then the workgroup meets once and fails if any wavefront did.
+// Every wait is bounded, so every wavefront reaches that meeting.
+QDEV bool wave_error(unsigned* err) { return __builtin_amdgcn_readfirstlane(ld_err(err)) != 0; }
+QDEV bool block_failed(bool wave_bad) {  // wave_bad is wavefront-uniform
+  __shared__ int s_bad[kWavesP];
+  if (threadIdx.x % kWave == 0) s_bad[threadIdx.x / kWave] = wave_bad ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesP; ++w) any |= s_bad[w];
+  return any != 0;
+}
+
 // Wait until the 2 * NPAIR words of the pairs at word offsets off(j) (even)
 // of base[0, nwords) all carry `tag`; then the 32-bit payload of word
 // 2j + h goes to *dst(2j + h).  False when the spin limit is reached or
@@ -65,33 +82,41 @@ QDEV bool poll_pairs(const u64* base, int nwords, Off off, Dst dst, unsigned tag
   constexpr int PER = (NPAIR + NT - 1) / NT;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(base), 0, nwords * 8, 0x00020000);
-  for (int spin = 0; spin < kSpin; ++spin) {
-    v4u v[PER];
-    bool ok = true;
+  v4u v[PER];
+  bool bad = false;
+  for (int spin = 0;; ++spin) {
+    // every load of the round is issued before any is checked, so one wait
+    // covers them all; slots past NPAIR re-read the last pair
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int i = threadIdx.x + j * NT;
-      if (i < NPAIR) {
-        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(i) * 8, 0, kCoherent);
-        ok = ok && v[j].y == tag && v[j].w == tag;
-      }
+      const int i = min((int)threadIdx.x + j * NT, NPAIR - 1);
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(i) * 8, 0, kCoherent);
     }
-    if (__syncthreads_and(ok)) {
+    bool ok = true;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int i = threadIdx.x + j * NT;
-        if (i < NPAIR) {
-          *dst(2 * i) = v[j].x;
-          *dst(2 * i + 1) = v[j].z;
-        }
-      }
-      __syncthreads();
-      return true;
+    for (int j = 0; j < PER; ++j) ok = ok && v[j].y == tag && v[j].w == tag;
+    if (__all(ok)) break;
+    if ((spin & 63) == 63 && wave_error(err)) {
+      bad = true;
+      break;
     }
-    if ((spin & 63) == 63 && __syncthreads_or(threadIdx.x == 0 && ld_err(err) != 0)) return false;
+    if (spin == kSpin) {
+      if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bad = true;
+      break;
+    }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return false;
+  if (block_failed(bad)) return false;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (i < NPAIR) {
+      *dst(2 * i) = v[j].x;
+      *dst(2 * i + 1) = v[j].z;
+    }
+  }
+  __syncthreads();
+  return true;
 }
 
 // The N (even) contiguous words at src into dst (LDS) as floats.
@@ -100,6 +125,45 @@ QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
   static_assert(N % 2 == 0, "pairs");
   unsigned* d = reinterpret_cast<unsigned*>(dst);
   return poll_pairs<N / 2>(src, N, [](int j) { return 2 * j; }, [&](int i) { return d + i; }, tag, err);
+}
+
+// The N words at src into registers, in the layout the register quantiser
+// takes: thread t receives words 1024 i + 4t .. 4t + 3 (i < N / 1024) as
+// x[4 i .. 4 i + 3].  No LDS copy and no barrier after the wait.
+template <int N>
+QDEV bool poll_vec_regs(const u64* src, unsigned tag, float (&x)[N / NT], unsigned* err) {
+  static_assert(N % (4 * NT) == 0, "whole passes of four words per thread");
+  constexpr int PER = N / (2 * NT);  // pairs per thread
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(src), 0, N * 8, 0x00020000);
+  v4u v[PER];
+  bool bad = false;
+  for (int spin = 0;; ++spin) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int pair = (j / 2) * (2 * NT) + 2 * (int)threadIdx.x + (j % 2);
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, pair * 16, 0, kCoherent);
+    }
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ok = ok && v[j].y == tag && v[j].w == tag;
+    if (__all(ok)) break;
+    if ((spin & 63) == 63 && wave_error(err)) {
+      bad = true;
+      break;
+    }
+    if (spin == kSpin) {
+      if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bad = true;
+      break;
+    }
+  }
+  if (block_failed(bad)) return false;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    x[2 * j] = __uint_as_float(v[j].x);
+    x[2 * j + 1] = __uint_as_float(v[j].z);
+  }
+  return true;
 }
 
 // An f64 as two tagged words (low half, then high half).
@@ -167,6 +231,58 @@ QDEV void quantize_lds(const float* s_x, const NormW<K>* nw, float eps, int8_t* 
     }
   }
   __syncthreads();
+}
+
+// quantize_lds with the values in registers (thread t holds values
+// 1024 i + 4t .. 4t + 3 as x[4 i ..]): the same arithmetic and summation
+// order, without the LDS copy of x.
+template <int K, bool NORM>
+QDEV void quantize_regs(const float (&x)[K / NT], const NormW<K>* nw, float eps, int8_t* s_qa, float* s_da,
+                        double* s_red) {
+  static_assert(K % (4 * NT) == 0, "whole passes");
+  double r = 1.0;
+  if (NORM) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < K / (4 * NT); ++i) {
+      const float* v = x + 4 * i;
+      ss += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
+    }
+    ss = block_sum_d<NT>(ss, s_red);
+    r = rms_scale(ss, K, eps);
+  }
+#pragma unroll
+  for (int i = 0; i < K / (4 * NT); ++i) {
+    const int c = i * NT * 4 + threadIdx.x * 4;
+    float v[4] = {x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+    if (NORM) {
+      const float4 w4 = nw->w[i];
+      v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
+      v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
+    }
+    float d;
+    const int packed = quant4_group8(v, &d);
+    *reinterpret_cast<int*>(s_qa + c) = packed;
+    if ((threadIdx.x & 7) == 0) s_da[c >> 5] = f16_round(d);
+  }
+  __syncthreads();
+}
+
+// Wait for the K words at src, then quantise them (RMSNorm'd with nw when
+// NORM) into s_qa / s_da: from registers where K fills whole passes of the
+// grid, else through LDS.
+template <int K, bool NORM>
+QDEV bool poll_quantize(const u64* src, unsigned tag, float* s_x, const NormW<K>* nw, float eps, int8_t* s_qa,
+                        float* s_da, double* s_red, unsigned* err) {
+  if constexpr (K % (4 * NT) == 0) {
+    float x[K / NT];
+    if (!poll_vec_regs<K>(src, tag, x, err)) return false;
+    quantize_regs<K, NORM>(x, nw, eps, s_qa, s_da, s_red);
+  } else {
+    if (!poll_vec<K>(src, tag, s_x, err)) return false;
+    quantize_lds<K, NORM>(s_x, nw, eps, s_qa, s_da, s_red);
+  }
+  return true;
 }
 
 // A workgroup's slice of a Q8_0 matrix: R rows of K values.  LPR lanes share
@@ -305,7 +421,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   __shared__ double s_red[kWavesP];
   __shared__ float s_xkeep[RC];   // this workgroup's rows of x entering o_proj
   __shared__ float s_xckeep[RC];  // ... and entering the down projection
-  __shared__ float s_gu[64];
+  __shared__ float s_gu[96];  // gate and up sums of an FFN block, then its SwiGLU values
   __shared__ float s_qf[G][HD];
   __shared__ float s_knew[HD];
   __shared__ float s_vnew[HD];
@@ -386,8 +502,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       w.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
       NormW<H> nw;
       nw.load(P.attn_norm);
-      if (!poll_vec<H>(a.xa, T, s_x, a.err)) goto fail;
-      quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
+      if (!poll_quantize<H, true>(a.xa, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
       w.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
     }
 
@@ -619,8 +734,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     {
       Slice<QW, RC> w;
       w.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
-      if (!poll_vec<QW>(a.att, T, s_x, a.err)) goto fail;
-      quantize_lds<QW, false>(s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red);
+      if (!poll_quantize<QW, false>(a.att, T, s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red,
+                                    a.err))
+        goto fail;
       w.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xkeep[lr] + (float)acc;
         put_tagged(a.xc + b * RC + lr, xn, T);
@@ -638,14 +754,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       w.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
       NormW<H> nw;
       nw.load(P.ffn_norm);
-      if (!poll_vec<H>(a.xc, T, s_x, a.err)) goto fail;
-      quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
+      if (!poll_quantize<H, true>(a.xc, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
       w.compute(s_qa, s_da, [&](int lr, double acc) { s_gu[lr] = (float)acc; });
+      __syncthreads();
+      // the block's 32 SwiGLU values, one per lane (each is an f64 exp and
+      // divide: spread over 32 lanes they cost one such chain, not four)
+      if (tid < 32) s_gu[64 + tid] = swiglu_f64(s_gu[tid], s_gu[32 + tid]);
       __syncthreads();
       if (tid < 8) {  // one 8-lane group: lane t quantises h[4t .. 4t+3]
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = swiglu_f64(s_gu[4 * tid + i], s_gu[32 + 4 * tid + i]);
+        for (int i = 0; i < 4; ++i) v[i] = s_gu[64 + 4 * tid + i];
         float d;
         const int packed = quant4_group8(v, &d);
         put_tagged(a.h + b * 9 + tid, __int_as_float(packed), T);
@@ -689,8 +808,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
     NormW<H> nw;
     nw.load(a.out_norm);
-    if (!poll_vec<H>(a.xa, T0 + (unsigned)a.L, s_x, a.err)) goto fail;
-    quantize_lds<H, true>(s_x, &nw, eps, s_qa, s_da, s_red);
+    if (!poll_quantize<H, true>(a.xa, T0 + (unsigned)a.L, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
     ArgBest best{-INFINITY, 0x7FFFFFFF};
     auto run = [&](const LS& w, int ps) {
       w.compute(s_qa, s_da, [&](int lr, double acc) {
