@@ -430,6 +430,43 @@ def bench_sampling(V: int, args) -> dict:
     return out
 
 
+def bench_prefill_gemms(shape, args) -> dict:
+    """Each projection GEMM of a 4096-token prefill timed alone: the op-level
+    Q8_0 linear (qwen3_q8_0_linear: the activation rows quantised, then the
+    MFMA GEMM the prefill runs) on 4096 random rows against a random Q8_0
+    matrix of the layer's shape, event-timed (median of repeats).  The int8
+    ops are 2 M N K; the rate includes the row quantisation, a few percent."""
+    import torch
+
+    from quantized_q8_dequant_amd import encode_q8_0, q8_0_linear, repack_q8_0
+
+    H, F = shape.hidden_size, shape.intermediate_size
+    M = 4096
+    g = torch.Generator(device="cuda:0").manual_seed(13)
+    out = {}
+    for name, N, K in (
+        ("qkv", shape.q_width + 2 * shape.kv_width, H),
+        ("o_proj", H, shape.q_width),
+        ("gate_up", 2 * F, H),
+        ("down", H, F),
+    ):
+        w = torch.randn((N, K), device="cuda:0", generator=g) * 0.02
+        qs, sc = repack_q8_0(encode_q8_0(w), N, K)
+        x = torch.randn((M, K), device="cuda:0", generator=g)
+        del w
+        ms = event_ms(lambda: q8_0_linear(x, qs, sc), max(args.warmup, 1), max(args.steps, 5))
+        ops = 2.0 * M * N * K
+        out[name] = {
+            "M": M, "N": N, "K": K,
+            "us": round(ms * 1000.0, 1),
+            "int8_TOPS": round(ops / (ms / 1000.0) / 1e12, 1),
+            "frac_of_int8_peak": round(ops / (ms / 1000.0) / INT8_PEAK_OPS, 4),
+        }
+        del qs, sc, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_peaks(args) -> dict:
     """Achievable peaks on this GPU, measured with the library's own probes:
     a streaming copy of 1 GiB (read plus write bytes over its event-timed
@@ -676,6 +713,7 @@ def main() -> int:
         m4.close()
         del m4
         torch.cuda.empty_cache()
+        p4["per_gemm"] = bench_prefill_gemms(shape, args)
     else:
         model.close()
         del model

@@ -43,12 +43,13 @@ constexpr int LDS_ROW = SK + 16; // padded row stride (bytes)
 constexpr int AL = BM * SK / 16 / 256;  // 16-byte loads of A per thread per stage (4)
 constexpr int BL = BN * SK / 16 / 256;  // ... of B (2)
 
-struct Stage {
+struct Stage {  // loaded values as they are in memory (converted when staged)
   v4i a[AL], b[BL];
-  float da[BM * KB / 256], dw[BN * KB / 256 > 0 ? BN * KB / 256 : 1];
+  float da[BM * KB / 256];
+  uint16_t dw[BN * KB / 256 > 0 ? BN * KB / 256 : 1];  // f16 bits
 };
 
-QDEV void gemm_lstore(const Stage& r, int8_t* sA, int8_t* sB, float (*sDa)[BM], float (*sDw)[BN]) {
+QDEV void gemm_lstore(const Stage& r, int8_t* sA, int8_t* sB, double (*sDa)[BM], double (*sDw)[BN]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
@@ -65,9 +66,9 @@ QDEV void gemm_lstore(const Stage& r, int8_t* sA, int8_t* sB, float (*sDa)[BM], 
 #pragma unroll
   for (int i = 0; i < BM * KB / 256; ++i) {
     const int idx = tid + 256 * i;
-    sDa[idx % KB][idx / KB] = r.da[i];
+    sDa[idx % KB][idx / KB] = (double)r.da[i];  // widened once here, not per use
   }
-  if (tid < BN * KB) sDw[tid % KB][tid / KB] = r.dw[0];
+  if (tid < BN * KB) sDw[tid % KB][tid / KB] = (double)f16_bits_to_f32(r.dw[0]);
 }
 
 QDEV void gemm_gload(const GemmArgs& a, Stage& r, int st, int m0, int n0, int nblk) {
@@ -95,7 +96,7 @@ QDEV void gemm_gload(const GemmArgs& a, Stage& r, int st, int m0, int n0, int nb
   {
     const int idx = tid % (BN * KB);
     const int gn = min(n0 + idx / KB, a.N - 1);
-    r.dw[0] = f16_bits_to_f32(a.sc[(int64_t)gn * nblk + st * KB + idx % KB]);
+    r.dw[0] = a.sc[(int64_t)gn * nblk + st * KB + idx % KB];
   }
 }
 
@@ -105,8 +106,8 @@ template <int EPI>
 __global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
   __shared__ __align__(16) int8_t sA[2][BM * LDS_ROW];
   __shared__ __align__(16) int8_t sB[2][BN * LDS_ROW];
-  __shared__ __align__(16) float sDa[2][KB][BM];
-  __shared__ __align__(16) float sDw[2][KB][BN];
+  __shared__ __align__(16) double sDa[2][KB][BM];  // scales widened to f64 when staged
+  __shared__ __align__(16) double sDw[2][KB][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave, wave = tid / kWave;
@@ -115,7 +116,6 @@ __global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
   const int nslice = a.K / SK / gridDim.z;  // K stages of this workgroup's slice
   const int st0 = blockIdx.z * nslice;
 
-  Stage rs;  // global -> register staging of the next stage
   // block terms d_a * d_w * S are exact in f64; the sum is rounded to f32
   // once, in the epilogue
   double acc[2][16];
@@ -125,12 +125,8 @@ __global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
     for (int j = 0; j < 16; ++j) acc[ni][j] = 0.0;
 
   const int lr = lane % 32, lg = lane / 32;
-  gemm_gload(a, rs, st0, m0, n0, nblk);
-  gemm_lstore(rs, sA[0], sB[0], sDa[0], sDw[0]);
-  __syncthreads();
-  for (int si = 0; si < nslice; ++si) {
-    const int buf = si & 1;
-    if (si + 1 < nslice) gemm_gload(a, rs, st0 + si + 1, m0, n0, nblk);
+  // one stage of K from LDS buffer buf into the accumulators
+  auto compute = [&](int buf) {
 #pragma unroll 2
     for (int kb = 0; kb < KB; ++kb) {
       const v4i af = *reinterpret_cast<const v4i*>(&sA[buf][(wave * 32 + lr) * LDS_ROW + kb * 32 + lg * 16]);
@@ -149,20 +145,44 @@ __global__ void __launch_bounds__(256, 2) k_gemm_q8(GemmArgs a) {
       }
       double dw[2];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) dw[ni] = (double)sDw[buf][kb][ni * 32 + lr];
+      for (int ni = 0; ni < 2; ++ni) dw[ni] = sDw[buf][kb][ni * 32 + lr];
       double da[16];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&sDa[buf][kb][wave * 32 + 8 * g4 + 4 * lg]);
-        da[4 * g4 + 0] = d4.x, da[4 * g4 + 1] = d4.y, da[4 * g4 + 2] = d4.z, da[4 * g4 + 3] = d4.w;
+        const double* d = &sDa[buf][kb][wave * 32 + 8 * g4 + 4 * lg];
+        const double2 lo = *reinterpret_cast<const double2*>(d), hi = *reinterpret_cast<const double2*>(d + 2);
+        da[4 * g4 + 0] = lo.x, da[4 * g4 + 1] = lo.y, da[4 * g4 + 2] = hi.x, da[4 * g4 + 3] = hi.y;
       }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[ni][j] += (double)S[ni][j] * (da[j] * dw[ni]);
     }
-    if (si + 1 < nslice) gemm_lstore(rs, sA[buf ^ 1], sB[buf ^ 1], sDa[buf ^ 1], sDw[buf ^ 1]);
+  };
+
+  // Stages go global -> registers two stages ahead of their use, then
+  // registers -> LDS one stage ahead, so each global load has a whole stage
+  // of compute more to land.  The two register sets take turns (the loop
+  // steps two stages at a time); loads past the slice re-read its last
+  // stage, so every load is issued unconditionally (a load under a branch
+  // would make the compiler drain all loads at the join).
+  Stage ra, rb;
+  const int last = st0 + nslice - 1;
+  gemm_gload(a, ra, st0, m0, n0, nblk);
+  gemm_gload(a, rb, min(st0 + 1, last), m0, n0, nblk);
+  gemm_lstore(ra, sA[0], sB[0], sDa[0], sDw[0]);
+  __syncthreads();
+  // stage si is in LDS buffer si & 1; `next` holds stage si + 1; `free`
+  // receives stage si + 2
+  auto step = [&](int si, Stage& free, Stage& next) {
+    gemm_gload(a, free, min(st0 + si + 2, last), m0, n0, nblk);
+    compute(si & 1);
+    if (si + 1 < nslice) gemm_lstore(next, sA[(si + 1) & 1], sB[(si + 1) & 1], sDa[(si + 1) & 1], sDw[(si + 1) & 1]);
     __syncthreads();
+  };
+  for (int si = 0; si < nslice; si += 2) {
+    step(si, ra, rb);
+    if (si + 1 < nslice) step(si + 1, rb, ra);
   }
 
   // epilogue: element j of tile ni is row 8*(j/4) + 4*lg + j%4, column lr
