@@ -166,12 +166,15 @@ QDEV bool poll_vec_regs(const u64* src, unsigned tag, float (&x)[N / NT], unsign
   return true;
 }
 
-// An f64 as two tagged words (low half, then high half).
-QDEV void put_tagged_d(u64* p, double v, unsigned tag) {
-  __hip_atomic_store(p, ((u64)tag << 32) | (u64)(unsigned)__double2loint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(p + 1, ((u64)tag << 32) | (u64)(unsigned)__double2hiint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// An f64 as two tagged words (low half, then high half) at the even word
+// offset `w` of base[0, nwords), written by one 16-byte store with the
+// device-scope policy: each 8-byte half still carries its own tag, and the
+// reader checks both, so the pair needs no atomicity beyond its halves; one
+// store request per value instead of two.
+QDEV void put_tagged_d(u64* base, int nwords, int w, double v, unsigned tag) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nwords * 8, 0x00020000);
+  const v4u q = {(unsigned)__double2loint(v), tag, (unsigned)__double2hiint(v), tag};
+  __builtin_amdgcn_raw_buffer_store_b128(q, rs, w * 8, 0, kCoherent);
 }
 
 // A norm weight vector of K floats held in registers, one float4 per thread
@@ -474,36 +477,75 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   const int cache_end = min(j1, p);
   const bool has_new = j0 < j1 && j1 == ctx;
   const int64_t cap = a.seq_cap[seq];
+  const int64_t head_elems = cap * HD;
+
+  // Weight slices and KV tiles.  The QKV slice of the next layer (after the
+  // last layer: the lm_head's first four passes) is requested during the down
+  // projection, ahead of its wait: a wait's loads complete, in order, after
+  // everything issued before them, and that wait is long enough for the slice
+  // to stream in, so the QKV phase finds it in registers instead of starting
+  // its fetch after its own wait.  The other slices are requested just
+  // before their own phase's wait (issuing them a phase early was measured
+  // slower: those windows already carry the phase's own traffic), and the
+  // KV tiles at the start of their layer.
+  using SA = Slice<H, RA, (H / 32 >= 32 && RA >= 16 ? 16 : 0)>;
+  using SC = Slice<QW, RC>;
+  using SD = Slice<H, 64, (H / 32 >= 32 ? 8 : 0)>;
+  using SE = Slice<F, RC>;
+  using LS = Slice<H, Slice<H, 1>::RPP>;  // lm_head: one pass of RPP rows per buffer
+  SA wA;
+  SC wC;
+  SD wD;
+  SE wE;
+  LS wa, wb, wc, wd;
+  KvTile<HD, KVBF16> tA, tB;
+  auto kbase_of = [&](int l) { return a.seq_base[seq] + ((int64_t)l * 2 * NKV + ag) * head_elems; };
+  // stream element i < nt is K tile i, nt <= i < 2 nt is V tile i - nt
+  auto stream_load = [&](KvTile<HD, KVBF16>& r, int i, int64_t kb) {
+    const bool isv = i >= nt;
+    const int t0 = j0 + (isv ? i - nt : i) * TJ;
+    const bool live = t0 < cache_end;
+    r.load(a.kv, isv ? kb + (int64_t)NKV * head_elems : kb, live ? t0 : 0, live ? min(TJ, cache_end - t0) : 1);
+  };
+  // the lm_head's rows of this workgroup
+  constexpr int RPP = LS::RPP;
+  const int V = a.V;
+  const int RV = (V + NWG - 1) / NWG;
+  const int r0 = b * RV;
+  const int rend = min(V, r0 + RV);
+  const int npass = r0 < rend ? (rend - r0 + RPP - 1) / RPP : 0;
+  auto rowof = [&](int ps) { return [&, ps](int lr) { return min(r0 + ps * RPP + lr, V - 1); }; };
+  // layer l's QKV slice; past the last layer, the lm_head's first four passes
+  auto prefetch_layer = [&](int l) {
+    if (l < a.L) {
+      const PLayer P = a.layers[l];
+      wA.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
+    } else {
+      if (npass > 0) wa.load(a.emb_qs, a.emb_sc, rowof(0));
+      if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
+      if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
+      if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
+    }
+  };
+  prefetch_layer(0);
 
   for (int l = 0; l < a.L; ++l) {
     const unsigned T = T0 + (unsigned)l;
     const PLayer P = a.layers[l];
-    const int64_t head_elems = cap * HD;
-    const int64_t kbase = a.seq_base[seq] + ((int64_t)l * 2 * NKV + ag) * head_elems;
+    const int64_t kbase = kbase_of(l);
     const int64_t vbase = kbase + (int64_t)NKV * head_elems;
-
-    // the attention split's first two tiles (stream element i < nt is K tile
-    // i, nt <= i < 2 nt is V tile i - nt) are requested before anything else
-    KvTile<HD, KVBF16> tA, tB;
-    auto stream_load = [&](KvTile<HD, KVBF16>& r, int i) {
-      const bool isv = i >= nt;
-      const int t0 = j0 + (isv ? i - nt : i) * TJ;
-      const bool live = t0 < cache_end;
-      r.load(a.kv, isv ? vbase : kbase, live ? t0 : 0, live ? min(TJ, cache_end - t0) : 1);
-    };
+    // the attention split's first two tiles
     if (attn_unit && nt > 0) {
-      stream_load(tA, 0);
-      stream_load(tB, 1);
+      stream_load(tA, 0, kbase);
+      stream_load(tB, 1, kbase);
     }
 
     // ---- A: QKV projection --------------------------------------------------
     {
-      Slice<H, RA, (H / 32 >= 32 && RA >= 16 ? 16 : 0)> w;
-      w.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
       NormW<H> nw;
       nw.load(P.attn_norm);
       if (!poll_quantize<H, true>(a.xa, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
-      w.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
+      wA.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
     }
 
     // ---- B: attention of KV head ag over rows [j0, j1) -------------------------
@@ -664,7 +706,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
             __syncthreads();
           }
           if (t0 < cache_end) tr.store(s_t);
-          if (prefetch) stream_load(tr, i + 2);
+          if (prefetch) stream_load(tr, i + 2, kbase);
           if (t0 + nrow > p) {  // row p from this step's values (after the tile store)
             __syncthreads();
             const float* src = isv ? s_vnew : s_knew;
@@ -689,11 +731,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       u64* part = a.part + ((int64_t)ag * S + asplit) * G * PWORDS;
       if (out_live) {
 #pragma unroll
-        for (int i2 = 0; i2 < DPT; ++i2) put_tagged_d(part + o_h * PWORDS + 2 * (o_d + i2), o[i2], T);
+        for (int i2 = 0; i2 < DPT; ++i2) put_tagged_d(part, G * PWORDS, o_h * PWORDS + 2 * (o_d + i2), o[i2], T);
       }
       if (tid < G) {
-        put_tagged_d(part + tid * PWORDS + 2 * HD, s_m[tid], T);
-        put_tagged_d(part + tid * PWORDS + 2 * (HD + 1), s_l[tid], T);
+        put_tagged_d(part, G * PWORDS, tid * PWORDS + 2 * HD, s_m[tid], T);
+        put_tagged_d(part, G * PWORDS, tid * PWORDS + 2 * (HD + 1), s_l[tid], T);
       }
       // ---- the combine of CPW outputs (query head ch, dims cd0 ..) over the
       // S splits: O = sum_s w_s o_s / sum_s w_s l_s, w_s = exp(m_s - max m),
@@ -730,14 +772,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       }
     }
 
+
     // ---- C: o_proj + residual ----------------------------------------------------
     {
-      Slice<QW, RC> w;
-      w.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
+      wC.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
       if (!poll_quantize<QW, false>(a.att, T, s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red,
                                     a.err))
         goto fail;
-      w.compute(s_qa, s_da, [&](int lr, double acc) {
+      wC.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xkeep[lr] + (float)acc;
         put_tagged(a.xc + b * RC + lr, xn, T);
         s_xckeep[lr] = xn;
@@ -750,12 +792,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // projection's prologue arithmetic): 8 words of four codes, then one word
     // with the f16-valued block scale.
     if (b < NUB) {
-      Slice<H, 64, (H / 32 >= 32 ? 8 : 0)> w;
-      w.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
+      wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
       NormW<H> nw;
       nw.load(P.ffn_norm);
       if (!poll_quantize<H, true>(a.xc, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
-      w.compute(s_qa, s_da, [&](int lr, double acc) { s_gu[lr] = (float)acc; });
+      wD.compute(s_qa, s_da, [&](int lr, double acc) { s_gu[lr] = (float)acc; });
       __syncthreads();
       // the block's 32 SwiGLU values, one per lane (each is an f64 exp and
       // divide: spread over 32 lanes they cost one such chain, not four)
@@ -774,8 +815,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 
     // ---- E: down + residual (x of the next layer) ----------------------------------
     {
-      Slice<F, RC> w;
-      w.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
+      wE.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
+      prefetch_layer(l + 1);
       {
         unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
         unsigned* da = reinterpret_cast<unsigned*>(s_da);
@@ -783,7 +824,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         static_assert(NUB % 2 == 0, "pairs of h words");
         if (!poll_pairs<9 * NUB / 2>(a.h, 9 * NUB, [](int j) { return 2 * j; }, dst, T, a.err)) goto fail;
       }
-      w.compute(s_qa, s_da, [&](int lr, double acc) {
+      wE.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xckeep[lr] + (float)acc;
         put_tagged(a.xa + b * RC + lr, xn, T + 1u);
         s_xkeep[lr] = xn;
@@ -793,19 +834,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 
   // ---- lm_head over rows [b*RV, ...) + greedy argmax ---------------------------------
   {
-    using LS = Slice<H, Slice<H, 1>::RPP>;  // one pass of RPP rows per buffer
-    constexpr int RPP = LS::RPP;
-    const int V = a.V;
-    const int RV = (V + NWG - 1) / NWG;
-    const int r0 = b * RV;
-    const int rend = min(V, r0 + RV);
-    const int npass = r0 < rend ? (rend - r0 + RPP - 1) / RPP : 0;
-    auto rowof = [&](int ps) { return [&, ps](int lr) { return min(r0 + ps * RPP + lr, V - 1); }; };
-    LS wa, wb, wc, wd;
-    if (npass > 0) wa.load(a.emb_qs, a.emb_sc, rowof(0));
-    if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
-    if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
-    if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
+    // (its first four passes were requested during the last layer's down projection)
     NormW<H> nw;
     nw.load(a.out_norm);
     if (!poll_quantize<H, true>(a.xa, T0 + (unsigned)a.L, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
