@@ -384,6 +384,21 @@ struct KvTile {
   }
 };
 
+// Register pins: one empty asm statement that takes every value of an array
+// of LDS loads as an operand, so the compiler issues all of the loads before
+// the first use and waits for them once (left alone, it interleaves each load
+// with its use and waits after every one).
+typedef float v4f __attribute__((ext_vector_type(4)));
+QDEV void pin(v4f (&v)[4]) { asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])); }
+QDEV void pin(v4f (&v)[8]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+QDEV void pin(double (&p)[8], float (&v)[8]) {
+  asm volatile(""
+               : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]), "+v"(p[7]),
+                 "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+
 struct ArgBest {
   float v;
   int i;
@@ -479,9 +494,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   const int64_t cap = a.seq_cap[seq];
   const int64_t head_elems = cap * HD;
 
-  // Weight slices and KV tiles.  The QKV slice of the next layer (after the
-  // last layer: the lm_head's first four passes) is requested during the down
-  // projection, ahead of its wait: a wait's loads complete, in order, after
+  // Weight slices and KV tiles.  The QKV slice of the next layer is requested
+  // during the down projection, ahead of its wait: a wait's loads complete, in order, after
   // everything issued before them, and that wait is long enough for the slice
   // to stream in, so the QKV phase finds it in registers instead of starting
   // its fetch after its own wait.  The other slices are requested just
@@ -492,12 +506,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   using SC = Slice<QW, RC>;
   using SD = Slice<H, 64, (H / 32 >= 32 ? 8 : 0)>;
   using SE = Slice<F, RC>;
-  using LS = Slice<H, Slice<H, 1>::RPP>;  // lm_head: one pass of RPP rows per buffer
   SA wA;
   SC wC;
   SD wD;
   SE wE;
-  LS wa, wb, wc, wd;
   KvTile<HD, KVBF16> tA, tB;
   auto kbase_of = [&](int l) { return a.seq_base[seq] + ((int64_t)l * 2 * NKV + ag) * head_elems; };
   // stream element i < nt is K tile i, nt <= i < 2 nt is V tile i - nt
@@ -507,25 +519,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     const bool live = t0 < cache_end;
     r.load(a.kv, isv ? kb + (int64_t)NKV * head_elems : kb, live ? t0 : 0, live ? min(TJ, cache_end - t0) : 1);
   };
-  // the lm_head's rows of this workgroup
-  constexpr int RPP = LS::RPP;
-  const int V = a.V;
-  const int RV = (V + NWG - 1) / NWG;
-  const int r0 = b * RV;
-  const int rend = min(V, r0 + RV);
-  const int npass = r0 < rend ? (rend - r0 + RPP - 1) / RPP : 0;
-  auto rowof = [&](int ps) { return [&, ps](int lr) { return min(r0 + ps * RPP + lr, V - 1); }; };
-  // layer l's QKV slice; past the last layer, the lm_head's first four passes
+  // layer l's QKV slice
   auto prefetch_layer = [&](int l) {
-    if (l < a.L) {
-      const PLayer P = a.layers[l];
-      wA.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
-    } else {
-      if (npass > 0) wa.load(a.emb_qs, a.emb_sc, rowof(0));
-      if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
-      if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
-      if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
-    }
+    const PLayer P = a.layers[l];
+    wA.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
   };
   prefetch_layer(0);
 
@@ -604,8 +601,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       __syncthreads();  // the rotated query (and the one-tile rows) in LDS
       const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_h = tid / (NP * RG);
       double qreg[DPP];
+      {
+        v4f q4[DPP / 4];
 #pragma unroll
-      for (int i = 0; i < DPP; ++i) qreg[i] = (double)s_qf[sc_h][4 * sc_pt + 4 * NP * (i / 4) + (i % 4)];
+        for (int i = 0; i < DPP / 4; ++i) q4[i] = *reinterpret_cast<const v4f*>(&s_qf[sc_h][4 * sc_pt + 4 * NP * i]);
+        pin(q4);
+#pragma unroll
+        for (int i = 0; i < DPP / 4; ++i) {
+          qreg[4 * i] = (double)q4[i].x, qreg[4 * i + 1] = (double)q4[i].y;
+          qreg[4 * i + 2] = (double)q4[i].z, qreg[4 * i + 3] = (double)q4[i].w;
+        }
+      }
       const bool out_live = tid < OUT_T;
       const int o_h = out_live ? tid / TPH : 0, o_d = out_live ? (tid % TPH) * DPT : 0;
       double o[DPT];
@@ -618,14 +624,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         for (int j = 0; j < RPT; ++j) {
           const int r = sc_rg * RPT + j;
           const float* kr = &s_t[r][4 * sc_pt];
+          v4f k4[DPP / 4];
+#pragma unroll
+          for (int d = 0; d < DPP; d += 4) k4[d / 4] = *reinterpret_cast<const v4f*>(kr + NP * d);
+          pin(k4);
           double ax = 0.0, ay = 0.0, az = 0.0, aw = 0.0;  // four independent FMA chains
 #pragma unroll
           for (int d = 0; d < DPP; d += 4) {
-            const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
-            ax += qreg[d] * (double)k4.x;
-            ay += qreg[d + 1] * (double)k4.y;
-            az += qreg[d + 2] * (double)k4.z;
-            aw += qreg[d + 3] * (double)k4.w;
+            ax += qreg[d] * (double)k4[d / 4].x;
+            ay += qreg[d + 1] * (double)k4[d / 4].y;
+            az += qreg[d + 2] * (double)k4[d / 4].z;
+            aw += qreg[d + 3] * (double)k4[d / 4].w;
           }
           double acc = (ax + ay) + (az + aw);
           acc = group_sum_d<NP>(acc);
@@ -658,6 +667,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 #pragma unroll
           for (int i2 = 0; i2 < DPT; ++i2) oa[c][i2] = 0.0;
         int r = 0;
+        if constexpr (DPT == 1) {  // eight rows per batch of LDS loads (two groups of four, in order)
+          for (; r + 8 <= nrow; r += 8) {
+            double pp[8];
+            float vv[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) pp[c] = pr[r + c], vv[c] = vt[r + c][o_d];
+            pin(pp, vv);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) oa[c % 4][0] += pp[c] * (double)vv[c];
+          }
+        }
         for (; r + 4 <= nrow; r += 4) {
 #pragma unroll
           for (int c = 0; c < 4; ++c)
@@ -816,7 +836,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // ---- E: down + residual (x of the next layer) ----------------------------------
     {
       wE.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
-      prefetch_layer(l + 1);
+      if (l + 1 < a.L) prefetch_layer(l + 1);
       {
         unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
         unsigned* da = reinterpret_cast<unsigned*>(s_da);
@@ -834,7 +854,19 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 
   // ---- lm_head over rows [b*RV, ...) + greedy argmax ---------------------------------
   {
-    // (its first four passes were requested during the last layer's down projection)
+    using LS = Slice<H, Slice<H, 1>::RPP>;  // one pass of RPP rows per buffer
+    constexpr int RPP = LS::RPP;
+    const int V = a.V;
+    const int RV = (V + NWG - 1) / NWG;
+    const int r0 = b * RV;
+    const int rend = min(V, r0 + RV);
+    const int npass = r0 < rend ? (rend - r0 + RPP - 1) / RPP : 0;
+    auto rowof = [&](int ps) { return [&, ps](int lr) { return min(r0 + ps * RPP + lr, V - 1); }; };
+    LS wa, wb, wc, wd;
+    if (npass > 0) wa.load(a.emb_qs, a.emb_sc, rowof(0));
+    if (npass > 1) wb.load(a.emb_qs, a.emb_sc, rowof(1));
+    if (npass > 2) wc.load(a.emb_qs, a.emb_sc, rowof(2));
+    if (npass > 3) wd.load(a.emb_qs, a.emb_sc, rowof(3));
     NormW<H> nw;
     nw.load(a.out_norm);
     if (!poll_quantize<H, true>(a.xa, T0 + (unsigned)a.L, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
