@@ -305,12 +305,15 @@ struct Slice {
   v4i w0[PASSES][BPL], w1[PASSES][BPL];
   uint16_t ws[PASSES][BPL];
 
-  // row(lr) maps a local row < R to a matrix row; rows past R load row(0)
+  // row(lr) maps a local row < R to a matrix row; rows past R load row(0).
+  // Passes [p0, p1) only (all by default).
   template <typename RowOf>
-  QDEV void load(const int8_t* __restrict__ qs, const uint16_t* __restrict__ sc, RowOf row) {
+  QDEV void load(const int8_t* __restrict__ qs, const uint16_t* __restrict__ sc, RowOf row, int p0 = 0,
+                 int p1 = PASSES) {
     const int li = threadIdx.x % LPR;
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
+      if (ps < p0 || ps >= p1) continue;
       const int lr = ps * RPP + threadIdx.x / LPR;
       const int64_t r = row(lr < R ? lr : 0);
       const QGLOBAL int8_t* wr = as_global(qs) + r * (int64_t)K;
@@ -498,10 +501,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   // during the down projection, ahead of its wait: a wait's loads complete, in order, after
   // everything issued before them, and that wait is long enough for the slice
   // to stream in, so the QKV phase finds it in registers instead of starting
-  // its fetch after its own wait.  The other slices are requested just
-  // before their own phase's wait (issuing them a phase early was measured
-  // slower: those windows already carry the phase's own traffic), and the
-  // KV tiles at the start of their layer.
+  // its fetch after its own wait.  The gate/up slice (64 KB per workgroup,
+  // the largest) is split: its first pass is requested with the o_proj
+  // slice, ahead of that wait, its second at its own phase.  The other
+  // slices are requested just before their own phase's wait, and the KV
+  // tiles at the start of their layer.  (Measured: issuing the whole gate/up
+  // slice, or the o_proj or down slices, a phase early was slower: those
+  // windows already carry the phase's own traffic, and the wait is then held
+  // until the early slice has arrived.)
   using SA = Slice<H, RA, (H / 32 >= 32 && RA >= 16 ? 16 : 0)>;
   using SC = Slice<QW, RC>;
   using SD = Slice<H, 64, (H / 32 >= 32 ? 8 : 0)>;
@@ -796,6 +803,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // ---- C: o_proj + residual ----------------------------------------------------
     {
       wC.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
+      if (b < NUB) wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; }, 0, 1);
       if (!poll_quantize<QW, false>(a.att, T, s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red,
                                     a.err))
         goto fail;
@@ -812,7 +820,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // projection's prologue arithmetic): 8 words of four codes, then one word
     // with the f16-valued block scale.
     if (b < NUB) {
-      wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; });
+      wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; }, 1, SD::PASSES);
       NormW<H> nw;
       nw.load(P.ffn_norm);
       if (!poll_quantize<H, true>(a.xc, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
