@@ -209,7 +209,7 @@ QDEV void quantize_lds(const float* s_x, const NormW<K>* nw, float eps, int8_t* 
       const float4 v = *reinterpret_cast<const float4*>(s_x + c);
       ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
     }
-    ss = block_sum_d<NT>(ss, s_red);
+    ss = block_sum_d_open<NT>(ss, s_red);  // (the barrier at the end covers s_red)
     r = rms_scale(ss, K, eps);
   }
 #pragma unroll
@@ -251,7 +251,7 @@ QDEV void quantize_regs(const float (&x)[K / NT], const NormW<K>* nw, float eps,
       const float* v = x + 4 * i;
       ss += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
     }
-    ss = block_sum_d<NT>(ss, s_red);
+    ss = block_sum_d_open<NT>(ss, s_red);  // (the barrier at the end covers s_red)
     r = rms_scale(ss, K, eps);
   }
 #pragma unroll
@@ -457,8 +457,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   constexpr int WPS = 4 + 2 * CPW;
   static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave && WPS % 2 == 0, "combine map");
   __shared__ unsigned s_pw[S * WPS];
-  __shared__ double s_cw[S];
-  __shared__ double s_cL;
   __shared__ ArgBest s_best[kWavesP];
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -780,22 +778,19 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       auto pw_d = [&](int sp, int k) {  // the f64 at words k, k + 1 of split sp
         return __hiloint2double((int)s_pw[sp * WPS + k + 1], (int)s_pw[sp * WPS + k]);
       };
-      if (wave == 0) {
-        const bool live = lane < S;
-        const double ms = live ? pw_d(lane, 0) : -INFINITY;
-        const double M = wave_max_all_d(ms);
-        const double wgt = (live && ms != -INFINITY) ? exp(ms - M) : 0.0;
-        if (live) s_cw[lane] = wgt;
-        const double L = wave_total_d(live ? wgt * pw_d(lane, 2) : 0.0);
-        if (lane == 0) s_cL = L;
-      }
-      __syncthreads();
-      {  // thread (k, sp) takes split sp's term of output k; a group sum over the splits
-        static_assert(CPW * S <= NT, "combine threads");
+      {  // thread (k, sp) takes split sp's term of output k.  Every group of S
+         // lanes holds all splits, so it forms the weights and L itself (no
+         // exchange through LDS and no barrier); the group sums are the same
+         // trees as a wavefront sum over S live lanes.
+        static_assert(CPW * S <= NT && (S == 16 || S == 32), "combine threads");
         const int sp = tid % S, k = tid / S;
-        double v = k < CPW ? s_cw[sp] * pw_d(sp, 4 + 2 * k) : 0.0;
+        const double ms = pw_d(sp, 0);
+        const double M = group_max_all_d<S>(ms);
+        const double wgt = ms != -INFINITY ? exp(ms - M) : 0.0;
+        const double L = group_sum_d<S>(wgt * pw_d(sp, 2));
+        double v = k < CPW ? wgt * pw_d(sp, 4 + 2 * k) : 0.0;
         v = group_sum_d<S>(v);
-        if (k < CPW && sp == S - 1) put_tagged(a.att + (ag * G + ch) * HD + cd0 + k, (float)(v / s_cL), T);
+        if (k < CPW && sp == S - 1) put_tagged(a.att + (ag * G + ch) * HD + cd0 + k, (float)(v / L), T);
       }
     }
 

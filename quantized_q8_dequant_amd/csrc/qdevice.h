@@ -146,6 +146,34 @@ QDEV double wave_max_all_d(double v) {
   return bcast_last_d(v);
 }
 
+// Block-wide sum of one double per thread (blockDim.x == NT, NT % 64 == 0),
+// without the trailing barrier: the caller passes another barrier before
+// s_red is written again.  Same summation order as block_sum_d.
+template <int NT>
+QDEV double block_sum_d_open(double v, double* s_red) {
+  v = group_sum_d<kWave>(v);
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == kWave - 1) s_red[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += s_red[i];
+  return t;
+}
+
+// The maximum over aligned groups of WIDTH lanes (16 or 32), in every lane
+// of the group.
+template <int WIDTH>
+QDEV double group_max_all_d(double v) {
+  static_assert(WIDTH == 16 || WIDTH == 32, "group width");
+  v = fmax(v, dpp_move_d<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmax(v, dpp_move_d<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmax(v, dpp_move_d<0x141>(v));  // row_half_mirror
+  v = fmax(v, dpp_move_d<0x140>(v));  // row_mirror: every lane holds its row's maximum
+  if (WIDTH == 32) v = fmax(v, __shfl_xor(v, 16));
+  return v;
+}
+
 // Block-wide sum of one double per thread (blockDim.x == NT, NT % 64 == 0).
 template <int NT>
 QDEV double block_sum_d(double v, double* s_red) {
