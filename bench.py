@@ -557,6 +557,50 @@ def cpu_baseline(shape, weights, prompt, decode_steps: int, sample: str | None =
     }
 
 
+def counters_decode(args) -> int:
+    """The default workload's decode steps alone, for hardware-counter runs.
+
+    The prompt enters the KV cache through one-token decode steps (the
+    prompt's own tokens fed in order), so no prefill kernel is launched; then
+    the workload's greedy decode steps (KV lengths prompt_len ..
+    prompt_len + steps - 1) as one qwen3_decode_greedy call, the one launch
+    the benchmark times; then one 1 GiB device-to-device copy whose bytes are
+    known (the counters' scale).
+    A line is printed after each part."""
+    import torch
+
+    from quantized_q8_dequant_amd import Qwen3Config, Qwen3Model
+    from synthetic import WORKLOADS, gen_prompt, gen_weights
+
+    wl = WORKLOADS["0.6b-decode"]
+    shape = wl.shape
+    model = Qwen3Model(Qwen3Config.from_shape(shape), gen_weights(shape, wl.weight_seed), [wl.kv_capacity])
+    if model.decode_launches() != 1:
+        print("the decode step is not one launch on this build", file=sys.stderr)
+        return 1
+    prompt = torch.tensor(gen_prompt(shape.vocab_size, wl.prompt_len, wl.prompt_seed), dtype=torch.int32,
+                          device="cuda:0")
+    for i in range(wl.prompt_len):
+        model.decode_step(token=prompt[i : i + 1], logits=False)
+    torch.cuda.synchronize()
+    model.step_status()
+    print(f"cache filled by {wl.prompt_len} decode steps", flush=True)
+    model.decode_greedy(wl.decode_steps)  # from the token the last fill step chose
+    torch.cuda.synchronize()
+    model.step_status()
+    print(f"{wl.decode_steps} greedy decode steps in one launch (KV length {wl.prompt_len}.."
+          f"{wl.prompt_len + wl.decode_steps - 1})", flush=True)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("1 GiB device-to-device copy", flush=True)
+    model.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,6 +617,12 @@ def main() -> int:
         help="KV cache type of the 8b-longctx workload (default: its bf16)",
     )
     ap.add_argument(
+        "--counters-decode",
+        action="store_true",
+        help="counter runs: only the default workload's decode steps (the cache filled by decode steps, no "
+        "prefill kernel), then a 1 GiB device-to-device copy of known size",
+    )
+    ap.add_argument(
         "--pmc-calibrate",
         action="store_true",
         help="finish with a 1 GiB device-to-device copy (the known-size kernel hardware counters are scaled by)",
@@ -584,6 +634,9 @@ def main() -> int:
             file=sys.stderr,
         )
         return 2
+
+    if args.counters_decode:
+        return counters_decode(args)
 
     import torch
 
@@ -601,14 +654,17 @@ def main() -> int:
     model = Qwen3Model(Qwen3Config.from_shape(shape), weights, [wl.kv_capacity])
     torch.cuda.synchronize()
 
+    # the greedy decode steps are one qwen3_decode_greedy call (with the
+    # one-launch step: one launch, the token handed between steps on the
+    # device); the same steps as single qwen3_decode_step calls are timed
+    # after the timed region
     def one_step():
         model.reset()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
         model.prefill(prompt)
         e[1].record()
-        for _ in range(wl.decode_steps):
-            model.decode_step()
+        model.decode_greedy(wl.decode_steps)
         e[2].record()
         return e
 
@@ -626,6 +682,21 @@ def main() -> int:
     prefill_tps = wl.prompt_len / (prefill_ms / 1000.0)
     step_bytes = sum(decode_token_bytes(shape, wl.prompt_len + i) for i in range(wl.decode_steps))
     decode_gbps = step_bytes / (decode_ms / 1000.0) / 1e9
+
+    # the same decode steps as single calls (one launch each)
+    single = []
+    for _ in range(2):
+        model.reset()
+        model.prefill(prompt)
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for _ in range(wl.decode_steps):
+            model.decode_step()
+        b_.record()
+        torch.cuda.synchronize()
+        single.append(a_.elapsed_time(b_))
+    model.step_status()
+    single_ms = single[-1]
 
     # per-kernel durations at the mean decode length (replayed in the step's
     # launch configuration, timed with events on the launch stream)
@@ -656,17 +727,17 @@ def main() -> int:
         }
     verify = None
     if args.workload == "0.6b-decode":
-        verify = bench_verify(model, prompt, shape, decode_ms / wl.decode_steps, args)
+        verify = bench_verify(model, prompt, shape, single_ms / wl.decode_steps, args)
     launches = model.decode_launches()
     if launches == 1:
-        # the decode step is one kernel: its algorithmic bytes per launch (the
-        # step at the mean KV length) over its event-timed duration
-        mean_bytes = step_bytes / wl.decode_steps
-        us = decode_ms * 1000.0 / wl.decode_steps
-        dom = "decode_step (one launch)"
-        achieved = round(mean_bytes / (us * 1e-6) / 1e9, 1)
+        # the decode steps are one kernel launch: its algorithmic bytes (every
+        # step at its KV length) over its event-timed duration
+        us = decode_ms * 1000.0
+        dom = f"decode_step (one launch running the {wl.decode_steps} greedy steps)"
+        achieved = round(step_bytes / (us * 1e-6) / 1e9, 1)
         traffic = measured_traffic("decode_step")
-        kernel_info = {"us_per_launch": round(us, 3), "bytes_per_launch": int(mean_bytes)}
+        kernel_info = {"us_per_launch": round(us, 1), "bytes_per_launch": int(step_bytes),
+                       "steps_per_launch": wl.decode_steps, "us_per_step": round(us / wl.decode_steps, 3)}
     else:
         dom = max(kernels, key=lambda k: kernels[k]["us_per_launch"] * kernels[k]["launches_per_token"])
         achieved = kernels[dom]["GBps"]
@@ -769,6 +840,9 @@ def main() -> int:
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(prefill_tps, 1),
         "decode_launches_per_token": launches,
+        "decode_call": "qwen3_decode_greedy (all steps in one call)",
+        "decode_single_step_calls_ms": round(single_ms, 3),
+        "decode_single_step_calls_tokens_per_s": round(wl.decode_steps / (single_ms / 1000.0), 2),
         "kernels_at_mean_ctx": kernels,
         "prefill_4096_one_call": p4,
         "verify": verify,
@@ -783,4 +857,6 @@ def main() -> int:
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    rc = main()
+    if rc:  # success ends the interpreter normally (a profiler writes its results during that shutdown)
+        sys.exit(rc)

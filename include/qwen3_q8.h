@@ -200,6 +200,27 @@ int qwen3_truncate(qwen3_t* h, int32_t seq, int32_t keep_len, void* stream);
 int qwen3_decode_step(qwen3_t* h, int32_t seq, const int32_t* d_token, float* d_logits,
                       int32_t* d_argmax, void* stream);
 
+/* n greedy decode steps of sequence `seq` in one call ("A transformer from
+ * scratch", sections 12.5-12.6: each step is the cached forward of the
+ * previous step's argmax, the generation loop of the greedy sampler): step 0
+ * reads its token on the device from d_token [1] (clamped into [0, vocab)
+ * like qwen3_decode_step); step i > 0 takes the token step i - 1 chose.
+ * Writes the n chosen tokens to d_tokens_out [n] (device, required) and the
+ * last step's logits to d_logits [vocab] (may be NULL).  Every step computes
+ * exactly what qwen3_decode_step computes, so the tokens and the last logits
+ * equal those of n qwen3_decode_step calls fed their own argmax.  Length L ->
+ * L + n; L + n > capacity is QWEN3_E_KV_CACHE_OVERFLOW and n < 1 is
+ * QWEN3_E_INVALID_ARGUMENT.  With the one-launch step (qwen3_decode_launches
+ * == 1) all n steps are one cooperative launch, the token handed from step to
+ * step on the device, so n - 1 launch gaps are saved; a device-side failure
+ * at step k (see qwen3_step_status) leaves steps < k done and their tokens
+ * written, writes -1 as the call's last token d_tokens_out[n - 1], leaves
+ * slots k .. n - 2 unwritten, and qwen3_step_status then sets the host
+ * length to L + k.  Otherwise the steps are n per-kernel steps enqueued on
+ * `stream`.  Allocates nothing. */
+int qwen3_decode_greedy(qwen3_t* h, int32_t seq, int32_t n, const int32_t* d_token, int32_t* d_tokens_out,
+                        float* d_logits, void* stream);
+
 /* Batched decode: one token for each of the `n` distinct sequences h_seqs
  * [n] (host) in one pass: weights are read once for all n rows, while RoPE
  * positions, KV appends and attention are per sequence ("A transformer from

@@ -38,6 +38,7 @@ EXPORTS = (
     "qwen3_sample_work_bytes",
     "qwen3_sample",
     "qwen3_decode_step",
+    "qwen3_decode_greedy",
     "qwen3_decode_batch",
     "qwen3_reset",
     "qwen3_step_status",
@@ -157,6 +158,7 @@ def lib() -> C.CDLL:
         "qwen3_sample_work_bytes": (C.c_size_t, [i32, i32]),
         "qwen3_sample": (C.c_int, [vp, i32, i32, C.POINTER(SamplerConfig), vp, i32, vp, vp, vp, vp, vp]),
         "qwen3_decode_step": (C.c_int, [vp, i32, vp, vp, vp, vp]),
+        "qwen3_decode_greedy": (C.c_int, [vp, i32, i32, vp, vp, vp, vp]),
         "qwen3_decode_batch": (C.c_int, [vp, p_i32, i32, vp, vp, vp, vp]),
         "qwen3_reset": (C.c_int, [vp, i32, vp]),
         "qwen3_step_status": (C.c_int, [vp, vp]),

@@ -458,12 +458,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave && WPS % 2 == 0, "combine map");
   __shared__ unsigned s_pw[S * WPS];
   __shared__ ArgBest s_best[kWavesP];
+  __shared__ unsigned s_tok[2];  // the next step's token (both words of its pair)
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int seq = a.seq;
-  const int p = a.len[seq];
-  const int ctx = p + 1;
-  const unsigned T0 = a.pstep * (unsigned)(a.L + 1) + 1u;  // epoch of layer 0
+  const int p0 = a.len[seq];  // the first step appends row p0; step st appends row p0 + st
   const float eps = a.eps;
 
   // a failed earlier step leaves the error word set: do nothing
@@ -472,26 +471,12 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     return;
   }
 
-  // ---- embedding rows of this workgroup (exact f16(d) * q) ------------------
-  {
-    // a device token cannot be checked by the host: clamp it into [0, V)
-    const int tok = min(max(a.token[0], 0), a.V - 1);
-    if (tid < RC) {
-      const int n = b * RC + tid;
-      const float x = f16_bits_to_f32(a.emb_sc[(int64_t)tok * (H / 32) + n / 32]) * (float)a.emb_qs[(int64_t)tok * H + n];
-      put_tagged(a.xa + n, x, T0);
-      s_xkeep[tid] = x;
-    }
-  }
-
-  // attention unit of this workgroup
+  // attention unit of this workgroup; its rows [j0, j1) of the step's context
   const bool attn_unit = b < NKV * S;
   const int ag = b / S, asplit = b % S;
-  const int chunk = (ctx + S - 1) / S;
-  const int j0 = min(ctx, asplit * chunk), j1 = min(ctx, j0 + chunk);
-  const int nt = j0 < j1 ? (j1 - j0 + TJ - 1) / TJ : 0;
-  const int cache_end = min(j1, p);
-  const bool has_new = j0 < j1 && j1 == ctx;
+  int p, ctx, j0, j1, nt, cache_end;
+  bool has_new;
+  unsigned T0;  // epoch of the step's layer 0
   const int64_t cap = a.seq_cap[seq];
   const int64_t head_elems = cap * HD;
 
@@ -529,6 +514,41 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     const PLayer P = a.layers[l];
     wA.load(P.qkv_qs, P.qkv_sc, [&](int lr) { return b * RA + lr; });
   };
+
+  // Greedy steps: each step is the decode step of the previous step's token.
+  // The workgroup that finishes a step's argmax publishes the token as a
+  // tagged word once its resets of the argmax state are visible, and every
+  // workgroup starts the next step from that word.
+  for (int st = 0; st < a.nsteps; ++st) {
+  p = p0 + st;
+  ctx = p + 1;
+  T0 = (a.pstep + (unsigned)st) * (unsigned)(a.L + 1) + 1u;
+  {
+    const int chunk = (ctx + S - 1) / S;
+    j0 = min(ctx, asplit * chunk);
+    j1 = min(ctx, j0 + chunk);
+    nt = j0 < j1 ? (j1 - j0 + TJ - 1) / TJ : 0;
+    cache_end = min(j1, p);
+    has_new = j0 < j1 && j1 == ctx;
+  }
+
+  // ---- embedding rows of this workgroup (exact f16(d) * q) ------------------
+  {
+    int tok;
+    if (st == 0) {
+      // a device token cannot be checked by the host: clamp it into [0, V)
+      tok = min(max(a.token[0], 0), a.V - 1);
+    } else {
+      if (!poll_pairs<1>(a.tok, 2, [](int) { return 0; }, [&](int i) { return s_tok + i; }, T0, a.err)) goto fail;
+      tok = (int)s_tok[0];
+    }
+    if (tid < RC) {
+      const int n = b * RC + tid;
+      const float x = f16_bits_to_f32(a.emb_sc[(int64_t)tok * (H / 32) + n / 32]) * (float)a.emb_qs[(int64_t)tok * H + n];
+      put_tagged(a.xa + n, x, T0);
+      s_xkeep[tid] = x;
+    }
+  }
   prefetch_layer(0);
 
   for (int l = 0; l < a.L; ++l) {
@@ -590,12 +610,12 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
             float kf = s_knew[d], vf = s_vnew[d];
             if (KVBF16) {
               const uint16_t kb = f32_to_bf16_bits(kf), vb = f32_to_bf16_bits(vf);
-              reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
-              reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
+              st_coherent(reinterpret_cast<uint16_t*>(a.kv) + ki, kb);
+              st_coherent(reinterpret_cast<uint16_t*>(a.kv) + vi, vb);
               kf = bf16_bits_to_f32(kb), vf = bf16_bits_to_f32(vb);
             } else {
-              reinterpret_cast<float*>(a.kv)[ki] = kf;
-              reinterpret_cast<float*>(a.kv)[vi] = vf;
+              st_coherent(reinterpret_cast<float*>(a.kv) + ki, kf);
+              st_coherent(reinterpret_cast<float*>(a.kv) + vi, vf);
             }
             s_t[p - j0][d] = kf;
             s_tv[p - j0][d] = vf;
@@ -709,13 +729,13 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
             const int64_t ki = kbase + (int64_t)p * HD + d, vi = vbase + (int64_t)p * HD + d;
             if (KVBF16) {
               const uint16_t kb = f32_to_bf16_bits(s_knew[d]), vb = f32_to_bf16_bits(s_vnew[d]);
-              reinterpret_cast<uint16_t*>(a.kv)[ki] = kb;
-              reinterpret_cast<uint16_t*>(a.kv)[vi] = vb;
+              st_coherent(reinterpret_cast<uint16_t*>(a.kv) + ki, kb);
+              st_coherent(reinterpret_cast<uint16_t*>(a.kv) + vi, vb);
               s_knew[d] = bf16_bits_to_f32(kb);
               s_vnew[d] = bf16_bits_to_f32(vb);
             } else {
-              reinterpret_cast<float*>(a.kv)[ki] = s_knew[d];
-              reinterpret_cast<float*>(a.kv)[vi] = s_vnew[d];
+              st_coherent(reinterpret_cast<float*>(a.kv) + ki, s_knew[d]);
+              st_coherent(reinterpret_cast<float*>(a.kv) + vi, s_vnew[d]);
             }
           }
         }
@@ -879,7 +899,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         const int row = r0 + ps * RPP + lr;
         if (row < rend) {
           const float y = (float)acc;
-          if (a.logits) a.logits[row] = y;
+          if (a.logits && st + 1 == a.nsteps) a.logits[row] = y;
           best = better(best, ArgBest{y, row});
         }
       });
@@ -911,6 +931,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       best = better(best, c);
     }
     if (lane == 0) s_best[wave] = best;
+    // every wavefront's stores of this step (the new KV rows among them,
+    // read by other workgroups in the next step) complete before the
+    // workgroup reports its arrival
+    wait_memory();
     __syncthreads();
     if (tid == 0) {
       ArgBest bb = s_best[0];
@@ -924,13 +948,23 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
       if (prev == gridDim.x - 1) {
         const unsigned long long k = __hip_atomic_fetch_add(a.best_key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool failed = ld_err(a.err) != 0;
-        a.argmax[0] = failed ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        const int32_t next = failed ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        a.argmax[0] = next;
+        if (a.tokens_out) a.tokens_out[st] = next;
         st_coherent(a.best_key, 0ull);
         st_coherent(a.am_cnt, 0u);
         if (!failed) a.len[seq] = p + 1;
+        if (!failed && st + 1 < a.nsteps) {
+          // the resets and this step's stores complete before the token is
+          // seen, so the next step's argmax starts from a cleared state
+          wait_memory();
+          put_tagged(a.tok, __int_as_float(next), T0 + (unsigned)(a.L + 1));
+          put_tagged(a.tok + 1, __int_as_float(next), T0 + (unsigned)(a.L + 1));
+        }
       }
     }
   }
+  }  // greedy steps
   return;
 fail:
   if (tid == 0) {

@@ -38,7 +38,10 @@ struct PersistArgs {
   unsigned long long* best_key;
   unsigned* am_cnt;
   unsigned* err;         // set on a timed-out wait
-  unsigned pstep;        // launch counter (epochs)
+  unsigned pstep;        // step counter (epochs) at the launch's first step
+  int nsteps;            // greedy steps in this launch (>= 1)
+  int32_t* tokens_out;   // [nsteps] the token of each step, or null
+  unsigned long long* tok;  // the token handed to the next step: two (value, epoch) words
 };
 struct PersistShape {
   int H, QW, F, HD, G;

@@ -147,6 +147,7 @@ struct qwen3_model {
   unsigned long long *p_xa = nullptr, *p_xc = nullptr, *p_qkv = nullptr, *p_att = nullptr, *p_h = nullptr;
   unsigned long long* p_part = nullptr;
   unsigned* p_err = nullptr;
+  unsigned long long* p_tok = nullptr;  // the token handed between greedy steps of one launch
   unsigned pstep = 0;
   size_t bytes = 0;
   // host
@@ -301,6 +302,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     m->p_h = cv.arr<unsigned long long>(F);
     m->p_part = cv.arr<unsigned long long>(persist_part_words(G, hd));
     m->p_err = cv.arr<unsigned>(1);
+    m->p_tok = cv.arr<unsigned long long>(2);
   }
   if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
   *total = align_up(cv.off);
@@ -803,6 +805,7 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
       HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_part, 0, persist_part_words(m->G, m->hd) * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
+      HIP_TRY(hipMemsetAsync(m->p_tok, 0, 16, s));
       HIP_TRY(hipStreamSynchronize(s));  // tab is a host temporary
     }
     HIP_TRY(hipStreamSynchronize(s));
@@ -984,6 +987,42 @@ static int replay_decode(qwen3_model* m, std::map<std::tuple<int, const void*, c
   return QWEN3_OK;
 }
 
+// One launch of the one-launch decode step running n greedy steps.
+static hipError_t launch_persistent(qwen3_model* m, int32_t seq, int n, const int32_t* d_token, int32_t* d_tokens_out,
+                                    float* d_logits, int32_t* d_argmax, hipStream_t s) {
+  PersistArgs a{};
+  a.layers = m->d_players;
+  a.L = m->L;
+  a.V = m->V;
+  a.eps = m->cfg.rms_norm_eps;
+  a.scale = 1.0 / std::sqrt((double)m->hd);
+  a.emb_qs = m->emb.qs;
+  a.emb_sc = m->emb.sc;
+  a.out_norm = m->out_norm;
+  a.rope_cos = m->rope_cos;
+  a.rope_sin = m->rope_sin;
+  a.kv = m->kv;
+  a.seq_base = m->d_seq_base;
+  a.seq_cap = m->d_seq_cap;
+  a.len = m->d_len;
+  a.seq = seq;
+  a.token = d_token;
+  a.logits = d_logits;
+  a.argmax = d_argmax;
+  a.xa = m->p_xa, a.xc = m->p_xc, a.qkv = m->p_qkv, a.att = m->p_att, a.h = m->p_h;
+  a.part = m->p_part;
+  a.best_key = m->am_key;
+  a.am_cnt = m->am_cnt;
+  a.err = m->p_err;
+  a.pstep = m->pstep;
+  a.nsteps = n;
+  a.tokens_out = d_tokens_out;
+  a.tok = m->p_tok;
+  const hipError_t e = q8k::decode_persistent(m->psh, m->kvbf16, a, s);
+  if (e == hipSuccess) m->pstep += (unsigned)n;
+  return e;
+}
+
 int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_logits, int32_t* d_argmax,
                       void* stream) {
   g_err.clear();
@@ -994,33 +1033,7 @@ int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_
     return fail(QWEN3_E_KV_CACHE_OVERFLOW, "decode at len " + std::to_string(m->h_len[seq]) + " exceeds capacity");
   hipStream_t s = S(stream);
   if (m->persist) {
-    PersistArgs a{};
-    a.layers = m->d_players;
-    a.L = m->L;
-    a.V = m->V;
-    a.eps = m->cfg.rms_norm_eps;
-    a.scale = 1.0 / std::sqrt((double)m->hd);
-    a.emb_qs = m->emb.qs;
-    a.emb_sc = m->emb.sc;
-    a.out_norm = m->out_norm;
-    a.rope_cos = m->rope_cos;
-    a.rope_sin = m->rope_sin;
-    a.kv = m->kv;
-    a.seq_base = m->d_seq_base;
-    a.seq_cap = m->d_seq_cap;
-    a.len = m->d_len;
-    a.seq = seq;
-    a.token = d_token;
-    a.logits = d_logits;
-    a.argmax = d_argmax;
-    a.xa = m->p_xa, a.xc = m->p_xc, a.qkv = m->p_qkv, a.att = m->p_att, a.h = m->p_h;
-    a.part = m->p_part;
-    a.best_key = m->am_key;
-    a.am_cnt = m->am_cnt;
-    a.err = m->p_err;
-    a.pstep = m->pstep;
-    HIP_TRY(q8k::decode_persistent(m->psh, m->kvbf16, a, s));
-    m->pstep += 1;
+    HIP_TRY(launch_persistent(m, seq, 1, d_token, nullptr, d_logits, d_argmax, s));
     m->h_len[seq] += 1;
     return QWEN3_OK;
   }
@@ -1032,6 +1045,32 @@ int qwen3_decode_step(qwen3_t* m, int32_t seq, const int32_t* d_token, float* d_
   auto key = std::make_tuple((int)seq, (const void*)d_token, (const void*)d_logits, (const void*)d_argmax);
   TRY(replay_decode(m, m->graphs, key, 1, d_token, m->d_seq_ids + seq, d_logits, d_argmax, s));
   m->h_len[seq] += 1;
+  return QWEN3_OK;
+}
+
+int qwen3_decode_greedy(qwen3_t* m, int32_t seq, int32_t n, const int32_t* d_token, int32_t* d_tokens_out,
+                        float* d_logits, void* stream) {
+  g_err.clear();
+  if (!m) return fail(QWEN3_E_INVALID_ARGUMENT, "null handle");
+  if (seq < 0 || seq >= (int)m->h_len.size()) return fail(QWEN3_E_INVALID_ARGUMENT, "bad sequence index");
+  if (n < 1) return fail(QWEN3_E_INVALID_ARGUMENT, "n must be at least 1");
+  if (!d_token || !d_tokens_out) return fail(QWEN3_E_INVALID_ARGUMENT, "d_token and d_tokens_out are required");
+  if ((int64_t)m->h_len[seq] + n > (int64_t)m->cap[seq])
+    return fail(QWEN3_E_KV_CACHE_OVERFLOW, "decoding " + std::to_string(n) + " tokens at len " +
+                                               std::to_string(m->h_len[seq]) + " exceeds capacity");
+  hipStream_t s = S(stream);
+  if (m->persist) {
+    HIP_TRY(launch_persistent(m, seq, n, d_token, d_tokens_out, d_logits, d_tokens_out + n - 1, s));
+    m->h_len[seq] += n;
+    return QWEN3_OK;
+  }
+  // per-kernel steps, each fed the previous step's token (no graph: every
+  // step has its own token pointer)
+  for (int i = 0; i < n; ++i) {
+    const int32_t* tok = i == 0 ? d_token : d_tokens_out + i - 1;
+    TRY(enqueue_decode(m, 1, tok, m->d_seq_ids + seq, i + 1 == n ? d_logits : nullptr, d_tokens_out + i, s));
+    m->h_len[seq] += 1;
+  }
   return QWEN3_OK;
 }
 

@@ -334,6 +334,21 @@ class Qwen3Model:
         check(lib().qwen3_decode_step(self.handle, seq, tok.data_ptr(), lg.data_ptr() if logits else None, am.data_ptr(), _stream()))
         return lg, am
 
+    def decode_greedy(self, n: int, seq: int = 0, token: torch.Tensor | None = None, logits: bool = True,
+                      out: torch.Tensor | None = None):
+        """n greedy decode steps in one call: step 0 is fed `token` (device
+        int32 [1]; default: the sequence's previous argmax), each later step
+        the token the step before chose.  Returns (tokens int32 [n], the last
+        step's logits); the last token is also left in the sequence's argmax
+        buffer, so decode_step can continue from it."""
+        lg, am = self.io(seq)
+        tok = am if token is None else token
+        toks = out if out is not None else torch.empty(n, dtype=torch.int32, device=self.device)
+        check(lib().qwen3_decode_greedy(self.handle, seq, n, tok.data_ptr(), toks.data_ptr(),
+                                         lg.data_ptr() if logits else None, _stream()))
+        am.copy_(toks[n - 1 : n])
+        return toks, lg
+
     def decode_batch(self, seqs, tokens: torch.Tensor, logits: torch.Tensor | None, argmax: torch.Tensor):
         s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
         check(

@@ -122,6 +122,7 @@ def test_null_handle_and_op_argument_errors():
     toks = (C.c_int32 * 2)(1, 2)
     assert lib.qwen3_prefill(None, 0, toks, 2, None, None, None) == -1
     assert lib.qwen3_decode_step(None, 0, None, None, None, None) == -1
+    assert lib.qwen3_decode_greedy(None, 0, 1, None, None, None, None) == -1
     assert lib.qwen3_reset(None, 0, None) == -1
     assert lib.qwen3_step_status(None, None) == -1
     assert lib.qwen3_inject_step_error(None, None) == -1
