@@ -8,7 +8,8 @@
 //   x = embed(token); per layer:
 //     A  qkv = W_qkv . quant(rmsnorm(x, attn_norm))
 //     B  per KV head g: q/k norm + RoPE, append k/v at row p, attention over
-//        rows 0..p split across workgroups, last arrival combines
+//        rows 0..p split across workgroups; every workgroup then combines
+//        the splits' partials for a slice of the head group's outputs
 //     C  x = x + W_o . quant(att)
 //     D  h = silu(W_gate . b) * (W_up . b), b = quant(rmsnorm(x, ffn_norm))
 //     E  x = x + W_down . quant(h)
@@ -425,6 +426,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   static_assert(RA * NWG == NQKV && RC * NWG == H && NUB * 32 == F && NUB <= NWG,
                 "shape does not split over the grid");
   static_assert(NKV * S <= NWG, "attention units exceed the grid");
+  static_assert(NWG == NT, "one argmax key per thread");
   constexpr int XMAX = (H > QW ? (H > F ? H : F) : (QW > F ? QW : F));
   // attention maps (as the decode attention kernel)
   constexpr int NP = (G == 1) ? 8 : 4;
@@ -458,7 +460,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave && WPS % 2 == 0, "combine map");
   __shared__ unsigned s_pw[S * WPS];
   __shared__ ArgBest s_best[kWavesP];
-  __shared__ unsigned s_tok[2];  // the next step's token (both words of its pair)
+  __shared__ unsigned s_keys[2 * NWG];  // every workgroup's argmax key of the step (low, high halves)
+  __shared__ u64 s_kmax[kWavesP];
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int seq = a.seq;
@@ -476,6 +479,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   const int ag = b / S, asplit = b % S;
   int p, ctx, j0, j1, nt, cache_end;
   bool has_new;
+  int next_tok = 0;  // the token the previous step chose (every workgroup forms it)
   unsigned T0;  // epoch of the step's layer 0
   const int64_t cap = a.seq_cap[seq];
   const int64_t head_elems = cap * HD;
@@ -516,9 +520,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   };
 
   // Greedy steps: each step is the decode step of the previous step's token.
-  // The workgroup that finishes a step's argmax publishes the token as a
-  // tagged word once its resets of the argmax state are visible, and every
-  // workgroup starts the next step from that word.
+  // Every workgroup publishes its rows' best (logit, index) key as a tagged
+  // word, reads all of them and forms the argmax itself, so the next step
+  // starts without a further hand-off.
   for (int st = 0; st < a.nsteps; ++st) {
   p = p0 + st;
   ctx = p + 1;
@@ -534,14 +538,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
 
   // ---- embedding rows of this workgroup (exact f16(d) * q) ------------------
   {
-    int tok;
-    if (st == 0) {
-      // a device token cannot be checked by the host: clamp it into [0, V)
-      tok = min(max(a.token[0], 0), a.V - 1);
-    } else {
-      if (!poll_pairs<1>(a.tok, 2, [](int) { return 0; }, [&](int i) { return s_tok + i; }, T0, a.err)) goto fail;
-      tok = (int)s_tok[0];
-    }
+    // a device token cannot be checked by the host: clamp it into [0, V)
+    const int tok = st == 0 ? min(max(a.token[0], 0), a.V - 1) : next_tok;
     if (tid < RC) {
       const int n = b * RC + tid;
       const float x = f16_bits_to_f32(a.emb_sc[(int64_t)tok * (H / 32) + n / 32]) * (float)a.emb_qs[(int64_t)tok * H + n];
@@ -933,34 +931,42 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     if (lane == 0) s_best[wave] = best;
     // every wavefront's stores of this step (the new KV rows among them,
     // read by other workgroups in the next step) complete before the
-    // workgroup reports its arrival
+    // workgroup publishes its key
     wait_memory();
     __syncthreads();
+    // the key (order-preserving bits of the logit << 32 | ~index): the
+    // largest key is the largest logit, ties going to the lowest index
+    const unsigned Tk = T0 + (unsigned)(a.L + 1);
     if (tid == 0) {
       ArgBest bb = s_best[0];
       for (int i = 1; i < kWavesP; ++i) bb = better(bb, s_best[i]);
       const uint32_t u = __float_as_uint(bb.v + 0.0f);
       const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      const unsigned long long key = ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (uint32_t)bb.i);
-      __hip_atomic_fetch_max(a.best_key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_memory();
-      const unsigned prev = arrive(a.am_cnt);
-      if (prev == gridDim.x - 1) {
-        const unsigned long long k = __hip_atomic_fetch_add(a.best_key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool failed = ld_err(a.err) != 0;
-        const int32_t next = failed ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-        a.argmax[0] = next;
-        if (a.tokens_out) a.tokens_out[st] = next;
-        st_coherent(a.best_key, 0ull);
-        st_coherent(a.am_cnt, 0u);
-        if (!failed) a.len[seq] = p + 1;
-        if (!failed && st + 1 < a.nsteps) {
-          // the resets and this step's stores complete before the token is
-          // seen, so the next step's argmax starts from a cleared state
-          wait_memory();
-          put_tagged(a.tok, __int_as_float(next), T0 + (unsigned)(a.L + 1));
-          put_tagged(a.tok + 1, __int_as_float(next), T0 + (unsigned)(a.L + 1));
-        }
+      const u64 key = ((u64)ord << 32) | (0xFFFFFFFFu - (uint32_t)bb.i);
+      put_tagged_d(a.keys, 2 * NWG, 2 * b, __longlong_as_double((long long)key), Tk);
+    }
+    // workgroup 0 reports the step; the others need the token only if a
+    // step follows
+    if (st + 1 < a.nsteps || b == 0) {
+      if (!poll_pairs<NWG>(a.keys, 2 * NWG, [](int j) { return 2 * j; }, [&](int i) { return s_keys + i; }, Tk,
+                           a.err))
+        goto fail;
+      u64 k = ((u64)s_keys[2 * tid + 1] << 32) | s_keys[2 * tid];
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const u64 c = __shfl_xor(k, o);
+        k = c > k ? c : k;
+      }
+      if (lane == 0) s_kmax[wave] = k;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kWavesP; ++w) k = s_kmax[w] > k ? s_kmax[w] : k;
+      next_tok = (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+      if (b == 0 && tid == 0) {
+        // every workgroup's key is there, so every workgroup finished the step
+        if (a.tokens_out) a.tokens_out[st] = next_tok;
+        if (st + 1 == a.nsteps) a.argmax[0] = next_tok;
+        a.len[seq] = p + 1;
       }
     }
   }

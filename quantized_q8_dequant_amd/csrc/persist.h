@@ -35,13 +35,12 @@ struct PersistArgs {
   // attention partials of every split as (32-bit half, epoch) words:
   // [nkv][splits per KV head][G][hd + 2 (o..., m, l)][2 (low, high half)]
   unsigned long long* part;
-  unsigned long long* best_key;
-  unsigned* am_cnt;
   unsigned* err;         // set on a timed-out wait
   unsigned pstep;        // step counter (epochs) at the launch's first step
   int nsteps;            // greedy steps in this launch (>= 1)
   int32_t* tokens_out;   // [nsteps] the token of each step, or null
-  unsigned long long* tok;  // the token handed to the next step: two (value, epoch) words
+  // each workgroup's argmax key of the step as two (32-bit half, epoch) words
+  unsigned long long* keys;  // [2 * kPersistWorkgroups]
 };
 struct PersistShape {
   int H, QW, F, HD, G;

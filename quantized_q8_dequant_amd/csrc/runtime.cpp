@@ -147,7 +147,7 @@ struct qwen3_model {
   unsigned long long *p_xa = nullptr, *p_xc = nullptr, *p_qkv = nullptr, *p_att = nullptr, *p_h = nullptr;
   unsigned long long* p_part = nullptr;
   unsigned* p_err = nullptr;
-  unsigned long long* p_tok = nullptr;  // the token handed between greedy steps of one launch
+  unsigned long long* p_keys = nullptr;  // the workgroups' argmax keys of a one-launch step
   unsigned pstep = 0;
   size_t bytes = 0;
   // host
@@ -302,7 +302,7 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     m->p_h = cv.arr<unsigned long long>(F);
     m->p_part = cv.arr<unsigned long long>(persist_part_words(G, hd));
     m->p_err = cv.arr<unsigned>(1);
-    m->p_tok = cv.arr<unsigned long long>(2);
+    m->p_keys = cv.arr<unsigned long long>(2 * kPersistWorkgroups);
   }
   if (cv.overflow) return fail(QWEN3_E_INVALID_WEIGHT_SHAPE, "workspace size overflows");
   *total = align_up(cv.off);
@@ -805,7 +805,7 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
       HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_part, 0, persist_part_words(m->G, m->hd) * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
-      HIP_TRY(hipMemsetAsync(m->p_tok, 0, 16, s));
+      HIP_TRY(hipMemsetAsync(m->p_keys, 0, 2 * kPersistWorkgroups * 8, s));
       HIP_TRY(hipStreamSynchronize(s));  // tab is a host temporary
     }
     HIP_TRY(hipStreamSynchronize(s));
@@ -871,9 +871,6 @@ int qwen3_step_status(qwen3_t* m, void* stream) {
   // the failed steps advanced no device length: the host lengths follow them
   std::vector<int32_t> dl(m->h_len.size());
   HIP_TRY(hipMemcpyAsync(dl.data(), m->d_len, dl.size() * 4, hipMemcpyDeviceToHost, s));
-  // a failed step leaves the argmax key and arrival counter part-way
-  HIP_TRY(hipMemsetAsync(m->am_key, 0, 8, s));
-  HIP_TRY(hipMemsetAsync(m->am_cnt, 0, 4, s));
   HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
   HIP_TRY(hipStreamSynchronize(s));
   m->h_len = dl;
@@ -1011,13 +1008,11 @@ static hipError_t launch_persistent(qwen3_model* m, int32_t seq, int n, const in
   a.argmax = d_argmax;
   a.xa = m->p_xa, a.xc = m->p_xc, a.qkv = m->p_qkv, a.att = m->p_att, a.h = m->p_h;
   a.part = m->p_part;
-  a.best_key = m->am_key;
-  a.am_cnt = m->am_cnt;
   a.err = m->p_err;
   a.pstep = m->pstep;
   a.nsteps = n;
   a.tokens_out = d_tokens_out;
-  a.tok = m->p_tok;
+  a.keys = m->p_keys;
   const hipError_t e = q8k::decode_persistent(m->psh, m->kvbf16, a, s);
   if (e == hipSuccess) m->pstep += (unsigned)n;
   return e;
