@@ -452,13 +452,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   __shared__ __align__(16) float s_tv[TJ][HD + 4];  // V tile of a one-tile split
   __shared__ double s_s[G][MAXR];
   __shared__ double s_m[G], s_l[G];
-  // the combine: this workgroup's CPW outputs of its KV head's G * HD, from
-  // every split's (m, l) of that query head and its slice of o (WPS words of
-  // 32-bit halves per split)
-  constexpr int CPW = G * HD / S;
+  // the combine: split s < NCB of KV head g also combines Q8_0 block s of
+  // that head group's G * HD outputs (CPW = 32 of them), from every split's
+  // (m, l) of the block's query head and its slice of o (WPS words of 32-bit
+  // halves per split)
+  constexpr int CPW = 32;
+  constexpr int NCB = G * HD / CPW;  // combined blocks per KV head
   constexpr int WPS = 4 + 2 * CPW;
-  static_assert(CPW * S == G * HD && HD % CPW == 0 && S <= kWave && WPS % 2 == 0, "combine map");
+  constexpr int NOB = QW / 32;       // Q8_0 blocks of the attention output
+  static_assert(NCB * CPW == G * HD && HD % CPW == 0 && NCB <= S && S <= kWave && NOB % 2 == 0, "combine map");
   __shared__ unsigned s_pw[S * WPS];
+  __shared__ float s_att[CPW];
   __shared__ ArgBest s_best[kWavesP];
   __shared__ unsigned s_keys[2 * NWG];  // every workgroup's argmax key of the step (low, high halves)
   __shared__ u64 s_kmax[kWavesP];
@@ -780,46 +784,67 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         put_tagged_d(part, G * PWORDS, tid * PWORDS + 2 * HD, s_m[tid], T);
         put_tagged_d(part, G * PWORDS, tid * PWORDS + 2 * (HD + 1), s_l[tid], T);
       }
-      // ---- the combine of CPW outputs (query head ch, dims cd0 ..) over the
-      // S splits: O = sum_s w_s o_s / sum_s w_s l_s, w_s = exp(m_s - max m),
-      // each sum taken in split order
-      const int ch = (asplit * CPW) / HD, cd0 = (asplit * CPW) % HD;
-      {
-        const int pb = ag * S * G * PWORDS + ch * PWORDS;  // word offset of (split 0, head ch)
-        auto off = [&](int j) {
-          const int sp = (2 * j) / WPS, k = (2 * j) % WPS;
-          return pb + sp * G * PWORDS + (k < 4 ? 2 * HD + k : 2 * cd0 + (k - 4));
+      // ---- the combine of Q8_0 block asplit of the head group's outputs
+      // (query head ch, dims cd0 ..) over the S splits:
+      // O = sum_s w_s o_s / sum_s w_s l_s, w_s = exp(m_s - max m), each sum
+      // taken in split order.  The block leaves quantised: o_proj's prologue
+      // arithmetic, moved to the producer.
+      if (asplit < NCB) {
+        const int ch = (asplit * CPW) / HD, cd0 = (asplit * CPW) % HD;
+        {
+          const int pb = ag * S * G * PWORDS + ch * PWORDS;  // word offset of (split 0, head ch)
+          auto off = [&](int j) {
+            const int sp = (2 * j) / WPS, k = (2 * j) % WPS;
+            return pb + sp * G * PWORDS + (k < 4 ? 2 * HD + k : 2 * cd0 + (k - 4));
+          };
+          auto dst = [&](int i) { return s_pw + i; };
+          if (!poll_pairs<S * WPS / 2>(a.part, NKV * S * G * PWORDS, off, dst, T, a.err)) goto fail;
+        }
+        auto pw_d = [&](int sp, int k) {  // the f64 at words k, k + 1 of split sp
+          return __hiloint2double((int)s_pw[sp * WPS + k + 1], (int)s_pw[sp * WPS + k]);
         };
-        auto dst = [&](int i) { return s_pw + i; };
-        if (!poll_pairs<S * WPS / 2>(a.part, NKV * S * G * PWORDS, off, dst, T, a.err)) goto fail;
-      }
-      auto pw_d = [&](int sp, int k) {  // the f64 at words k, k + 1 of split sp
-        return __hiloint2double((int)s_pw[sp * WPS + k + 1], (int)s_pw[sp * WPS + k]);
-      };
-      {  // thread (k, sp) takes split sp's term of output k.  Every group of S
-         // lanes holds all splits, so it forms the weights and L itself (no
-         // exchange through LDS and no barrier); the group sums are the same
-         // trees as a wavefront sum over S live lanes.
-        static_assert(CPW * S <= NT && (S == 16 || S == 32), "combine threads");
-        const int sp = tid % S, k = tid / S;
-        const double ms = pw_d(sp, 0);
-        const double M = group_max_all_d<S>(ms);
-        const double wgt = ms != -INFINITY ? exp(ms - M) : 0.0;
-        const double L = group_sum_d<S>(wgt * pw_d(sp, 2));
-        double v = k < CPW ? wgt * pw_d(sp, 4 + 2 * k) : 0.0;
-        v = group_sum_d<S>(v);
-        if (k < CPW && sp == S - 1) put_tagged(a.att + (ag * G + ch) * HD + cd0 + k, (float)(v / L), T);
+        {  // thread (kk, sp) takes split sp's terms of outputs kk, kk + NT / S, ...
+           // Every group of S lanes holds all splits, so it forms the weights
+           // and L itself; the group sums are the same trees as a wavefront
+           // sum over S live lanes.
+          static_assert((S == 16 || S == 32) && CPW % (NT / S) == 0, "combine threads");
+          const int sp = tid % S, kk = tid / S;
+          const double ms = pw_d(sp, 0);
+          const double M = group_max_all_d<S>(ms);
+          const double wgt = ms != -INFINITY ? exp(ms - M) : 0.0;
+          const double L = group_sum_d<S>(wgt * pw_d(sp, 2));
+#pragma unroll
+          for (int i = 0; i < CPW / (NT / S); ++i) {
+            const int k = kk + i * (NT / S);
+            const double v = group_sum_d<S>(wgt * pw_d(sp, 4 + 2 * k));
+            if (sp == S - 1) s_att[k] = (float)(v / L);
+          }
+        }
+        __syncthreads();
+        if (tid < 8) {  // one 8-lane group: lane t quantises outputs 4t .. 4t+3
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = s_att[4 * tid + i];
+          float d;
+          const int packed = quant4_group8(v, &d);
+          u64* ob = a.att + (ag * NCB + asplit) * 9;
+          put_tagged(ob + tid, __int_as_float(packed), T);
+          if (tid == 0) put_tagged(ob + 8, f16_round(d), T);
+        }
       }
     }
-
 
     // ---- C: o_proj + residual ----------------------------------------------------
     {
       wC.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
       if (b < NUB) wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; }, 0, 1);
-      if (!poll_quantize<QW, false>(a.att, T, s_x, static_cast<const NormW<QW>*>(nullptr), eps, s_qa, s_da, s_red,
-                                    a.err))
-        goto fail;
+      {  // the attention output arrives quantised: 8 words of four codes and a
+         // scale word per block
+        unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
+        unsigned* da = reinterpret_cast<unsigned*>(s_da);
+        auto dst = [&](int i) { return (i % 9) < 8 ? qa + (i / 9) * 8 + (i % 9) : da + i / 9; };
+        if (!poll_pairs<9 * NOB / 2>(a.att, 9 * NOB, [](int j) { return 2 * j; }, dst, T, a.err)) goto fail;
+      }
       wC.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xkeep[lr] + (float)acc;
         put_tagged(a.xc + b * RC + lr, xn, T);
