@@ -74,6 +74,38 @@ QDEV bool block_failed(bool wave_bad) {  // wave_bad is wavefront-uniform
   return any != 0;
 }
 
+// One wavefront's wait: rounds of loads (issue(j, r) loads slot j < PER of
+// this thread into r) until every word carries `tag`; the words end in v.
+// A slot whose pair has arrived is not read again (its tag cannot change
+// before every reader of this epoch is done), so a round only fetches what
+// is still missing.  False at the spin limit (the error word is then set) or
+// when another workgroup has reported an error (checked every 64 rounds).
+template <int PER, typename Issue>
+QDEV bool poll_wave(Issue issue, unsigned tag, unsigned* err, v4u (&v)[PER]) {
+  bool have[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) have[j] = false;
+  for (int spin = 0;; ++spin) {
+    // every load of the round is issued before any is checked, so one wait
+    // covers them all
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (!have[j]) issue(j, v[j]);
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      have[j] = have[j] || (v[j].y == tag && v[j].w == tag);
+      ok = ok && have[j];
+    }
+    if (__all(ok)) return true;
+    if ((spin & 63) == 63 && wave_error(err)) return false;
+    if (spin == kSpin) {
+      if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+}
+
 // Wait until the 2 * NPAIR words of the pairs at word offsets off(j) (even)
 // of base[0, nwords) all carry `tag`; then the 32-bit payload of word
 // 2j + h goes to *dst(2j + h).  False when the spin limit is reached or
@@ -83,30 +115,13 @@ QDEV bool poll_pairs(const u64* base, int nwords, Off off, Dst dst, unsigned tag
   constexpr int PER = (NPAIR + NT - 1) / NT;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(base), 0, nwords * 8, 0x00020000);
+  // slots past NPAIR re-read the last pair
+  auto issue = [&](int j, v4u& r) {
+    const int i = min((int)threadIdx.x + j * NT, NPAIR - 1);
+    r = __builtin_amdgcn_raw_buffer_load_b128(rs, off(i) * 8, 0, kCoherent);
+  };
   v4u v[PER];
-  bool bad = false;
-  for (int spin = 0;; ++spin) {
-    // every load of the round is issued before any is checked, so one wait
-    // covers them all; slots past NPAIR re-read the last pair
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = min((int)threadIdx.x + j * NT, NPAIR - 1);
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off(i) * 8, 0, kCoherent);
-    }
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) ok = ok && v[j].y == tag && v[j].w == tag;
-    if (__all(ok)) break;
-    if ((spin & 63) == 63 && wave_error(err)) {
-      bad = true;
-      break;
-    }
-    if (spin == kSpin) {
-      if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bad = true;
-      break;
-    }
-  }
+  const bool bad = !poll_wave<PER>(issue, tag, err, v);
   if (block_failed(bad)) return false;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -136,28 +151,12 @@ QDEV bool poll_vec_regs(const u64* src, unsigned tag, float (&x)[N / NT], unsign
   static_assert(N % (4 * NT) == 0, "whole passes of four words per thread");
   constexpr int PER = N / (2 * NT);  // pairs per thread
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u64*>(src), 0, N * 8, 0x00020000);
+  auto issue = [&](int j, v4u& r) {
+    const int pair = (j / 2) * (2 * NT) + 2 * (int)threadIdx.x + (j % 2);
+    r = __builtin_amdgcn_raw_buffer_load_b128(rs, pair * 16, 0, kCoherent);
+  };
   v4u v[PER];
-  bool bad = false;
-  for (int spin = 0;; ++spin) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int pair = (j / 2) * (2 * NT) + 2 * (int)threadIdx.x + (j % 2);
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, pair * 16, 0, kCoherent);
-    }
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) ok = ok && v[j].y == tag && v[j].w == tag;
-    if (__all(ok)) break;
-    if ((spin & 63) == 63 && wave_error(err)) {
-      bad = true;
-      break;
-    }
-    if (spin == kSpin) {
-      if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bad = true;
-      break;
-    }
-  }
+  const bool bad = !poll_wave<PER>(issue, tag, err, v);
   if (block_failed(bad)) return false;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
