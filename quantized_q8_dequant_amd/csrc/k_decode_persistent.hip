@@ -135,6 +135,36 @@ QDEV bool poll_pairs(const u64* base, int nwords, Off off, Dst dst, unsigned tag
   return true;
 }
 
+// A Q8_0 block handed over quantised: 8 words of four codes, then the
+// f16-valued scale in words 8 and 9 (one pair), padded to a 128-byte line so
+// that no two workgroups write into one line (a shared partial line was seen
+// much later by the readers).
+constexpr int kBlockWords = 16;
+constexpr int kBlockPairs = 5;
+// Lane t < 8 of one 8-lane group stores code word t; lane 0 also the scale.
+QDEV void put_block(u64* blk, int packed, float d16, unsigned tag) {
+  const int t = threadIdx.x % 8;
+  put_tagged(blk + t, __int_as_float(packed), tag);
+  if (t == 0) {
+    put_tagged(blk + 8, d16, tag);
+    put_tagged(blk + 9, d16, tag);
+  }
+}
+// Wait for the NB blocks at base, then their codes go to s_qa (block-major)
+// and their scales to s_da.
+template <int NB>
+QDEV bool poll_blocks(const u64* base, unsigned tag, int8_t* s_qa, float* s_da, unsigned* err) {
+  __shared__ unsigned s_spare;
+  unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
+  unsigned* da = reinterpret_cast<unsigned*>(s_da);
+  auto off = [](int j) { return (j / kBlockPairs) * kBlockWords + 2 * (j % kBlockPairs); };
+  auto dst = [&](int i) {
+    const int blk = i / (2 * kBlockPairs), w = i % (2 * kBlockPairs);
+    return w < 8 ? qa + blk * 8 + w : w == 8 ? da + blk : &s_spare;
+  };
+  return poll_pairs<NB * kBlockPairs>(base, NB * kBlockWords, off, dst, tag, err);
+}
+
 // The N (even) contiguous words at src into dst (LDS) as floats.
 template <int N>
 QDEV bool poll_vec(const u64* src, unsigned tag, float* dst, unsigned* err) {
@@ -826,9 +856,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
           for (int i = 0; i < 4; ++i) v[i] = s_att[4 * tid + i];
           float d;
           const int packed = quant4_group8(v, &d);
-          u64* ob = a.att + (ag * NCB + asplit) * 9;
-          put_tagged(ob + tid, __int_as_float(packed), T);
-          if (tid == 0) put_tagged(ob + 8, f16_round(d), T);
+          put_block(a.att + (ag * NCB + asplit) * kBlockWords, packed, f16_round(d), T);
         }
       }
     }
@@ -837,13 +865,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     {
       wC.load(P.o_qs, P.o_sc, [&](int lr) { return b * RC + lr; });
       if (b < NUB) wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; }, 0, 1);
-      {  // the attention output arrives quantised: 8 words of four codes and a
-         // scale word per block
-        unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
-        unsigned* da = reinterpret_cast<unsigned*>(s_da);
-        auto dst = [&](int i) { return (i % 9) < 8 ? qa + (i / 9) * 8 + (i % 9) : da + i / 9; };
-        if (!poll_pairs<9 * NOB / 2>(a.att, 9 * NOB, [](int j) { return 2 * j; }, dst, T, a.err)) goto fail;
-      }
+      // the attention output arrives quantised
+      if (!poll_blocks<NOB>(a.att, T, s_qa, s_da, a.err)) goto fail;
       wC.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xkeep[lr] + (float)acc;
         put_tagged(a.xc + b * RC + lr, xn, T);
@@ -854,8 +877,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     // ---- D: gate/up + SwiGLU + the Q8_0 quantisation of h.  Workgroup u < F/32
     // owns FFN block u: gate rows 64u .. 64u+31 and up rows 64u+32 .. 64u+63 of
     // the interleaved matrix.  h leaves already quantised (the down
-    // projection's prologue arithmetic): 8 words of four codes, then one word
-    // with the f16-valued block scale.
+    // projection's prologue arithmetic) as one padded block (put_block).
     if (b < NUB) {
       wD.load(P.gu_qs, P.gu_sc, [&](int lr) { return b * 64 + lr; }, 1, SD::PASSES);
       NormW<H> nw;
@@ -873,8 +895,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
         for (int i = 0; i < 4; ++i) v[i] = s_gu[64 + 4 * tid + i];
         float d;
         const int packed = quant4_group8(v, &d);
-        put_tagged(a.h + b * 9 + tid, __int_as_float(packed), T);
-        if (tid == 0) put_tagged(a.h + b * 9 + 8, f16_round(d), T);
+        put_block(a.h + b * kBlockWords, packed, f16_round(d), T);
       }
     }
 
@@ -882,13 +903,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     {
       wE.load(P.dn_qs, P.dn_sc, [&](int lr) { return b * RC + lr; });
       if (l + 1 < a.L) prefetch_layer(l + 1);
-      {
-        unsigned* qa = reinterpret_cast<unsigned*>(s_qa);
-        unsigned* da = reinterpret_cast<unsigned*>(s_da);
-        auto dst = [&](int i) { return (i % 9) < 8 ? qa + (i / 9) * 8 + (i % 9) : da + i / 9; };
-        static_assert(NUB % 2 == 0, "pairs of h words");
-        if (!poll_pairs<9 * NUB / 2>(a.h, 9 * NUB, [](int j) { return 2 * j; }, dst, T, a.err)) goto fail;
-      }
+      if (!poll_blocks<NUB>(a.h, T, s_qa, s_da, a.err)) goto fail;
       wE.compute(s_qa, s_da, [&](int lr, double acc) {
         const float xn = s_xckeep[lr] + (float)acc;
         put_tagged(a.xa + b * RC + lr, xn, T + 1u);

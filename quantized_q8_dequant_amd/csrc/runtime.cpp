@@ -298,8 +298,8 @@ int plan(qwen3_model* m, uint8_t* base, size_t* total) {
     m->p_xa = cv.arr<unsigned long long>(H);
     m->p_xc = cv.arr<unsigned long long>(H);
     m->p_qkv = cv.arr<unsigned long long>(nqkv);
-    m->p_att = cv.arr<unsigned long long>(qw / 32 * 9);  // Q8_0 blocks: 8 code words and a scale word each
-    m->p_h = cv.arr<unsigned long long>(F);
+    m->p_att = cv.arr<unsigned long long>(qw / 32 * 16);  // Q8_0 blocks of 16 words (codes, scale, padding)
+    m->p_h = cv.arr<unsigned long long>(F / 32 * 16);  // Q8_0 blocks of 16 words
     m->p_part = cv.arr<unsigned long long>(persist_part_words(G, hd));
     m->p_err = cv.arr<unsigned>(1);
     m->p_keys = cv.arr<unsigned long long>(2 * kPersistWorkgroups);
@@ -801,8 +801,8 @@ int qwen3_create(const qwen3_config* cfg, const qwen3_weights* w, void* d_worksp
       HIP_TRY(hipMemsetAsync(m->p_xa, 0, (size_t)m->H * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_xc, 0, (size_t)m->H * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_qkv, 0, (size_t)m->nqkv * 8, s));
-      HIP_TRY(hipMemsetAsync(m->p_att, 0, (size_t)m->qw / 32 * 9 * 8, s));
-      HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_att, 0, (size_t)m->qw / 32 * 16 * 8, s));
+      HIP_TRY(hipMemsetAsync(m->p_h, 0, (size_t)m->F / 32 * 16 * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_part, 0, persist_part_words(m->G, m->hd) * 8, s));
       HIP_TRY(hipMemsetAsync(m->p_err, 0, 4, s));
       HIP_TRY(hipMemsetAsync(m->p_keys, 0, 2 * kPersistWorkgroups * 8, s));
