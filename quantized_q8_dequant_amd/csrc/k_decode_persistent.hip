@@ -841,12 +841,21 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
           const double ms = pw_d(sp, 0);
           const double M = group_max_all_d<S>(ms);
           const double wgt = ms != -INFINITY ? exp(ms - M) : 0.0;
+          // all sums first, then the divisions, then one guarded store, so
+          // the trees and the divisions of the outputs overlap
+          constexpr int KPT = CPW / (NT / S);  // outputs per thread
+          double v[KPT];
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) v[i] = wgt * pw_d(sp, 4 + 2 * (kk + i * (NT / S)));
           const double L = group_sum_d<S>(wgt * pw_d(sp, 2));
 #pragma unroll
-          for (int i = 0; i < CPW / (NT / S); ++i) {
-            const int k = kk + i * (NT / S);
-            const double v = group_sum_d<S>(wgt * pw_d(sp, 4 + 2 * k));
-            if (sp == S - 1) s_att[k] = (float)(v / L);
+          for (int i = 0; i < KPT; ++i) v[i] = group_sum_d<S>(v[i]);
+          float o[KPT];
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) o[i] = (float)(v[i] / L);
+          if (sp == S - 1) {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) s_att[kk + i * (NT / S)] = o[i];
           }
         }
         __syncthreads();
