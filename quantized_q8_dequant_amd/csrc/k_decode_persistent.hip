@@ -78,26 +78,33 @@ QDEV bool block_failed(bool wave_bad) {  // wave_bad is wavefront-uniform
 // this thread into r) until every word carries `tag`; the words end in v.
 // A slot whose pair has arrived is not read again (its tag cannot change
 // before every reader of this epoch is done), so a round only fetches what
-// is still missing.  False at the spin limit (the error word is then set) or
-// when another workgroup has reported an error (checked every 64 rounds).
+// is still missing; and while none of the wavefront's pairs has arrived, a
+// round reads one pair only.  The device-coherent reads go to the memory
+// side, where they compete with the weight streams.  False at the spin limit
+// (the error word is then set) or when another workgroup has reported an
+// error (checked every 64 rounds).
 template <int PER, typename Issue>
 QDEV bool poll_wave(Issue issue, unsigned tag, unsigned* err, v4u (&v)[PER]) {
   bool have[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) have[j] = false;
+  bool started = true;  // the first round reads every pair
   for (int spin = 0;; ++spin) {
     // every load of the round is issued before any is checked, so one wait
-    // covers them all
+    // covers them all.  While none of the wavefront's pairs has arrived, a
+    // round re-reads only one pair (slot 0 of lane 0)
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if (!have[j]) issue(j, v[j]);
-    bool ok = true;
+      if (!have[j] && (started || (j == 0 && threadIdx.x % kWave == 0))) issue(j, v[j]);
+    bool ok = true, any = false;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       have[j] = have[j] || (v[j].y == tag && v[j].w == tag);
       ok = ok && have[j];
+      any = any || have[j];
     }
     if (__all(ok)) return true;
+    started = __any(any);
     if ((spin & 63) == 63 && wave_error(err)) return false;
     if (spin == kSpin) {
       if (threadIdx.x % kWave == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
