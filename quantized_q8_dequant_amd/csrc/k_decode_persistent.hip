@@ -532,10 +532,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
   // the largest) is split: its first pass is requested with the o_proj
   // slice, ahead of that wait, its second at its own phase.  The other
   // slices are requested just before their own phase's wait, and the KV
-  // tiles at the start of their layer.  (Measured: issuing the whole gate/up
-  // slice, or the o_proj or down slices, a phase early was slower: those
-  // windows already carry the phase's own traffic, and the wait is then held
-  // until the early slice has arrived.)
+  // tiles once the QKV phase has its input (ahead of that phase's compute,
+  // not of its wait).  (Measured: issuing the whole gate/up slice, or the
+  // o_proj or down slices, a phase early was slower: those windows already
+  // carry the phase's own traffic, and the wait is then held until the
+  // early slice has arrived.)
   using SA = Slice<H, RA, (H / 32 >= 32 && RA >= 16 ? 16 : 0)>;
   using SC = Slice<QW, RC>;
   using SD = Slice<H, 64, (H / 32 >= 32 ? 8 : 0)>;
@@ -594,17 +595,16 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs a) {
     const PLayer P = a.layers[l];
     const int64_t kbase = kbase_of(l);
     const int64_t vbase = kbase + (int64_t)NKV * head_elems;
-    // the attention split's first two tiles
-    if (attn_unit && nt > 0) {
-      stream_load(tA, 0, kbase);
-      stream_load(tB, 1, kbase);
-    }
 
     // ---- A: QKV projection --------------------------------------------------
     {
       NormW<H> nw;
       nw.load(P.attn_norm);
       if (!poll_quantize<H, true>(a.xa, T, s_x, &nw, eps, s_qa, s_da, s_red, a.err)) goto fail;
+      if (attn_unit && nt > 0) {
+        stream_load(tA, 0, kbase);
+        stream_load(tB, 1, kbase);
+      }
       wA.compute(s_qa, s_da, [&](int lr, double acc) { put_tagged(a.qkv + b * RA + lr, (float)acc, T); });
     }
 
