@@ -20,7 +20,8 @@
 // agent-coherent store; a reader polls the words it needs until all carry
 // the epoch it expects, so the data is its own flag and no barrier or fence
 // is used.  A phase issues the loads of its weight slice before it starts
-// polling, so HBM streams while the workgroup waits.  Each buffer is
+// polling, so HBM streams while the workgroup waits (the placement of each
+// slice and of the KV tiles is given where the slices are declared).  Each buffer is
 // written once per layer with a new epoch, and the phase order guarantees
 // that every reader of one epoch has finished before the next is written.
 //
@@ -49,7 +50,7 @@ QDEV void put_tagged(u64* p, float v, unsigned tag) {
 }
 QDEV unsigned ld_err(const unsigned* err) { return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-// Polling.  A poll round re-reads every word it waits for with
+// Polling.  A poll round re-reads the words it still waits for with
 // device-coherent loads, and on this chip the cost of such a round grows with
 // the number of load instructions, not with bytes: each load here takes two
 // adjacent tagged words (16 bytes) through a buffer resource whose bounds
