@@ -14,9 +14,12 @@
 // Grid (nsplit_max, nkv, nrows): workgroup (split, g, row) serves the G query
 // heads of KV head g, so each K/V row is read once for all of them.  The
 // positions [0, p] are cut into min(nsplit_max, ceil((p+1)/min_rows)) equal
-// ranges; each workgroup keeps an online softmax (running max m, sum l,
-// unnormalised o) and writes it as a partial; the last workgroup to arrive
-// (atomic counter) merges the partials and writes the normalised output.
+// ranges; each workgroup computes its range's max m, sum l and unnormalised
+// o (scores in LDS, one softmax, then P.V) and writes them as a partial; the
+// last workgroup to arrive (atomic counter) merges the partials and writes
+// the normalised output.  Within a workgroup a thread serves up to four
+// query heads at once, so each K or V element is read from LDS and widened
+// to f64 once for all of them.
 // The position is read on the device, so a captured graph replays unchanged.
 #include "kernels.h"
 #include "qdevice.h"
@@ -40,6 +43,56 @@ constexpr int kCombineRegs = 80; // f64 partial values a thread of the combine h
 
 template <int G, int HD>
 constexpr int direct_slots() { return G * HD; }
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+// cache policy of the partials' 16-byte loads and stores: device scope (sc1),
+// the policy of the agent-scope atomic loads and stores
+constexpr int kCoherent = 16;
+
+// The value of the lane whose index differs in bit M (M = 1, 2, 4, 8 with
+// DPP moves inside a row of 16 lanes: the partner differs in bit M and
+// possibly in lower bits, never in higher ones; otherwise an exact xor
+// through the LDS permute).
+template <int M, bool DPP>
+QDEV double partner_d(double v) {
+  if constexpr (DPP && M == 1) return dpp_move_d<0xB1>(v);   // quad_perm [1,0,3,2]
+  else if constexpr (DPP && M == 2) return dpp_move_d<0x4E>(v);  // quad_perm [2,3,0,1]
+  else if constexpr (DPP && M == 4) return dpp_move_d<0x141>(v);  // row_half_mirror
+  else if constexpr (DPP && M == 8) return dpp_move_d<0x140>(v);  // row_mirror
+  else return __shfl_xor(v, M);
+}
+
+// Sums of V slots over a group of NL lanes (lane masks M * S for M < NL),
+// scattered: each halving step keeps the upper or lower half of the slots
+// by the lane's bit M and adds the partner's values for that half, so that
+// afterwards group member p holds in v[0 .. V/W - 1] (W = min(V, NL)) the
+// totals of slots (p / (NL / W)) * (V / W) + u; when V < NL the last steps
+// add whole totals, so the NL / W members of a block agree.
+template <int M, int N, int NL, int V, int S, bool DPP>
+QDEV void scatter_steps(double (&v)[V], int p) {
+  constexpr int W = V < NL ? V : NL;
+  if constexpr (M >= 1) {
+    if constexpr (N > V / W) {
+      constexpr int H = N / 2;
+      const bool up = (p & M) != 0;
+#pragma unroll
+      for (int u = 0; u < H; ++u) {
+        const double send = up ? v[u] : v[u + H];
+        const double keep = up ? v[u + H] : v[u];
+        v[u] = keep + partner_d<M * S, DPP>(send);
+      }
+      scatter_steps<M / 2, H, NL, V, S, DPP>(v, p);
+    } else {
+      v[0] += partner_d<M * S, DPP>(v[0]);
+      scatter_steps<M / 2, N, NL, V, S, DPP>(v, p);
+    }
+  }
+}
+template <int NL, int V, int S, bool DPP>
+QDEV void scatter_sum_d(double (&v)[V], int p) {
+  scatter_steps<NL / 2, V, NL, V, S, DPP>(v, p);
+}
 
 // One tile of K or V rows staged through registers: every thread issues all
 // of its 16-byte loads for a tile at once; two tiles are in flight ahead of
@@ -126,19 +179,35 @@ QDEV void norm_rope_pair(float xa, float xb, float wa, float wb, double c, doubl
 template <int HD, int G, int KVT>
 __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   constexpr int TJ = kTileRows<KVT>;
-  // scores: thread -> (head h, d-part pt, row group rg of RPT rows); part pt
-  // holds dims 4*pt + 4*NP*i + c (c < 4), interleaved so that the float4
-  // reads of 16 lanes (4 rows x 4 parts, rows 132 or 68 floats apart) fall
-  // on distinct LDS banks; the thread keeps its q dims in f64 registers
-  constexpr int NP = (G == 1) ? 8 : 4;
+  // A thread serves HG query heads at once: each K or V element it reads
+  // from LDS is widened to f64 once and feeds HG products.
+  constexpr int HG = G < 4 ? G : 4;  // query heads per thread
+  constexpr int NHG = G / HG;        // head groups
+  // scores: thread -> (head group, row group rg of RPT consecutive rows,
+  // d-part pt); part pt holds dims 4*pt + 4*NP*i + c (c < 4), so the float4
+  // reads of 8 consecutive lanes cover 128 consecutive bytes of one row (no
+  // LDS bank conflict); the thread keeps the q dims of its heads in f64
+  // registers and its HG x RPT partial dots are summed over the NP parts
+  // scattered (one total per lane)
+  constexpr int NP = cmax(cmax(8, HG * HD / 32), kThreads / (NHG * TJ));
   constexpr int DPP = HD / NP;
-  constexpr int RPT = TJ * G * NP / kThreads;
-  constexpr int RG = TJ / RPT;  // row groups
-  static_assert(RPT >= 1 && RPT * kThreads == TJ * G * NP, "score map");
-  // outputs: thread -> (head, DPT consecutive dims); threads >= OUT_T idle
-  constexpr int DPT = (G * HD / kThreads) > 0 ? G * HD / kThreads : 1;
-  constexpr int OUT_T = G * HD / DPT;
-  constexpr int TPH = HD / DPT;  // output threads per head
+  constexpr int RG = kThreads / (NHG * NP);  // row groups
+  constexpr int RPT = TJ / RG;
+  constexpr int SV = HG * RPT;  // partial dots per thread, slot j * HG + k
+  constexpr int SW = SV < NP ? SV : NP;
+  static_assert(DPP % 4 == 0 && RPT >= 1 && NHG * NP * RG == kThreads && RG * RPT == TJ, "score map");
+  // P.V: thread -> (head group, row group of RPV consecutive rows, d-chunk
+  // dc); chunk dc holds dims 4*dc + 4*DC*i + c, the thread sums w_j V_j of
+  // its rows for its HG heads; the row groups' sums are added once per split
+  constexpr int DPV = cmin(cmin(16 / HG > 4 ? 16 / HG : 4, HD * NHG * TJ / kThreads), HD / 8);
+  constexpr int DC = HD / DPV;
+  constexpr int RGV = kThreads / (NHG * DC);
+  constexpr int RPV = TJ / RGV;
+  constexpr int OV = HG * DPV;    // sums per thread, slot k * DPV + i
+  constexpr int RW = kWave / DC;  // row groups per wavefront
+  constexpr int OW = OV < RW ? OV : RW;
+  constexpr int WPG = kWaves / NHG;  // wavefronts per head group
+  static_assert(DPV % 4 == 0 && RPV >= 1 && NHG * DC * RGV == kThreads && RGV * RPV == TJ && RW >= 1, "P.V map");
   constexpr int MAXR = kScoreSlots / G;  // rows per split
   __shared__ float s_qf[G][HD];
   __shared__ float s_knew[HD];
@@ -281,17 +350,18 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     }
   }
 
-  // this thread's score role and q slice (f64)
-  const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_h = tid / (NP * RG);
-  double qreg[DPP];
+  // this thread's score role and the q dims of its heads (f64)
+  const int sc_pt = tid % NP, sc_rg = (tid / NP) % RG, sc_hg = tid / (NP * RG);
+  double qreg[HG][DPP];
 #pragma unroll
-  for (int i = 0; i < DPP; ++i) qreg[i] = (double)s_qf[sc_h][4 * sc_pt + 4 * NP * (i / 4) + (i % 4)];
-  // this thread's outputs
-  const bool out_live = tid < OUT_T;
-  const int o_h = out_live ? tid / TPH : 0, o_d = out_live ? (tid % TPH) * DPT : 0;
-  double o[DPT];
+  for (int k = 0; k < HG; ++k)
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) o[i] = 0.0;
+    for (int i = 0; i < DPP; ++i) qreg[k][i] = (double)s_qf[sc_hg * HG + k][4 * sc_pt + 4 * NP * (i / 4) + (i % 4)];
+  // this thread's P.V role and sums
+  const int pv_dc = tid % DC, pv_rg = (tid / DC) % RGV, pv_hg = tid / (DC * RGV);
+  double pv[OV];
+#pragma unroll
+  for (int i = 0; i < OV; ++i) pv[i] = 0.0;
   const double scale = a.scale;
 
   // softmax over the split's scores, once (f64): s_s becomes exp(s - m)
@@ -334,49 +404,58 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
     }
     __syncthreads();
     if (!isv) {
+      double acc[SV];
+#pragma unroll
+      for (int v = 0; v < SV; ++v) acc[v] = 0.0;
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
-        const int r = sc_rg * RPT + j;
-        const float* kr = &s_t[r][4 * sc_pt];
-        double acc = 0.0;
+        const float* kr = &s_t[sc_rg * RPT + j][4 * sc_pt];
 #pragma unroll
         for (int d = 0; d < DPP; d += 4) {
           const float4 k4 = *reinterpret_cast<const float4*>(kr + NP * d);
-          acc += qreg[d] * (double)k4.x;
-          acc += qreg[d + 1] * (double)k4.y;
-          acc += qreg[d + 2] * (double)k4.z;
-          acc += qreg[d + 3] * (double)k4.w;
-        }
-        acc = group_sum_d<NP>(acc);
-        if (sc_pt == NP - 1 && r < nrow) s_s[sc_h][t0 - j0 + r] = acc * scale;
-      }
-    } else if (out_live) {
-      const double* pr = &s_s[o_h][t0 - j0];
-      auto pv_row = [&](int r) {
-        const double w = pr[r];
-        const float* vr = &s_t[r][o_d];
-        if (DPT == 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(vr);
-          o[0] += w * (double)v4.x;
-          o[DPT > 1 ? 1 : 0] += w * (double)v4.y;
-          o[DPT > 2 ? 2 : 0] += w * (double)v4.z;
-          o[DPT > 3 ? 3 : 0] += w * (double)v4.w;
-        } else if (DPT == 2) {
-          const float2 v2 = *reinterpret_cast<const float2*>(vr);
-          o[0] += w * (double)v2.x;
-          o[DPT > 1 ? 1 : 0] += w * (double)v2.y;
-        } else {
-          o[0] += w * (double)vr[0];
-        }
-      };
-      // full tiles unrolled, so the LDS reads of many rows are in flight
-      // together (row by row, each would wait out the LDS latency)
-      if (nrow == TJ) {
+          const double kx = k4.x, ky = k4.y, kz = k4.z, kw = k4.w;
 #pragma unroll
-        for (int r = 0; r < TJ; ++r) pv_row(r);
-      } else {
-#pragma unroll 8
-        for (int r = 0; r < nrow; ++r) pv_row(r);
+          for (int k = 0; k < HG; ++k) {
+            double& s = acc[j * HG + k];
+            s += qreg[k][d] * kx;
+            s += qreg[k][d + 1] * ky;
+            s += qreg[k][d + 2] * kz;
+            s += qreg[k][d + 3] * kw;
+          }
+        }
+      }
+      // rows past nrow hold stale values; their slots are never written
+      scatter_sum_d<NP, SV, 1, true>(acc, sc_pt);
+      if (sc_pt % (NP / SW) == 0) {
+#pragma unroll
+        for (int u = 0; u < SV / SW; ++u) {
+          const int v = (sc_pt / (NP / SW)) * (SV / SW) + u;
+          const int r = sc_rg * RPT + v / HG;
+          if (r < nrow) s_s[sc_hg * HG + v % HG][t0 - j0 + r] = acc[u] * scale;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPV; ++j) {
+        const int r = pv_rg * RPV + j;
+        if (r < nrow) {
+          double w[HG];
+#pragma unroll
+          for (int k = 0; k < HG; ++k) w[k] = s_s[pv_hg * HG + k][t0 - j0 + r];
+          const float* vr = &s_t[r][4 * pv_dc];
+#pragma unroll
+          for (int i = 0; i < DPV; i += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(vr + DC * i);
+            const double vx = v4.x, vy = v4.y, vz = v4.z, vw = v4.w;
+#pragma unroll
+            for (int k = 0; k < HG; ++k) {
+              pv[k * DPV + i] += w[k] * vx;
+              pv[k * DPV + i + 1] += w[k] * vy;
+              pv[k * DPV + i + 2] += w[k] * vz;
+              pv[k * DPV + i + 3] += w[k] * vw;
+            }
+          }
+        }
       }
     }
   };
@@ -396,29 +475,81 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   }
   __syncthreads();
 
+  // the P.V sums of the row groups: scattered over the row groups of each
+  // wavefront, then the WPG wavefronts of a head group through LDS (the
+  // score buffer, no longer read), added in wavefront order
+  scatter_sum_d<RW, OV, DC, false>(pv, lane / DC);
+  {
+    double* buf = &s_s[0][0];  // [WPG][G][HD]
+    const int rgw = lane / DC;
+    if (rgw % (RW / OW) == 0) {
+#pragma unroll
+      for (int u = 0; u < OV / OW; ++u) {
+        const int v = (rgw / (RW / OW)) * (OV / OW) + u;
+        const int k = v / DPV, ii = v % DPV;
+        const int d = 4 * pv_dc + DC * (ii / 4 * 4) + ii % 4;
+        buf[((wave % WPG) * G + pv_hg * HG + k) * HD + d] = pv[u];
+      }
+    }
+  }
+  __syncthreads();
+  // this split's o, in pairs of adjacent dims: pair pe of the E = G*HD
+  // outputs is dims 2pe, 2pe + 1 of head 2pe / HD (HD is even, so a pair
+  // never straddles two heads); thread tid owns pairs tid + 256k
+  constexpr int E = G * HD;
+  constexpr int P = E / 2;
+  constexpr int PPT = P >= kThreads ? P / kThreads : 1;  // pairs per thread
+  double o[PPT][2];
+#pragma unroll
+  for (int k = 0; k < PPT; ++k) {
+    const int pe = tid + k * kThreads;
+    double t0 = 0.0, t1 = 0.0;
+    if (pe < P) {
+      const double* buf = &s_s[0][0];
+      const int h = 2 * pe / HD, d = 2 * pe % HD;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) {
+        t0 += buf[(w * G + h) * HD + d];
+        t1 += buf[(w * G + h) * HD + d + 1];
+      }
+    }
+    o[k][0] = t0, o[k][1] = t1;
+  }
+
   // one split: its own o and l are the result (the combine below would
   // weigh it by exp(0) = 1 and divide by l, so the output is the same); o
   // goes through LDS to the combine's thread map, no memory round trip
   const bool direct = nsplit == 1;
   __shared__ double s_o[direct_slots<G, HD>()];
   if (direct) {
-    if (out_live) {
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) s_o[o_h * HD + o_d + i] = o[i];
+    for (int k = 0; k < PPT; ++k) {
+      const int pe = tid + k * kThreads;
+      if (pe < P) s_o[2 * pe] = o[k][0], s_o[2 * pe + 1] = o[k][1];
     }
     __syncthreads();
   }
 
-  // write this split's partial: [row][g][split][h][0..HD-1] = o, [HD] = m, [HD+1] = l
-  const int64_t pstride = (int64_t)G * (HD + 2);
-  double* part = a.part + (((int64_t)row * nkv + g) * a.nsplit_max + split) * pstride;
-  if (!direct && out_live) {
+  // write this split's partial: [row][g][split][h][0..HD-1] = o, [HD] = m,
+  // [HD+1] = l; every pair of doubles (o pairs, (m, l)) is one 16-byte store
+  // with the device-scope policy (16-byte aligned: HD + 2 and the split
+  // stride are even)
+  const int pstride = G * (HD + 2);
+  const int pbytes = a.nsplit_max * pstride * 8;  // one (row, KV head)'s partials
+  double* pb = a.part + ((int64_t)row * nkv + g) * a.nsplit_max * pstride;
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(pb, 0, pbytes, 0x00020000);
+  auto put2 = [&](int idx, double x, double y) {  // doubles idx, idx + 1 of split `split`
+    const v4u q = {(unsigned)__double2loint(x), (unsigned)__double2hiint(x), (unsigned)__double2loint(y),
+                   (unsigned)__double2hiint(y)};
+    __builtin_amdgcn_raw_buffer_store_b128(q, prs, (split * pstride + idx) * 8, 0, kCoherent);
+  };
+  if (!direct) {
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) st_coherent(part + o_h * (HD + 2) + o_d + i, o[i]);
-  }
-  if (!direct && tid < G) {
-    st_coherent(part + tid * (HD + 2) + HD, s_m[tid]);
-    st_coherent(part + tid * (HD + 2) + HD + 1, s_l[tid]);
+    for (int k = 0; k < PPT; ++k) {
+      const int pe = tid + k * kThreads;
+      if (pe < P) put2(2 * pe / HD * (HD + 2) + 2 * pe % HD, o[k][0], o[k][1]);
+    }
+    if (tid < G) put2(tid * (HD + 2) + HD, s_m[tid], s_l[tid]);
   }
   wait_memory();
   __syncthreads();
@@ -434,59 +565,59 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   if (!s_last) return;
   // combine the nsplit partials of the G heads (f64), rounded once to f32.
   // Every O load of a batch and the (m, l) loads are issued before any is
-  // used (one memory round trip); wave w takes heads w, w + 4, ... and lane s
-  // split s for the max and the weighted sum of l (nsplit <= 64 = lanes).
-  // Thread map: E = G*HD output dims; with E >= 256 a thread owns dims
-  // tid + 256k, otherwise dim tid % E for the splits = tid / E (mod NQ).
-  const double* pb = a.part + (((int64_t)row * nkv + g) * a.nsplit_max) * pstride;
-  constexpr int E = G * HD;
-  constexpr int NQ = E >= kThreads ? 1 : kThreads / E;   // split phases
-  constexpr int EPT = E >= kThreads ? E / kThreads : 1;  // dims per thread
-  constexpr int SB = kCombineRegs / EPT < kMaxSplit / NQ ? kCombineRegs / EPT : kMaxSplit / NQ;  // splits per thread per batch
+  // used (one memory round trip), 16 bytes (a pair) per load; wave w takes
+  // heads w, w + 4, ... and lane s split s for the max and the weighted sum
+  // of l (nsplit <= 64 = lanes).  Thread map: with P >= 256 pairs a thread
+  // owns pairs tid + 256k, otherwise pair tid % P for the splits
+  // = tid / P (mod NQ).
+  constexpr int NQ = P >= kThreads ? 1 : kThreads / P;  // split phases
+  constexpr int SB = cmin(kCombineRegs / (2 * PPT), kMaxSplit / NQ);  // splits per thread per batch
   const int cq = tid / (kThreads / NQ);
   const int ce = tid % (kThreads / NQ);
   __shared__ double s_w[G][kMaxSplit];
   __shared__ double s_L[G];
   __shared__ double s_red[NQ > 1 ? NQ : 1][NQ > 1 ? E : 1];
-  int64_t eoff[EPT];
-  int eh[EPT];
+  int poff[PPT], ph[PPT];
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int e = ce + k * kThreads;
-    eh[k] = e / HD;
-    eoff[k] = (int64_t)eh[k] * (HD + 2) + e % HD;
+  for (int k = 0; k < PPT; ++k) {
+    const int e0 = 2 * (ce + k * kThreads);
+    ph[k] = e0 / HD;
+    poff[k] = (ph[k] * (HD + 2) + e0 % HD) * 8;
   }
-  double O[EPT];
+  double O[PPT][2];
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) O[k] = 0.0;
+  for (int k = 0; k < PPT; ++k) O[k][0] = O[k][1] = 0.0;
+  auto lo_d = [](const v4u& v) { return __hiloint2double((int)v.y, (int)v.x); };
+  auto hi_d = [](const v4u& v) { return __hiloint2double((int)v.w, (int)v.z); };
   // batches of B splits per thread; B is the smallest of SB/4, SB/2, SB that
   // covers this thread's splits, so short caches issue few clamped repeats
   auto batches = [&](auto bsz) {
     constexpr int B = decltype(bsz)::value;
     for (int s0 = 0; s0 < nsplit; s0 += NQ * B) {
-      double v[B][EPT];
+      v4u v[B][PPT];
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const int sidx = min(s0 + cq + NQ * j, nsplit - 1);
 #pragma unroll
-        for (int k = 0; k < EPT; ++k) v[j][k] = ld_coherent(pb + sidx * pstride + eoff[k]);
+        for (int k = 0; k < PPT; ++k)
+          v[j][k] = __builtin_amdgcn_raw_buffer_load_b128(prs, sidx * pstride * 8 + poff[k], 0, kCoherent);
       }
       if (s0 == 0) {
         const int sl = min(lane, nsplit - 1);
-        double m[QH], l[QH];
+        v4u ml[QH];
 #pragma unroll
         for (int k = 0; k < QH; ++k) {
           const int h = min(wave + k * kWaves, G - 1);
-          m[k] = ld_coherent(pb + sl * pstride + h * (HD + 2) + HD);
-          l[k] = ld_coherent(pb + sl * pstride + h * (HD + 2) + HD + 1);
+          ml[k] = __builtin_amdgcn_raw_buffer_load_b128(prs, (sl * pstride + h * (HD + 2) + HD) * 8, 0, kCoherent);
         }
 #pragma unroll
         for (int k = 0; k < QH; ++k) {
           const int h = wave + k * kWaves;
           const bool live = lane < nsplit;
-          const double M = wave_max_all_d(live ? m[k] : -INFINITY);
-          const double w = live ? exp(m[k] - M) : 0.0;
-          const double L = wave_total_d(w * l[k]);
+          const double m = lo_d(ml[k]), l = hi_d(ml[k]);
+          const double M = wave_max_all_d(live ? m : -INFINITY);
+          const double w = live ? exp(m - M) : 0.0;
+          const double L = wave_total_d(w * l);
           if (h < G) {
             s_w[h][lane] = w;
             if (lane == 0) s_L[h] = L;
@@ -499,7 +630,11 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
         const int sidx = s0 + cq + NQ * j;
         if (sidx < nsplit) {
 #pragma unroll
-          for (int k = 0; k < EPT; ++k) O[k] += s_w[eh[k]][sidx] * v[j][k];
+          for (int k = 0; k < PPT; ++k) {
+            const double w = s_w[ph[k]][sidx];
+            O[k][0] += w * lo_d(v[j][k]);
+            O[k][1] += w * hi_d(v[j][k]);
+          }
         }
       }
     }
@@ -508,7 +643,10 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   if (direct) {
     if (cq == 0) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) O[k] = s_o[ce + k * kThreads];
+      for (int k = 0; k < PPT; ++k) {
+        const int e0 = 2 * (ce + k * kThreads);
+        O[k][0] = s_o[e0], O[k][1] = s_o[e0 + 1];
+      }
     }
     if (tid < G) s_L[tid] = s_l[tid];
     __syncthreads();
@@ -519,33 +657,39 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   else
     batches(std::integral_constant<int, SB>{});
   if (NQ > 1 && !direct) {
-    s_red[cq][ce] = O[0];
+    s_red[cq][2 * ce] = O[0][0];
+    s_red[cq][2 * ce + 1] = O[0][1];
     __syncthreads();
     if (cq == 0) {
-      double t = s_red[0][ce];
-      for (int q = 1; q < NQ; ++q) t += s_red[q][ce];
-      O[0] = t;
+      double t0 = s_red[0][2 * ce], t1 = s_red[0][2 * ce + 1];
+      for (int q = 1; q < NQ; ++q) t0 += s_red[q][2 * ce], t1 += s_red[q][2 * ce + 1];
+      O[0][0] = t0, O[0][1] = t1;
     }
   }
   if (cq == 0) {
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      const float y = (float)(O[k] / s_L[eh[k]]);
-      const int col = g * E + ce + k * kThreads;
-      a.out[(int64_t)row * a.out_stride + col] = y;
+    for (int k = 0; k < PPT; ++k) {
+      const int col = g * E + 2 * (ce + k * kThreads);
+      const float y0 = (float)(O[k][0] / s_L[ph[k]]);
+      const float y1 = (float)(O[k][1] / s_L[ph[k]]);
+      float* dst = a.out + (int64_t)row * a.out_stride + col;
+      dst[0] = y0;
+      dst[1] = y1;
       if (a.q_out) {
         // Q8_0 of the output row, block by block: a block's 32 values sit
-        // in 32 consecutive lanes (E and g * E are multiples of 32); the
-        // arithmetic is k_rows_quant's (max over the block, d = amax / 127,
-        // codes rint(v / d) clamped, scale rounded to f16)
-        float am = fabsf(y);
+        // in 16 consecutive lanes, two each (E and g * E are multiples of
+        // 32); the arithmetic is k_rows_quant's (max over the block,
+        // d = amax / 127, codes rint(v / d) clamped, scale rounded to f16)
+        float am = fmaxf(fabsf(y0), fabsf(y1));
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
         const float d = am / 127.0f;
         const float inv = d == 0.f ? 0.f : 1.0f / d;
-        const float q = fminf(fmaxf(rintf(y * inv), -127.f), 127.f);
+        const float q0 = fminf(fmaxf(rintf(y0 * inv), -127.f), 127.f);
+        const float q1 = fminf(fmaxf(rintf(y1 * inv), -127.f), 127.f);
         const int64_t bi = (int64_t)(col / 32) * gridDim.z + row;
-        a.q_out[bi * 32 + col % 32] = (int8_t)(int)q;
+        a.q_out[bi * 32 + col % 32] = (int8_t)(int)q0;
+        a.q_out[bi * 32 + col % 32 + 1] = (int8_t)(int)q1;
         if (col % 32 == 0) a.q_scale[bi] = f16_round(d);
       }
     }
