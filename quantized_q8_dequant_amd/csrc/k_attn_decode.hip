@@ -11,10 +11,12 @@
 //   for query head h reading KV head g = h / (nh/nkv) (section 12.3.5):
 //     s_j = (q_h . K_j) / sqrt(hd) over j <= p, softmax, o_h = sum_j w_j V_j.
 //
-// Grid (nsplit_max, nkv, nrows): workgroup (split, g, row) serves the G query
-// heads of KV head g, so each K/V row is read once for all of them.  The
-// positions [0, p] are cut into min(nsplit_max, ceil((p+1)/min_rows)) equal
-// ranges; each workgroup computes its range's max m, sum l and unnormalised
+// Grid (nkv, nsplit_max, nrows): workgroup (g, split, row) serves the G query
+// heads of KV head g, so each K/V row is read once for all of them; the KV
+// head varies fastest, so the workgroups dispatched first (which run ahead
+// of those sharing their CU) hold splits of every head.  The positions
+// [0, p] are cut into about min(nsplit_max, ceil((p+1)/min_rows)) ranges of
+// whole tiles; each workgroup computes its range's max m, sum l and unnormalised
 // o (scores in LDS, one softmax, then P.V) and writes them as a partial; the
 // last workgroup to arrive (atomic counter) merges the partials and writes
 // the normalised output.  Within a workgroup a thread serves up to four
@@ -218,7 +220,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   __shared__ double s_l[G];
   __shared__ int s_last;
 
-  const int split = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
+  const int g = blockIdx.x, split = blockIdx.y, row = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int seq = a.row_seq ? a.row_seq[row] : 0;
   const int p = a.len[seq];
@@ -227,8 +229,13 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
   if (nsplit > a.nsplit_max) nsplit = a.nsplit_max;
   const int need = (ctx + MAXR - 1) / MAXR;  // the host keeps ctx <= kMaxSplit * MAXR
   if (nsplit < need) nsplit = need;
+  // whole tiles per split: the range rounded up to a multiple of TJ rows and
+  // the count recomputed (no more tile steps per split, fewer splits, so
+  // fewer partials to combine); still at most MAXR rows, a multiple of TJ
+  int chunk = (ctx + nsplit - 1) / nsplit;
+  chunk = (chunk + TJ - 1) / TJ * TJ;
+  nsplit = (ctx + chunk - 1) / chunk;
   if (split >= nsplit) return;  // uniform per workgroup; not counted below
-  const int chunk = (ctx + nsplit - 1) / nsplit;
   const int j0 = split * chunk;
   const int j1 = min(ctx, j0 + chunk);
 
@@ -698,7 +705,7 @@ __global__ void __launch_bounds__(kThreads) k_attn_decode(AttnDecodeArgs a) {
 
 template <int HD, int G>
 hipError_t launch(const AttnDecodeArgs& a, int kvt, int nrows, hipStream_t s) {
-  const dim3 grid(a.nsplit_max, a.nkv, nrows);
+  const dim3 grid(a.nkv, a.nsplit_max, nrows);
   switch (kvt) {
     case KV_F32: hipLaunchKernelGGL((k_attn_decode<HD, G, KV_F32>), grid, dim3(kThreads), 0, s, a); break;
     case KV_BF16: hipLaunchKernelGGL((k_attn_decode<HD, G, KV_BF16>), grid, dim3(kThreads), 0, s, a); break;

@@ -95,7 +95,8 @@ struct Layer {
 // take one split each and skip the partial round trip), at most 64 by that
 // rule (each split also keeps at least 64 rows, so short caches get fewer),
 // and never fewer than the longest cache needs (a split holds at most
-// 4096 / group rows).
+// 4096 / group rows).  The kernel then rounds a split's range up to whole
+// K/V tiles, which can only lower the count.
 int decode_splits_needed(int max_cap, int group) { return (max_cap + 4096 / group - 1) / (4096 / group); }
 int decode_nsplit_max(int nkv, int nrows, int needed) {
   const int units = nkv * nrows;
