@@ -257,21 +257,27 @@ int gemm_splits(int M, int N, int K, size_t part_bytes) {
   return sp;
 }
 
+hipError_t gemm_reduce(const double* part, int splits, int M, int N, float* out, int64_t ldc, int epi, hipStream_t s) {
+  const int NO = epi == EPI_SWIGLU ? N / 2 : N;
+  const dim3 rg((unsigned)(((int64_t)M * NO + 255) / 256));
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(k_gemm_reduce<EPI_STORE>, rg, dim3(256), 0, s, part, splits, M, N, out, ldc); break;
+    case EPI_RESIDUAL: hipLaunchKernelGGL(k_gemm_reduce<EPI_RESIDUAL>, rg, dim3(256), 0, s, part, splits, M, N, out, ldc); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_reduce<EPI_SWIGLU>, rg, dim3(256), 0, s, part, splits, M, N, out, ldc); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const int sp = a.part ? gemm_splits(a.M, a.N, a.K, a.part_bytes) : 1;
   if (sp > 1) {
     const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, sp);
     hipLaunchKernelGGL(k_gemm_q8<EPI_PARTIAL>, grid, dim3(256), 0, s, a);
-    const int NO = epi == EPI_SWIGLU ? a.N / 2 : a.N;
-    const dim3 rg((unsigned)(((int64_t)a.M * NO + 255) / 256));
-    switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL(k_gemm_reduce<EPI_STORE>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
-      case EPI_RESIDUAL: hipLaunchKernelGGL(k_gemm_reduce<EPI_RESIDUAL>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_reduce<EPI_SWIGLU>, rg, dim3(256), 0, s, a.part, sp, a.M, a.N, a.out, a.ldc); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return gemm_reduce(a.part, sp, a.M, a.N, a.out, a.ldc, epi, s);
   }
   const dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
   switch (epi) {

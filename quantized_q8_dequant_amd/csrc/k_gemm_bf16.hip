@@ -14,6 +14,12 @@
 // and then stored, added to the residual stream, paired into SwiGLU outputs
 // (the gate/up plane interleaves 32 gate rows with the 32 matching up rows),
 // or reduced to the greedy argmax.
+//
+// Split K: while the tile grid is under two workgroups per CU (the batched
+// decode step's 64-row products have 16 to 96 tiles), K is cut into slices of
+// whole slabs over grid.z; each slice writes its f64 tile sums to a scratch
+// plane and k_gemm_reduce adds the planes in slice order, rounds once to f32
+// and applies the epilogue.
 #include "kernels.h"
 #include "qdevice.h"
 
@@ -26,6 +32,7 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int kBK = 32;
 constexpr int kLds = kBK + 4;  // f32 words per staged row
 constexpr int kBN = 64;
+constexpr int kEpiPartial = 7;  // f64 sums of one K slice to the scratch plane
 
 struct Best {
   float v;
@@ -102,15 +109,18 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmBf16Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
 
+  // this workgroup's slabs [kt0, kt1): slice blockIdx.z of gridDim.z (the
+  // slice count divides the slab count)
   const int nk = K / kBK;
-  load(0);
+  const int kt0 = (int)blockIdx.z * nk / (int)gridDim.z, kt1 = ((int)blockIdx.z + 1) * nk / (int)gridDim.z;
+  load(kt0);
   store(smem);
   __syncthreads();
   const int fr = lane % 16, fk = lane / 16;
-  for (int kt = 0; kt < nk; ++kt) {
-    const float* sa = smem + (kt & 1) * STAGE;
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const float* sa = smem + ((kt - kt0) & 1) * STAGE;
     const float* sb = sa + BM * kLds;
-    if (kt + 1 < nk) load(kt + 1);
+    if (kt + 1 < kt1) load(kt + 1);
 #pragma unroll
     for (int kk = 0; kk < kBK; kk += 4) {
       double af[FM], bf[FN];
@@ -123,8 +133,24 @@ __global__ void __launch_bounds__(256) k_gemm_bf16(GemmBf16Args a) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(smem + ((kt + 1) & 1) * STAGE);
+    if (kt + 1 < kt1) store(smem + ((kt + 1 - kt0) & 1) * STAGE);
     __syncthreads();
+  }
+
+  if constexpr (EPI == kEpiPartial) {
+    // the slice's f64 sums, unrounded: block (i, j) item t is
+    // C[wm0 + 16i + 4t + lane/16][wn0 + 16j + lane%16]
+    double* pp = a.part + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t m = m0 + wm0 + 16 * i + 4 * t + fk, n = n0 + wn0 + 16 * j + fr;
+          if (m < M && n < N) pp[m * N + n] = acc[i][j][t];
+        }
+    return;
   }
 
   // round once to f32 into the LDS tile: block (i, j) item t holds
@@ -227,8 +253,28 @@ __global__ void __launch_bounds__(256) k_rows_norm(const float* __restrict__ x, 
   }
 }
 
+// K slices for a grid of `tiles` workgroups (the rule of the Q8_0 GEMM):
+// doubled while the grid is under two workgroups per CU, the slices stay
+// whole slabs and the planes fit the scratch; never for the argmax epilogue.
+int bf16_splits(const GemmBf16Args& a, int bm, int epi) {
+  if (!a.part || epi == EPI_ARGMAX) return 1;
+  const int tiles = ((a.N + kBN - 1) / kBN) * ((a.M + bm - 1) / bm);
+  const int nk = a.K / kBK;
+  int sp = 1;
+  while (tiles * sp < 512 && nk % (2 * sp) == 0 && (size_t)2 * sp * a.M * a.N * 8 <= a.part_bytes) sp *= 2;
+  return sp;
+}
+
 template <int BM>
 hipError_t launch_bm(const GemmBf16Args& a, int epi, hipStream_t s) {
+  const int sp = bf16_splits(a, BM, epi);
+  if (sp > 1) {
+    const dim3 grid((unsigned)((a.N + kBN - 1) / kBN), (unsigned)((a.M + BM - 1) / BM), (unsigned)sp);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, kEpiPartial>), grid, dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return q8k::gemm_reduce(a.part, sp, a.M, a.N, a.out, a.ldc, epi, s);
+  }
   const dim3 grid((unsigned)((a.N + kBN - 1) / kBN), (unsigned)((a.M + BM - 1) / BM));
 #define BF_CASE(E)                                                                 \
   if (epi == E) {                                                                  \

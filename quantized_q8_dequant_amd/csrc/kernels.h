@@ -193,10 +193,16 @@ struct GemmBf16Args {
   int32_t* len_ptr;
   const int32_t* len_seq;
   int32_t len_add;
+  // split-K scratch (f64 planes [splits][M][N]) or null for one pass
+  double* part;
+  size_t part_bytes;
 };
 
 namespace q8k {
 hipError_t gemm(const GemmArgs& a, int epi, hipStream_t s);
+// out (STORE, RESIDUAL, SWIGLU epilogue) from `splits` f64 planes [splits][M][N]
+// added in slice order and rounded once (see k_gemm.hip).
+hipError_t gemm_reduce(const double* part, int splits, int M, int N, float* out, int64_t ldc, int epi, hipStream_t s);
 // Small-M form (see k_gemm_skinny.hip): M <= kSkinnyMaxRows, K % 128 == 0;
 // STORE, RESIDUAL, SWIGLU; no scratch.
 constexpr int kSkinnyMaxRows = 64;

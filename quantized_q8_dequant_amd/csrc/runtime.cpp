@@ -363,6 +363,15 @@ GemmBf16Args bf16_args(const QPlane& p, const float* x, int64_t lda, int M, floa
   return g;
 }
 
+// ... with the model's scratch, for split-K on grids under two workgroups per CU
+GemmBf16Args bf16_args_m(const qwen3_model* m, const QPlane& p, const float* x, int64_t lda, int M, float* out,
+                         int64_t ldc) {
+  GemmBf16Args g = bf16_args(p, x, lda, M, out, ldc);
+  g.part = m->gemm_part;
+  g.part_bytes = m->gemm_part_bytes;
+  return g;
+}
+
 int copy_f32(float* dst, const void* src, int64_t n, hipStream_t s) {
   if (!src) return fail(QWEN3_E_INVALID_ARGUMENT, "a norm weight pointer is null");
   HIP_TRY(hipMemcpyAsync(dst, src, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
@@ -442,7 +451,7 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
     const int64_t H = m->H;
     if (kind == 5) {
       HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, m->out_norm, eps, m->xn, H, s));
-      GemmBf16Args g = bf16_args(m->emb, m->xn, H, nrows, nullptr, 0);
+      GemmBf16Args g = bf16_args_m(m, m->emb, m->xn, H, nrows, nullptr, 0);
       g.logits = d_logits;
       g.best_key = m->am_key;
       g.counter = m->am_cnt;
@@ -457,17 +466,17 @@ int launch_decode_kernel(qwen3_model* m, int kind, int l, int nrows, const int32
     switch (kind) {
       case 0:
         HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, ly.attn_norm, eps, m->xn, H, s));
-        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.qkv, m->xn, H, nrows, m->qkv, m->nqkv), EPI_STORE, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.qkv, m->xn, H, nrows, m->qkv, m->nqkv), EPI_STORE, s));
         break;
       case 2:
-        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.o, m->attn, m->qw, nrows, m->x, H), EPI_RESIDUAL, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.o, m->attn, m->qw, nrows, m->x, H), EPI_RESIDUAL, s));
         break;
       case 3:
         HIP_TRY(q8k::rows_norm(m->x, H, nrows, m->H, ly.ffn_norm, eps, m->xn, H, s));
-        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.gateup, m->xn, H, nrows, m->h, m->F), EPI_SWIGLU, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.gateup, m->xn, H, nrows, m->h, m->F), EPI_SWIGLU, s));
         break;
       case 4:
-        HIP_TRY(q8k::gemm_bf16(bf16_args(ly.down, m->h, m->F, nrows, m->x, H), EPI_RESIDUAL, s));
+        HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.down, m->h, m->F, nrows, m->x, H), EPI_RESIDUAL, s));
         break;
       default:
         return fail(QWEN3_E_INVALID_ARGUMENT, "bad kernel kind");
@@ -596,7 +605,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     // attention input: RMSNorm + quantise, fused QKV GEMM
     if (m->wbf16) {
       HIP_TRY(q8k::rows_norm(m->x, m->H, T, m->H, ly.attn_norm, eps, m->xn, m->H, s));
-      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.qkv, m->xn, m->H, T, m->qkv, m->nqkv), EPI_STORE, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.qkv, m->xn, m->H, T, m->qkv, m->nqkv), EPI_STORE, s));
     } else {
       HIP_TRY(q8k::rows_quant(m->x, T, m->H, ly.attn_norm, eps, m->qa, m->da, nullptr, s, small));
       g.qs = ly.qkv.qs, g.sc = ly.qkv.sc, g.N = (int)ly.qkv.rows, g.K = m->H, g.out = m->qkv, g.ldc = m->nqkv;
@@ -637,10 +646,10 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     HIP_TRY(q8k::attn_prefill(ap, m->hd, m->G, m->kvt, s));
     if (m->wbf16) {
       const int64_t H = m->H;
-      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.o, m->attn, m->qw, T, m->x, H), EPI_RESIDUAL, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.o, m->attn, m->qw, T, m->x, H), EPI_RESIDUAL, s));
       HIP_TRY(q8k::rows_norm(m->x, H, T, m->H, ly.ffn_norm, eps, m->xn, H, s));
-      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.gateup, m->xn, H, T, m->h, m->F), EPI_SWIGLU, s));
-      HIP_TRY(q8k::gemm_bf16(bf16_args(ly.down, m->h, m->F, T, m->x, H), EPI_RESIDUAL, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.gateup, m->xn, H, T, m->h, m->F), EPI_SWIGLU, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, ly.down, m->h, m->F, T, m->x, H), EPI_RESIDUAL, s));
       continue;
     }
     // o_proj + residual
@@ -660,7 +669,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
     const int64_t H = m->H;
     if (m->wbf16) {
       HIP_TRY(q8k::rows_norm(m->x, H, T, m->H, m->out_norm, eps, m->xn, H, s));
-      HIP_TRY(q8k::gemm_bf16(bf16_args(m->emb, m->xn, H, T, d_logits, m->V), EPI_STORE, s));
+      HIP_TRY(q8k::gemm_bf16(bf16_args_m(m, m->emb, m->xn, H, T, d_logits, m->V), EPI_STORE, s));
     } else {
       const bool head_small = skinny_rows(m, T);
       HIP_TRY(q8k::rows_quant(m->x, T, m->H, m->out_norm, eps, m->qa, m->da, nullptr, s, head_small));
@@ -674,7 +683,7 @@ int enqueue_prefill_chunk(qwen3_model* m, int seq, int pos0, int T, bool last, f
   } else if (last && (d_logits || d_argmax) && m->wbf16) {
     const int64_t H = m->H;
     HIP_TRY(q8k::rows_norm(m->x + (int64_t)(T - 1) * H, H, 1, m->H, m->out_norm, eps, m->xn, H, s));
-    GemmBf16Args g = bf16_args(m->emb, m->xn, H, 1, nullptr, 0);
+    GemmBf16Args g = bf16_args_m(m, m->emb, m->xn, H, 1, nullptr, 0);
     g.logits = d_logits;
     g.best_key = m->am_key;
     g.counter = m->am_cnt;
