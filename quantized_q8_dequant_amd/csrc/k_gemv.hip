@@ -8,8 +8,9 @@
 // loads: LPR lanes cover one row and each lane owns whole 32-byte blocks
 // b = lane + j*LPR (two 16-byte loads; the pair of load instructions covers
 // the row's bytes contiguously), so S is formed in one lane by 8 x v_dot4.
-// Weight loads are issued before the prologue (weights do not depend on the
-// activation); the prologue quantises the activation into LDS.
+// The activation is loaded first and the first two tiles' weights next
+// (weights do not depend on the activation), so the prologue, which
+// quantises the activation into LDS, waits for the activation alone.
 //
 // Prologues: RMSNorm + quantise (the norm of "A transformer from scratch",
 // section 12.3.2) or quantise only.  Epilogues: store, residual add (section
@@ -24,32 +25,37 @@ using namespace q8;
 namespace {
 
 
-// Quantise src [K] (optionally RMSNorm'd with w) into LDS: s_qa [K] bytes,
-// s_da [K/32] f32 (the value of f16(d)).
-template <bool NORM, int NT>
-QDEV void prologue_quant(const float* __restrict__ src, const float* __restrict__ w, float eps, int K,
-                         int8_t* s_qa, float* s_da, double* s_red) {
+// Quantise the activation [K] (optionally RMSNorm'd with w) into LDS: s_qa
+// [K] bytes, s_da [K/32] f32 (the value of f16(d)).  The activation and the
+// norm weights arrive in registers: chunk i of thread t holds elements
+// 4 * (t + i * NT) .. + 3 (XN chunks; those past K are unused).
+template <bool NORM, int NT, int XN>
+QDEV void prologue_quant(const float4 (&xv)[XN], const float4 (&wv)[XN], float eps, int K, int8_t* s_qa,
+                              float* s_da, double* s_red) {
   double r = 1.0;
   if (NORM) {
     double ss = 0.0;
-    for (int c = threadIdx.x * 4; c < K; c += NT * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + c);
-      ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+#pragma unroll
+    for (int i = 0; i < XN; ++i) {
+      const int c = 4 * ((int)threadIdx.x + i * NT);
+      if (c < K) {
+        const float4 v = xv[i];
+        ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+      }
     }
     ss = block_sum_d<NT>(ss, s_red);
     r = rms_scale(ss, K, eps);
   }
-  for (int base = 0; base < K; base += NT * 4) {
-    const int c = base + threadIdx.x * 4;
+#pragma unroll
+  for (int i = 0; i < XN; ++i) {
+    const int c = 4 * ((int)threadIdx.x + i * NT);
     const bool live = c < K;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (live) {
-      const float4 t = *reinterpret_cast<const float4*>(src + c);
-      v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+      v[0] = xv[i].x, v[1] = xv[i].y, v[2] = xv[i].z, v[3] = xv[i].w;
       if (NORM) {
-        const float4 w4 = *reinterpret_cast<const float4*>(w + c);
-        v[0] = rms_apply(v[0], r, w4.x), v[1] = rms_apply(v[1], r, w4.y);
-        v[2] = rms_apply(v[2], r, w4.z), v[3] = rms_apply(v[3], r, w4.w);
+        v[0] = rms_apply(v[0], r, wv[i].x), v[1] = rms_apply(v[1], r, wv[i].y);
+        v[2] = rms_apply(v[2], r, wv[i].z), v[3] = rms_apply(v[3], r, wv[i].w);
       }
     }
     float d;
@@ -196,28 +202,43 @@ __global__ void __launch_bounds__(64 * WAVES) k_gemv(GemvArgs a) {
   };
 
   // grid-stride over tiles: the activation is quantised once per workgroup
-  // (weights of the first tile already in flight), later tiles' weights are
-  // loaded one tile ahead
+  // (weights of the first two tiles already in flight), later tiles' weights
+  // are loaded one tile ahead
   // (the prefetch is issued unconditionally -- past the last tile it
-  // re-reads the tile just loaded, a cache hit -- so that the compiler keeps
+  // re-reads a tile already loaded, a cache hit -- so that the compiler keeps
   // it in flight while it waits for the older tile)
   int tile = blockIdx.x;
   if (tile < a.ntiles) {
     WTile A, B;
+    // the activation first, then the first two tiles' weights: loads
+    // complete in order, so the prologue waits for the activation alone
+    // while both tiles are in flight
+    constexpr int XN = (K + 4 * kThreads - 1) / (4 * kThreads);
+    float4 xv[XN], wv[XN];
+#pragma unroll
+    for (int i = 0; i < XN; ++i) {
+      const int c = 4 * ((int)threadIdx.x + i * kThreads);
+      const int cc = c < K ? c : 0;
+      xv[i] = *reinterpret_cast<const float4*>(src + cc);
+      wv[i] = NORM ? *reinterpret_cast<const float4*>(a.norm_w + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     load(A, tile);
-    prologue_quant<NORM, kThreads>(src, a.norm_w, a.eps, K, s_qa, s_da, s_red);
-    if (tile + (int)gridDim.x >= a.ntiles) {
+    if (tile + (int)gridDim.x >= a.ntiles) {  // one tile
+      prologue_quant<NORM, kThreads, XN>(xv, wv, a.eps, K, s_qa, s_da, s_red);
       compute(A, tile);
     } else {
+      load(B, tile + (int)gridDim.x);
+      prologue_quant<NORM, kThreads, XN>(xv, wv, a.eps, K, s_qa, s_da, s_red);
+      // A holds tile, B tile + G: the next tile's loads are in flight while
+      // one is reduced
       for (;;) {
-        const int t1 = tile + gridDim.x;
-        load(B, t1 < a.ntiles ? t1 : tile);
+        const int t1 = tile + gridDim.x, t2 = t1 + gridDim.x, t3 = t2 + gridDim.x;
         compute(A, tile);
         if (t1 >= a.ntiles) break;
-        const int t2 = t1 + gridDim.x;
         load(A, t2 < a.ntiles ? t2 : t1);
         compute(B, t1);
         if (t2 >= a.ntiles) break;
+        load(B, t3 < a.ntiles ? t3 : t2);
         tile = t2;
       }
     }
